@@ -1,0 +1,256 @@
+"""The operations of one tensor-parallel rank's MLP share, in float64.
+
+Sources (page title, section):
+  [TP]   "Tensor parallelism" (algorithm page): "How it works" (the MLP
+         Y = GeLU(X.A).B with A split by columns and B by rows; one sum of
+         partials in forward, one in backward), "Code" (the Megatron MLP
+         checker: ReLU, its derivative taken as 1 only where z > 0, and the
+         backward of the loss 1/2 ||Y||^2 so that dY = Y).
+  [TSP]  "Tensor and sequence parallelism": "Derive column-parallel linear
+         algebra" (Y_t = X W_t; dW_t = X^T dY_t; dX_t = dY_t W_t^T is a full
+         [M,K] partial), "Derive row-parallel linear algebra" (partial
+         Y_t = X_t W_t of shape [M,N]; Y = sum_t Y_t; dW_t = X_t^T dY;
+         dX_t = dY W_t^T), "Pair adjacent transformer projections".
+  [CG]   "Collective GEMMs in Tensor Sequence Parallelism": "Collective GEMMs
+         (CGEMM)" (sequence chunks give distinct output rows, no accumulation;
+         the reduce-scatter delivers each rank its token range of the summed
+         partial), "Supported quantization recipes" (FP8 current scaling).
+
+Matrices are row-major [rows, cols] as the pages write them: X[M,K], W[K,N].
+Every function takes float64 arrays holding exactly the values the GPU
+receives (decoded from bf16 / e4m3fn by oracle.formats).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+from . import formats
+
+ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
+_SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+_GELU_TANH_C = 0.044715
+
+
+# ---------------------------------------------------------------- activations
+def relu(z):
+    """[TP] "Code": max(z, 0)."""
+    return np.maximum(z, 0.0)
+
+
+def relu_grad(z):
+    """[TP] "Code": the derivative is taken as 1 where z > 0 and 0 elsewhere
+    (including z == 0)."""
+    return (z > 0.0).astype(np.float64)
+
+
+def gelu_erf(z):
+    """GeLU, exact form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2))."""
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def gelu_erf_grad(z):
+    """d/dz [z Phi(z)] = Phi(z) + z phi(z)."""
+    cdf = 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    return cdf + z * pdf
+
+
+def gelu_tanh(z):
+    """GeLU, tanh approximation (Hendrycks & Gimpel):
+    0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
+    u = _SQRT_2_OVER_PI * (z + _GELU_TANH_C * z ** 3)
+    return 0.5 * z * (1.0 + np.tanh(u))
+
+
+def gelu_tanh_grad(z):
+    u = _SQRT_2_OVER_PI * (z + _GELU_TANH_C * z ** 3)
+    t = np.tanh(u)
+    du = _SQRT_2_OVER_PI * (1.0 + 3.0 * _GELU_TANH_C * z * z)
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * du
+
+
+def act_fwd(z, act: int):
+    if act == ACT_NONE:
+        return np.array(z, dtype=np.float64, copy=True)
+    if act == ACT_RELU:
+        return relu(z)
+    if act == ACT_GELU_ERF:
+        return gelu_erf(z)
+    if act == ACT_GELU_TANH:
+        return gelu_tanh(z)
+    raise ValueError(f"unknown activation {act}")
+
+
+def act_grad(z, act: int):
+    if act == ACT_NONE:
+        return np.ones_like(z, dtype=np.float64)
+    if act == ACT_RELU:
+        return relu_grad(z)
+    if act == ACT_GELU_ERF:
+        return gelu_erf_grad(z)
+    if act == ACT_GELU_TANH:
+        return gelu_tanh_grad(z)
+    raise ValueError(f"unknown activation {act}")
+
+
+# ---------------------------------------------------------------------- GEMM
+def gemm(a, b):
+    """C = A.B in float64 (library matmul as the step)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.ndim == 2 and b.ndim == 2 and a.shape[1] == b.shape[0], (a.shape, b.shape)
+    return a @ b
+
+
+def op(m, trans: bool):
+    """op(M) = M or M^T (a transpose by index, as the page's transpose())."""
+    return np.asarray(m, dtype=np.float64).T if trans else np.asarray(m, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ sharding
+def col_block(w, T: int, t: int):
+    """Columns [t*N/T, (t+1)*N/T) of W[K,N] -- the column-parallel shard
+    ([TSP] "Derive column-parallel linear algebra"; [TP] "Code" col_block)."""
+    n = w.shape[1]
+    assert n % T == 0
+    s = n // T
+    return w[:, t * s:(t + 1) * s]
+
+
+def row_block(w, T: int, t: int):
+    """Rows [t*K/T, (t+1)*K/T) of W[K,N] -- the row-parallel shard
+    ([TSP] "Derive row-parallel linear algebra")."""
+    k = w.shape[0]
+    assert k % T == 0
+    s = k // T
+    return w[t * s:(t + 1) * s, :]
+
+
+# ---------------------------------------------------------- seq_chunk_gemm
+def seq_chunk_gemm(a, b, *, trans_a=False, trans_b=False, a_scale=1.0, b_scale=1.0,
+                   act=ACT_NONE, dact_z=None, chunk_rows=None, chunk_order=None):
+    """Y = act(op(A).op(B) * sa * sb), or, with dact_z given, the backward
+    epilogue Y = (op(A).op(B) * sa * sb) * act'(Z).
+
+    Returns (Y, Zpre) where Zpre is the pre-activation product.
+    Chunking: the rows of Y (tokens) arrive as chunks in `chunk_order`; each
+    chunk produces distinct output rows with no accumulation ([CG]
+    "Collective GEMMs (CGEMM)", all-gather + GEMM), so the result is the
+    unchunked product whatever the order; the arguments are only checked."""
+    A = op(a, trans_a)
+    B = op(b, trans_b)
+    z = gemm(A, B) * (float(a_scale) * float(b_scale))
+    if chunk_order is not None:
+        assert chunk_rows is not None and z.shape[0] % chunk_rows == 0
+        assert sorted(chunk_order) == list(range(z.shape[0] // chunk_rows))
+    if dact_z is not None:
+        return z * act_grad(np.asarray(dact_z, dtype=np.float64), act), z
+    return act_fwd(z, act), z
+
+
+# -------------------------------------------------------------- tp_mlp_fwd
+def tp_mlp_fwd(x, w_up_t, w_down_t, act=ACT_GELU_ERF):
+    """One rank's MLP share in exact arithmetic ([TP] "How it works"; [TSP]
+    "Pair adjacent transformer projections"):
+        Z_t = X . W_up,t        (column-parallel, [M, F/T])
+        H_t = act(Z_t)          (local activation)
+        P_t = H_t . W_down,t    (row-parallel partial, [M, D])
+    """
+    z = gemm(x, w_up_t)
+    h = act_fwd(z, act)
+    p = gemm(h, w_down_t)
+    return dict(Z=z, H=h, P=p)
+
+
+def tp_mlp_fwd_fp8(xq, sx, wq_up, s_up, wq_down, s_down, act=ACT_GELU_ERF):
+    """fp8 current-scaling variant ([CG] "Supported quantization recipes",
+    FP8 with current scaling), with the rounding points of the GPU path:
+        Z   = (Xq . Wq_up) * sX * sWup            (operands decoded exactly)
+        H_b = bf16(act(Z))                        (stored intermediate)
+        amax = max |H_b|
+        inv = fp32(448 / amax)   (1 when amax == 0)
+        Hq  = e4m3(fp32(H_b * inv))               (nearest even, satfinite)
+        sH  = fp32(amax / 448)   (1 when amax == 0)
+        P   = (Hq . Wq_down) * sH * sWdown
+    Inputs are decoded values (float64) of the e4m3 codes and fp32 scales."""
+    z = gemm(xq, wq_up) * (float(np.float32(sx)) * float(np.float32(s_up)))
+    h = act_fwd(z, act)
+    hb = formats.round_bf16(h)
+    amax = float(np.max(np.abs(hb))) if hb.size else 0.0
+    if amax == 0.0:
+        inv32 = np.float32(1.0)
+        sh32 = np.float32(1.0)
+    else:
+        inv32 = np.float32(np.float32(448.0) / np.float32(amax))
+        sh32 = np.float32(np.float32(amax) / np.float32(448.0))
+    prod32 = (hb.astype(np.float32) * inv32).astype(np.float32)
+    hq_codes = formats.e4m3_encode(prod32.astype(np.float64))
+    hq = formats.e4m3_to_f64(hq_codes)
+    p = gemm(hq, wq_down) * (float(sh32) * float(np.float32(s_down)))
+    return dict(Z=z, H=h, Hb=hb, amax=amax, inv=float(inv32), sH=float(sh32),
+                Hq_codes=hq_codes, P=p)
+
+
+# ------------------------------------------------- partial_reduce_seqshard
+def partial_reduce_seqshard(partials, rank: int):
+    """Local arithmetic of the reduce-scatter that follows a row-parallel GEMM
+    ([CG] "Collective GEMMs (CGEMM)", GEMM + reduce-scatter; [TSP] "Derive
+    row-parallel linear algebra"): rank r receives rows
+    [r*M/T, (r+1)*M/T) of sum_t P_t.  partials: [T, M, D]."""
+    p = np.asarray(partials, dtype=np.float64)
+    T, M, _ = p.shape
+    assert M % T == 0
+    s = M // T
+    return p[:, rank * s:(rank + 1) * s, :].sum(axis=0)
+
+
+# -------------------------------------------------------------- tp_mlp_bwd
+def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF):
+    """Backward of one rank's MLP share ([TSP] both derivations; [TP] "Code"):
+        dH_t      = dY . W_down,t^T        (row-parallel input gradient shard)
+        dZ_t      = dH_t * act'(Z_t)
+        dW_down,t = H_t^T . dY             (row-parallel weight gradient)
+        dW_up,t   = X^T . dZ_t             (column-parallel weight gradient)
+        dX_t      = dZ_t . W_up,t^T        (full [M,D] partial, summed across
+                                            ranks by all-reduce / reduce-scatter)
+    Z and H are the saved forward values (inputs here)."""
+    dh = gemm(dy, np.asarray(w_down_t, dtype=np.float64).T)
+    dz = dh * act_grad(np.asarray(z, dtype=np.float64), act)
+    dw_down = gemm(np.asarray(h, dtype=np.float64).T, dy)
+    dw_up = gemm(np.asarray(x, dtype=np.float64).T, dz)
+    dx = gemm(dz, np.asarray(w_up_t, dtype=np.float64).T)
+    return dict(dH=dh, dZ=dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
+
+
+def linear_bwd(x, w, dy):
+    """Backward of Y = X W: dW = X^T dY, dX = dY W^T ([TSP] derivations)."""
+    return dict(dW=gemm(np.asarray(x, dtype=np.float64).T, dy),
+                dX=gemm(dy, np.asarray(w, dtype=np.float64).T))
+
+
+# ------------------------------------------------------- unsharded reference
+def mlp_unsharded(x, a, b, act=ACT_RELU):
+    """The unsharded layer Y = act(X A) B that the sharded ranks must match
+    ([TP] "Overview" / "Code")."""
+    pre = gemm(x, a)
+    return dict(pre=pre, Y=gemm(act_fwd(pre, act), b))
+
+
+def mlp_unsharded_bwd(x, a, b, pre, dy, act=ACT_RELU):
+    dh = gemm(dy, np.asarray(b, dtype=np.float64).T) * act_grad(pre, act)
+    return dict(dA=gemm(np.asarray(x, dtype=np.float64).T, dh),
+                dB=gemm(np.asarray(act_fwd(pre, act)).T, dy),
+                dX=gemm(dh, np.asarray(a, dtype=np.float64).T))
+
+
+# ---------------------------------------------------------------- comparison
+def normalized_error(gpu, ref):
+    """max |g - r| / (1 + |r|), the parity measure of this path."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if g.size == 0:
+        return 0.0
+    return float(np.max(np.abs(g - r) / (1.0 + np.abs(r))))

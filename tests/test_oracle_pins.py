@@ -1,0 +1,304 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle:
+bit definitions, library casts, brute force, closed forms, finite
+differences, the pages' own invariants and printed numbers."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute, formats, ops, schedule, shapes
+import synthetic_inputs as si
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+
+
+# ------------------------------------------------------------------ formats
+def test_e4m3_table_from_definition():
+    t = formats.E4M3_TABLE
+    assert t[0x38] == 1.0 and t[0x40] == 2.0 and t[0x44] == 3.0 and t[0x48] == 4.0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.isfinite(t).sum() == 254
+
+
+def test_e4m3_matches_torch_cast():
+    # independent implementation: PyTorch's float8_e4m3fn cast
+    g = np.random.default_rng(5)
+    x = np.concatenate([g.standard_normal(200000) * s for s in (1e-3, 0.1, 1, 30, 300)]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ours = formats.e4m3_encode(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3_roundtrip_ties_and_saturation():
+    codes = np.array([c for c in range(256) if not math.isnan(formats.E4M3_TABLE[c])], dtype=np.uint8)
+    vals = formats.e4m3_to_f64(codes)
+    assert np.array_equal(formats.e4m3_encode(vals), codes)
+    pos = formats.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    enc = formats.e4m3_encode(mids).astype(int)
+    lo = np.arange(0x7E)
+    expect = np.where(lo % 2 == 0, lo, lo + 1)     # tie -> even code
+    assert np.array_equal(enc, expect)
+    assert formats.e4m3_encode(np.array([1000.0, 449.0, -1e9]))[0] == 0x7E
+    assert formats.e4m3_encode(np.array([-1e9]))[0] == 0xFE
+    assert formats.e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_bf16_matches_torch_and_ties():
+    g = np.random.default_rng(7)
+    bits = g.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    # structured mantissa tails around the rounding point, every exponent
+    exps = np.arange(0, 255, dtype=np.uint32) << np.uint32(23)
+    tails = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x18000, 0x10000, 0x7F8000], dtype=np.uint32)
+    hi = np.array([0, 0x10000, 0x7E0000, 0x7F0000], dtype=np.uint32)
+    struct = (exps[:, None, None] | hi[None, :, None] | tails[None, None, :]).ravel()
+    bits = np.concatenate([bits, struct, struct | np.uint32(0x80000000)])
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    ours = formats.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    # explicit ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1.0)
+    assert formats.f32_to_bf16_bits(np.array([1.0 + 2 ** -8], np.float32))[0] == 0x3F80
+    assert formats.f32_to_bf16_bits(np.array([1.0 + 3 * 2 ** -8], np.float32))[0] == 0x3F82
+
+
+# -------------------------------------------------------------- activations
+@pytest.mark.parametrize("act", [ops.ACT_RELU, ops.ACT_GELU_ERF, ops.ACT_GELU_TANH, ops.ACT_NONE])
+def test_activation_derivatives_by_central_differences(act):
+    z = np.linspace(-6, 6, 2401) + 1e-3      # avoid the ReLU kink
+    h = 1e-6
+    fd = (ops.act_fwd(z + h, act) - ops.act_fwd(z - h, act)) / (2 * h)
+    assert np.max(np.abs(fd - ops.act_grad(z, act))) < 1e-7
+
+
+def test_activation_closed_forms():
+    assert ops.gelu_erf(np.array([0.0]))[0] == 0.0
+    assert ops.gelu_erf_grad(np.array([0.0]))[0] == 0.5
+    assert ops.gelu_tanh_grad(np.array([0.0]))[0] == 0.5
+    assert ops.relu_grad(np.array([0.0]))[0] == 0.0            # page: 1 only where z > 0
+    big = np.array([10.0, -10.0])
+    assert np.allclose(ops.gelu_erf(big), [10.0, 0.0], atol=1e-12)
+    z = np.linspace(-8, 8, 100001)
+    diff = np.max(np.abs(ops.gelu_erf(z) - ops.gelu_tanh(z)))
+    assert 1e-4 < diff < 5e-4
+    # Phi(1) from the standard normal table
+    assert abs(ops.gelu_erf(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+
+
+# ------------------------------------------------------------- brute force
+@pytest.mark.parametrize("m,k,n", [(8, 32, 32), (37, 19, 23), (1, 1, 1), (5, 64, 3)])
+def test_gemm_vs_brute(m, k, n):
+    g = np.random.default_rng(m * 1000 + k)
+    a = g.standard_normal((m, k))
+    b = g.standard_normal((k, n))
+    ref = np.array(brute.matmul(brute.to_lists(a), brute.to_lists(b)))
+    assert np.max(np.abs(ops.gemm(a, b) - ref)) <= 1e-12 * (1 + np.max(np.abs(ref)))
+    # transposed operands by index
+    y, _ = ops.seq_chunk_gemm(np.ascontiguousarray(a.T), np.ascontiguousarray(b.T), trans_a=True, trans_b=True)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * (1 + np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_mlp_fwd_bwd_vs_brute(act):
+    g = np.random.default_rng(11)
+    M, D, Ft = 6, 10, 7
+    x, wu, wd = g.standard_normal((M, D)), g.standard_normal((D, Ft)) * 0.3, g.standard_normal((Ft, D)) * 0.3
+    dy = g.standard_normal((M, D))
+    a = ops.ACT_RELU if act == "relu" else ops.ACT_GELU_ERF
+    f = ops.tp_mlp_fwd(x, wu, wd, a)
+    z, h, p = brute.mlp_fwd(brute.to_lists(x), brute.to_lists(wu), brute.to_lists(wd), act)
+    assert np.allclose(f["P"], p, rtol=0, atol=1e-12)
+    b = ops.tp_mlp_bwd(x, wu, wd, f["Z"], f["H"], dy, a)
+    bb = brute.mlp_bwd(brute.to_lists(x), brute.to_lists(wu), brute.to_lists(wd), z, h, brute.to_lists(dy), act)
+    for key in ("dW_down", "dW_up", "dX", "dZ"):
+        assert np.allclose(b[key], bb[key], rtol=0, atol=1e-12), key
+
+
+# ------------------------------------------------------ sharding invariants
+def _rand_or_int(kind, shape, seed):
+    g = np.random.default_rng(seed)
+    return g.integers(-3, 4, size=shape).astype(np.float64) if kind == "int" else g.standard_normal(shape)
+
+
+@pytest.mark.parametrize("kind", ["int", "float"])
+def test_column_and_row_parallel_invariants(kind):
+    M, K, N, T = 16, 24, 32, 4
+    x = _rand_or_int(kind, (M, K), 1)
+    w = _rand_or_int(kind, (K, N), 2)
+    full = ops.gemm(x, w)
+    tol = 0 if kind == "int" else 1e-12
+    # I1 concat_t X W_t = X W
+    cat = np.concatenate([ops.gemm(x, ops.col_block(w, T, t)) for t in range(T)], axis=1)
+    assert np.max(np.abs(cat - full)) <= tol * (1 + np.max(np.abs(full)))
+    # I2 sum_t X_t W_t = X W
+    s = sum(ops.gemm(ops.col_block(x, T, t), ops.row_block(w, T, t)) for t in range(T))
+    assert np.max(np.abs(s - full)) <= tol * (1 + np.max(np.abs(full)))
+    # I8 concat_r reduce(r) = sum_t P_t (all-reduce = reduce-scatter + all-gather)
+    parts = np.stack([_rand_or_int(kind, (M, N), 10 + t) for t in range(T)])
+    cat = np.concatenate([ops.partial_reduce_seqshard(parts, r) for r in range(T)], axis=0)
+    assert np.max(np.abs(cat - parts.sum(axis=0))) <= tol * (1 + np.max(np.abs(parts)))
+    for r in range(T):
+        assert ops.partial_reduce_seqshard(parts, r).shape == (M // T, N)
+
+
+@pytest.mark.parametrize("act", [ops.ACT_RELU, ops.ACT_GELU_ERF])
+def test_sharded_mlp_equals_unsharded(act):
+    # I3-I7 on the page's own Megatron MLP shapes (8, 32, 128, 4)
+    m, d, f, T = 8, 32, 128, 4
+    g = np.random.default_rng(3)
+    x, a, b = g.standard_normal((m, d)), g.standard_normal((d, f)) * 0.2, g.standard_normal((f, d)) * 0.2
+    dy = g.standard_normal((m, d))
+    un = ops.mlp_unsharded(x, a, b, act)
+    unb = ops.mlp_unsharded_bwd(x, a, b, un["pre"], dy, act)
+    P = []
+    dX = np.zeros((m, d))
+    for t in range(T):
+        wu, wd = ops.col_block(a, T, t), ops.row_block(b, T, t)
+        fw = ops.tp_mlp_fwd(x, wu, wd, act)
+        P.append(fw["P"])
+        bw = ops.tp_mlp_bwd(x, wu, wd, fw["Z"], fw["H"], dy, act)
+        assert bw["dW_up"].shape == wu.shape and bw["dW_down"].shape == wd.shape      # I7
+        assert bw["dX"].shape == (m, d)                                              # full partial
+        assert np.allclose(bw["dW_up"], ops.col_block(unb["dA"], T, t), atol=1e-12)  # I4
+        assert np.allclose(bw["dW_down"], ops.row_block(unb["dB"], T, t), atol=1e-12)  # I6
+        dX += bw["dX"]
+    assert np.allclose(sum(P), un["Y"], atol=1e-12)                                  # I3
+    assert np.allclose(dX, unb["dX"], atol=1e-12)                                    # I5
+
+
+@pytest.mark.parametrize("act", [ops.ACT_GELU_ERF, ops.ACT_GELU_TANH, ops.ACT_RELU])
+def test_gradients_by_finite_differences(act):
+    # I10: L = <G, P>; dP = G; gradients must be derivatives of L
+    M, D, Ft = 5, 6, 4
+    g = np.random.default_rng(21)
+    x, wu, wd, G = (g.standard_normal((M, D)), g.standard_normal((D, Ft)) * 0.5,
+                    g.standard_normal((Ft, D)) * 0.5, g.standard_normal((M, D)))
+    if act == ops.ACT_RELU:  # stay away from the kink
+        z = x @ wu
+        assert np.min(np.abs(z)) > 1e-3
+    fw = ops.tp_mlp_fwd(x, wu, wd, act)
+    bw = ops.tp_mlp_bwd(x, wu, wd, fw["Z"], fw["H"], G, act)
+
+    def loss(x_, wu_, wd_):
+        return float(np.sum(G * ops.tp_mlp_fwd(x_, wu_, wd_, act)["P"]))
+
+    eps = 1e-6
+    for name, arr, grad in (("X", x, bw["dX"]), ("Wup", wu, bw["dW_up"]), ("Wdown", wd, bw["dW_down"])):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            args_p = [x, wu, wd]
+            args_m = [x, wu, wd]
+            k = {"X": 0, "Wup": 1, "Wdown": 2}[name]
+            args_p[k], args_m[k] = ap, am
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.max(np.abs(fd - grad)) <= 1e-7 * (1 + np.max(np.abs(grad))), name
+
+
+def test_page3_checker_reproduced():
+    # P1: the page's generator with seeds 1,2,3 and its three asserts
+    c = si.c1_tiny_mlp("page3")
+    m, d, f, T = c["m"], c["d"], c["f"], c["t"]
+    gold = GOLDEN["megatron_mlp_checker"]
+    assert (m, d, f, T) == (gold["m"], gold["d"], gold["f"], gold["t"])
+    x, a, b = (c[k].astype(np.float64) for k in ("x", "a", "b"))
+    assert x[0, 0] == np.float32(0.001) - np.float32(0.5)    # (0*2654435761 + 1) % 1000 = 1
+    un = ops.mlp_unsharded(x, a, b, ops.ACT_RELU)
+    parts, pre, dx_parts = [], [], []
+    for t in range(T):
+        fw = ops.tp_mlp_fwd(x, ops.col_block(a, T, t), ops.row_block(b, T, t), ops.ACT_RELU)
+        parts.append(fw["P"])
+        pre.append(fw["Z"])
+    y = sum(parts)
+    close = lambda u, v: np.all(np.abs(u - v) < gold["rtol"] * (1 + np.abs(v)))
+    assert close(y, un["Y"])
+    dy = y.copy()                              # loss 1/2 ||Y||^2
+    unb = ops.mlp_unsharded_bwd(x, a, b, un["pre"], dy, ops.ACT_RELU)
+    for t in range(T):
+        bw = ops.tp_mlp_bwd(x, ops.col_block(a, T, t), ops.row_block(b, T, t), pre[t],
+                            ops.relu(pre[t]), dy, ops.ACT_RELU)
+        assert close(bw["dW_up"], ops.col_block(unb["dA"], T, t))
+        dx_parts.append(bw["dX"])
+    assert close(sum(dx_parts), unb["dX"])
+
+
+def test_special_cases():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((8, 8))
+    w = g.standard_normal((8, 8))
+    eye = np.eye(8)
+    assert np.array_equal(ops.gemm(eye, w), w)                       # X = I -> Y = W
+    f = ops.tp_mlp_fwd(x, w, eye, ops.ACT_NONE)                      # W_down = I -> P = H
+    assert np.allclose(f["P"], f["H"], atol=1e-14)
+    parts = g.standard_normal((1, 8, 8))
+    assert np.array_equal(ops.partial_reduce_seqshard(parts, 0), parts[0])   # T = 1
+    y, _ = ops.seq_chunk_gemm(x, w, chunk_rows=2, chunk_order=[3, 0, 2, 1])
+    assert np.array_equal(y, ops.gemm(x, w))                         # order-free
+
+
+def test_fp8_mirror_error_bound_and_scale_direction():
+    g = np.random.default_rng(4)
+    M, D, Ft = 16, 64, 32
+    xq, sx = si.to_e4m3_current(g.standard_normal((M, D)).astype(np.float32))
+    wuq, su = si.to_e4m3_current((g.standard_normal((D, Ft)) * 0.02).astype(np.float32))
+    wdq, sd = si.to_e4m3_current((g.standard_normal((Ft, D)) * 0.02).astype(np.float32))
+    X, WU, WD = (formats.e4m3_to_f64(q.numpy()) for q in (xq, wuq, wdq))
+    r = ops.tp_mlp_fwd_fp8(X, sx, WU, su, WD, sd, ops.ACT_GELU_ERF)
+    # the largest |H_b| maps to the largest finite code
+    assert np.max(np.abs(formats.e4m3_to_f64(r["Hq_codes"]))) == 448.0
+    deq = formats.e4m3_to_f64(r["Hq_codes"]) * r["sH"]
+    # e4m3 nearest rounding: half an ulp (2^-4 relative) in the normal range,
+    # half the subnormal spacing (2^-10 * sH) below it
+    assert np.all(np.abs(deq - r["Hb"]) <= 2.0 ** -4 * np.abs(r["Hb"]) * (1 + 1e-6) + 2.0 ** -10 * r["sH"] * 1.001)
+    exact = ops.tp_mlp_fwd(X * sx, WU * su, WD * sd, ops.ACT_GELU_ERF)
+    # the quantised path stays close to the exact layer in the normalised measure
+    assert ops.normalized_error(r["P"], exact["P"]) < 0.06
+    # amax does not depend on order
+    assert r["amax"] == float(np.max(np.abs(r["Hb"][::-1])))
+
+
+# --------------------------------------------- pages' printed numbers (golden)
+def test_fig3_schedule_numbers():
+    gold = GOLDEN["fig3_boundary_units"]
+    n = gold["chunks"]
+    assert schedule.serial(n) == gold["serial"]
+    assert schedule.allgather_gemm(n) == gold["allgather_overlapped"]
+    assert schedule.gemm_reducescatter(n) == gold["reducescatter_overlapped"]
+    # the target is max(compute, comm) per boundary ("Choosing the chunk count")
+    assert schedule.allgather_gemm(16, c=1.0, m=0.5) == 16.0
+
+
+def test_shapes_and_payloads_from_pages():
+    o = GOLDEN["column_parallel_opening_example"]
+    cp = shapes.column_parallel(o["M"], o["K"], o["N"], o["T"])
+    assert list(cp["W_t"]) == o["W_t"] and list(cp["Y_t"]) == o["Y_t"]
+    w = GOLDEN["mlp_pair_worked_example"]
+    up = shapes.column_parallel(w["M"], w["D"], w["F"], w["T"])
+    down = shapes.row_parallel(w["M"], w["F"], w["D"], w["T"])
+    assert list(up["W_t"]) == w["expansion_shard"] and list(up["Y_t"]) == w["intermediate"]
+    assert list(down["W_t"]) == w["contraction_shard"] and list(down["Y_t"]) == w["partial"]
+    pb = shapes.partial_payload_bytes(w["M"], w["D"])
+    assert pb == w["payload_bytes"] and round(pb / 1e6, 1) == w["payload_MB_printed"]
+    assert w["F"] // 8 == w["F_shard_at_T8"]
+    c = GOLDEN["allreduce_cost_example"]
+    ar = 2 * c["b"] * c["s"] * c["h"]
+    assert ar == c["bytes"] and round(ar / 1e6) == c["MB_printed"]
+
+
+def test_chunk_and_range_orders():
+    assert si.ring_chunk_order(4, 4, 0) == [0, 3, 2, 1]
+    assert si.ring_chunk_order(8, 8, 0) == [0, 7, 6, 5, 4, 3, 2, 1]
+    o = si.ring_chunk_order(8, 16, 0)
+    assert o[:4] == [0, 1, 14, 15] and o[-2:] == [2, 3] and sorted(o) == list(range(16))
+    assert si.dest_range_order(8, 0) == [1, 2, 3, 4, 5, 6, 7, 0]
