@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's layer share on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch of a
+Llama3-70B-shaped TP=8 rank (4096 tokens, hidden 8192, bf16):
+
+  forward   QKV projection (column-parallel [8192,1280]), input rows arriving
+            as 8 sequence chunks from a side stream (stand-in for the
+            all-gather); O projection (row-parallel [1024,8192]) -> partial;
+            reduction of 8 partials onto this rank's 512-token slice;
+            MLP (up [8192,3584] chunk-fed + GeLU, down [3584,8192] -> partial);
+            reduction onto the slice.
+  backward  MLP (dY arriving in chunks; dZ, dW_down, dW_up, dX partial);
+            reduction of dX; O (dY arriving in chunks; dA, dW_o);
+            QKV (dW_qkv, dX partial); reduction of dX.
+
+The 8 partials of each reduction are this rank's own (written by the GEMM
+into its slot) plus 7 seeded stand-ins for the peers' contributions.
+
+value = algorithmic GEMM work of the step (12 GEMMs, 2*M*N*K each,
+1907.0 GFLOP) / step time.  Extra lines: the same step with inputs resident
+(no chunk arrival), the 8 x [8192,8192] -> [1024,8192] reduction (GB/s), and
+the Llama3-70B (bf16) / 405B (fp8) shaped MLP forwards.
+
+python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+FP8_PEAK_TFLOPS = 5033.2
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+class Layer:
+    """Device buffers and the step of the C5 workload (one TP=8 rank)."""
+
+    def __init__(self, torch, tpm, si, M=4096, D=8192, F=28672, T=8, rank=0, heads=8, kv=1, hd=128):
+        self.torch, self.tpm = torch, tpm
+        self.M, self.D, self.T, self.rank = M, D, T, rank
+        self.Ft = F // T
+        self.Nqkv = (heads + 2 * kv) * hd            # 1280
+        self.Dattn = heads * hd                      # 1024
+        self.C = T
+        dev = "cuda"
+        bf = lambda x: si.to_bf16(x).to(dev)
+        M, D, Ft, Nq, Da = self.M, self.D, self.Ft, self.Nqkv, self.Dattn
+        # seeds follow the workload recipe: X 1, W_up 2, W_down 3, dY_mlp 4,
+        # W_qkv 5, W_o 6, attention output 7, dY_qkv 8, dY_o 9
+        x = bf(si.normal_f32((M, D), 1))
+        self.x_src = x                                # the gathered rows as they land
+        self.x_qkv = torch.empty_like(x)
+        self.x_mlp = torch.empty_like(x)
+        self.w_qkv = bf(si.normal_f32((D, Nq), 5, 0.02))
+        self.w_up = bf(si.normal_f32((D, Ft), 2, 0.02))
+        self.w_o = bf(si.normal_f32((Da, D), 6, 0.02))
+        self.w_down = bf(si.normal_f32((Ft, D), 3, 0.02))
+        self.attn = bf(si.normal_f32((M, Da), 7))
+        self.dy_qkv = bf(si.normal_f32((M, Nq), 8))
+        self.dy_mlp_src = bf(si.normal_f32((M, D), 4))
+        self.dy_o_src = bf(si.normal_f32((M, D), 9))
+        self.dy_mlp = torch.empty_like(self.dy_mlp_src)
+        self.dy_o = torch.empty_like(self.dy_o_src)
+        for dst, src in ((self.x_qkv, x), (self.x_mlp, x), (self.dy_mlp, self.dy_mlp_src),
+                         (self.dy_o, self.dy_o_src)):
+            dst.copy_(src)
+        e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+        self.qkv = e(M, Nq)
+        self.z, self.h = e(M, Ft), e(M, Ft)
+        self.d_attn = e(M, Da)
+        self.g_qkv, self.g_up, self.g_o, self.g_down = e(D, Nq), e(D, Ft), e(Da, D), e(Ft, D)
+        # partial stack: slot `rank` is written by the GEMMs, the other slots
+        # hold the peers' stand-in partials (N(0,1), seeds 100 + t)
+        self.stack = e(T, M, D)
+        for t in range(T):
+            if t != rank:
+                self.stack[t] = bf(si.normal_f32((M, D), 100 + t))
+        self.slice_o, self.slice_mlp, self.slice_dxm, self.slice_dxq = (e(M // T, D) for _ in range(4))
+        self.ws_fwd = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, self.C, tpm.BF16)
+        self.ws_bwd = tpm.alloc_workspace(tpm.OP_MLP_BWD, M, D, F, T, self.C, tpm.BF16)
+        self.ws_g = [tpm.alloc_workspace(tpm.OP_SEQ_CHUNK_GEMM, M, D, D) for _ in range(4)]
+        self.flags = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
+        self.order = si.ring_chunk_order(T, self.C, rank)
+        self.dest = si.dest_range_order(T, rank)
+        self.side = torch.cuda.Stream()
+        self.gemm_events = []
+        fl = lambda m, n, k: 2.0 * m * n * k
+        self.flops = (3 * fl(M, Nq, D) + 3 * fl(M, Ft, D) + 3 * fl(M, D, Da) + 3 * fl(M, D, Ft))
+
+    # -- chunk arrival: side stream copies the remote chunks and signals flags
+    def _arrive(self, which, dst, src, epoch):
+        torch, tpm = self.torch, self.tpm
+        rows = self.M // self.C
+        own = set(range(self.rank * (self.C // self.T), (self.rank + 1) * (self.C // self.T)))
+        boundary = torch.cuda.Event()
+        boundary.record(torch.cuda.current_stream())
+        self.side.wait_event(boundary)            # communication starts at the layer boundary
+        with torch.cuda.stream(self.side):
+            for c in self.order:
+                if c not in own:
+                    dst[c * rows:(c + 1) * rows].copy_(src[c * rows:(c + 1) * rows])
+                tpm.signal_chunk(self.flags[which], c, epoch, stream=self.side)
+
+    def _timed(self, fn, record):
+        if not record:
+            fn()
+            return
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.gemm_events.append((a, b))
+
+    def step(self, epoch: int, arrive: bool = True, record: bool = False):
+        torch, tpm = self.torch, self.tpm
+        T, r, C = self.T, self.rank, self.C
+        ready = (lambda i: self.flags[i]) if arrive else (lambda i: None)
+        ws = lambda i: self.ws_g[i] if arrive else None
+        own_slot = self.stack[r]
+        # ---- forward, attention projections
+        if arrive:
+            self._arrive(0, self.x_qkv, self.x_src, epoch)
+        self._timed(lambda: tpm.seq_chunk_gemm(self.x_qkv, self.w_qkv, self.qkv, num_chunks=C,
+                                               chunk_order=self.order, chunk_ready=ready(0), epoch=epoch,
+                                               workspace=ws(0)), record)
+        self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
+                                               chunk_order=self.dest), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
+        # ---- forward, MLP
+        if arrive:
+            self._arrive(1, self.x_mlp, self.x_src, epoch)
+        self._timed(lambda: tpm.tp_mlp_fwd(self.x_mlp, self.w_up, self.w_down, self.h, own_slot, T=T, rank=r,
+                                           act=tpm.ACT_GELU_ERF, Z_t=self.z, num_chunks=C,
+                                           chunk_order=self.order, chunk_ready=ready(1), epoch=epoch,
+                                           workspace=self.ws_fwd), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
+        # ---- backward, MLP
+        if arrive:
+            self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch)
+        self._timed(lambda: tpm.tp_mlp_bwd(self.x_mlp, self.w_up, self.w_down, self.z, self.h, self.dy_mlp,
+                                           self.g_up, self.g_down, own_slot, T=T, rank=r,
+                                           act=tpm.ACT_GELU_ERF, num_chunks=C, dy_chunk_order=self.order,
+                                           dy_ready=ready(2), epoch=epoch, workspace=self.ws_bwd), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
+        # ---- backward, O projection: dA = dY_o W_o^T (chunk-fed), dW_o = A^T dY_o
+        if arrive:
+            self._arrive(3, self.dy_o, self.dy_o_src, epoch)
+
+        def o_bwd():
+            tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
+                               chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=ws(3))
+            tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True)
+        self._timed(o_bwd, record)
+
+        # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T (partial)
+        def qkv_bwd():
+            tpm.seq_chunk_gemm(self.x_qkv, self.dy_qkv, self.g_qkv, trans_a=True)
+            tpm.seq_chunk_gemm(self.dy_qkv, self.w_qkv, own_slot, trans_b=True)
+        self._timed(qkv_bwd, record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
+        if arrive:
+            done = torch.cuda.Event()
+            done.record(self.side)
+            torch.cuda.current_stream().wait_event(done)
+
+
+def time_steps(torch, layer, steps, warmup, arrive, epoch0):
+    for i in range(warmup):
+        layer.step(epoch0 + i, arrive=arrive)
+    torch.cuda.synchronize()
+    layer.gemm_events = []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        layer.step(epoch0 + warmup + i, arrive=arrive, record=True)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    gemm_ms = sum(a.elapsed_time(b) for a, b in layer.gemm_events) / steps
+    return ms, gemm_ms, wall
+
+
+def bench_reduce(torch, tpm, si, iters=40):
+    """8 bf16 partials [8192, 8192] -> rank slice [1024, 8192]; the rank
+    rotates 0..7 so each launch reads a different 134 MB (the 1 GiB stack
+    does not fit the 256 MB last-level cache)."""
+    T, M, D = 8, 8192, 8192
+    P = torch.empty(T, M, D, dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        P[t] = si.to_bf16(si.normal_f32((M, D), 100 + t)).cuda()
+    out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+    for r in range(T):
+        tpm.partial_reduce_seqshard(P, out, T=T, rank=r)
+    torch.cuda.synchronize()
+    evs = []
+    for i in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        tpm.partial_reduce_seqshard(P, out, T=T, rank=i % T)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[len(ms) // 2]
+    nbytes = T * (M // T) * D * 2 + (M // T) * D * 2
+    del P
+    return dict(bytes=nbytes, ms_median=med, ms_min=ms[0], GBs=nbytes / (med * 1e-3) / 1e9,
+                frac_hbm_peak=nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
+def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
+    Ft = F // T
+    dev = "cuda"
+    x = si.normal_f32((M, D), 1)
+    wu = si.normal_f32((D, Ft), 2, 0.02)
+    wd = si.normal_f32((Ft, D), 3, 0.02)
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    if fp8:
+        import numpy as np
+        xq, sx = si.to_e4m3_current(x)
+        wuq, su = si.to_e4m3_current(np.ascontiguousarray(wu.T))
+        wdq, sd = si.to_e4m3_current(np.ascontiguousarray(wd.T))
+        X, WU, WD = xq.to(dev), wuq.to(dev), wdq.to(dev)
+        scales = torch.tensor([sx, su, sd], dtype=torch.float32, device=dev)
+        ws = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
+        call = lambda: tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, scales=scales,
+                                      num_chunks=C, workspace=ws)
+    else:
+        X, WU, WD = si.to_bf16(x).to(dev), si.to_bf16(wu).to(dev), si.to_bf16(wd).to(dev)
+        call = lambda: tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, num_chunks=C)
+    del x, wu, wd
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    flops = 2.0 * M * Ft * D * 2
+    peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+    tf = flops / (ms * 1e-3) / 1e12
+    return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="fp8_e4m3" if fp8 else "bf16", ms=ms, TFLOPS=tf,
+                frac_mfma_peak=tf / peak)
+
+
+def cpu_baseline(sample_tokens: int, target_s: float = 20.0):
+    """The fp64 oracle, as it stands, on the first m tokens of the same layer
+    (all weights, D = 8192, F/T = 3584): the 12 GEMMs of the step at M = m.
+    A calibration run on `sample_tokens` tokens sets m so that the timed run
+    takes about `target_s` seconds (at most the full 4096 tokens).  Reported
+    in the step metric's unit."""
+    cal = _cpu_oracle_run(sample_tokens)
+    per_token_s = cal["seconds"] / sample_tokens
+    m = int(min(4096, max(256, (target_s / per_token_s) // 256 * 256)))
+    r = _cpu_oracle_run(m)
+    return dict(value=r["flops"] / r["seconds"] / 1e12, unit="TFLOPS", cores=r["threads"], kind="oracle",
+                sample=f"fp64 oracle, the 12 GEMMs + GeLU of the layer step on {m} of 4096 tokens "
+                       f"({r['flops'] / 1e9:.1f} GFLOP in {r['seconds']:.1f} s)")
+
+
+def _cpu_oracle_run(sample_tokens: int):
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import synthetic_inputs as si
+    from oracle import ops
+    m, D, Ft, Nq, Da = sample_tokens, 8192, 3584, 1280, 1024
+    f64 = lambda a: si.to_bf16(a).to(dtype=__import__("torch").float64).numpy()
+    x = f64(si.normal_f32((4096, D), 1)[:m])
+    w_qkv = f64(si.normal_f32((D, Nq), 5, 0.02))
+    w_up = f64(si.normal_f32((D, Ft), 2, 0.02))
+    w_o = f64(si.normal_f32((Da, D), 6, 0.02))
+    w_down = f64(si.normal_f32((Ft, D), 3, 0.02))
+    attn = f64(si.normal_f32((4096, Da), 7)[:m])
+    dy_qkv = f64(si.normal_f32((4096, Nq), 8)[:m])
+    dy_mlp = f64(si.normal_f32((4096, D), 4)[:m])
+    dy_o = f64(si.normal_f32((4096, D), 9)[:m])
+    t0 = time.perf_counter()
+    ops.seq_chunk_gemm(x, w_qkv)
+    ops.seq_chunk_gemm(attn, w_o)
+    fw = ops.tp_mlp_fwd(x, w_up, w_down, ops.ACT_GELU_ERF, store="bf16")
+    ops.tp_mlp_bwd(x, w_up, w_down, fw["Z"], fw["H"], dy_mlp, ops.ACT_GELU_ERF, store="bf16")
+    ops.linear_bwd(attn, w_o, dy_o)
+    ops.linear_bwd(x, w_qkv, dy_qkv)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * m * (3 * D * Nq + 3 * D * Ft + 3 * Da * D + 3 * Ft * D)
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    if threads == 0:
+        threads = len(os.sched_getaffinity(0))
+    return dict(seconds=dt, flops=flops, threads=threads)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import sequence_transformer_gemms_amd as tpm
+    import synthetic_inputs as si
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    layer = Layer(torch, tpm, si)
+    torch.cuda.synchronize()
+    ms, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1)
+    flops = layer.flops
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "TFLOPS/GPU on TP-rank MLP fwd+bwd (% of MFMA peak); reduce GB/s",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama3-70B-shaped TP=8 rank layer share fwd+bwd: QKV [8192,1280], O [1024,8192], "
+                               "MLP up [8192,3584] + GeLU, down [3584,8192]; 4096 tokens, 8 sequence chunks "
+                               "arriving on a side stream; 4 sequence-sharded reductions of 8 partials",
+                   "tokens": 4096, "hidden": 8192, "ffn": 28672, "tp": 8, "chunks": 8,
+                   "gflop_per_step": round(flops / 1e9, 1), "frac_mfma_peak": round(value / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel (bf16 MFMA), all 12 GEMM launches of the step",
+                     "gemm_ms_per_step": round(gemm_ms, 4)},
+    }
+    if not args.no_extra:
+        ms_r, gemm_ms_r, _ = time_steps(torch, layer, max(5, args.steps // 2), 2, arrive=False, epoch0=0)
+        extra = {"resident_step": {"ms": round(ms_r, 4), "TFLOPS": round(flops / (ms_r * 1e-3) / 1e12, 2),
+                                   "gemm_TFLOPS": round(flops / (gemm_ms_r * 1e-3) / 1e12, 2)}}
+        del layer
+        torch.cuda.empty_cache()
+        extra["reduce_c3"] = bench_reduce(torch, tpm, si)
+        torch.cuda.empty_cache()
+        extra["mlp_fwd_c3_bf16"] = bench_mlp_fwd(torch, tpm, si, 8192, 8192, 28672, 8, 8, False)
+        torch.cuda.empty_cache()
+        extra["mlp_fwd_c4_fp8"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
+        rec["extra"] = extra
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * tpmlp -- one tensor-parallel rank's share of a transformer MLP under
+ * tensor-sequence parallelism, on one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no framework types.  All matrices are
+ * row-major with an explicit leading dimension (elements between consecutive
+ * rows), as the pages write them: X[M,K], W[K,N] ("Tensor and sequence
+ * parallelism", section "Derive column-parallel linear algebra").
+ *
+ * Ownership: the caller owns every buffer (device memory unless marked host)
+ * and every stream.  The library never allocates, frees or synchronises a
+ * stream; it only enqueues kernels on the `stream` argument (a hipStream_t;
+ * NULL is the default stream).  Calls are asynchronous.
+ *
+ * Errors: every argument check runs on the host before anything is
+ * enqueued; on failure the call returns a negative tpm_status, enqueues
+ * nothing, and tpm_last_error() describes the problem (thread-local).  A
+ * launch failure returns TPM_EHIP.  A device-side wait that gives up
+ * (watchdog) is reported by tpm_poll_device_error() after the stream has
+ * been synchronised.
+ *
+ * Device pointers used by the matrix-core path must be 16-byte aligned and
+ * leading dimensions must be multiples of 8 (bf16) or 16 (fp8); N and K
+ * must be multiples of 8 (bf16) or 16 (fp8).  M is free.  The fp32 path has
+ * no alignment or size restriction.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  TPM_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf). */
+typedef enum { TPM_F32 = 0, TPM_BF16 = 1, TPM_FP8_E4M3 = 2 } tpm_dtype;
+
+/* Activations.  GELU_ERF: 0.5 z (1 + erf(z / sqrt 2)); GELU_TANH: the tanh
+ * approximation; RELU: max(z, 0) with derivative 1 only where z > 0
+ * ("Tensor parallelism" algorithm page, section "Code"). */
+typedef enum { TPM_ACT_NONE = 0, TPM_ACT_RELU = 1, TPM_ACT_GELU_ERF = 2, TPM_ACT_GELU_TANH = 3 } tpm_act;
+
+/* Epilogue of seq_chunk_gemm. */
+typedef enum {
+  TPM_EPI_FWD = 0,  /* Y = act(acc * sa * sb); aux (optional) receives the pre-activation */
+  TPM_EPI_DACT = 1  /* Y = acc * sa * sb * act'(aux): aux is the saved pre-activation Z */
+} tpm_epilogue;
+
+typedef enum {
+  TPM_OK = 0,
+  TPM_EINVAL = -1,       /* bad pointer, size, leading dimension or order */
+  TPM_EUNSUPPORTED = -2, /* valid but not implemented (dtype / layout / alignment combination) */
+  TPM_EHIP = -3,         /* a HIP launch failed */
+  TPM_ETIMEOUT = -4,     /* a device-side wait for a chunk gave up (watchdog) */
+  TPM_EWORKSPACE = -5    /* workspace missing or smaller than tpm_workspace_bytes() */
+} tpm_status;
+
+/* Operation ids for tpm_workspace_bytes(). */
+typedef enum { TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2 } tpm_op;
+
+#define TPM_MAX_CHUNKS 256
+
+/*
+ * seq_chunk_gemm -- one local GEMM of a tensor-parallel rank, fed by
+ * sequence chunks in arrival order ("Collective GEMMs in Tensor Sequence
+ * Parallelism", section "Collective GEMMs (CGEMM)", all-gather + GEMM: each
+ * chunk of tokens yields distinct output rows, written in place with no
+ * accumulation).
+ *
+ *   Y[M,N] = epilogue( op(A)[M,K] . op(B)[K,N] )
+ *
+ * A: trans_a = 0 -> A is [M, lda >= K] (K contiguous, e.g. the activation
+ *    X[tokens, K]); trans_a = 1 -> A is stored [K, lda >= M] and op(A) = A^T
+ *    (e.g. X^T in a weight gradient).
+ * B: trans_b = 0 -> B is [K, ldb >= N] (the pages' W[K,N]); trans_b = 1 ->
+ *    B is stored [N, ldb >= K] and op(B) = B^T (e.g. W^T in dX = dY W^T).
+ * a_dtype == b_dtype in {F32, BF16, FP8_E4M3}.  fp8 operands must be
+ *    stored K-major (trans_a = 0, trans_b = 1); fp32 accumulation always.
+ * a_scale, b_scale: device fp32 dequantisation factors (value = code *
+ *    scale), or NULL for 1.
+ * Y: [M, ldy >= N], y_dtype F32 or BF16 (round to nearest even).
+ * epilogue/act/aux: see tpm_epilogue; aux is [M, ldaux >= N] of y_dtype
+ *    (FWD: written if non-NULL; DACT: required, read).
+ * amax_out: device fp32 or NULL; set to max |Y| as stored (zeroed by the
+ *    call first).
+ * Chunks: the M rows of Y are cut into num_chunks equal chunks (M %
+ *    num_chunks == 0, 1 <= num_chunks <= TPM_MAX_CHUNKS).  chunk_order
+ *    (HOST, num_chunks entries, a permutation) is the arrival order, or NULL
+ *    for ascending.  chunk_ready (DEVICE, num_chunks uint32) or NULL: when
+ *    given, no row of chunk c is read before chunk_ready[c] >= epoch
+ *    (wrap-around compare); the flags are written by the producer of the
+ *    chunk (tpm_signal_chunk).  The result does not depend on the order.
+ * workspace: device, >= tpm_workspace_bytes(TPM_OP_SEQ_CHUNK_GEMM, ...);
+ *    required when chunk_ready or amax_out is given, else may be NULL.
+ */
+int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda, int trans_a, int a_dtype, const float* a_scale,
+                   const void* B, int64_t ldb, int trans_b, int b_dtype, const float* b_scale,
+                   void* Y, int64_t ldy, int y_dtype,
+                   int epilogue, int act, void* aux, int64_t ldaux, float* amax_out,
+                   int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_fwd -- rank `rank` of a T-way tensor-parallel MLP ("Tensor
+ * parallelism" algorithm page, section "How it works"; "Tensor and sequence
+ * parallelism", section "Pair adjacent transformer projections"):
+ *
+ *   Z_t = X . W_up,t            column-parallel, [M, F/T], chunk-fed
+ *   H_t = act(Z_t)              local activation
+ *   P_t = H_t . W_down,t        row-parallel partial [M, D]
+ *
+ * X: [M, D] (the all-gathered token rows), W_up_t: [D, F/T], W_down_t:
+ * [F/T, D], all dense (leading dimension = row width), dtype BF16, F32 or
+ * FP8_E4M3.  Z_t (optional), H_t: [M, F/T]; P_t: [M, D]; stored as BF16
+ * (F32 when dtype is F32).
+ * FP8 (current scaling, "Supported quantization recipes"): scales = device
+ * fp32[3] = {s_X, s_Wup, s_Wdown}; H is stored bf16, its amax taken over the
+ * stored values, and GEMM2 reads H quantised to e4m3 with inv = 448/amax;
+ * s_H = amax/448 is written to h_scale_out (device fp32) when non-NULL.
+ * F % T == 0, M % T == 0, M % num_chunks == 0.
+ * Chunk arguments as in seq_chunk_gemm, for GEMM1's rows (tokens);
+ * chunk_order NULL means the ring all-gather arrival order at `rank`: own
+ * chunks first, then those of ranks rank-1, rank-2, ... (needs
+ * num_chunks % T == 0; else ascending).
+ * GEMM2 produces destination token ranges (T ranges of M/T rows) in
+ * range_order (HOST, T entries) or, when NULL, rank+1, rank+2, ..., rank
+ * (own range last), so finished ranges could leave first ("Collective
+ * GEMMs", GEMM + reduce-scatter); range_done (DEVICE, T uint32, or NULL) is
+ * set to epoch when a range is fully stored.
+ * workspace >= tpm_workspace_bytes(TPM_OP_MLP_FWD, M, D, F, T, ...).
+ */
+int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+               const void* X, const void* W_up_t, const void* W_down_t,
+               int dtype, const float* scales, int act,
+               void* Z_t, void* H_t, void* P_t, float* h_scale_out,
+               int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+               const int32_t* range_order, uint32_t* range_done,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_bwd -- backward of tp_mlp_fwd ("Tensor and sequence parallelism",
+ * sections "Derive column-parallel linear algebra" and "Derive row-parallel
+ * linear algebra"; "Tensor parallelism", section "Code"):
+ *
+ *   dZ_t      = (dY . W_down,t^T) * act'(Z_t)    chunk-fed by dY rows
+ *   dW_down,t = H_t^T . dY                       [F/T, D]
+ *   dW_up,t   = X^T . dZ_t                       [D, F/T]
+ *   dX_t      = dZ_t . W_up,t^T                  [M, D] partial (to be summed
+ *                                                across ranks)
+ * Inputs as in tp_mlp_fwd plus Z_t, H_t (saved forward values) and dY
+ * [M, D]; dtype BF16 or F32.  dW outputs in dw_dtype (BF16 or F32; F32 only
+ * with dtype F32), dX_t in dtype.  dZ_t lives in the workspace.
+ * dy_chunk_order / dy_ready / epoch gate the rows of dY as in seq_chunk_gemm.
+ * workspace >= tpm_workspace_bytes(TPM_OP_MLP_BWD, M, D, F, T, ...).
+ */
+int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+               const void* X, const void* W_up_t, const void* W_down_t,
+               const void* Z_t, const void* H_t, const void* dY,
+               int dtype, int act,
+               void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+               int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * partial_reduce_seqshard -- the arithmetic a rank performs in the
+ * reduce-scatter that follows a row-parallel GEMM ("Collective GEMMs in
+ * Tensor Sequence Parallelism", section "Collective GEMMs (CGEMM)"; "Tensor
+ * and sequence parallelism", section "Derive row-parallel linear algebra"):
+ *
+ *   out[i, j] = sum_{t=0}^{T-1} P_t[row0 + i, j],   0 <= i < M/T,
+ *
+ * with row0 = rank * M/T, or row0 = 0 when rank == -1 (each P_t then holds
+ * only this rank's M/T rows, e.g. a receive buffer [T, M/T, D]).
+ * P_t starts at partials + t * partial_stride elements and has leading
+ * dimension ld >= D; out is [M/T, ldo >= D].  Sum in fp32 in ascending t,
+ * one rounding at the end.  in_dtype/out_dtype: BF16 or F32.  M % T == 0.
+ */
+int partial_reduce_seqshard(int T, int64_t M, int64_t D, int rank,
+                            const void* partials, int64_t partial_stride, int64_t ld, int in_dtype,
+                            void* out, int64_t ldo, int out_dtype, void* stream);
+
+/* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
+ * TPM_OP_MLP_BWD pass (M, N = D, K = F, T); for TPM_OP_SEQ_CHUNK_GEMM the
+ * sizes are (M, N, K) and T is ignored. */
+size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int num_chunks, int dtype);
+
+/* Enqueue on `stream` a release store of `value` into the device word
+ * `flag` (marks a chunk as landed after the copies enqueued before it). */
+int tpm_signal_chunk(void* stream, uint32_t* flag, uint32_t value);
+
+/* After synchronising the stream: TPM_OK, or TPM_ETIMEOUT if a chunk wait
+ * of the last chunk-gated call on this workspace gave up.  Blocking copy of
+ * one device word. */
+int tpm_poll_device_error(const void* workspace, size_t workspace_bytes);
+
+/* Number of polls a device-side chunk wait makes before it gives up and
+ * flags TPM_ETIMEOUT (default 1 << 22, a few seconds).  Process-wide. */
+int tpm_set_wait_limit(uint32_t polls);
+
+/* Thread-local description of the last error; never NULL. */
+const char* tpm_last_error(void);
+
+const char* tpm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

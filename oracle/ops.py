@@ -152,16 +152,28 @@ def seq_chunk_gemm(a, b, *, trans_a=False, trans_b=False, a_scale=1.0, b_scale=1
 
 
 # -------------------------------------------------------------- tp_mlp_fwd
-def tp_mlp_fwd(x, w_up_t, w_down_t, act=ACT_GELU_ERF):
-    """One rank's MLP share in exact arithmetic ([TP] "How it works"; [TSP]
-    "Pair adjacent transformer projections"):
+def _stored(v, store):
+    """The value a later step reads back: exact (store=None) or rounded to
+    the storage format the path keeps intermediates in (store='bf16')."""
+    if store is None:
+        return v
+    if store == "bf16":
+        return formats.round_bf16(v)
+    raise ValueError(store)
+
+
+def tp_mlp_fwd(x, w_up_t, w_down_t, act=ACT_GELU_ERF, store=None):
+    """One rank's MLP share ([TP] "How it works"; [TSP] "Pair adjacent
+    transformer projections"):
         Z_t = X . W_up,t        (column-parallel, [M, F/T])
         H_t = act(Z_t)          (local activation)
         P_t = H_t . W_down,t    (row-parallel partial, [M, D])
-    """
+    store='bf16': the second GEMM reads H_t as stored in bf16 (the
+    intermediate activation is kept in the activation dtype); otherwise all
+    of it is exact."""
     z = gemm(x, w_up_t)
     h = act_fwd(z, act)
-    p = gemm(h, w_down_t)
+    p = gemm(_stored(h, store), w_down_t)
     return dict(Z=z, H=h, P=p)
 
 
@@ -199,16 +211,20 @@ def partial_reduce_seqshard(partials, rank: int):
     """Local arithmetic of the reduce-scatter that follows a row-parallel GEMM
     ([CG] "Collective GEMMs (CGEMM)", GEMM + reduce-scatter; [TSP] "Derive
     row-parallel linear algebra"): rank r receives rows
-    [r*M/T, (r+1)*M/T) of sum_t P_t.  partials: [T, M, D]."""
+    [r*M/T, (r+1)*M/T) of sum_t P_t.  partials: [T, M, D].
+    rank = -1: each partial already holds only this rank's rows (a receive
+    buffer [T, M/T, D]); the result is their sum."""
     p = np.asarray(partials, dtype=np.float64)
     T, M, _ = p.shape
+    if rank < 0:
+        return p.sum(axis=0)
     assert M % T == 0
     s = M // T
     return p[:, rank * s:(rank + 1) * s, :].sum(axis=0)
 
 
 # -------------------------------------------------------------- tp_mlp_bwd
-def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF):
+def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None):
     """Backward of one rank's MLP share ([TSP] both derivations; [TP] "Code"):
         dH_t      = dY . W_down,t^T        (row-parallel input gradient shard)
         dZ_t      = dH_t * act'(Z_t)
@@ -216,12 +232,14 @@ def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF):
         dW_up,t   = X^T . dZ_t             (column-parallel weight gradient)
         dX_t      = dZ_t . W_up,t^T        (full [M,D] partial, summed across
                                             ranks by all-reduce / reduce-scatter)
-    Z and H are the saved forward values (inputs here)."""
+    Z and H are the saved forward values (inputs here).  store='bf16': the
+    two GEMMs that consume dZ_t read it as stored in bf16."""
     dh = gemm(dy, np.asarray(w_down_t, dtype=np.float64).T)
     dz = dh * act_grad(np.asarray(z, dtype=np.float64), act)
     dw_down = gemm(np.asarray(h, dtype=np.float64).T, dy)
-    dw_up = gemm(np.asarray(x, dtype=np.float64).T, dz)
-    dx = gemm(dz, np.asarray(w_up_t, dtype=np.float64).T)
+    dzs = _stored(dz, store)
+    dw_up = gemm(np.asarray(x, dtype=np.float64).T, dzs)
+    dx = gemm(dzs, np.asarray(w_up_t, dtype=np.float64).T)
     return dict(dH=dh, dZ=dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
 
 

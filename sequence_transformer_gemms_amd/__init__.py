@@ -1,0 +1,150 @@
+"""One tensor-parallel rank's MLP hot path on AMD MI355X (gfx950).
+
+Python face of libtpmlp: the four operations of include/tpmlp.h under the same
+names, taking torch tensors for device memory and torch's current stream.
+Arguments are marshalled to the C ABI; nothing is computed here.
+
+    seq_chunk_gemm          chunk-fed local GEMM with fused epilogue
+    tp_mlp_fwd              Z = X W_up,t; H = act(Z); P = H W_down,t (partial)
+    tp_mlp_bwd              dZ, dW_down,t, dW_up,t, dX_t (partial)
+    partial_reduce_seqshard sum of T partials over this rank's token slice
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, BF16, EPI_DACT, EPI_FWD, F32,  # noqa: F401
+                   FP8_E4M3, OP_MLP_BWD, OP_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+
+__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "partial_reduce_seqshard",
+           "workspace_bytes", "alloc_workspace", "signal_chunk", "poll_device_error",
+           "set_wait_limit", "dtype_code", "TpmError", "lib"]
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ld(t: torch.Tensor) -> int:
+    assert t.dim() == 2 and t.stride(1) == 1, "row-major 2-D tensors with unit inner stride"
+    return t.stride(0)
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int, T: int = 1, num_chunks: int = 1, dtype: int = BF16) -> int:
+    return int(lib.tpm_workspace_bytes(op, M, N, K, T, num_chunks, dtype))
+
+
+def alloc_workspace(op: int, M: int, N: int, K: int, T: int = 1, num_chunks: int = 1, dtype: int = BF16,
+                    device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(op, M, N, K, T, num_chunks, dtype), 1), dtype=torch.uint8, device=device)
+
+
+def seq_chunk_gemm(A, B, Y, *, trans_a=False, trans_b=False, a_scale=None, b_scale=None,
+                   epilogue=EPI_FWD, act=ACT_NONE, aux=None, amax_out=None, num_chunks=1,
+                   chunk_order=None, chunk_ready=None, epoch=0, workspace=None, stream=None,
+                   M=None, N=None, K=None):
+    """Y = epilogue(op(A) . op(B)); shapes are taken from the tensors."""
+    if M is None:
+        M = A.shape[1] if trans_a else A.shape[0]
+    if K is None:
+        K = A.shape[0] if trans_a else A.shape[1]
+    if N is None:
+        N = B.shape[0] if trans_b else B.shape[1]
+    order = _abi.int_array(chunk_order)
+    rc = lib.seq_chunk_gemm(M, N, K,
+                            _ptr(A), _ld(A), int(trans_a), dtype_code(A.dtype), _ptr(a_scale),
+                            _ptr(B), _ld(B), int(trans_b), dtype_code(B.dtype), _ptr(b_scale),
+                            _ptr(Y), _ld(Y), dtype_code(Y.dtype),
+                            epilogue, act, _ptr(aux), _ld(aux) if aux is not None else 0, _ptr(amax_out),
+                            num_chunks, order, _ptr(chunk_ready), epoch,
+                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                            _stream(stream))
+    return check(rc)
+
+
+def tp_mlp_fwd(X, W_up_t, W_down_t, H_t, P_t, *, T, rank, act=ACT_GELU_ERF, Z_t=None, scales=None,
+               h_scale_out=None, num_chunks=1, chunk_order=None, chunk_ready=None, epoch=0,
+               range_order=None, range_done=None, workspace=None, stream=None):
+    """One rank's forward.  Dense tensors: X [M,D], W_up_t [D,F/T], W_down_t
+    [F/T,D] (fp8: stored transposed, [F/T,D] and [D,F/T]), H_t/Z_t [M,F/T],
+    P_t [M,D]."""
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    dt = dtype_code(X.dtype)
+    rc = lib.tp_mlp_fwd(M, D, Ft * T, T, rank,
+                        _ptr(X), _ptr(W_up_t), _ptr(W_down_t),
+                        dt, _ptr(scales), act,
+                        _ptr(Z_t), _ptr(H_t), _ptr(P_t), _ptr(h_scale_out),
+                        num_chunks, _abi.int_array(chunk_order), _ptr(chunk_ready), epoch,
+                        _abi.int_array(range_order), _ptr(range_done),
+                        _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                        _stream(stream))
+    return check(rc)
+
+
+def tp_mlp_bwd(X, W_up_t, W_down_t, Z_t, H_t, dY, dW_up_t, dW_down_t, dX_t, *, T, rank,
+               act=ACT_GELU_ERF, num_chunks=1, dy_chunk_order=None, dy_ready=None, epoch=0,
+               workspace=None, stream=None):
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_mlp_bwd(M, D, Ft * T, T, rank,
+                        _ptr(X), _ptr(W_up_t), _ptr(W_down_t),
+                        _ptr(Z_t), _ptr(H_t), _ptr(dY),
+                        dtype_code(X.dtype), act,
+                        _ptr(dW_up_t), _ptr(dW_down_t), _ptr(dX_t), dtype_code(dW_up_t.dtype),
+                        num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch,
+                        _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                        _stream(stream))
+    return check(rc)
+
+
+def partial_reduce_seqshard(partials, out, *, T, rank, M=None, stream=None):
+    """partials: [T, M, D] (or [T, M/T, D] with rank=-1); out: [M/T, D]."""
+    assert partials.dim() == 3 and partials.stride(2) == 1
+    Tn, rows, D = partials.shape
+    assert Tn == T
+    if M is None:
+        M = rows if rank >= 0 else rows * T
+    rc = lib.partial_reduce_seqshard(T, M, D, rank, _ptr(partials), partials.stride(0), partials.stride(1),
+                                     dtype_code(partials.dtype), _ptr(out), _ld(out), dtype_code(out.dtype),
+                                     _stream(stream))
+    return check(rc)
+
+
+def signal_chunk(flag_tensor, index: int, value: int, stream=None):
+    """Release-store `value` into flag_tensor[index] (device uint32/int32) on `stream`."""
+    ptr = flag_tensor.data_ptr() + 4 * index
+    return check(lib.tpm_signal_chunk(_stream(stream), ptr, value))
+
+
+def poll_device_error(workspace) -> int:
+    return int(lib.tpm_poll_device_error(_ptr(workspace), workspace.numel()))
+
+
+def set_wait_limit(polls: int) -> None:
+    check(lib.tpm_set_wait_limit(ctypes.c_uint32(polls).value))

@@ -1,0 +1,395 @@
+// C-ABI layer of libtpmlp: argument validation (host-side, before anything
+// is enqueued), kernel selection, workspace carving, launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/tpmlp.h"
+#include "tpm_internal.hpp"
+
+using namespace tpm;
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+uint32_t g_wait_limit = 1u << 22;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TPM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// control words at the head of every workspace
+constexpr int kCtrlErr = 0, kCtrlAmax = 1, kCtrlScale = 2, kCtrlCnt = 4;
+constexpr int kCtrlWords = kCtrlCnt + kMaxGroups;
+constexpr size_t kCtrlBytes = 2048;
+static_assert(kCtrlWords * 4 <= (int)kCtrlBytes, "control block");
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int esize(int dt) { return dt == TPM_F32 ? 4 : dt == TPM_BF16 ? 2 : 1; }
+bool valid_dt(int dt) { return dt == TPM_F32 || dt == TPM_BF16 || dt == TPM_FP8_E4M3; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct GemmDesc {
+  int64_t M, N, K;
+  const void* A; int64_t lda; bool ta; int adt; const float* asc;
+  const void* B; int64_t ldb; bool tb; int bdt; const float* bsc;
+  void* Y; int64_t ldy; int ydt;
+  int epi, act; void* aux; int64_t ldaux; float* amax;
+  int groups; const int32_t* order; const uint32_t* ready; uint32_t* done; uint32_t epoch;
+  uint32_t* ctrl;   // device control words (err, amax, counters) or null
+};
+
+// Full host-side validation of one GEMM; returns TPM_OK or an error code.
+int check_gemm(const GemmDesc& g, const char* who) {
+  if (g.M < 0 || g.N < 0 || g.K < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (g.M > INT32_MAX || g.N > INT32_MAX || g.K > INT32_MAX) return fail(TPM_EUNSUPPORTED, "%s: size >= 2^31", who);
+  if (!valid_dt(g.adt) || g.adt != g.bdt) return fail(TPM_EINVAL, "%s: operand dtypes must match", who);
+  if (g.ydt != TPM_F32 && g.ydt != TPM_BF16) return fail(TPM_EINVAL, "%s: output dtype must be F32 or BF16", who);
+  if (g.epi != TPM_EPI_FWD && g.epi != TPM_EPI_DACT) return fail(TPM_EINVAL, "%s: bad epilogue", who);
+  if (g.act < TPM_ACT_NONE || g.act > TPM_ACT_GELU_TANH) return fail(TPM_EINVAL, "%s: bad activation", who);
+  if (g.groups < 1 || g.groups > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks must be in [1, %d]", who, TPM_MAX_CHUNKS);
+  if (g.M % g.groups != 0) return fail(TPM_EINVAL, "%s: M (%lld) %% num_chunks (%d) != 0", who, (long long)g.M, g.groups);
+  if (g.order) {
+    std::vector<char> seen(g.groups, 0);
+    for (int i = 0; i < g.groups; ++i) {
+      const int c = g.order[i];
+      if (c < 0 || c >= g.groups || seen[c]) return fail(TPM_EINVAL, "%s: chunk order is not a permutation", who);
+      seen[c] = 1;
+    }
+  }
+  if (g.M == 0 || g.N == 0) return TPM_OK;
+  if (!g.Y) return fail(TPM_EINVAL, "%s: null output", who);
+  if (g.K > 0 && (!g.A || !g.B)) return fail(TPM_EINVAL, "%s: null operand", who);
+  const int64_t a_cols = g.ta ? g.M : g.K, b_cols = g.tb ? g.K : g.N;
+  if (g.ldy < g.N || (g.K > 0 && (g.lda < a_cols || g.ldb < b_cols)))
+    return fail(TPM_EINVAL, "%s: leading dimension smaller than the row width", who);
+  if (g.epi == TPM_EPI_DACT && !g.aux) return fail(TPM_EINVAL, "%s: DACT epilogue needs aux (Z)", who);
+  if (g.aux && g.ldaux < g.N) return fail(TPM_EINVAL, "%s: ldaux < N", who);
+  if ((g.ready || g.amax || g.done) && !g.ctrl) return fail(TPM_EWORKSPACE, "%s: workspace required", who);
+  if (g.adt == TPM_F32) {
+    if (g.ydt != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 operands give fp32 output", who);
+    if (g.ready || g.done) return fail(TPM_EUNSUPPORTED, "%s: chunk gating is implemented on the bf16/fp8 path", who);
+    return TPM_OK;
+  }
+  const int q = g.adt == TPM_BF16 ? 8 : 16;
+  if (g.adt == TPM_FP8_E4M3 && (g.ta || !g.tb))
+    return fail(TPM_EUNSUPPORTED, "%s: fp8 operands must be stored K-major (trans_a=0, trans_b=1)", who);
+  if (g.N % 8 != 0 || g.K % q != 0) return fail(TPM_EUNSUPPORTED, "%s: N %% 8 and K %% %d must be 0", who, q);
+  if (g.ldy % 4 != 0 || (g.aux && g.ldaux % 4 != 0)) return fail(TPM_EUNSUPPORTED, "%s: ldy/ldaux %% 4 != 0", who);
+  if (((uintptr_t)g.Y & 15) || (g.aux && ((uintptr_t)g.aux & 15)))
+    return fail(TPM_EUNSUPPORTED, "%s: device pointers must be 16-byte aligned", who);
+  if (g.K == 0) return TPM_OK;  // Y = epilogue(0): the operands are never read
+  if (g.ta && g.M % 8 != 0) return fail(TPM_EUNSUPPORTED, "%s: M %% 8 must be 0 with trans_a", who);
+  if (g.lda % q != 0 || g.ldb % q != 0) return fail(TPM_EUNSUPPORTED, "%s: lda/ldb must be multiples of %d", who, q);
+  if (!aligned16(g.A) || !aligned16(g.B)) return fail(TPM_EUNSUPPORTED, "%s: operands must be 16-byte aligned", who);
+  const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
+  const double a_ext = (double)a_rows * g.lda * esize(g.adt), b_ext = (double)b_rows * g.ldb * esize(g.bdt);
+  if (a_ext >= 4294967040.0 || b_ext >= 4294967040.0)
+    return fail(TPM_EUNSUPPORTED, "%s: an operand spans >= 4 GiB", who);
+  return TPM_OK;
+}
+
+int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
+  if (g.M == 0 || g.N == 0) return TPM_OK;
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.A = g.A; p.B = g.B; p.Y = g.Y; p.aux = g.aux;
+  p.a_scale = g.asc; p.b_scale = g.bsc; p.amax = g.amax;
+  p.ready = g.ready; p.done = g.done;
+  p.err = g.ctrl ? g.ctrl + kCtrlErr : nullptr;
+  p.group_cnt = g.ctrl ? g.ctrl + kCtrlCnt : nullptr;
+  p.lda = g.lda; p.ldb = g.ldb; p.ldy = g.ldy; p.ldaux = g.ldaux;
+  p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K;
+  p.num_groups = g.groups;
+  p.group_rows = (int)(g.M / g.groups);
+  p.epoch = g.epoch;
+  p.wait_limit = g_wait_limit;
+  p.act = g.act; p.epi = g.epi; p.y_f32 = g.ydt == TPM_F32; p.aux_f32 = p.y_f32;
+  for (int i = 0; i < g.groups; ++i) p.order[i] = (int16_t)(g.order ? g.order[i] : i);
+  hipError_t e;
+  if (g.adt == TPM_F32) {
+    e = launch_gemm_f32(p, g.ta, g.tb, s);
+    return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+  }
+  const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
+  p.a_bytes = g.K == 0 ? 0u : (uint32_t)(a_rows * g.lda * esize(g.adt));
+  p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
+  p.mt_per_group = (p.group_rows + kTileM - 1) / kTileM;
+  p.nt = (p.N + kTileN - 1) / kTileN;
+  p.tiles_per_group = p.mt_per_group * p.nt;
+  p.total_tiles = p.tiles_per_group * p.num_groups;
+  p.band_m = std::min(p.mt_per_group, 4);
+  // persistent grid: one work-group per CU; when chunks are gated on flags
+  // written by another stream, leave one CU per XCD free for the producer.
+  int cus = num_cus();
+  int grid = g.ready ? cus - 8 : cus;
+  grid = std::max(8, grid);
+  grid = std::min(grid, p.total_tiles);
+  if (g.adt == TPM_BF16) e = launch_gemm_bf16(p, !g.ta, g.tb, grid, s);
+  else e = launch_gemm_fp8(p, !g.ta, g.tb, grid, s);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+uint32_t* ctrl_of(void* ws, size_t bytes) { return (ws && bytes >= kCtrlBytes) ? (uint32_t*)ws : nullptr; }
+
+void ring_order(int T, int C, int rank, int32_t* out) {
+  if (T >= 1 && C % T == 0 && rank >= 0 && rank < T) {
+    const int per = C / T;
+    int n = 0;
+    for (int step = 0; step < T; ++step) {
+      const int q = ((rank - step) % T + T) % T;
+      for (int i = 0; i < per; ++i) out[n++] = q * per + i;
+    }
+  } else {
+    for (int i = 0; i < C; ++i) out[i] = i;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tpm_version(void) { return "tpmlp 0.1 (gfx950)"; }
+const char* tpm_last_error(void) { return g_err; }
+
+int tpm_set_wait_limit(uint32_t polls) {
+  g_wait_limit = polls == 0 ? 1 : polls;
+  return TPM_OK;
+}
+
+size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int num_chunks, int dtype) {
+  (void)num_chunks;
+  if (M < 0 || N < 0 || K < 0) return 0;
+  switch (op) {
+    case TPM_OP_SEQ_CHUNK_GEMM: return kCtrlBytes;
+    case TPM_OP_MLP_FWD: {
+      if (T <= 0) return 0;
+      const size_t ft = (size_t)(K / T);
+      return kCtrlBytes + (dtype == TPM_FP8_E4M3 ? round_up((size_t)M * ft, 256) : 0);
+    }
+    case TPM_OP_MLP_BWD: {
+      if (T <= 0) return 0;
+      const size_t ft = (size_t)(K / T);
+      return kCtrlBytes + round_up((size_t)M * ft * (size_t)esize(dtype == TPM_F32 ? TPM_F32 : TPM_BF16), 256);
+    }
+    default: return 0;
+  }
+}
+
+int tpm_signal_chunk(void* stream, uint32_t* flag, uint32_t value) {
+  if (!flag) return fail(TPM_EINVAL, "tpm_signal_chunk: null flag");
+  hipError_t e = launch_signal(flag, value, (hipStream_t)stream);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, "tpm_signal_chunk");
+}
+
+int tpm_poll_device_error(const void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < kCtrlBytes) return fail(TPM_EWORKSPACE, "tpm_poll_device_error: workspace");
+  uint32_t w = 0;
+  hipError_t e = hipMemcpy(&w, workspace, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "tpm_poll_device_error");
+  if (w != 0) return fail(TPM_ETIMEOUT, "a device-side chunk wait gave up (watchdog)");
+  return TPM_OK;
+}
+
+int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda, int trans_a, int a_dtype, const float* a_scale,
+                   const void* B, int64_t ldb, int trans_b, int b_dtype, const float* b_scale,
+                   void* Y, int64_t ldy, int y_dtype,
+                   int epilogue, int act, void* aux, int64_t ldaux, float* amax_out,
+                   int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "seq_chunk_gemm";
+  uint32_t* ctrl = ctrl_of(workspace, workspace_bytes);
+  if ((chunk_ready || amax_out) && workspace && !ctrl)
+    return fail(TPM_EWORKSPACE, "%s: workspace smaller than %zu bytes", who, kCtrlBytes);
+  GemmDesc g{M, N, K, A, lda, trans_a != 0, a_dtype, a_scale, B, ldb, trans_b != 0, b_dtype, b_scale,
+             Y, ldy, y_dtype, epilogue, act, aux, ldaux, amax_out,
+             num_chunks, chunk_order, chunk_ready, nullptr, epoch, ctrl};
+  int rc = check_gemm(g, who);
+  if (rc != TPM_OK) return rc;
+  if (amax_out && a_dtype == TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: amax on the fp32 path", who);
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 0 || N == 0) return TPM_OK;
+  if (chunk_ready || amax_out) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if (amax_out) {
+      e = launch_ctrl_init((uint32_t*)amax_out, 1, s);
+      if (e != hipSuccess) return hip_fail(e, who);
+    }
+  }
+  return run_gemm(g, s, who);
+}
+
+int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+               const void* X, const void* W_up_t, const void* W_down_t,
+               int dtype, const float* scales, int act,
+               void* Z_t, void* H_t, void* P_t, float* h_scale_out,
+               int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+               const int32_t* range_order, uint32_t* range_done,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_mlp_fwd";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0) return fail(TPM_EINVAL, "%s: F %% T != 0", who);
+  if (M % T != 0) return fail(TPM_EINVAL, "%s: M %% T != 0", who);
+  if (!valid_dt(dtype)) return fail(TPM_EINVAL, "%s: bad dtype", who);
+  if (dtype == TPM_FP8_E4M3 && !scales) return fail(TPM_EINVAL, "%s: fp8 needs scales", who);
+  if (!H_t || !P_t) return fail(TPM_EINVAL, "%s: null H_t or P_t", who);
+  const int64_t Ft = F / T;
+  const size_t need = tpm_workspace_bytes(TPM_OP_MLP_FWD, M, D, F, T, num_chunks, dtype);
+  const bool need_ctrl = chunk_ready || range_done || dtype == TPM_FP8_E4M3;
+  if (need_ctrl && (!workspace || workspace_bytes < need))
+    return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  uint32_t* ctrl = need_ctrl ? (uint32_t*)workspace : nullptr;
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
+  int32_t corder[TPM_MAX_CHUNKS], rorder[TPM_MAX_CHUNKS];
+  if (chunk_order) std::memcpy(corder, chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  if (range_order) std::memcpy(rorder, range_order, sizeof(int32_t) * T);
+  else for (int i = 0; i < T; ++i) rorder[i] = (rank + 1 + i) % T;
+
+  const int ydt = dtype == TPM_F32 ? TPM_F32 : TPM_BF16;
+  const bool fp8 = dtype == TPM_FP8_E4M3;
+  float* amax = fp8 ? (float*)(ctrl + kCtrlAmax) : nullptr;
+  // GEMM1: column-parallel, chunk-fed.  fp8 weights arrive as W[K,N]
+  // row-major like every other dtype; the fp8 kernel wants K-major B, so
+  // fp8 W_up,t / W_down,t are taken as stored transposed ([N, K]).
+  GemmDesc g1{M, Ft, D, X, D, false, dtype, fp8 ? scales + 0 : nullptr,
+              W_up_t, fp8 ? D : Ft, fp8, dtype, fp8 ? scales + 1 : nullptr,
+              H_t, Ft, ydt, TPM_EPI_FWD, act, Z_t, Ft, amax,
+              num_chunks, corder, chunk_ready, nullptr, epoch, ctrl};
+  int rc = check_gemm(g1, who);
+  if (rc != TPM_OK) return rc;
+  uint8_t* hq = fp8 ? (uint8_t*)workspace + kCtrlBytes : nullptr;
+  float* sH = fp8 ? (h_scale_out ? h_scale_out : (float*)(ctrl + kCtrlScale)) : nullptr;
+  GemmDesc g2{M, D, Ft, fp8 ? (const void*)hq : (const void*)H_t, Ft, false, dtype, sH,
+              W_down_t, fp8 ? Ft : D, fp8, dtype, fp8 ? scales + 2 : nullptr,
+              P_t, D, ydt, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+              T, rorder, nullptr, range_done, epoch, ctrl};
+  rc = check_gemm(g2, who);
+  if (rc != TPM_OK) return rc;
+  if (M == 0 || D == 0) return TPM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (need_ctrl) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  rc = run_gemm(g1, s, who);
+  if (rc != TPM_OK) return rc;
+  if (fp8) {
+    hipError_t e = launch_quant_e4m3((const uint16_t*)H_t, M, Ft, Ft, amax, hq, Ft, sH, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  return run_gemm(g2, s, who);
+}
+
+int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+               const void* X, const void* W_up_t, const void* W_down_t,
+               const void* Z_t, const void* H_t, const void* dY,
+               int dtype, int act,
+               void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+               int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_mlp_bwd";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0 || M % T != 0) return fail(TPM_EINVAL, "%s: F %% T or M %% T != 0", who);
+  if (dtype != TPM_BF16 && dtype != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: backward dtype BF16 or F32", who);
+  if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
+  if (dtype == TPM_F32 && dw_dtype != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 inputs give fp32 dW", who);
+  if (!Z_t || !H_t || !dY || !dW_up_t || !dW_down_t || !dX_t || !X || !W_up_t || !W_down_t)
+    return fail(TPM_EINVAL, "%s: null pointer", who);
+  const int64_t Ft = F / T;
+  const size_t need = tpm_workspace_bytes(TPM_OP_MLP_BWD, M, D, F, T, num_chunks, dtype);
+  if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
+  uint32_t* ctrl = (uint32_t*)workspace;
+  void* dZ = (char*)workspace + kCtrlBytes;
+  int32_t corder[TPM_MAX_CHUNKS];
+  if (dy_chunk_order) std::memcpy(corder, dy_chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  const int adt = dtype, zdt = dtype == TPM_F32 ? TPM_F32 : TPM_BF16;
+  // dZ = (dY . W_down^T) * act'(Z)           W_down_t [Ft, D]: op(B) = W_down^T, stored [N=Ft, K=D]
+  GemmDesc g_dz{M, Ft, D, dY, D, false, adt, nullptr, W_down_t, D, true, adt, nullptr,
+                dZ, Ft, zdt, TPM_EPI_DACT, act, const_cast<void*>(Z_t), Ft, nullptr,
+                num_chunks, corder, dy_ready, nullptr, epoch, ctrl};
+  // dW_down = H^T . dY                        H [M, Ft] stored: op(A) = H^T
+  GemmDesc g_wd{Ft, D, M, H_t, Ft, true, adt, nullptr, dY, D, false, adt, nullptr,
+                dW_down_t, D, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, epoch, ctrl};
+  // dW_up = X^T . dZ
+  GemmDesc g_wu{D, Ft, M, X, D, true, adt, nullptr, dZ, Ft, false, adt, nullptr,
+                dW_up_t, Ft, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, epoch, ctrl};
+  // dX = dZ . W_up^T                          W_up_t [D, Ft]: op(B) = W_up^T, stored [N=D, K=Ft]
+  GemmDesc g_dx{M, D, Ft, dZ, Ft, false, adt, nullptr, W_up_t, Ft, true, adt, nullptr,
+                dX_t, D, zdt, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, epoch, ctrl};
+  for (const GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (dy_ready) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  for (const GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
+    int rc = run_gemm(*g, s, who);
+    if (rc != TPM_OK) return rc;
+  }
+  return TPM_OK;
+}
+
+int partial_reduce_seqshard(int T, int64_t M, int64_t D, int rank,
+                            const void* partials, int64_t partial_stride, int64_t ld, int in_dtype,
+                            void* out, int64_t ldo, int out_dtype, void* stream) {
+  const char* who = "partial_reduce_seqshard";
+  if (T < 1) return fail(TPM_EINVAL, "%s: T < 1", who);
+  if (M < 0 || D < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (M % T != 0) return fail(TPM_EINVAL, "%s: M %% T != 0", who);
+  if (rank < -1 || rank >= T) return fail(TPM_EINVAL, "%s: bad rank", who);
+  if ((in_dtype != TPM_BF16 && in_dtype != TPM_F32) || (out_dtype != TPM_BF16 && out_dtype != TPM_F32))
+    return fail(TPM_EINVAL, "%s: dtypes BF16 or F32", who);
+  const int64_t rows = M / T;
+  if (rows == 0 || D == 0) return TPM_OK;
+  if (!partials || !out) return fail(TPM_EINVAL, "%s: null pointer", who);
+  if (ld < D || ldo < D) return fail(TPM_EINVAL, "%s: leading dimension < D", who);
+  const int64_t held_rows = rank < 0 ? rows : M;
+  if (T > 1 && partial_stride < (held_rows - 1) * ld + D)
+    return fail(TPM_EINVAL, "%s: partials overlap (partial_stride too small)", who);
+  const int64_t row0 = rank < 0 ? 0 : (int64_t)rank * rows;
+  const int in_f32 = in_dtype == TPM_F32;
+  const char* base = (const char*)partials + row0 * ld * (in_f32 ? 4 : 2);
+  hipError_t e = launch_reduce(T, rows, D, base, partial_stride, ld, in_f32, out, ldo, out_dtype == TPM_F32,
+                               (hipStream_t)stream);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+// Bandwidth-bound kernels of the path and the fp32 correctness GEMM:
+//   * sequence-sharded partial reduction (local arithmetic of the
+//     reduce-scatter after a row-parallel GEMM: "Collective GEMMs in Tensor
+//     Sequence Parallelism", section "Collective GEMMs (CGEMM)", GEMM +
+//     reduce-scatter; "Tensor and sequence parallelism", section "Derive
+//     row-parallel linear algebra": Y = sum_t Y_t)
+//   * fp8 current scaling of the intermediate activation (FP8 current-scaling
+//     recipe, "Supported quantization recipes")
+//   * control-word initialisation and chunk-ready signalling
+//   * an LDS-tiled fp32 FMA GEMM for the small fp32 configuration.
+#include "tpm_device.hpp"
+#include "tpm_internal.hpp"
+
+namespace tpm {
+
+namespace {
+
+// ------------------------------------------------------------- reduction
+// out[i, :] = sum_{t=0}^{T-1} P_t[i, :] for i < rows, with the partials at
+// partials + t * pstride.  One lane owns 8 bf16 (16 bytes) of one row: T
+// sixteen-byte nontemporal loads, fp32 sum in ascending t, one rounding to
+// bf16, one 16-byte store.  Grid-stride over (row, 8-column group).
+__global__ void __launch_bounds__(256) reduce_bf16_vec(int T, int64_t rows, int64_t D8, const uint16_t* __restrict__ P,
+                                                       int64_t pstride, int64_t ld, uint16_t* __restrict__ out,
+                                                       int64_t ldo) {
+  const int64_t total = rows * D8;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / D8;
+    const int64_t c = (v - r * D8) * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* src = P + r * ld + c;
+    for (int t = 0; t < T; ++t) {
+      const i32x4 w = __builtin_nontemporal_load((const i32x4*)(src + (int64_t)t * pstride));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)w[e];
+        s[2 * e] += bf16_to_f32((uint16_t)(u & 0xFFFFu));
+        s[2 * e + 1] += bf16_to_f32((uint16_t)(u >> 16));
+      }
+    }
+    i32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (int)((uint32_t)f32_to_bf16_rne(s[2 * e]) | ((uint32_t)f32_to_bf16_rne(s[2 * e + 1]) << 16));
+    __builtin_nontemporal_store(o, (i32x4*)(out + r * ldo + c));
+  }
+}
+
+// General element-wise form: any D, any leading dimensions, fp32 or bf16 on
+// either side (fp32 partials for the fp32 configuration).
+__global__ void __launch_bounds__(256) reduce_scalar(int T, int64_t rows, int64_t D, const void* __restrict__ P,
+                                                     int64_t pstride, int64_t ld, int in_f32, void* __restrict__ out,
+                                                     int64_t ldo, int out_f32) {
+  const int64_t total = rows * D;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / D;
+    const int64_t c = v - r * D;
+    float s = 0.f;
+    for (int t = 0; t < T; ++t) {
+      const int64_t off = (int64_t)t * pstride + r * ld + c;
+      s += in_f32 ? ((const float*)P)[off] : bf16_to_f32(((const uint16_t*)P)[off]);
+    }
+    if (out_f32) ((float*)out)[r * ldo + c] = s;
+    else ((uint16_t*)out)[r * ldo + c] = f32_to_bf16_rne(s);
+  }
+}
+
+// --------------------------------------------------------- fp8 quantiser
+// amax (fp32 bits, from the producing GEMM's epilogue) -> inv = 448/amax,
+// s = amax/448 (both 1 when amax == 0); q = e4m3(fp32(h * inv)).
+__global__ void __launch_bounds__(256) quant_e4m3(const uint16_t* __restrict__ h, int64_t M, int64_t N8, int64_t ldh,
+                                                  const float* __restrict__ amax_p, uint8_t* __restrict__ q,
+                                                  int64_t ldq, float* __restrict__ s_out) {
+  const float amax = *amax_p;
+  const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && s_out) *s_out = amax > 0.f ? amax / 448.0f : 1.0f;
+  const int64_t total = M * N8;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / N8;
+    const int64_t c = (v - r * N8) * 8;
+    const i32x4 w = __builtin_nontemporal_load((const i32x4*)(h + r * ldh + c));
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = (uint32_t)w[e];
+      const uint32_t c0 = f32_to_e4m3_rne_sat(bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv);
+      const uint32_t c1 = f32_to_e4m3_rne_sat(bf16_to_f32((uint16_t)(u >> 16)) * inv);
+      const uint32_t pair = c0 | (c1 << 8);
+      if (e < 2) lo |= pair << (16 * e);
+      else hi |= pair << (16 * (e - 2));
+    }
+    *(uint2*)(q + r * ldq + c) = make_uint2(lo, hi);
+  }
+}
+
+__global__ void ctrl_init(uint32_t* w, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+
+__global__ void signal_flag(uint32_t* flag, uint32_t value) {
+  __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// ------------------------------------------------------------ fp32 GEMM
+// 16 x 16 output tile per 256-thread block, K staged through LDS in steps
+// of 16; one output element per thread, fp32 FMA accumulation in ascending k.
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmParams p, int trans_a, int trans_b) {
+  __shared__ float As[16][17];
+  __shared__ float Bs[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int row = blockIdx.y * 16 + ty;
+  const int col = blockIdx.x * 16 + tx;
+  const float* A = (const float*)p.A;
+  const float* B = (const float*)p.B;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    {  // A tile: As[ty][tx] = op(A)[blockIdx.y*16 + ty][k0 + tx]
+      const int r = blockIdx.y * 16 + ty, k = k0 + tx;
+      float v = 0.f;
+      if (r < p.M && k < p.K) v = trans_a ? A[(int64_t)k * p.lda + r] : A[(int64_t)r * p.lda + k];
+      As[ty][tx] = v;
+    }
+    {  // B tile: Bs[ty][tx] = op(B)[k0 + ty][blockIdx.x*16 + tx]
+      const int k = k0 + ty, c = blockIdx.x * 16 + tx;
+      float v = 0.f;
+      if (k < p.K && c < p.N) v = trans_b ? B[(int64_t)c * p.ldb + k] : B[(int64_t)k * p.ldb + c];
+      Bs[ty][tx] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[kk][tx], acc);
+    __syncthreads();
+  }
+  if (row >= p.M || col >= p.N) return;
+  float s = 1.f;
+  if (p.a_scale) s *= *p.a_scale;
+  if (p.b_scale) s *= *p.b_scale;
+  float v = acc * s;
+  if (p.epi == EPI_DACT) {
+    const float z = p.aux_f32 ? ((const float*)p.aux)[(int64_t)row * p.ldaux + col]
+                              : bf16_to_f32(((const uint16_t*)p.aux)[(int64_t)row * p.ldaux + col]);
+    v *= act_grad(z, p.act);
+  } else {
+    if (p.aux) {
+      if (p.aux_f32) ((float*)p.aux)[(int64_t)row * p.ldaux + col] = v;
+      else ((uint16_t*)p.aux)[(int64_t)row * p.ldaux + col] = f32_to_bf16_rne(v);
+    }
+    v = act_fwd(v, p.act);
+  }
+  if (p.y_f32) ((float*)p.Y)[(int64_t)row * p.ldy + col] = v;
+  else ((uint16_t*)p.Y)[(int64_t)row * p.ldy + col] = f32_to_bf16_rne(v);
+}
+
+int grid_for(int64_t work, int per_block) {
+  int64_t b = (work + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > 8192) b = 8192;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, int64_t pstride, int64_t ld, int in_f32,
+                         void* out, int64_t ldo, int out_f32, hipStream_t s) {
+  if (rows <= 0 || D <= 0) return hipSuccess;
+  const bool vec = !in_f32 && !out_f32 && (D % 8 == 0) && (ld % 8 == 0) && (ldo % 8 == 0) && (pstride % 8 == 0) &&
+                   (((uintptr_t)partials & 15) == 0) && (((uintptr_t)out & 15) == 0);
+  if (vec) {
+    const int64_t work = rows * (D / 8);
+    reduce_bf16_vec<<<grid_for(work, 256), 256, 0, s>>>(T, rows, D / 8, (const uint16_t*)partials, pstride, ld,
+                                                        (uint16_t*)out, ldo);
+  } else {
+    reduce_scalar<<<grid_for(rows * D, 256), 256, 0, s>>>(T, rows, D, partials, pstride, ld, in_f32, out, ldo, out_f32);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ldh, const float* amax, uint8_t* q,
+                             int64_t ldq, float* s_out, hipStream_t s) {
+  const int64_t work = M * (N / 8);
+  quant_e4m3<<<grid_for(work, 256), 256, 0, s>>>(h, M, N / 8, ldh, amax, q, ldq, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s) {
+  ctrl_init<<<1, 256, 0, s>>>(words, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s) {
+  signal_flag<<<1, 1, 0, s>>>(flag, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s) {
+  dim3 grid((p.N + 15) / 16, (p.M + 15) / 16);
+  gemm_f32_kernel<<<grid, 256, 0, s>>>(p, trans_a ? 1 : 0, trans_b ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace tpm

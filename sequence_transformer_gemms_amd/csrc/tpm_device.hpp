@@ -1,0 +1,121 @@
+// Device-side helpers shared by the gfx950 kernels of libtpmlp: vector types,
+// bf16 / e4m3fn conversions, activations, buffer-resource loads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+
+// Raw buffer descriptor (gfx9 family: 32-bit data format, no swizzle).
+// A load whose byte offset is past `bytes` returns zeros, which is how every
+// tile edge (ragged M, N or K) is predicated.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0xFFFFFFF0u;  // an offset no descriptor here covers
+
+// 16 bytes per lane from global memory straight into LDS; lane i of the wave
+// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address `lds`.
+__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// ---------------------------------------------------------------- formats
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// OCP e4m3fn encode of an fp32 value: nearest, ties to even, saturating to
+// +-448, NaN -> 0x7F, sign kept for zero.  Integer arithmetic on the fp32
+// bits, so the result does not depend on any hardware conversion mode.
+__device__ inline uint8_t f32_to_e4m3_rne_sat(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;
+  // 448 = 1.75 * 2^8 -> fp32 bits 0x43E00000; the rounding midpoint to the
+  // (non-existent) next value 480 is 464 (0x43E80000): everything at or
+  // above 448 after rounding saturates.
+  if (a >= 0x43E00000u) return (uint8_t)(sign | 0x7E);
+  int e = (int)(a >> 23) - 127;  // unbiased exponent
+  uint8_t code;
+  if (e >= -6) {
+    // normal e4m3: keep 3 mantissa bits, round the 20 dropped bits
+    uint32_t mant = a & 0x7FFFFFu;
+    uint32_t keep = mant >> 20;
+    uint32_t rest = mant & 0xFFFFFu;
+    uint32_t half = 0x80000u;
+    uint32_t q = ((uint32_t)(e + 7) << 3) | keep;
+    if (rest > half || (rest == half && (keep & 1u))) q += 1;  // may carry into exponent
+    if (q > 0x7E) q = 0x7E;
+    code = (uint8_t)q;
+  } else {
+    // subnormal e4m3: value = m * 2^-9, m in 0..7 (m = 8 rounds up to the
+    // smallest normal, code 0x08).  x / 2^-9 = significand * 2^(e + 9).
+    if (e < -10) return (uint8_t)sign;  // below half the smallest subnormal
+    uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;  // 24-bit significand, value sig * 2^(e-23)
+    int shift = 14 - e;                          // m = sig >> shift (shift in 21..24)
+    uint32_t m = sig >> shift;
+    uint32_t rest = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rest > half || (rest == half && (m & 1u))) m += 1;
+    code = (uint8_t)m;
+  }
+  return (uint8_t)(sign | code);
+}
+
+// ------------------------------------------------------------ activations
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
+
+__device__ inline float act_fwd(float z, int act) {
+  switch (act) {
+    case ACT_RELU: return z > 0.f ? z : 0.f;
+    case ACT_GELU_ERF: return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+    case ACT_GELU_TANH: {
+      float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+      return 0.5f * z * (1.f + tanhf(u));
+    }
+    default: return z;
+  }
+}
+
+__device__ inline float act_grad(float z, int act) {
+  switch (act) {
+    case ACT_RELU: return z > 0.f ? 1.f : 0.f;
+    case ACT_GELU_ERF: {
+      float cdf = 0.5f * (1.f + erff(z * 0.70710678118654752f));
+      float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+      return cdf + z * pdf;
+    }
+    case ACT_GELU_TANH: {
+      float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+      float t = tanhf(u);
+      float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
+      return 0.5f * (1.f + t) + 0.5f * z * (1.f - t * t) * du;
+    }
+    default: return 1.f;
+  }
+}
+
+}  // namespace tpm

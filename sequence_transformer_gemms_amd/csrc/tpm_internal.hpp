@@ -1,0 +1,52 @@
+// Private interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpm {
+
+constexpr int kMaxGroups = 256;  // chunks or destination ranges per call
+
+// One GEMM launch: Y[M,N] = epilogue(op(A)[M,K] . op(B)[K,N]).
+// Rows of Y are cut into `num_groups` equal groups of `group_rows` rows
+// (sequence chunks, or destination token ranges); tiles never straddle a
+// group, and groups are visited in `order`.
+struct GemmParams {
+  const void* A;
+  const void* B;
+  void* Y;
+  void* aux;                 // FWD: pre-activation save (or null); DACT: Z input
+  const float* a_scale;      // device fp32 dequant factor or null (= 1)
+  const float* b_scale;
+  float* amax;               // device: atomic max of |Y as stored| (or null)
+  const uint32_t* ready;     // device, per group: tile waits for ready[g] >= epoch (or null)
+  uint32_t* done;            // device, per group: set to epoch when all its tiles are stored
+  uint32_t* err;             // device error word (watchdog), needed when ready != null
+  uint32_t* group_cnt;       // device per-group finished-tile counters (zeroed per call)
+  uint32_t a_bytes, b_bytes;  // extents of A and B for the buffer descriptors
+  int64_t lda, ldb, ldy, ldaux;  // elements
+  int M, N, K;
+  int group_rows, num_groups;
+  int mt_per_group, nt, tiles_per_group, total_tiles, band_m;
+  uint32_t epoch;
+  uint32_t wait_limit;       // polls before a wait gives up (watchdog)
+  int act, epi, y_f32, aux_f32;
+  int16_t order[kMaxGroups];
+};
+
+enum { EPI_FWD = 0, EPI_DACT = 1 };
+
+// kernels' launchers (return hipError_t of the launch)
+hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
+hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s);
+hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, int64_t pstride,
+                         int64_t ld, int in_f32, void* out, int64_t ldo, int out_f32, hipStream_t s);
+hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ldh, const float* amax,
+                             uint8_t* q, int64_t ldq, float* s_out, hipStream_t s);
+hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
+
+constexpr int kTileM = 256, kTileN = 256;
+
+}  // namespace tpm

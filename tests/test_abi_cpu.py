@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every symbol include/tpmlp.h declares,
+and rejects bad arguments on the host before touching a device (no GPU
+needed: every call here fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sequence_transformer_gemms_amd", "libtpmlp.so")
+HDR = os.path.join(ROOT, "include", "tpmlp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libtpmlp.so not built")
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    from sequence_transformer_gemms_amd import _abi
+    names = declared_functions()
+    assert set(names) >= {"seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "partial_reduce_seqshard"}
+    for n in names:
+        assert hasattr(_abi.lib, n), n
+    assert set(_abi.EXPORTS) == set(names)
+    assert b"gfx950" in _abi.lib.tpm_version()
+
+
+def test_workspace_sizes():
+    from sequence_transformer_gemms_amd import _abi
+    ws = _abi.lib.tpm_workspace_bytes
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 128, 128, 128, 1, 1, _abi.BF16) == 2048
+    # bwd keeps dZ [M, F/T] bf16 after the 2 KiB control block
+    assert ws(_abi.OP_MLP_BWD, 4096, 8192, 28672, 8, 8, _abi.BF16) == 2048 + 4096 * 3584 * 2
+    # fp8 fwd keeps the quantised H [M, F/T]
+    assert ws(_abi.OP_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048 + 8192 * 6656
+    assert ws(_abi.OP_MLP_FWD, 8192, 8192, 28672, 8, 8, _abi.BF16) == 2048
+
+
+FAKE = 1 << 20  # a non-null, 16-byte-aligned address that is never dereferenced
+
+
+def gemm(**kw):
+    from sequence_transformer_gemms_amd import _abi
+    a = dict(M=256, N=256, K=256, A=FAKE, lda=256, ta=0, adt=_abi.BF16, asc=None,
+             B=FAKE, ldb=256, tb=0, bdt=_abi.BF16, bsc=None, Y=FAKE, ldy=256, ydt=_abi.BF16,
+             epi=0, act=0, aux=None, ldaux=0, amax=None, C=1, order=None, ready=None, epoch=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return _abi.lib.seq_chunk_gemm(a["M"], a["N"], a["K"], a["A"], a["lda"], a["ta"], a["adt"], a["asc"],
+                                   a["B"], a["ldb"], a["tb"], a["bdt"], a["bsc"], a["Y"], a["ldy"], a["ydt"],
+                                   a["epi"], a["act"], a["aux"], a["ldaux"], a["amax"], a["C"], a["order"],
+                                   a["ready"], a["epoch"], a["ws"], a["wsb"], None)
+
+
+def test_seq_chunk_gemm_validation():
+    from sequence_transformer_gemms_amd import _abi as X
+    assert gemm(M=-1) == X.EINVAL
+    assert gemm(C=3) == X.EINVAL                          # 256 % 3 != 0
+    assert gemm(C=0) == X.EINVAL
+    assert gemm(C=4, order=X.int_array([0, 1, 1, 3])) == X.EINVAL  # not a permutation
+    assert gemm(lda=100) == X.EINVAL                      # lda < K
+    assert gemm(bdt=X.F32) == X.EINVAL                    # mixed operand dtypes
+    assert gemm(ydt=X.FP8_E4M3) == X.EINVAL
+    assert gemm(epi=X.EPI_DACT) == X.EINVAL               # DACT needs Z
+    assert gemm(act=9) == X.EINVAL
+    assert gemm(N=100) == X.EUNSUPPORTED                  # N % 8
+    assert gemm(K=100, lda=256) == X.EUNSUPPORTED         # K % 8
+    assert gemm(A=FAKE + 2) == X.EUNSUPPORTED             # misaligned
+    assert gemm(adt=X.FP8_E4M3, bdt=X.FP8_E4M3, tb=0) == X.EUNSUPPORTED  # fp8 wants K-major B
+    assert gemm(ready=FAKE) == X.EWORKSPACE               # flags need the workspace
+    assert gemm(adt=X.F32, bdt=X.F32, ydt=X.BF16) == X.EUNSUPPORTED
+    assert "seq_chunk_gemm" in X.last_error()
+
+
+def test_mlp_and_reduce_validation():
+    from sequence_transformer_gemms_amd import _abi as X
+    L = X.lib
+    args = lambda **kw: dict(dict(M=512, D=256, F=1024, T=4, rank=0), **kw)
+
+    def fwd(**kw):
+        a = args(**kw)
+        return L.tp_mlp_fwd(a["M"], a["D"], a["F"], a["T"], a["rank"], FAKE, FAKE, FAKE, X.BF16, None,
+                            X.ACT_GELU_ERF, None, FAKE, FAKE, None, 4, None, None, 0, None, None, None, 0, None)
+    assert fwd(F=1002) == X.EINVAL      # F % T
+    assert fwd(F=1000) == X.EUNSUPPORTED  # F/T = 250 is not a multiple of 8
+    assert fwd(M=510) == X.EINVAL       # M % T
+    assert fwd(rank=4) == X.EINVAL
+    assert fwd(T=0) == X.EINVAL
+    rc = L.tp_mlp_bwd(512, 256, 1024, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, X.BF16, X.ACT_GELU_ERF,
+                      FAKE, FAKE, FAKE, X.BF16, 4, None, None, 0, None, 0, None)
+    assert rc == X.EWORKSPACE
+    assert L.partial_reduce_seqshard(8, 100, 64, 0, FAKE, 6400, 64, X.BF16, FAKE, 64, X.BF16, None) == X.EINVAL
+    assert L.partial_reduce_seqshard(8, 64, 64, 8, FAKE, 4096, 64, X.BF16, FAKE, 64, X.BF16, None) == X.EINVAL
+    assert L.partial_reduce_seqshard(8, 64, 64, 0, FAKE, 100, 64, X.BF16, FAKE, 64, X.BF16, None) == X.EINVAL
+    assert L.partial_reduce_seqshard(8, 64, 64, 0, FAKE, 4096, 32, X.BF16, FAKE, 64, X.BF16, None) == X.EINVAL
+    # empty input: nothing to do, nothing enqueued
+    assert L.partial_reduce_seqshard(8, 0, 64, 0, None, 0, 64, X.BF16, None, 64, X.BF16, None) == X.OK

@@ -1,0 +1,375 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.  Bars: bit-exact for integer-valued inputs and for
+chunk-order permutations; max |gpu - ref| / (1 + |ref|) <= 1e-4 (fp32),
+2e-2 (bf16), 6e-2 (fp8 e4m3)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+from oracle import formats, ops
+from tests._util import TOL, f64, nerr
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import sequence_transformer_gemms_amd as tpm
+    from sequence_transformer_gemms_amd import _abi
+
+
+def dev_bf16(x):
+    return si.to_bf16(x).cuda()
+
+
+def dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ reduction
+@pytest.mark.parametrize("D", [1024, 136])
+def test_reduce_bf16_all_ranks(D):
+    T, M = 4, 64
+    parts = np.stack([si.normal_f32((M, D), 100 + t) for t in range(T)])
+    P = si.to_bf16(parts).cuda()
+    ref_in = f64(P)
+    outs = []
+    for r in range(T):
+        out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+        tpm.partial_reduce_seqshard(P, out, T=T, rank=r)
+        outs.append(out)
+    sync()
+    for r in range(T):
+        assert nerr(outs[r], ops.partial_reduce_seqshard(ref_in, r)) <= TOL["bf16"]
+    # concatenation over ranks = full sum (all-reduce = reduce-scatter + all-gather)
+    cat = np.concatenate([f64(o) for o in outs])
+    assert nerr(cat, ref_in.sum(axis=0)) <= TOL["bf16"]
+
+
+def test_reduce_integer_exact_and_receive_buffer_layout():
+    T, M, D = 8, 128, 256
+    parts = np.stack([si.small_ints((M, D), 200 + t, -15, 15) for t in range(T)])
+    P = si.to_bf16(parts).cuda()
+    out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+    tpm.partial_reduce_seqshard(P, out, T=T, rank=5)
+    # receive-buffer layout [T, M/T, D] (rank = -1)
+    recv = P[:, 5 * (M // T):6 * (M // T), :].contiguous()
+    out2 = torch.empty_like(out)
+    tpm.partial_reduce_seqshard(recv, out2, T=T, rank=-1)
+    sync()
+    ref = ops.partial_reduce_seqshard(parts.astype(np.float64), 5)
+    assert np.array_equal(f64(out), ref)          # |sum| <= 120 < 256: exact in bf16
+    assert torch.equal(out, out2)
+
+
+def test_reduce_fp32():
+    T, M, D = 4, 8, 32
+    parts = np.stack([si.uniform_f32((M, D), 300 + t) for t in range(T)])
+    P = dev_f32(parts)
+    out = torch.empty(M // T, D, dtype=torch.float32, device="cuda")
+    tpm.partial_reduce_seqshard(P, out, T=T, rank=1)
+    sync()
+    assert nerr(out, ops.partial_reduce_seqshard(parts.astype(np.float64), 1)) <= TOL["f32"]
+
+
+def test_reduce_c3_full_size():
+    # 8 seeded bf16 partials [8192, 8192] -> rank slice [1024, 8192]
+    T, M, D = 8, 8192, 8192
+    P = torch.empty(T, M, D, dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        P[t] = dev_bf16(si.normal_f32((M, D), 100 + t))
+    out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+    for r in (0, 3, 7):
+        tpm.partial_reduce_seqshard(P, out, T=T, rank=r)
+        sync()
+        held = np.stack([f64(P[t, r * (M // T):(r + 1) * (M // T)]) for t in range(T)])
+        assert nerr(out, ops.partial_reduce_seqshard(held, -1)) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ GEMM
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _operands(M, N, K, ta, tb, gen, seed):
+    a = gen((M, K), seed)
+    b = gen((K, N), seed + 1)
+    A = np.ascontiguousarray(a.T) if ta else a
+    B = np.ascontiguousarray(b.T) if tb else b
+    return a, b, A, B
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_gemm_bf16_integer_exact_all_layouts(ta, tb):
+    # small integers: every fp32 partial sum is exact, so the result is
+    # independent of tiling and must equal the oracle bit for bit
+    M, N, K = (296 if ta else 300), 264, 200
+    gen = lambda s, seed: si.small_ints(s, seed)
+    a, b, A, B = _operands(M, N, K, ta, tb, gen, 11)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(dev_bf16(A), dev_bf16(B), Y, trans_a=ta, trans_b=tb, M=M, N=N, K=K)
+    sync()
+    ref, _ = ops.seq_chunk_gemm(A, B, trans_a=ta, trans_b=tb)
+    assert np.array_equal(f64(Y), ref)
+
+
+@pytest.mark.parametrize("act", [_abi.ACT_NONE, _abi.ACT_RELU, _abi.ACT_GELU_ERF, _abi.ACT_GELU_TANH]
+                         if torch.cuda.is_available() else [])
+def test_gemm_bf16_activations_and_zsave(act):
+    M, N, K = 640, 392, 328
+    a, b, A, B = _operands(M, N, K, False, False, lambda s, seed: si.normal_f32(s, seed, 0.5), 21)
+    Ad, Bd = dev_bf16(A), dev_bf16(B)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(Ad, Bd, Y, act=act, aux=Z)
+    sync()
+    y, z = ops.seq_chunk_gemm(f64(Ad), f64(Bd), act=act)
+    assert nerr(Y, y) <= TOL["bf16"]
+    assert nerr(Z, z) <= TOL["bf16"]
+
+
+def test_gemm_chunk_order_is_bitwise_invariant():
+    M, N, K = 1024, 512, 256
+    a, b, A, B = _operands(M, N, K, False, False, lambda s, seed: si.normal_f32(s, seed), 31)
+    Ad, Bd = dev_bf16(A), dev_bf16(B)
+    outs = []
+    for C, order in ((1, None), (4, [0, 3, 2, 1]), (8, [5, 0, 7, 1, 6, 2, 4, 3]), (16, list(range(15, -1, -1)))):
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tpm.seq_chunk_gemm(Ad, Bd, Y, act=_abi.ACT_GELU_ERF, num_chunks=C, chunk_order=order)
+        outs.append(Y)
+    sync()
+    for Y in outs[1:]:
+        assert torch.equal(Y, outs[0])
+    y, _ = ops.seq_chunk_gemm(f64(Ad), f64(Bd), act=_abi.ACT_GELU_ERF)
+    assert nerr(outs[0], y) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("act", [_abi.ACT_RELU, _abi.ACT_GELU_ERF] if torch.cuda.is_available() else [])
+def test_gemm_dact_epilogue(act):
+    M, N, K = 520, 256, 384
+    a, b, A, B = _operands(M, N, K, False, True, lambda s, seed: si.normal_f32(s, seed), 41)
+    Ad, Bd = dev_bf16(A), dev_bf16(B)
+    Zd = dev_bf16(si.normal_f32((M, N), 43))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(Ad, Bd, Y, trans_b=True, epilogue=_abi.EPI_DACT, act=act, aux=Zd)
+    sync()
+    y, _ = ops.seq_chunk_gemm(f64(Ad), f64(Bd), trans_b=True, act=act, dact_z=f64(Zd))
+    assert nerr(Y, y) <= TOL["bf16"]
+
+
+def test_gemm_empty_and_k_zero():
+    A = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(A, B, Y)
+    A = torch.zeros(64, 0, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    Y = torch.full((64, 64), 7.0, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(A, B, Y, M=64, N=64, K=0)
+    sync()
+    assert torch.count_nonzero(Y).item() == 0
+
+
+def test_gemm_fp8_integer_exact_and_scaled():
+    M, N, K = 300, 264, 320
+    a = si.small_ints((M, K), 51, -4, 4)
+    bt = si.small_ints((N, K), 52, -4, 4)        # B stored [N, K] (K-major)
+    Aq, Bq = si.to_e4m3_exact(a).cuda(), si.to_e4m3_exact(bt).cuda()
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(Aq, Bq, Y, trans_b=True)
+    sync()
+    assert np.array_equal(f64(Y), a.astype(np.float64) @ bt.astype(np.float64).T)
+    # normal values with per-tensor current scales
+    x = si.normal_f32((M, K), 53)
+    w = si.normal_f32((N, K), 54, 0.02)
+    xq, sx = si.to_e4m3_current(x)
+    wq, sw = si.to_e4m3_current(w)
+    scales = dev_f32(np.array([sx, sw], dtype=np.float32))
+    Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    tpm.seq_chunk_gemm(xq.cuda(), wq.cuda(), Yb, trans_b=True, a_scale=scales[0:1], b_scale=scales[1:2],
+                       act=_abi.ACT_GELU_ERF, amax_out=amax, workspace=ws)
+    sync()
+    y, _ = ops.seq_chunk_gemm(f64(xq), f64(wq), trans_b=True, a_scale=sx, b_scale=sw, act=_abi.ACT_GELU_ERF)
+    assert nerr(Yb, y) <= TOL["fp8"]
+    assert amax.item() == float(np.max(np.abs(f64(Yb))))
+
+
+# ------------------------------------------------------------- MLP, fp32 (C1)
+@pytest.mark.parametrize("generator", ["page3", "pcg"])
+def test_c1_tiny_mlp_fp32_fwd_bwd(generator):
+    c = si.c1_tiny_mlp(generator)
+    m, d, f, T = c["m"], c["d"], c["f"], c["t"]
+    x, a, b = c["x"], c["a"], c["b"]
+    X = dev_f32(x)
+    P_all = torch.empty(T, m, d, dtype=torch.float32, device="cuda")
+    Zs, Hs = [], []
+    for t in range(T):
+        wu = dev_f32(ops.col_block(a, T, t))
+        wd = dev_f32(ops.row_block(b, T, t))
+        Z = torch.empty(m, f // T, dtype=torch.float32, device="cuda")
+        H = torch.empty_like(Z)
+        tpm.tp_mlp_fwd(X, wu, wd, H, P_all[t], T=T, rank=t, act=_abi.ACT_RELU, Z_t=Z)
+        Zs.append(Z)
+        Hs.append(H)
+    # all-reduce = reduce-scatter (each rank's slice) + all-gather
+    Y = torch.empty(m, d, dtype=torch.float32, device="cuda")
+    for r in range(T):
+        tpm.partial_reduce_seqshard(P_all, Y[r * (m // T):(r + 1) * (m // T)], T=T, rank=r)
+    sync()
+    un = ops.mlp_unsharded(x.astype(np.float64), a.astype(np.float64), b.astype(np.float64), ops.ACT_RELU)
+    for t in range(T):
+        ref = ops.tp_mlp_fwd(x, ops.col_block(a, T, t), ops.row_block(b, T, t), ops.ACT_RELU)
+        assert nerr(P_all[t], ref["P"]) <= TOL["f32"]
+    assert nerr(Y, un["Y"]) <= TOL["f32"]
+    # backward with the page's loss 1/2 ||Y||^2 -> dY = Y
+    dY = Y.clone()
+    dX_all = torch.empty(T, m, d, dtype=torch.float32, device="cuda")
+    dWu, dWd = [], []
+    for t in range(T):
+        wu = dev_f32(ops.col_block(a, T, t))
+        wd = dev_f32(ops.row_block(b, T, t))
+        gu = torch.empty(d, f // T, dtype=torch.float32, device="cuda")
+        gd = torch.empty(f // T, d, dtype=torch.float32, device="cuda")
+        ws = tpm.alloc_workspace(_abi.OP_MLP_BWD, m, d, f, T, 1, _abi.F32)
+        tpm.tp_mlp_bwd(X, wu, wd, Zs[t], Hs[t], dY, gu, gd, dX_all[t], T=T, rank=t, act=_abi.ACT_RELU,
+                       workspace=ws)
+        dWu.append(gu)
+        dWd.append(gd)
+    dX = torch.empty(m, d, dtype=torch.float32, device="cuda")
+    for r in range(T):
+        tpm.partial_reduce_seqshard(dX_all, dX[r * (m // T):(r + 1) * (m // T)], T=T, rank=r)
+    sync()
+    dy = f64(dY)
+    unb = ops.mlp_unsharded_bwd(x.astype(np.float64), a.astype(np.float64), b.astype(np.float64), un["pre"], dy,
+                                ops.ACT_RELU)
+    for t in range(T):
+        assert nerr(dWu[t], ops.col_block(unb["dA"], T, t)) <= TOL["f32"]
+        assert nerr(dWd[t], ops.row_block(unb["dB"], T, t)) <= TOL["f32"]
+    assert nerr(dX, unb["dX"]) <= TOL["f32"]
+
+
+# ------------------------------------------------------------- MLP, bf16
+def _mlp_inputs(M, D, F, T, seed=1, sx=1.0, sw=0.02):
+    Ft = F // T
+    x = si.normal_f32((M, D), seed, sx)
+    wu = si.normal_f32((D, Ft), seed + 1, sw)
+    wd = si.normal_f32((Ft, D), seed + 2, sw)
+    return x, wu, wd
+
+
+@pytest.mark.parametrize("act", [_abi.ACT_GELU_ERF, _abi.ACT_RELU] if torch.cuda.is_available() else [])
+def test_mlp_fwd_bwd_bf16_small(act):
+    M, D, F, T, C = 512, 256, 1024, 4, 8
+    x, wu, wd = _mlp_inputs(M, D, F, T, sw=0.05)
+    X, WU, WD = dev_bf16(x), dev_bf16(wu), dev_bf16(wd)
+    Ft = F // T
+    Z = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    H = torch.empty_like(Z)
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.BF16)
+    done = torch.zeros(T, dtype=torch.int32, device="cuda")
+    tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=1, act=act, Z_t=Z, num_chunks=C, epoch=3, range_done=done,
+                   workspace=ws)
+    sync()
+    ref = ops.tp_mlp_fwd(f64(X), f64(WU), f64(WD), act, store="bf16")
+    assert nerr(Z, ref["Z"]) <= TOL["bf16"]
+    assert nerr(H, ref["H"]) <= TOL["bf16"]
+    assert nerr(P, ref["P"]) <= TOL["bf16"]
+    assert done.tolist() == [3] * T          # every destination range published
+    dy = si.normal_f32((M, D), 4)
+    dY = dev_bf16(dy)
+    gu = torch.empty(D, Ft, dtype=torch.bfloat16, device="cuda")
+    gd = torch.empty(Ft, D, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    wsb = tpm.alloc_workspace(_abi.OP_MLP_BWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_mlp_bwd(X, WU, WD, Z, H, dY, gu, gd, dX, T=T, rank=1, act=act, num_chunks=C, workspace=wsb)
+    sync()
+    rb = ops.tp_mlp_bwd(f64(X), f64(WU), f64(WD), f64(Z), f64(H), f64(dY), act, store="bf16")
+    assert nerr(gu, rb["dW_up"]) <= TOL["bf16"]
+    assert nerr(gd, rb["dW_down"]) <= TOL["bf16"]
+    assert nerr(dX, rb["dX"]) <= TOL["bf16"]
+    # the workspace holds dZ after the call
+    dZ = wsb[2048:2048 + M * Ft * 2].view(torch.bfloat16).view(M, Ft)
+    assert nerr(dZ, rb["dZ"]) <= TOL["bf16"]
+
+
+def test_mlp_fwd_fp8_small():
+    M, D, F, T, C = 512, 512, 2048, 4, 8
+    Ft = F // T
+    x = si.normal_f32((M, D), 1)
+    wu = si.normal_f32((D, Ft), 2, 0.02)
+    wd = si.normal_f32((Ft, D), 3, 0.02)
+    xq, sx = si.to_e4m3_current(x)
+    wuq, su = si.to_e4m3_current(np.ascontiguousarray(wu.T))   # K-major copies of the weights
+    wdq, sd = si.to_e4m3_current(np.ascontiguousarray(wd.T))
+    scales = dev_f32(np.array([sx, su, sd], dtype=np.float32))
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    sH = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.FP8_E4M3)
+    tpm.tp_mlp_fwd(xq.cuda(), wuq.cuda(), wdq.cuda(), H, P, T=T, rank=0, act=_abi.ACT_GELU_ERF, scales=scales,
+                   h_scale_out=sH, num_chunks=C, workspace=ws)
+    sync()
+    r = ops.tp_mlp_fwd_fp8(f64(xq), sx, f64(wuq).T, su, f64(wdq).T, sd, ops.ACT_GELU_ERF)
+    assert nerr(H, r["H"]) <= TOL["fp8"]
+    assert nerr(P, r["P"]) <= TOL["fp8"]
+    hq = ws[2048:2048 + M * Ft].cpu().numpy().reshape(M, Ft)
+    flips = np.mean(hq != r["Hq_codes"])
+    assert flips < 1e-2, flips
+    assert abs(sH.item() - r["sH"]) <= 1e-2 * r["sH"]
+
+
+# --------------------------------------------- chunk arrival on a side stream
+def test_chunks_arrive_from_side_stream():
+    M, N, K, C = 2048, 1024, 512, 8
+    x = si.normal_f32((M, K), 61)
+    w = si.normal_f32((K, N), 62, 0.05)
+    Xsrc, W = dev_bf16(x), dev_bf16(w)
+    ref = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(Xsrc, W, ref, act=_abi.ACT_GELU_ERF)
+    sync()
+    Xdst = torch.zeros_like(Xsrc)
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    Y = torch.empty_like(ref)
+    order = si.ring_chunk_order(4, C, 2)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    rows = M // C
+    epoch = 1
+    tpm.seq_chunk_gemm(Xdst, W, Y, act=_abi.ACT_GELU_ERF, num_chunks=C, chunk_order=order, chunk_ready=flags,
+                       epoch=epoch, workspace=ws, stream=main)
+    with torch.cuda.stream(side):
+        for c in order:
+            Xdst[c * rows:(c + 1) * rows].copy_(Xsrc[c * rows:(c + 1) * rows])
+            tpm.signal_chunk(flags, c, epoch, stream=side)
+    sync()
+    assert tpm.poll_device_error(ws) == 0
+    assert torch.equal(Y, ref)
+
+
+def test_watchdog_reports_timeout_and_kernel_exits():
+    M, N, K, C = 512, 256, 128, 2
+    X = dev_bf16(si.normal_f32((M, K), 71))
+    W = dev_bf16(si.normal_f32((K, N), 72))
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.set_wait_limit(2000)
+    try:
+        # chunk 1 is never signalled; chunk 0 is
+        tpm.signal_chunk(flags, 0, 5)
+        tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_ready=flags, epoch=5, workspace=ws)
+        sync()
+        assert tpm.poll_device_error(ws) == _abi.ETIMEOUT
+    finally:
+        tpm.set_wait_limit(1 << 22)
+    # the next gated call clears the error word
+    flags.fill_(5)
+    tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_ready=flags, epoch=5, workspace=ws)
+    sync()
+    assert tpm.poll_device_error(ws) == 0

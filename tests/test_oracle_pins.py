@@ -302,3 +302,24 @@ def test_chunk_and_range_orders():
     o = si.ring_chunk_order(8, 16, 0)
     assert o[:4] == [0, 1, 14, 15] and o[-2:] == [2, 3] and sorted(o) == list(range(16))
     assert si.dest_range_order(8, 0) == [1, 2, 3, 4, 5, 6, 7, 0]
+
+
+def test_store_bf16_rounds_only_the_consumed_intermediate():
+    g = np.random.default_rng(8)
+    M, D, Ft = 16, 32, 24
+    # integer-valued activations are exact in bf16: rounding them changes nothing
+    x = g.integers(-3, 4, size=(M, D)).astype(np.float64)
+    wu = g.integers(-2, 3, size=(D, Ft)).astype(np.float64)
+    wd = g.integers(-2, 3, size=(Ft, D)).astype(np.float64)
+    a = ops.tp_mlp_fwd(x, wu, wd, ops.ACT_RELU, store="bf16")
+    b = ops.tp_mlp_fwd(x, wu, wd, ops.ACT_RELU)
+    assert np.array_equal(a["P"], b["P"]) and np.array_equal(a["H"], b["H"])
+    # general values: P is the product of the rounded H, and Z/H are unrounded
+    x = g.standard_normal((M, D))
+    a = ops.tp_mlp_fwd(x, wu * 0.1, wd * 0.1, ops.ACT_GELU_ERF, store="bf16")
+    assert np.array_equal(a["P"], formats.round_bf16(a["H"]) @ (wd * 0.1))
+    assert np.array_equal(a["Z"], x @ (wu * 0.1))
+    dy = g.standard_normal((M, D))
+    r = ops.tp_mlp_bwd(x, wu, wd, a["Z"], a["H"], dy, ops.ACT_GELU_ERF, store="bf16")
+    assert np.array_equal(r["dW_up"], x.T @ formats.round_bf16(r["dZ"]))
+    assert np.array_equal(r["dW_down"], a["H"].T @ dy)
