@@ -21,6 +21,8 @@
 // four consecutive output columns of one row: stores are 8 or 16 bytes wide.
 // fp8 (OCP e4m3fn) operands take the same 128-byte-per-row K-major staging
 // (128 K elements per step) and v_mfma_f32_32x32x64_f8f6f4.
+#include <type_traits>
+
 #include "tpm_device.hpp"
 #include "tpm_internal.hpp"
 
@@ -31,7 +33,6 @@ namespace {
 constexpr int BM = kTileM, BN = kTileN;
 constexpr int THREADS = 256;
 constexpr int TILE_BYTES = 32768;            // one operand stage: 256 rows x 128 bytes of K
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // A + B
 
 // K-major tile: 256 rows x 8 chunks of 16 bytes; chunk c of row r is stored
 // at slot c ^ swz_k(r), which spreads the 32 rows read by one ds_read_b128
@@ -153,7 +154,7 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ bool wait_group(const GemmParams& p, int g) {
+__device__ __forceinline__ bool wait_group(const GemmParams& p, int g) {
   __shared__ int timed_out;
   if (threadIdx.x == 0) {
     int bad = 0;
@@ -174,11 +175,76 @@ __device__ bool wait_group(const GemmParams& p, int g) {
   return timed_out != 0;
 }
 
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Epilogue of four consecutive output columns (row, col..col+3) of one lane.
+__device__ __forceinline__ void epi_quad(const GemmParams& p, f32x4 v, int row, int col, float& lmax) {
+  if (p.epi == EPI_DACT) {
+    f32x4 z;
+    if (p.aux_f32) {
+      z = *(const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
+    } else {
+      const uint2 zz = *(const uint2*)((const uint16_t*)p.aux + (int64_t)row * p.ldaux + col);
+      z[0] = bf16_to_f32((uint16_t)(zz.x & 0xFFFFu));
+      z[1] = bf16_to_f32((uint16_t)(zz.x >> 16));
+      z[2] = bf16_to_f32((uint16_t)(zz.y & 0xFFFFu));
+      z[3] = bf16_to_f32((uint16_t)(zz.y >> 16));
+    }
+    v[0] *= act_grad(z[0], p.act);
+    v[1] *= act_grad(z[1], p.act);
+    v[2] *= act_grad(z[2], p.act);
+    v[3] *= act_grad(z[3], p.act);
+  } else {
+    if (p.aux) {
+      if (p.aux_f32) {
+        *(f32x4*)((float*)p.aux + (int64_t)row * p.ldaux + col) = v;
+      } else {
+        uint2 zz;
+        zz.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        zz.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *(uint2*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
+      }
+    }
+    if (p.act != ACT_NONE) {
+      v[0] = act_fwd(v[0], p.act);
+      v[1] = act_fwd(v[1], p.act);
+      v[2] = act_fwd(v[2], p.act);
+      v[3] = act_fwd(v[3], p.act);
+    }
+  }
+  if (p.y_f32) {
+    *(f32x4*)((float*)p.Y + (int64_t)row * p.ldy + col) = v;
+    if (p.amax) lmax = fmaxf(lmax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  } else {
+    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    uint2 yy;
+    yy.x = b0 | (b1 << 16);
+    yy.y = b2 | (b3 << 16);
+    *(uint2*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;
+    if (p.amax) {
+      const float m01 = fmaxf(fabsf(bf16_to_f32((uint16_t)b0)), fabsf(bf16_to_f32((uint16_t)b1)));
+      const float m23 = fmaxf(fabsf(bf16_to_f32((uint16_t)b2)), fabsf(bf16_to_f32((uint16_t)b3)));
+      lmax = fmaxf(lmax, fmaxf(m01, m23));
+    }
+  }
+}
+
 template <bool FP8, bool AK, bool BKM>
 __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = 128 / ESZ;  // K elements per staged step (128 bytes per row)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -205,121 +271,82 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    issue_tile<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, 0, p.K, smem);
-    issue_tile<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, 0, p.K, smem + TILE_BYTES);
+    // K loop over two LDS stages (A and B tiles of 32 KB each per stage).
+    auto issue = [&](char* As, char* Bs, int k0) {
+      issue_tile<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, As);
+      issue_tile<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, k0, p.K, Bs);
+    };
+    // One K step, software-pipelined: the fragments of substep kk+1 are read
+    // from LDS before the MFMAs of substep kk are issued (sched_barrier keeps
+    // the scheduler from sinking them), and the global loads of the next
+    // stage go out right after the first fragment reads.
+    using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
+    constexpr int KSUB = FP8 ? 2 : 4;
+    auto read_set = [&](const char* As, const char* Bs, int kk, Frag (&af)[4], Frag (&bfr)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FP8) af[i] = read_frag_fp8(As, wm + 32 * i, kk);
+        else af[i] = read_frag<AK>(As, wm + 32 * i, kk);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8) bfr[j] = read_frag_fp8(Bs, wn + 32 * j, kk);
+        else bfr[j] = read_frag<BKM>(Bs, wn + 32 * j, kk);
+      }
+    };
+    auto mfma_set = [&](const Frag (&af)[4], const Frag (&bfr)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (FP8)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
+    };
+    // The restrict qualifiers tell the compiler that the two stages do not
+    // overlap, so the fragment reads do not wait for the loads just issued.
+    auto iteration = [&](const char* __restrict__ cur, char* __restrict__ nxt, int k_next) {
+      Frag fa[2][4], fb[2][4];
+      read_set(cur, cur + TILE_BYTES, 0, fa[0], fb[0]);
+      if (k_next >= 0) issue(nxt, nxt + TILE_BYTES, k_next);
+      static_for<KSUB>([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        if constexpr (kk + 1 < KSUB) read_set(cur, cur + TILE_BYTES, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_set(fa[kk & 1], fb[kk & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+
+    issue(smem, smem + TILE_BYTES, 0);
     wait_vmem();
     __syncthreads();
-
     for (int kt = 0; kt < nk; ++kt) {
-      char* cur = smem + (kt & 1) * STAGE_BYTES;
-      if (kt + 1 < nk) {
-        char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
-        issue_tile<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, (kt + 1) * KSTEP, p.K, nxt);
-        issue_tile<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, (kt + 1) * KSTEP, p.K, nxt + TILE_BYTES);
-      }
-      if constexpr (FP8) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          i32x8 af[4], bfr[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) af[i] = read_frag_fp8(cur, wm + 32 * i, kk);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bfr[j] = read_frag_fp8(cur + TILE_BYTES, wn + 32 * j, kk);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          bf16x8 af[4], bfr[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) af[i] = read_frag<AK>(cur, wm + 32 * i, kk);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bfr[j] = read_frag<BKM>(cur + TILE_BYTES, wn + 32 * j, kk);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        }
-      }
+      char* cur = smem + (kt & 1) * (2 * TILE_BYTES);
+      char* nxt = smem + ((kt + 1) & 1) * (2 * TILE_BYTES);
+      iteration(cur, nxt, kt + 1 < nk ? (kt + 1) * KSTEP : -1);
       wait_vmem();
       __syncthreads();
     }
 
     // ---- epilogue: lane holds rows m0+wm+32i+lane%32, columns
-    //      n0+wn+32j+8q+4*(lane/32)+{0..3} in acc[i][j][4q..4q+3]
+    //      n0+wn+32j+8q+4*(lane/32)+{0..3} in acc[i][j][4q..4q+3].  Every
+    //      index is a compile-time constant so the accumulators stay in
+    //      registers.
     float lmax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    static_for<64>([&](auto ijq) {
+      constexpr int i = decltype(ijq)::value / 16;
+      constexpr int j = (decltype(ijq)::value / 4) % 4;
+      constexpr int q = decltype(ijq)::value % 4;
       const int row = tl.m0 + wm + 32 * i + (lane & 31);
-      const bool row_ok = row < tl.m_end;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tl.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
-          if (!row_ok || col >= p.N) continue;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * scale;
-          if (p.epi == EPI_DACT) {
-            float z[4];
-            if (p.aux_f32) {
-              const f32x4 zz = *(const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
-              for (int e = 0; e < 4; ++e) z[e] = zz[e];
-            } else {
-              const uint2 zz = *(const uint2*)((const uint16_t*)p.aux + (int64_t)row * p.ldaux + col);
-              z[0] = bf16_to_f32((uint16_t)(zz.x & 0xFFFF));
-              z[1] = bf16_to_f32((uint16_t)(zz.x >> 16));
-              z[2] = bf16_to_f32((uint16_t)(zz.y & 0xFFFF));
-              z[3] = bf16_to_f32((uint16_t)(zz.y >> 16));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] *= act_grad(z[e], p.act);
-          } else {
-            if (p.aux) {
-              if (p.aux_f32) {
-                f32x4 zz = {v[0], v[1], v[2], v[3]};
-                *(f32x4*)((float*)p.aux + (int64_t)row * p.ldaux + col) = zz;
-              } else {
-                uint2 zz;
-                zz.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-                zz.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-                *(uint2*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
-              }
-            }
-            if (p.act != ACT_NONE) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = act_fwd(v[e], p.act);
-            }
-          }
-          if (p.y_f32) {
-            f32x4 yy = {v[0], v[1], v[2], v[3]};
-            *(f32x4*)((float*)p.Y + (int64_t)row * p.ldy + col) = yy;
-            if (p.amax) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) lmax = fmaxf(lmax, fabsf(v[e]));
-            }
-          } else {
-            uint16_t b[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne(v[e]);
-            uint2 yy;
-            yy.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-            yy.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-            *(uint2*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;
-            if (p.amax) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) lmax = fmaxf(lmax, fabsf(bf16_to_f32(b[e])));
-            }
-          }
-        }
+      const int col = tl.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
+      if (row < tl.m_end && col < p.N) {
+        f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        epi_quad(p, v * scale, row, col, lmax);
       }
-    }
+    });
     if (p.amax) {
       lmax = wave_max(lmax);
       if (lane == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));
