@@ -32,15 +32,31 @@ namespace {
 
 constexpr int BM = kTileM, BN = kTileN;
 constexpr int THREADS = 256;
-constexpr int TILE_BYTES = 32768;            // one operand stage: 256 rows x 128 bytes of K
+constexpr int ROW_BYTES = 64;                    // K bytes per staged row (32 bf16 / 64 fp8)
+constexpr int TILE_BYTES = 256 * ROW_BYTES;      // one operand tile of one K step: 16 KB
+constexpr int SLOT_BYTES = 2 * TILE_BYTES;       // A + B
+constexpr int NSLOT = 4;                         // ring of K steps in LDS
+constexpr int DIST = NSLOT - 1;                  // K steps loaded ahead of the one computed
+constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per operand tile (4)
+constexpr int EPI_LD = 68;                       // staged epilogue row: 64 floats + 4 pad
+constexpr int EPI_WAVE_FLOATS = 128 * EPI_LD;
+constexpr int SMEM_BYTES =
+    (NSLOT * SLOT_BYTES > 4 * EPI_WAVE_FLOATS * 4) ? NSLOT * SLOT_BYTES : 4 * EPI_WAVE_FLOATS * 4;
 
-// K-major tile: 256 rows x 8 chunks of 16 bytes; chunk c of row r is stored
-// at slot c ^ swz_k(r), which spreads the 32 rows read by one ds_read_b128
-// over distinct banks.
-__device__ __forceinline__ uint32_t swz_k(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
-// MN-major tile (bf16): 64 rows of K x 32 chunks; the four K rows read by one
+// K-major tile: 256 rows x 4 chunks of 16 bytes; chunk c of row r is stored
+// at slot c ^ swz_k(r).  The 16 (or 8) rows one ds_read_b128 phase touches
+// then fall in distinct bank groups.
+__device__ __forceinline__ uint32_t swz_k(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+// MN-major tile (bf16): 32 rows of K x 32 chunks; the four K rows read by one
 // transposed read land in distinct bank groups.
 __device__ __forceinline__ uint32_t swz_mn(uint32_t k) { return ((k & 3u) << 2) ^ ((k & 3u) << 1); }
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 struct Tile {
   int g, m0, m_end, n0;
@@ -75,46 +91,44 @@ __device__ __forceinline__ Tile map_tile(const GemmParams& p, int t) {
   return tl;
 }
 
-// Issue this thread's 8 sixteen-byte loads of one operand tile (256 x 64 bf16).
-// kmajor: rows are the M (or N) index, 128 bytes of K each.
-// otherwise: rows are K, 512 bytes (256 elements) of M or N each.
+// One of the LOADS sixteen-byte loads per thread that stage an operand tile
+// of one K step: thread t of the work-group fills LDS chunk P = j * 256 + t.
+// kmajor: rows are the M (or N) index, 64 bytes of K each.  Otherwise: rows
+// are K (32 of them), 512 bytes (256 bf16) of M or N each.
 template <bool KMAJ, int ESZ>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end,
-                                           int k0, int K, char* lds_tile) {
+__device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end, int k0,
+                                          int K, char* lds_tile, int j) {
   static_assert(KMAJ || ESZ == 2, "MN-major staging is bf16 only");
   constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t P = (uint32_t)(j * 256 + tid);
-    uint32_t voff;
-    if (KMAJ) {
-      const uint32_t row = P >> 3;
-      const uint32_t c = (P & 7u) ^ swz_k(row);
-      const int k = k0 + (int)c * EPC;
-      const bool ok = (mn0 + (int)row < mn_end) && (k < K);
-      voff = ok ? (uint32_t)((int64_t)(mn0 + (int)row) * ld_bytes + (int64_t)k * ESZ) : kOOB;
-    } else {
-      const uint32_t row = P >> 5;
-      const uint32_t c = (P & 31u) ^ swz_mn(row);
-      const int mn = mn0 + (int)c * 8;
-      const bool ok = (k0 + (int)row < K) && (mn < mn_end);
-      voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)mn * 2) : kOOB;
-    }
-    load16_to_lds(rs, voff, lds_tile + (j * 256 + wave * 64) * 16);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t P = (uint32_t)(j * 256 + tid);
+  uint32_t voff;
+  if (KMAJ) {
+    const uint32_t row = P >> 2;
+    const uint32_t c = (P & 3u) ^ swz_k(row);
+    const int k = k0 + (int)c * EPC;
+    const bool ok = (mn0 + (int)row < mn_end) && (k < K);
+    voff = ok ? (uint32_t)((int64_t)(mn0 + (int)row) * ld_bytes + (int64_t)k * ESZ) : kOOB;
+  } else {
+    const uint32_t row = P >> 5;
+    const uint32_t c = (P & 31u) ^ swz_mn(row);
+    const int mn = mn0 + (int)c * 8;
+    const bool ok = (k0 + (int)row < K) && (mn < mn_end);
+    voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)mn * 2) : kOOB;
   }
+  load16_to_lds(rs, voff, lds_tile + (j * 256 + wave * 64) * 16);
 }
 
 // One 32 (rows) x 16 (K) bf16 fragment for a 32x32x16 MFMA operand:
-// lane l holds row rb + l%32, K elements 8*(l/32) .. +7 of substep kk.
+// lane l holds row rb + l%32, K elements 8*(l/32) .. +7 of substep kk (0, 1).
 template <bool KMAJ>
 __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk) {
   const int lane = threadIdx.x & 63;
   if (KMAJ) {
     const uint32_t r = (uint32_t)(rb + (lane & 31));
     const uint32_t c = (uint32_t)(2 * kk + (lane >> 5));
-    const uint32_t addr = r * 128u + ((c ^ swz_k(r)) << 4);
+    const uint32_t addr = r * (uint32_t)ROW_BYTES + ((c ^ swz_k(r)) << 4);
     i32x4 v = *(const lds_i32x4*)((lds_void*)(lds_tile + addr));
     return __builtin_bit_cast(bf16x8, v);
   } else {
@@ -136,14 +150,15 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk
 }
 
 // One 32 (rows) x 64 (K) fp8 fragment for a 32x32x64 MFMA operand (K-major
-// tile only): lane l holds row rb + l%32, K bytes 32*(l/32) .. +31 of substep kk.
-__device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb, int kk) {
+// tile only, one substep per K step): lane l holds row rb + l%32, K bytes
+// 32*(l/32) .. +31.
+__device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb) {
   const int lane = threadIdx.x & 63;
   const uint32_t r = (uint32_t)(rb + (lane & 31));
-  const uint32_t c0 = (uint32_t)(4 * kk + 2 * (lane >> 5));
+  const uint32_t c0 = (uint32_t)(2 * (lane >> 5));
   const uint32_t sw = swz_k(r);
-  const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + r * 128u + ((c0 ^ sw) << 4)));
-  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + r * 128u + (((c0 + 1u) ^ sw) << 4)));
+  const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + r * (uint32_t)ROW_BYTES + ((c0 ^ sw) << 4)));
+  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + r * (uint32_t)ROW_BYTES + (((c0 + 1u) ^ sw) << 4)));
   i32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return v;
 }
@@ -187,64 +202,70 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Epilogue of four consecutive output columns (row, col..col+3) of one lane.
-__device__ __forceinline__ void epi_quad(const GemmParams& p, f32x4 v, int row, int col, float& lmax) {
+// Epilogue of eight consecutive output columns (row, col..col+7) of one lane.
+__device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax) {
   if (p.epi == EPI_DACT) {
-    f32x4 z;
+    float z[8];
     if (p.aux_f32) {
-      z = *(const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
+      const f32x4* src = (const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
+      const f32x4 z0 = src[0], z1 = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { z[e] = z0[e]; z[4 + e] = z1[e]; }
     } else {
-      const uint2 zz = *(const uint2*)((const uint16_t*)p.aux + (int64_t)row * p.ldaux + col);
-      z[0] = bf16_to_f32((uint16_t)(zz.x & 0xFFFFu));
-      z[1] = bf16_to_f32((uint16_t)(zz.x >> 16));
-      z[2] = bf16_to_f32((uint16_t)(zz.y & 0xFFFFu));
-      z[3] = bf16_to_f32((uint16_t)(zz.y >> 16));
+      const i32x4 zz = *(const i32x4*)((const uint16_t*)p.aux + (int64_t)row * p.ldaux + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[2 * e] = bf16_to_f32((uint16_t)((uint32_t)zz[e] & 0xFFFFu));
+        z[2 * e + 1] = bf16_to_f32((uint16_t)((uint32_t)zz[e] >> 16));
+      }
     }
-    v[0] *= act_grad(z[0], p.act);
-    v[1] *= act_grad(z[1], p.act);
-    v[2] *= act_grad(z[2], p.act);
-    v[3] *= act_grad(z[3], p.act);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= act_grad(z[e], p.act);
   } else {
     if (p.aux) {
       if (p.aux_f32) {
-        *(f32x4*)((float*)p.aux + (int64_t)row * p.ldaux + col) = v;
+        f32x4* dst = (f32x4*)((float*)p.aux + (int64_t)row * p.ldaux + col);
+        dst[0] = (f32x4){v[0], v[1], v[2], v[3]};
+        dst[1] = (f32x4){v[4], v[5], v[6], v[7]};
       } else {
-        uint2 zz;
-        zz.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        zz.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-        *(uint2*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
+        i32x4 zz;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          zz[e] = (int)((uint32_t)f32_to_bf16_rne(v[2 * e]) | ((uint32_t)f32_to_bf16_rne(v[2 * e + 1]) << 16));
+        *(i32x4*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
       }
     }
     if (p.act != ACT_NONE) {
-      v[0] = act_fwd(v[0], p.act);
-      v[1] = act_fwd(v[1], p.act);
-      v[2] = act_fwd(v[2], p.act);
-      v[3] = act_fwd(v[3], p.act);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = act_fwd(v[e], p.act);
     }
   }
   if (p.y_f32) {
-    *(f32x4*)((float*)p.Y + (int64_t)row * p.ldy + col) = v;
-    if (p.amax) lmax = fmaxf(lmax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-  } else {
-    const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-    const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-    uint2 yy;
-    yy.x = b0 | (b1 << 16);
-    yy.y = b2 | (b3 << 16);
-    *(uint2*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;
+    f32x4* dst = (f32x4*)((float*)p.Y + (int64_t)row * p.ldy + col);
+    dst[0] = (f32x4){v[0], v[1], v[2], v[3]};
+    dst[1] = (f32x4){v[4], v[5], v[6], v[7]};
     if (p.amax) {
-      const float m01 = fmaxf(fabsf(bf16_to_f32((uint16_t)b0)), fabsf(bf16_to_f32((uint16_t)b1)));
-      const float m23 = fmaxf(fabsf(bf16_to_f32((uint16_t)b2)), fabsf(bf16_to_f32((uint16_t)b3)));
-      lmax = fmaxf(lmax, fmaxf(m01, m23));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lmax = fmaxf(lmax, fabsf(v[e]));
     }
+  } else {
+    i32x4 yy;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b0 = f32_to_bf16_rne(v[2 * e]), b1 = f32_to_bf16_rne(v[2 * e + 1]);
+      yy[e] = (int)(b0 | (b1 << 16));
+      if (p.amax) lmax = fmaxf(lmax, fmaxf(fabsf(bf16_to_f32((uint16_t)b0)), fabsf(bf16_to_f32((uint16_t)b1))));
+    }
+    *(i32x4*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;
   }
 }
 
 template <bool FP8, bool AK, bool BKM>
 __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
   constexpr int ESZ = FP8 ? 1 : 2;
-  constexpr int KSTEP = 128 / ESZ;  // K elements per staged step (128 bytes per row)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+  constexpr int KSTEP = ROW_BYTES / ESZ;  // K elements per staged step
+  constexpr int KSUB = FP8 ? 1 : 2;        // MFMA substeps per K step
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -261,6 +282,7 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
 
   for (int t = blockIdx.x; t < p.total_tiles; t += gridDim.x) {
     const Tile tl = map_tile(p, t);
+    __syncthreads();  // the previous tile's epilogue staging is done with the LDS
     if (p.ready) wait_group(p, tl.g);
 
     f32x16 acc[4][4];
@@ -271,80 +293,119 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // K loop over two LDS stages (A and B tiles of 32 KB each per stage).
-    auto issue = [&](char* As, char* Bs, int k0) {
-      issue_tile<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, As);
-      issue_tile<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, k0, p.K, Bs);
-    };
-    // One K step, software-pipelined: the fragments of substep kk+1 are read
-    // from LDS before the MFMAs of substep kk are issued (sched_barrier keeps
-    // the scheduler from sinking them), and the global loads of the next
-    // stage go out right after the first fragment reads.
     using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-    constexpr int KSUB = FP8 ? 2 : 4;
+    auto slot = [&](int k) { return smem + (k % NSLOT) * SLOT_BYTES; };
+    auto load_one = [&](char* dst, int L, int k0) {
+      if (L < LOADS) issue_one<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
+      else issue_one<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS);
+    };
     auto read_set = [&](const char* As, const char* Bs, int kk, Frag (&af)[4], Frag (&bfr)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FP8) af[i] = read_frag_fp8(As, wm + 32 * i, kk);
+        if constexpr (FP8) af[i] = read_frag_fp8(As, wm + 32 * i);
         else af[i] = read_frag<AK>(As, wm + 32 * i, kk);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (FP8) bfr[j] = read_frag_fp8(Bs, wn + 32 * j, kk);
+        if constexpr (FP8) bfr[j] = read_frag_fp8(Bs, wn + 32 * j);
         else bfr[j] = read_frag<BKM>(Bs, wn + 32 * j, kk);
       }
     };
-    auto mfma_set = [&](const Frag (&af)[4], const Frag (&bfr)[4]) {
+    auto mfma_row = [&](const Frag& a, const Frag (&bfr)[4], f32x16 (&accrow)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (FP8)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-        }
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8)
+          accrow[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], a, accrow[j], 0, 0, 0, 0, 0, 0);
+        else
+          accrow[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], a, accrow[j], 0, 0, 0);
+      }
     };
-    // The restrict qualifiers tell the compiler that the two stages do not
-    // overlap, so the fragment reads do not wait for the loads just issued.
+    // One K step: the 2 * LOADS loads of step k + DIST are spread between
+    // the MFMA groups of this step, the fragments of substep kk+1 are read
+    // before the MFMAs of substep kk (sched_barrier keeps the scheduler from
+    // sinking them).  The restrict qualifiers tell the compiler that the slot
+    // being filled and the slot being read do not overlap.
+    constexpr int LOADS_PER_GROUP = (2 * LOADS) / (KSUB * 4);
     auto iteration = [&](const char* __restrict__ cur, char* __restrict__ nxt, int k_next) {
       Frag fa[2][4], fb[2][4];
       read_set(cur, cur + TILE_BYTES, 0, fa[0], fb[0]);
-      if (k_next >= 0) issue(nxt, nxt + TILE_BYTES, k_next);
+      const bool more = k_next >= 0;
       static_for<KSUB>([&](auto kkc) {
         constexpr int kk = decltype(kkc)::value;
         if constexpr (kk + 1 < KSUB) read_set(cur, cur + TILE_BYTES, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_set(fa[kk & 1], fb[kk & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        static_for<4>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          mfma_row(fa[kk & 1][i], fb[kk & 1], acc[i]);
+          if (more) {
+            static_for<LOADS_PER_GROUP>([&](auto rc) {
+              constexpr int L = (kk * 4 + i) * LOADS_PER_GROUP + decltype(rc)::value;
+              load_one(nxt, L, k_next);
+            });
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
       });
     };
 
-    issue(smem, smem + TILE_BYTES, 0);
-    wait_vmem();
-    __syncthreads();
+    // Ring of NSLOT K steps.  Before computing step kt, this thread waits
+    // until its loads for step kt have landed: the loads still allowed in
+    // flight are those of the (at most DIST - 1) later steps already issued.
+    // The barrier then makes every thread's loads visible and guarantees
+    // that step kt-1's slot, which step kt+DIST refills, is no longer read.
+#pragma unroll
+    for (int k = 0; k < DIST; ++k)
+      if (k < nk)
+#pragma unroll
+        for (int L = 0; L < 2 * LOADS; ++L) load_one(slot(k), L, k * KSTEP);
     for (int kt = 0; kt < nk; ++kt) {
-      char* cur = smem + (kt & 1) * (2 * TILE_BYTES);
-      char* nxt = smem + ((kt + 1) & 1) * (2 * TILE_BYTES);
-      iteration(cur, nxt, kt + 1 < nk ? (kt + 1) * KSTEP : -1);
-      wait_vmem();
-      __syncthreads();
+      const int ahead = nk - 1 - kt;  // steps after kt already issued: min(DIST - 1, ahead)
+      if (ahead >= 2) wait_vmcnt<2 * 2 * LOADS>();
+      else if (ahead == 1) wait_vmcnt<2 * LOADS>();
+      else wait_vmcnt<0>();
+      // a bare s_barrier: __syncthreads() would also wait for the loads of
+      // the later steps.  The empty asm statements keep the compiler from
+      // moving LDS accesses across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int kn = kt + DIST;
+      iteration(slot(kt), slot(kn), kn < nk ? kn * KSTEP : -1);
     }
+    __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
 
-    // ---- epilogue: lane holds rows m0+wm+32i+lane%32, columns
-    //      n0+wn+32j+8q+4*(lane/32)+{0..3} in acc[i][j][4q..4q+3].  Every
-    //      index is a compile-time constant so the accumulators stay in
-    //      registers.
+    // ---- epilogue.  Lane l holds rows m0+wm+32i+l%32 and columns
+    //      n0+wn+32j+8q+4*(l/32)+{0..3} in acc[i][j][4q..4q+3].  Each wave
+    //      stages its 128 x 128 fp32 block through a private LDS region, 64
+    //      columns at a time (rows padded to 68 floats against bank
+    //      conflicts), and reads it back as 8 consecutive columns per lane:
+    //      the element-wise code then runs in one compact loop and every
+    //      global store is 16 bytes wide.
     float lmax = 0.f;
-    static_for<64>([&](auto ijq) {
-      constexpr int i = decltype(ijq)::value / 16;
-      constexpr int j = (decltype(ijq)::value / 4) % 4;
-      constexpr int q = decltype(ijq)::value % 4;
-      const int row = tl.m0 + wm + 32 * i + (lane & 31);
-      const int col = tl.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
-      if (row < tl.m_end && col < p.N) {
-        f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        epi_quad(p, v * scale, row, col, lmax);
+    float* stage = reinterpret_cast<float*>(smem) + wave * EPI_WAVE_FLOATS;
+    static_for<2>([&](auto pc) {
+      constexpr int pass = decltype(pc)::value;
+      static_for<32>([&](auto c) {
+        constexpr int i = decltype(c)::value / 8;
+        constexpr int jj = (decltype(c)::value / 4) % 2;
+        constexpr int q = decltype(c)::value % 4;
+        constexpr int j = 2 * pass + jj;
+        const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        *(f32x4*)(stage + (32 * i + (lane & 31)) * EPI_LD + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
+      });
+#pragma unroll 1
+      for (int it = 0; it < 16; ++it) {
+        const int rl = it * 8 + (lane >> 3);
+        const int cl = (lane & 7) * 8;
+        const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
+        const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+        const int row = tl.m0 + wm + rl;
+        const int col = tl.n0 + wn + 64 * pass + cl;
+        if (row < tl.m_end && col < p.N) {
+          float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                        v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+          epi_oct(p, v, row, col, lmax);
+        }
       }
     });
     if (p.amax) {
