@@ -97,7 +97,11 @@ class Layer:
         self.slice_o, self.slice_mlp, self.slice_dxm, self.slice_dxq = (e(M // T, D) for _ in range(4))
         self.ws_fwd = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, self.C, tpm.BF16)
         self.ws_bwd = tpm.alloc_workspace(tpm.OP_MLP_BWD, M, D, F, T, self.C, tpm.BF16)
-        self.ws_g = [tpm.alloc_workspace(tpm.OP_SEQ_CHUNK_GEMM, M, D, D) for _ in range(4)]
+        # one workspace for all seq_chunk_gemm calls (stream-ordered): control
+        # words plus the split-K scratch of the narrowest projections
+        shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1)]
+        self.ws_g = torch.empty(max(tpm.workspace_bytes(tpm.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
+                                dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.order = si.ring_chunk_order(T, self.C, rank)
         self.dest = si.dest_range_order(T, rank)
@@ -135,16 +139,16 @@ class Layer:
         torch, tpm = self.torch, self.tpm
         T, r, C = self.T, self.rank, self.C
         ready = (lambda i: self.flags[i]) if arrive else (lambda i: None)
-        ws = lambda i: self.ws_g[i] if arrive else None
+        wsg = self.ws_g
         own_slot = self.stack[r]
         # ---- forward, attention projections
         if arrive:
             self._arrive(0, self.x_qkv, self.x_src, epoch)
         self._timed(lambda: tpm.seq_chunk_gemm(self.x_qkv, self.w_qkv, self.qkv, num_chunks=C,
                                                chunk_order=self.order, chunk_ready=ready(0), epoch=epoch,
-                                               workspace=ws(0)), record)
+                                               workspace=wsg), record)
         self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
-                                               chunk_order=self.dest), record)
+                                               chunk_order=self.dest, workspace=wsg), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
         # ---- forward, MLP
         if arrive:
@@ -168,14 +172,14 @@ class Layer:
 
         def o_bwd():
             tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
-                               chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=ws(3))
-            tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True)
+                               chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=wsg)
+            tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg)
         self._timed(o_bwd, record)
 
         # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T (partial)
         def qkv_bwd():
-            tpm.seq_chunk_gemm(self.x_qkv, self.dy_qkv, self.g_qkv, trans_a=True)
-            tpm.seq_chunk_gemm(self.dy_qkv, self.w_qkv, own_slot, trans_b=True)
+            tpm.seq_chunk_gemm(self.x_qkv, self.dy_qkv, self.g_qkv, trans_a=True, workspace=wsg)
+            tpm.seq_chunk_gemm(self.dy_qkv, self.w_qkv, own_slot, trans_b=True, workspace=wsg)
         self._timed(qkv_bwd, record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
         if arrive:

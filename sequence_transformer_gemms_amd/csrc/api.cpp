@@ -54,6 +54,35 @@ int esize(int dt) { return dt == TPM_F32 ? 4 : dt == TPM_BF16 ? 2 : 1; }
 bool valid_dt(int dt) { return dt == TPM_F32 || dt == TPM_BF16 || dt == TPM_FP8_E4M3; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Split-K plan.  A GEMM with fewer output tiles than about three quarters of
+// the CUs leaves the chip idle; its K range is then cut into S pieces whose
+// fp32 partial sums are added in a fixed order by a second kernel.  S
+// minimises rounds(tiles * S) / S with a small per-split cost, keeping at
+// least 8 K steps per piece.  The plan assumes 256 CUs (MI355X) so that the
+// workspace size can be computed without a device.
+constexpr int kPlanCUs = 256;
+
+int plan_splits(int64_t M, int64_t N, int64_t K, int groups, int dt) {
+  if (dt == TPM_F32 || M <= 0 || N <= 0 || K <= 0) return 1;
+  const int64_t group_rows = M / std::max(groups, 1);
+  const int64_t tiles = ((group_rows + kTileM - 1) / kTileM) * groups * ((N + kTileN - 1) / kTileN);
+  if (tiles * 4 >= (int64_t)kPlanCUs * 3) return 1;
+  const int64_t nk = (K * esize(dt) + kStepBytes - 1) / kStepBytes;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int S = 1; S <= 8; ++S) {
+    if (S > 1 && nk / S < 8) break;
+    const double rounds = (double)((tiles * S + kPlanCUs - 1) / kPlanCUs);
+    const double cost = rounds / S * (1.0 + 0.04 * S);
+    if (cost < best_cost) { best_cost = cost; best = S; }
+  }
+  return best;
+}
+
+size_t partial_bytes(int64_t M, int64_t N, int S) {
+  return S > 1 ? round_up((size_t)S * (size_t)M * (size_t)N * 4, 256) : 0;
+}
+
 struct GemmDesc {
   int64_t M, N, K;
   const void* A; int64_t lda; bool ta; int adt; const float* asc;
@@ -62,6 +91,8 @@ struct GemmDesc {
   int epi, act; void* aux; int64_t ldaux; float* amax;
   int groups; const int32_t* order; const uint32_t* ready; uint32_t* done; uint32_t epoch;
   uint32_t* ctrl;   // device control words (err, amax, counters) or null
+  float* part = nullptr;   // device scratch for split-K partial sums
+  size_t part_bytes = 0;
 };
 
 // Full host-side validation of one GEMM; returns TPM_OK or an error code.
@@ -136,6 +167,14 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
     e = launch_gemm_f32(p, g.ta, g.tb, s);
     return e == hipSuccess ? TPM_OK : hip_fail(e, who);
   }
+  // split-K when the plan asks for it and the scratch is there (chunk-gated
+  // GEMMs split too; range-done signalling needs whole tiles)
+  int S = g.done ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+  if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
+  const int64_t nk = (g.K * esize(g.adt) + kStepBytes - 1) / kStepBytes;
+  p.splits = S;
+  p.ksteps_per_split = (int)((nk + S - 1) / S);
+  p.partial = S > 1 ? g.part : nullptr;
   const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
   p.a_bytes = g.K == 0 ? 0u : (uint32_t)(a_rows * g.lda * esize(g.adt));
   p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
@@ -149,7 +188,7 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   int cus = num_cus();
   int grid = g.ready ? cus - 8 : cus;
   grid = std::max(8, grid);
-  grid = std::min(grid, p.total_tiles);
+  grid = std::min(grid, p.total_tiles * p.splits);
   if (g.adt == TPM_BF16) e = launch_gemm_bf16(p, !g.ta, g.tb, grid, s);
   else e = launch_gemm_fp8(p, !g.ta, g.tb, grid, s);
   return e == hipSuccess ? TPM_OK : hip_fail(e, who);
@@ -183,19 +222,27 @@ int tpm_set_wait_limit(uint32_t polls) {
 }
 
 size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int num_chunks, int dtype) {
-  (void)num_chunks;
-  if (M < 0 || N < 0 || K < 0) return 0;
+  if (M < 0 || N < 0 || K < 0 || num_chunks < 1) return 0;
   switch (op) {
-    case TPM_OP_SEQ_CHUNK_GEMM: return kCtrlBytes;
+    case TPM_OP_SEQ_CHUNK_GEMM:
+      return kCtrlBytes + partial_bytes(M, N, plan_splits(M, N, K, num_chunks, dtype));
     case TPM_OP_MLP_FWD: {
       if (T <= 0) return 0;
-      const size_t ft = (size_t)(K / T);
-      return kCtrlBytes + (dtype == TPM_FP8_E4M3 ? round_up((size_t)M * ft, 256) : 0);
+      const int64_t D = N, Ft = K / T;
+      const size_t hq = dtype == TPM_FP8_E4M3 ? round_up((size_t)M * (size_t)Ft, 256) : 0;
+      const size_t part = std::max(partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype)),
+                                   partial_bytes(M, D, plan_splits(M, D, Ft, T, dtype)));
+      return kCtrlBytes + hq + part;
     }
     case TPM_OP_MLP_BWD: {
       if (T <= 0) return 0;
-      const size_t ft = (size_t)(K / T);
-      return kCtrlBytes + round_up((size_t)M * ft * (size_t)esize(dtype == TPM_F32 ? TPM_F32 : TPM_BF16), 256);
+      const int64_t D = N, Ft = K / T;
+      const size_t dz = round_up((size_t)M * (size_t)Ft * (size_t)esize(dtype == TPM_F32 ? TPM_F32 : TPM_BF16), 256);
+      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype));
+      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, dtype)));
+      part = std::max(part, partial_bytes(D, Ft, plan_splits(D, Ft, M, 1, dtype)));
+      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, dtype)));
+      return kCtrlBytes + dz + part;
     }
     default: return 0;
   }
@@ -230,6 +277,10 @@ int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
   GemmDesc g{M, N, K, A, lda, trans_a != 0, a_dtype, a_scale, B, ldb, trans_b != 0, b_dtype, b_scale,
              Y, ldy, y_dtype, epilogue, act, aux, ldaux, amax_out,
              num_chunks, chunk_order, chunk_ready, nullptr, epoch, ctrl};
+  if (ctrl) {
+    g.part = (float*)((char*)workspace + kCtrlBytes);
+    g.part_bytes = workspace_bytes - kCtrlBytes;
+  }
   int rc = check_gemm(g, who);
   if (rc != TPM_OK) return rc;
   if (amax_out && a_dtype == TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: amax on the fp32 path", who);
@@ -266,7 +317,7 @@ int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
   const bool need_ctrl = chunk_ready || range_done || dtype == TPM_FP8_E4M3;
   if (need_ctrl && (!workspace || workspace_bytes < need))
     return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
-  uint32_t* ctrl = need_ctrl ? (uint32_t*)workspace : nullptr;
+  uint32_t* ctrl = (workspace && workspace_bytes >= kCtrlBytes) ? (uint32_t*)workspace : nullptr;
   if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
   int32_t corder[TPM_MAX_CHUNKS], rorder[TPM_MAX_CHUNKS];
   if (chunk_order) std::memcpy(corder, chunk_order, sizeof(int32_t) * num_chunks);
@@ -294,6 +345,11 @@ int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
               T, rorder, nullptr, range_done, epoch, ctrl};
   rc = check_gemm(g2, who);
   if (rc != TPM_OK) return rc;
+  if (workspace && workspace_bytes >= need) {
+    const size_t hq_bytes = fp8 ? round_up((size_t)M * (size_t)Ft, 256) : 0;
+    g1.part = g2.part = (float*)((char*)workspace + kCtrlBytes + hq_bytes);
+    g1.part_bytes = g2.part_bytes = workspace_bytes - kCtrlBytes - hq_bytes;
+  }
   if (M == 0 || D == 0) return TPM_OK;
   hipStream_t s = (hipStream_t)stream;
   if (need_ctrl) {
@@ -351,6 +407,13 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
   GemmDesc g_dx{M, D, Ft, dZ, Ft, false, adt, nullptr, W_up_t, Ft, true, adt, nullptr,
                 dX_t, D, zdt, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
                 1, nullptr, nullptr, nullptr, epoch, ctrl};
+  {
+    const size_t dz_bytes = round_up((size_t)M * (size_t)Ft * (size_t)esize(zdt), 256);
+    for (GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
+      g->part = (float*)((char*)workspace + kCtrlBytes + dz_bytes);
+      g->part_bytes = workspace_bytes - kCtrlBytes - dz_bytes;
+    }
+  }
   for (const GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
     int rc = check_gemm(*g, who);
     if (rc != TPM_OK) return rc;

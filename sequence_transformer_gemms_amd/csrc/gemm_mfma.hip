@@ -62,16 +62,32 @@ struct Tile {
   int g, m0, m_end, n0;
 };
 
-__device__ __forceinline__ Tile map_tile(const GemmParams& p, int t) {
+struct Unit {
+  Tile tl;
+  int split;
+};
+
+// Work unit u -> (split, tile).  Units of one XCD (work-group ids congruent
+// mod 8, which the dispatcher places round-robin on the 8 XCDs) are made
+// contiguous in the logical order, and the logical order walks the groups
+// (chunks / destination ranges) in the caller's order, each group in bands
+// of band_m row tiles, so the 32 tiles an XCD works on at once share few
+// A row panels and B column panels in its L2.  Splits of the K range are the
+// outermost index.
+__device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
   const int G = gridDim.x;
-  int L = t;
+  const int total = p.total_tiles * p.splits;
+  int L = u;
   if ((G & 7) == 0) {
-    const int r = t / G;
-    if ((r + 1) * G <= p.total_tiles) {
-      const int s = t - r * G;
-      L = r * G + (s & 7) * (G >> 3) + (s >> 3);  // tiles of one XCD are contiguous in L
+    const int r = u / G;
+    if ((r + 1) * G <= total) {
+      const int s = u - r * G;
+      L = r * G + (s & 7) * (G >> 3) + (s >> 3);
     }
   }
+  Unit un;
+  un.split = L / p.total_tiles;
+  L -= un.split * p.total_tiles;
   const int pos = L / p.tiles_per_group;
   const int q = L - pos * p.tiles_per_group;
   const int g = p.order[pos];
@@ -81,14 +97,14 @@ __device__ __forceinline__ Tile map_tile(const GemmParams& p, int t) {
   const int idx = q - band * p.band_m * p.nt;
   const int mt = band * p.band_m + idx % gm;
   const int ntile = idx / gm;
-  Tile tl;
+  Tile& tl = un.tl;
   tl.g = g;
   const int gstart = g * p.group_rows;
   tl.m0 = gstart + mt * BM;
   const int gend = gstart + p.group_rows;
   tl.m_end = (tl.m0 + BM < gend) ? tl.m0 + BM : gend;
   tl.n0 = ntile * BN;
-  return tl;
+  return un;
 }
 
 // One of the LOADS sixteen-byte loads per thread that stage an operand tile
@@ -280,8 +296,14 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
   if (p.a_scale) scale *= *p.a_scale;
   if (p.b_scale) scale *= *p.b_scale;
 
-  for (int t = blockIdx.x; t < p.total_tiles; t += gridDim.x) {
-    const Tile tl = map_tile(p, t);
+  const int total_units = p.total_tiles * p.splits;
+  for (int u = blockIdx.x; u < total_units; u += gridDim.x) {
+    const Unit un = map_unit(p, u);
+    const Tile& tl = un.tl;
+    // K steps [kbeg, kend) of this split
+    const int kbeg = un.split * p.ksteps_per_split;
+    const int kend = min(nk, kbeg + p.ksteps_per_split);
+    const int nks = kend - kbeg;
     __syncthreads();  // the previous tile's epilogue staging is done with the LDS
     if (p.ready) wait_group(p, tl.g);
 
@@ -355,11 +377,11 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
     // that step kt-1's slot, which step kt+DIST refills, is no longer read.
 #pragma unroll
     for (int k = 0; k < DIST; ++k)
-      if (k < nk)
+      if (k < nks)
 #pragma unroll
-        for (int L = 0; L < 2 * LOADS; ++L) load_one(slot(k), L, k * KSTEP);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = nk - 1 - kt;  // steps after kt already issued: min(DIST - 1, ahead)
+        for (int L = 0; L < 2 * LOADS; ++L) load_one(slot(k), L, (kbeg + k) * KSTEP);
+    for (int kt = 0; kt < nks; ++kt) {
+      const int ahead = nks - 1 - kt;  // steps after kt already issued: min(DIST - 1, ahead)
       if (ahead >= 2) wait_vmcnt<2 * 2 * LOADS>();
       else if (ahead == 1) wait_vmcnt<2 * LOADS>();
       else wait_vmcnt<0>();
@@ -370,7 +392,7 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const int kn = kt + DIST;
-      iteration(slot(kt), slot(kn), kn < nk ? kn * KSTEP : -1);
+      iteration(slot(kt), slot(kn), kn < nks ? (kbeg + kn) * KSTEP : -1);
     }
     __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
 
@@ -402,9 +424,16 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
         const int row = tl.m0 + wm + rl;
         const int col = tl.n0 + wn + 64 * pass + cl;
         if (row < tl.m_end && col < p.N) {
-          float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
-                        v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
-          epi_oct(p, v, row, col, lmax);
+          if (p.splits > 1) {
+            // raw fp32 partial of this K range; splitk_finalize sums them
+            f32x4* dst = (f32x4*)(p.partial + ((int64_t)un.split * p.M + row) * p.N + col);
+            dst[0] = v0;
+            dst[1] = v1;
+          } else {
+            float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                          v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+            epi_oct(p, v, row, col, lmax);
+          }
         }
       }
     });
@@ -424,20 +453,62 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
   }
 }
 
+
+// Split-K finalisation: Y = epilogue(scale * sum_{s=0}^{S-1} partial_s),
+// summed in ascending s (deterministic), 8 consecutive columns per lane.
+__global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
+  float scale = 1.f;
+  if (p.a_scale) scale *= *p.a_scale;
+  if (p.b_scale) scale *= *p.b_scale;
+  const int64_t n8 = p.N / 8;
+  const int64_t total = (int64_t)p.M * n8;
+  const int64_t plane = (int64_t)p.M * p.N;
+  float lmax = 0.f;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total; w += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(w / n8);
+    const int col = (int)(w - (int64_t)row * n8) * 8;
+    const float* src = p.partial + (int64_t)row * p.N + col;
+    f32x4 a0 = __builtin_nontemporal_load((const f32x4*)src);
+    f32x4 a1 = __builtin_nontemporal_load((const f32x4*)src + 1);
+    for (int sp = 1; sp < p.splits; ++sp) {
+      a0 += __builtin_nontemporal_load((const f32x4*)(src + sp * plane));
+      a1 += __builtin_nontemporal_load((const f32x4*)(src + sp * plane) + 1);
+    }
+    float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
+                  a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
+    epi_oct(p, v, row, col, lmax);
+  }
+  if (p.amax) {
+    lmax = wave_max(lmax);
+    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));
+  }
+}
+
 }  // namespace
+
+static hipError_t finalize_if_split(const GemmParams& p, hipStream_t s) {
+  if (p.splits <= 1) return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t work = (int64_t)p.M * (p.N / 8);
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  splitk_finalize<<<(int)blocks, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (a_kmajor && !b_kmajor) gemm_kernel<false, true, false><<<grid, THREADS, 0, s>>>(p);
   else if (a_kmajor && b_kmajor) gemm_kernel<false, true, true><<<grid, THREADS, 0, s>>>(p);
   else if (!a_kmajor && !b_kmajor) gemm_kernel<false, false, false><<<grid, THREADS, 0, s>>>(p);
   else gemm_kernel<false, false, true><<<grid, THREADS, 0, s>>>(p);
-  return hipGetLastError();
+  return finalize_if_split(p, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (!a_kmajor || !b_kmajor) return hipErrorInvalidValue;  // rejected on the host first
   gemm_kernel<true, true, true><<<grid, THREADS, 0, s>>>(p);
-  return hipGetLastError();
+  return finalize_if_split(p, s);
 }
 
 }  // namespace tpm

@@ -31,6 +31,9 @@ struct GemmParams {
   uint32_t epoch;
   uint32_t wait_limit;       // polls before a wait gives up (watchdog)
   int act, epi, y_f32, aux_f32;
+  int splits;                // K-range splits (1: none); > 1 needs `partial`
+  int ksteps_per_split;      // K steps (of 32 bf16 / 64 fp8) per split
+  float* partial;            // device fp32 [splits][M][N] partial sums
   int16_t order[kMaxGroups];
 };
 
@@ -48,5 +51,6 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
 
 constexpr int kTileM = 256, kTileN = 256;
+constexpr int kStepBytes = 64;  // K bytes per staged step of the MFMA kernel
 
 }  // namespace tpm

@@ -33,7 +33,11 @@ def test_exports_every_declared_symbol():
 def test_workspace_sizes():
     from sequence_transformer_gemms_amd import _abi
     ws = _abi.lib.tpm_workspace_bytes
-    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 128, 128, 128, 1, 1, _abi.BF16) == 2048
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 128, 128, 128, 1, 1, _abi.BF16) == 2048   # too little K to split
+    # a full chip's worth of tiles: no split-K scratch
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 8192, 8192, 8192, 1, 1, _abi.BF16) == 2048
+    # QKV projection of one TP=8 rank: 80 tiles -> K cut in 3, fp32 partials [3, 4096, 1280]
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4096, 1280, 8192, 1, 8, _abi.BF16) == 2048 + 3 * 4096 * 1280 * 4
     # bwd keeps dZ [M, F/T] bf16 after the 2 KiB control block
     assert ws(_abi.OP_MLP_BWD, 4096, 8192, 28672, 8, 8, _abi.BF16) == 2048 + 4096 * 3584 * 2
     # fp8 fwd keeps the quantised H [M, F/T]

@@ -330,11 +330,12 @@ def test_chunks_arrive_from_side_stream():
     w = si.normal_f32((K, N), 62, 0.05)
     Xsrc, W = dev_bf16(x), dev_bf16(w)
     ref = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    tpm.seq_chunk_gemm(Xsrc, W, ref, act=_abi.ACT_GELU_ERF)
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    # same workspace, hence the same split-K plan: the gated result must be bitwise equal
+    tpm.seq_chunk_gemm(Xsrc, W, ref, act=_abi.ACT_GELU_ERF, num_chunks=C, workspace=ws)
     sync()
     Xdst = torch.zeros_like(Xsrc)
     flags = torch.zeros(C, dtype=torch.int32, device="cuda")
-    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
     Y = torch.empty_like(ref)
     order = si.ring_chunk_order(4, C, 2)
     side = torch.cuda.Stream()
@@ -373,3 +374,41 @@ def test_watchdog_reports_timeout_and_kernel_exits():
     tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_ready=flags, epoch=5, workspace=ws)
     sync()
     assert tpm.poll_device_error(ws) == 0
+
+
+# ------------------------------------------------------------ split-K path
+def test_split_k_narrow_gemm():
+    # 2 output tiles, K = 4096: the plan cuts K into pieces whose fp32 partial
+    # sums a second kernel adds in a fixed order
+    M, N, K = 512, 264, 4096
+    assert tpm.workspace_bytes(_abi.OP_SEQ_CHUNK_GEMM, M, N, K) > 2048      # split planned
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    a = si.small_ints((M, K), 81)
+    b = si.small_ints((K, N), 82)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(dev_bf16(a), dev_bf16(b), Y, workspace=ws)
+    sync()
+    assert np.array_equal(f64(Y), a.astype(np.float64) @ b.astype(np.float64))   # exact
+    # float inputs, GeLU + Z save, chunk-gated (flags already set), amax
+    x = dev_bf16(si.normal_f32((M, K), 83))
+    w = dev_bf16(si.normal_f32((K, N), 84, 0.02))
+    Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty_like(Yb)
+    flags = torch.full((4,), 9, dtype=torch.int32, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(x, w, Yb, act=_abi.ACT_GELU_ERF, aux=Z, num_chunks=4, chunk_order=[2, 0, 3, 1],
+                       chunk_ready=flags, epoch=9, amax_out=amax, workspace=ws)
+    sync()
+    y, z = ops.seq_chunk_gemm(f64(x), f64(w), act=_abi.ACT_GELU_ERF)
+    assert nerr(Yb, y) <= TOL["bf16"] and nerr(Z, z) <= TOL["bf16"]
+    assert amax.item() == float(np.max(np.abs(f64(Yb))))
+    assert tpm.poll_device_error(ws) == 0
+    # DACT epilogue through the split path, K-major B
+    wt = dev_bf16(si.normal_f32((N, K), 85, 0.02))
+    zin = dev_bf16(si.normal_f32((M, N), 86))
+    Yd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(x, wt, Yd, trans_b=True, epilogue=_abi.EPI_DACT, act=_abi.ACT_GELU_ERF, aux=zin,
+                       workspace=ws)
+    sync()
+    yd, _ = ops.seq_chunk_gemm(f64(x), f64(wt), trans_b=True, act=_abi.ACT_GELU_ERF, dact_z=f64(zin))
+    assert nerr(Yd, yd) <= TOL["bf16"]
