@@ -110,13 +110,20 @@ class Layer:
         fl = lambda m, n, k: 2.0 * m * n * k
         self.flops = (3 * fl(M, Nq, D) + 3 * fl(M, Ft, D) + 3 * fl(M, D, Da) + 3 * fl(M, D, Ft))
 
-    # -- chunk arrival: side stream copies the remote chunks and signals flags
-    def _arrive(self, which, dst, src, epoch):
+    # -- chunk arrival: side stream copies the remote chunks and signals flags.
+    # The boundary event is recorded on the compute stream before the
+    # chunk-fed GEMM is enqueued; the copies are enqueued after it (so the
+    # host-side launch cost of the copies overlaps the GEMM), but start at
+    # the boundary.
+    def _boundary(self):
+        ev = self.torch.cuda.Event()
+        ev.record(self.torch.cuda.current_stream())
+        return ev
+
+    def _arrive(self, which, dst, src, epoch, boundary):
         torch, tpm = self.torch, self.tpm
         rows = self.M // self.C
         own = set(range(self.rank * (self.C // self.T), (self.rank + 1) * (self.C // self.T)))
-        boundary = torch.cuda.Event()
-        boundary.record(torch.cuda.current_stream())
         self.side.wait_event(boundary)            # communication starts at the layer boundary
         with torch.cuda.stream(self.side):
             for c in self.order:
@@ -142,39 +149,43 @@ class Layer:
         wsg = self.ws_g
         own_slot = self.stack[r]
         # ---- forward, attention projections
-        if arrive:
-            self._arrive(0, self.x_qkv, self.x_src, epoch)
+        b = self._boundary()
         self._timed(lambda: tpm.seq_chunk_gemm(self.x_qkv, self.w_qkv, self.qkv, num_chunks=C,
                                                chunk_order=self.order, chunk_ready=ready(0), epoch=epoch,
                                                workspace=wsg), record)
+        if arrive:
+            self._arrive(0, self.x_qkv, self.x_src, epoch, b)
         self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
                                                chunk_order=self.dest, workspace=wsg), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
         # ---- forward, MLP
-        if arrive:
-            self._arrive(1, self.x_mlp, self.x_src, epoch)
+        b = self._boundary()
         self._timed(lambda: tpm.tp_mlp_fwd(self.x_mlp, self.w_up, self.w_down, self.h, own_slot, T=T, rank=r,
                                            act=tpm.ACT_GELU_ERF, Z_t=self.z, num_chunks=C,
                                            chunk_order=self.order, chunk_ready=ready(1), epoch=epoch,
                                            workspace=self.ws_fwd), record)
+        if arrive:
+            self._arrive(1, self.x_mlp, self.x_src, epoch, b)
         tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
         # ---- backward, MLP
-        if arrive:
-            self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch)
+        b = self._boundary()
         self._timed(lambda: tpm.tp_mlp_bwd(self.x_mlp, self.w_up, self.w_down, self.z, self.h, self.dy_mlp,
                                            self.g_up, self.g_down, own_slot, T=T, rank=r,
                                            act=tpm.ACT_GELU_ERF, num_chunks=C, dy_chunk_order=self.order,
                                            dy_ready=ready(2), epoch=epoch, workspace=self.ws_bwd), record)
+        if arrive:
+            self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
         # ---- backward, O projection: dA = dY_o W_o^T (chunk-fed), dW_o = A^T dY_o
-        if arrive:
-            self._arrive(3, self.dy_o, self.dy_o_src, epoch)
+        b = self._boundary()
 
         def o_bwd():
             tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
                                chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=wsg)
             tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg)
         self._timed(o_bwd, record)
+        if arrive:
+            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
 
         # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T (partial)
         def qkv_bwd():

@@ -191,7 +191,9 @@ __device__ __forceinline__ bool wait_group(const GemmParams& p, int g) {
     int bad = 0;
     uint32_t polls = 0;
     for (;;) {
-      const uint32_t v = __hip_atomic_load(p.ready + g, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+      // relaxed device-coherent read of the flag; see the acquire at kernel
+      // start for why no cache invalidation is needed per chunk
+      const uint32_t v = __hip_atomic_load(p.ready + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int32_t)(v - p.epoch) >= 0) break;
       if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++polls > p.wait_limit) {
         __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -296,6 +298,13 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
   if (p.a_scale) scale *= *p.a_scale;
   if (p.b_scale) scale *= *p.b_scale;
 
+  // Chunk-gated GEMM: invalidate this XCD's caches once, before any
+  // operand is loaded.  A row of chunk c is only ever loaded after
+  // ready[c] has been seen set, and the producer publishes the data before
+  // the flag (release), so no cache can hold a stale copy of it afterwards:
+  // the per-chunk wait needs no further invalidation (which would throw away
+  // every tile's cached operands on each chunk arrival).
+  if (p.ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int total_units = p.total_tiles * p.splits;
   for (int u = blockIdx.x; u < total_units; u += gridDim.x) {
     const Unit un = map_unit(p, u);

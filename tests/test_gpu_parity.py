@@ -412,3 +412,36 @@ def test_split_k_narrow_gemm():
     sync()
     yd, _ = ops.seq_chunk_gemm(f64(x), f64(wt), trans_b=True, act=_abi.ACT_GELU_ERF, dact_z=f64(zin))
     assert nerr(Yd, yd) <= TOL["bf16"]
+
+
+def test_chunk_gating_reads_fresh_data_after_stale_reads():
+    # The consumer GEMM first reads X while it holds zeros (so caches may hold
+    # those lines), then the chunks are rewritten with real data on a side
+    # stream while the gated GEMM waits: the result must use the new data.
+    M, N, K, C = 2048, 512, 1024, 8
+    Xsrc = dev_bf16(si.normal_f32((M, K), 91))
+    W = dev_bf16(si.normal_f32((K, N), 92, 0.05))
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    ref = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(Xsrc, W, ref, num_chunks=C, workspace=ws)
+    X = torch.zeros_like(Xsrc)
+    Y0 = torch.empty_like(ref)
+    tpm.seq_chunk_gemm(X, W, Y0, num_chunks=C, workspace=ws)      # caches see zeros
+    sync()
+    assert torch.count_nonzero(Y0).item() == 0
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    rows = M // C
+    Y = torch.empty_like(ref)
+    ev = torch.cuda.Event()
+    ev.record()
+    tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_order=list(range(C)), chunk_ready=flags, epoch=3,
+                       workspace=ws)
+    side.wait_event(ev)
+    with torch.cuda.stream(side):
+        for c in range(C):
+            X[c * rows:(c + 1) * rows].copy_(Xsrc[c * rows:(c + 1) * rows])
+            tpm.signal_chunk(flags, c, 3, stream=side)
+    sync()
+    assert tpm.poll_device_error(ws) == 0
+    assert torch.equal(Y, ref)
