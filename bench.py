@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -286,6 +288,24 @@ def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
                 frac_mfma_peak=tf / peak)
 
 
+def recorded_traffic():
+    """HBM bytes per step of the GEMM launches, as measured with rocprofv3
+    FETCH_SIZE / WRITE_SIZE (profiles/gemm_traffic.md), or None when the GEMM
+    source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", "gemm_traffic.md")).read()
+        src = open(os.path.join(ROOT, "sequence_transformer_gemms_amd", "csrc", "gemm_mfma.hip"), "rb").read()
+    except OSError:
+        return None
+    m_b = re.search(r"traffic_bytes_per_step:\s*(\d+)", text)
+    m_h = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_b or not m_h or m_h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(m_b.group(1))
+
+
 def cpu_baseline(sample_tokens: int, target_s: float = 20.0):
     """The fp64 oracle, as it stands, on the first m tokens of the same layer
     (all weights, D = 8192, F/T = 3584): the 12 GEMMs of the step at M = m.
@@ -347,6 +367,12 @@ def main():
     import sequence_transformer_gemms_amd as tpm
     import synthetic_inputs as si
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     layer = Layer(torch, tpm, si)
     torch.cuda.synchronize()
     ms, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1)
@@ -364,7 +390,8 @@ def main():
                    "tokens": 4096, "hidden": 8192, "ffn": 28672, "tp": 8, "chunks": 8,
                    "gflop_per_step": round(flops / 1e9, 1), "frac_mfma_peak": round(value / BF16_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(),
+                     "traffic_unit": "bytes per step (12 GEMM launches + split-K finalisation)",
                      "kernel": "gemm_kernel (bf16 MFMA), all 12 GEMM launches of the step",
                      "gemm_ms_per_step": round(gemm_ms, 4)},
     }
