@@ -31,22 +31,40 @@ namespace tpm {
 namespace {
 
 constexpr int BM = kTileM, BN = kTileN;
-constexpr int THREADS = 256;
 constexpr int ROW_BYTES = 64;                    // K bytes per staged row (32 bf16 / 64 fp8)
 constexpr int TILE_BYTES = 256 * ROW_BYTES;      // one operand tile of one K step: 16 KB
 constexpr int SLOT_BYTES = 2 * TILE_BYTES;       // A + B
 constexpr int NSLOT = 4;                         // ring of K steps in LDS
 constexpr int DIST = NSLOT - 1;                  // K steps loaded ahead of the one computed
-constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per operand tile (4)
-constexpr int EPI_LD = 68;                       // staged epilogue row: 64 floats + 4 pad
-constexpr int EPI_WAVE_FLOATS = 128 * EPI_LD;
-constexpr int SMEM_BYTES =
-    (NSLOT * SLOT_BYTES > 4 * EPI_WAVE_FLOATS * 4) ? NSLOT * SLOT_BYTES : 4 * EPI_WAVE_FLOATS * 4;
+// Wave layouts of the 256 x 256 tile: NW = 4 waves as 2 x 2 (128 x 128 per
+// wave, one wave per SIMD) or NW = 8 waves as 2 x 4 (128 x 64 per wave, two
+// waves per SIMD so that one issues MFMAs while the other waits).
+template <int NW>
+struct Layout {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WAVES_N = NW / 2;              // waves along N
+  static constexpr int NF = 4 * 2 / WAVES_N;          // 32-wide N fragments per wave (4 or 2)
+  static constexpr int WN = 32 * NF;                  // wave tile width (128 or 64)
+  static constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // loads per thread per operand tile
+  static constexpr int EPI_COLS = NW == 4 ? 64 : 32;  // columns staged per epilogue pass
+  static constexpr int EPI_LD = EPI_COLS + 4;         // padded staging row (floats)
+  static constexpr int EPI_WAVE_FLOATS = 128 * EPI_LD;
+  static constexpr int PASSES = WN / EPI_COLS;
+  static constexpr int SMEM = (NSLOT * SLOT_BYTES > NW * EPI_WAVE_FLOATS * 4) ? NSLOT * SLOT_BYTES
+                                                                               : NW * EPI_WAVE_FLOATS * 4;
+};
 
-// K-major tile: 256 rows x 4 chunks of 16 bytes; chunk c of row r is stored
-// at slot c ^ swz_k(r).  The 16 (or 8) rows one ds_read_b128 phase touches
-// then fall in distinct bank groups.
-__device__ __forceinline__ uint32_t swz_k(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+// K-major tile: 256 rows x 64 bytes of K, stored as 128 LDS lines of 128
+// bytes; line L holds row L in its first half and row L + 128 in its second
+// half, so the 32 consecutive rows one ds_read_b128 touches are 128 bytes
+// apart.  Within a line the 16-byte chunk h*4 + c (h = row / 128, c = K
+// chunk) sits at position (h*4 + c) ^ swz_k(L), which spreads those rows over
+// distinct banks.
+__device__ __forceinline__ uint32_t swz_k(uint32_t line) { return (line ^ (line >> 3)) & 7u; }
+__device__ __forceinline__ uint32_t kmaj_offset(uint32_t row, uint32_t c) {
+  const uint32_t line = row & 127u;
+  return line * 128u + ((((row >> 7) << 2) | c) ^ swz_k(line)) * 16u;
+}
 // MN-major tile (bf16): 32 rows of K x 32 chunks; the four K rows read by one
 // transposed read land in distinct bank groups.
 __device__ __forceinline__ uint32_t swz_mn(uint32_t k) { return ((k & 3u) << 2) ^ ((k & 3u) << 1); }
@@ -107,22 +125,24 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
   return un;
 }
 
-// One of the LOADS sixteen-byte loads per thread that stage an operand tile
-// of one K step: thread t of the work-group fills LDS chunk P = j * 256 + t.
+// One of the sixteen-byte loads per thread that stage an operand tile of
+// one K step: thread t of the work-group fills LDS chunk P = j * THREADS + t.
 // kmajor: rows are the M (or N) index, 64 bytes of K each.  Otherwise: rows
 // are K (32 of them), 512 bytes (256 bf16) of M or N each.
-template <bool KMAJ, int ESZ>
+template <bool KMAJ, int ESZ, int THREADS>
 __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end, int k0,
                                           int K, char* lds_tile, int j) {
   static_assert(KMAJ || ESZ == 2, "MN-major staging is bf16 only");
   constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t P = (uint32_t)(j * 256 + tid);
+  const uint32_t P = (uint32_t)(j * THREADS + tid);
   uint32_t voff;
   if (KMAJ) {
-    const uint32_t row = P >> 2;
-    const uint32_t c = (P & 3u) ^ swz_k(row);
+    const uint32_t line = P >> 3;
+    const uint32_t hc = (P & 7u) ^ swz_k(line);   // inverse of kmaj_offset
+    const uint32_t row = ((hc >> 2) << 7) | line;
+    const uint32_t c = hc & 3u;
     const int k = k0 + (int)c * EPC;
     const bool ok = (mn0 + (int)row < mn_end) && (k < K);
     voff = ok ? (uint32_t)((int64_t)(mn0 + (int)row) * ld_bytes + (int64_t)k * ESZ) : kOOB;
@@ -133,7 +153,7 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
     const bool ok = (k0 + (int)row < K) && (mn < mn_end);
     voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)mn * 2) : kOOB;
   }
-  load16_to_lds(rs, voff, lds_tile + (j * 256 + wave * 64) * 16);
+  load16_to_lds(rs, voff, lds_tile + (j * THREADS + wave * 64) * 16);
 }
 
 // One 32 (rows) x 16 (K) bf16 fragment for a 32x32x16 MFMA operand:
@@ -144,7 +164,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk
   if (KMAJ) {
     const uint32_t r = (uint32_t)(rb + (lane & 31));
     const uint32_t c = (uint32_t)(2 * kk + (lane >> 5));
-    const uint32_t addr = r * (uint32_t)ROW_BYTES + ((c ^ swz_k(r)) << 4);
+    const uint32_t addr = kmaj_offset(r, c);
     i32x4 v = *(const lds_i32x4*)((lds_void*)(lds_tile + addr));
     return __builtin_bit_cast(bf16x8, v);
   } else {
@@ -172,9 +192,8 @@ __device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb) {
   const int lane = threadIdx.x & 63;
   const uint32_t r = (uint32_t)(rb + (lane & 31));
   const uint32_t c0 = (uint32_t)(2 * (lane >> 5));
-  const uint32_t sw = swz_k(r);
-  const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + r * (uint32_t)ROW_BYTES + ((c0 ^ sw) << 4)));
-  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + r * (uint32_t)ROW_BYTES + (((c0 + 1u) ^ sw) << 4)));
+  const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0)));
+  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0 + 1u)));
   i32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return v;
 }
@@ -278,17 +297,19 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
   }
 }
 
-template <bool FP8, bool AK, bool BKM>
-__global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
+template <bool FP8, bool AK, bool BKM, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
+  using LY = Layout<NW>;
+  constexpr int THREADS = LY::THREADS, LOADS = LY::LOADS, NF = LY::NF;
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = ROW_BYTES / ESZ;  // K elements per staged step
   constexpr int KSUB = FP8 ? 1 : 2;        // MFMA substeps per K step
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[LY::SMEM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = (wave >> 1) * 128;
-  const int wn = (wave & 1) * 128;
+  const int wm = (wave / LY::WAVES_N) * 128;
+  const int wn = (wave % LY::WAVES_N) * LY::WN;
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
@@ -316,35 +337,35 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
     __syncthreads();  // the previous tile's epilogue staging is done with the LDS
     if (p.ready) wait_group(p, tl.g);
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NF];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NF; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
     auto slot = [&](int k) { return smem + (k % NSLOT) * SLOT_BYTES; };
     auto load_one = [&](char* dst, int L, int k0) {
-      if (L < LOADS) issue_one<AK, ESZ>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
-      else issue_one<BKM, ESZ>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS);
+      if (L < LOADS) issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
+      else issue_one<BKM, ESZ, THREADS>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS);
     };
-    auto read_set = [&](const char* As, const char* Bs, int kk, Frag (&af)[4], Frag (&bfr)[4]) {
+    auto read_set = [&](const char* As, const char* Bs, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (FP8) af[i] = read_frag_fp8(As, wm + 32 * i);
         else af[i] = read_frag<AK>(As, wm + 32 * i, kk);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NF; ++j) {
         if constexpr (FP8) bfr[j] = read_frag_fp8(Bs, wn + 32 * j);
         else bfr[j] = read_frag<BKM>(Bs, wn + 32 * j, kk);
       }
     };
-    auto mfma_row = [&](const Frag& a, const Frag (&bfr)[4], f32x16 (&accrow)[4]) {
+    auto mfma_row = [&](const Frag& a, const Frag (&bfr)[NF], f32x16 (&accrow)[NF]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NF; ++j) {
         if constexpr (FP8)
           accrow[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], a, accrow[j], 0, 0, 0, 0, 0, 0);
         else
@@ -356,9 +377,9 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
     // before the MFMAs of substep kk (sched_barrier keeps the scheduler from
     // sinking them).  The restrict qualifiers tell the compiler that the slot
     // being filled and the slot being read do not overlap.
-    constexpr int LOADS_PER_GROUP = (2 * LOADS) / (KSUB * 4);
+    constexpr int TOTAL_LOADS = 2 * LOADS, GROUPS = KSUB * 4;
     auto iteration = [&](const char* __restrict__ cur, char* __restrict__ nxt, int k_next) {
-      Frag fa[2][4], fb[2][4];
+      Frag fa[2][4], fb[2][NF];
       read_set(cur, cur + TILE_BYTES, 0, fa[0], fb[0]);
       const bool more = k_next >= 0;
       static_for<KSUB>([&](auto kkc) {
@@ -369,9 +390,10 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
           constexpr int i = decltype(ic)::value;
           mfma_row(fa[kk & 1][i], fb[kk & 1], acc[i]);
           if (more) {
-            static_for<LOADS_PER_GROUP>([&](auto rc) {
-              constexpr int L = (kk * 4 + i) * LOADS_PER_GROUP + decltype(rc)::value;
-              load_one(nxt, L, k_next);
+            // load L goes out after MFMA group L * GROUPS / TOTAL_LOADS
+            static_for<TOTAL_LOADS>([&](auto lc) {
+              constexpr int L = decltype(lc)::value;
+              if constexpr (L * GROUPS / TOTAL_LOADS == kk * 4 + i) load_one(nxt, L, k_next);
             });
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -413,25 +435,36 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_kernel(const GemmParams p) {
     //      the element-wise code then runs in one compact loop and every
     //      global store is 16 bytes wide.
     float lmax = 0.f;
-    float* stage = reinterpret_cast<float*>(smem) + wave * EPI_WAVE_FLOATS;
-    static_for<2>([&](auto pc) {
+    float* stage = reinterpret_cast<float*>(smem) + wave * LY::EPI_WAVE_FLOATS;
+    constexpr int EPI_LD = LY::EPI_LD, EPI_COLS = LY::EPI_COLS;
+    constexpr int FPP = EPI_COLS / 32;                 // fragments per pass
+    static_for<LY::PASSES>([&](auto pc) {
       constexpr int pass = decltype(pc)::value;
-      static_for<32>([&](auto c) {
-        constexpr int i = decltype(c)::value / 8;
-        constexpr int jj = (decltype(c)::value / 4) % 2;
+      static_for<4 * FPP * 4>([&](auto c) {
+        constexpr int i = decltype(c)::value / (FPP * 4);
+        constexpr int jj = (decltype(c)::value / 4) % FPP;
         constexpr int q = decltype(c)::value % 4;
-        constexpr int j = 2 * pass + jj;
+        constexpr int j = FPP * pass + jj;
         const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         *(f32x4*)(stage + (32 * i + (lane & 31)) * EPI_LD + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
       });
+      // read back 8 consecutive columns per lane
+      constexpr int LPR = EPI_COLS / 8;                // lanes per staged row
+      constexpr int RPI = 64 / LPR;                    // rows per iteration
 #pragma unroll 1
-      for (int it = 0; it < 16; ++it) {
-        const int rl = it * 8 + (lane >> 3);
-        const int cl = (lane & 7) * 8;
+      for (int it = 0; it < 128 / RPI; ++it) {
+        int rl, cl;
+        if constexpr (NW == 4) {
+          rl = it * RPI + lane / LPR;
+          cl = (lane % LPR) * 8;
+        } else {
+          rl = it * RPI + (lane % RPI);  // consecutive lanes on consecutive rows: no bank conflicts
+          cl = (lane / RPI) * 8;
+        }
         const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
         const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
         const int row = tl.m0 + wm + rl;
-        const int col = tl.n0 + wn + 64 * pass + cl;
+        const int col = tl.n0 + wn + EPI_COLS * pass + cl;
         if (row < tl.m_end && col < p.N) {
           if (p.splits > 1) {
             // raw fp32 partial of this K range; splitk_finalize sums them
@@ -506,17 +539,23 @@ static hipError_t finalize_if_split(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef TPM_GEMM_WAVES
+#define TPM_GEMM_WAVES 8
+#endif
+constexpr int kWaves = TPM_GEMM_WAVES;
+constexpr int kThreads = 64 * kWaves;
+
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
-  if (a_kmajor && !b_kmajor) gemm_kernel<false, true, false><<<grid, THREADS, 0, s>>>(p);
-  else if (a_kmajor && b_kmajor) gemm_kernel<false, true, true><<<grid, THREADS, 0, s>>>(p);
-  else if (!a_kmajor && !b_kmajor) gemm_kernel<false, false, false><<<grid, THREADS, 0, s>>>(p);
-  else gemm_kernel<false, false, true><<<grid, THREADS, 0, s>>>(p);
+  if (a_kmajor && !b_kmajor) gemm_kernel<false, true, false, kWaves><<<grid, kThreads, 0, s>>>(p);
+  else if (a_kmajor && b_kmajor) gemm_kernel<false, true, true, kWaves><<<grid, kThreads, 0, s>>>(p);
+  else if (!a_kmajor && !b_kmajor) gemm_kernel<false, false, false, kWaves><<<grid, kThreads, 0, s>>>(p);
+  else gemm_kernel<false, false, true, kWaves><<<grid, kThreads, 0, s>>>(p);
   return finalize_if_split(p, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (!a_kmajor || !b_kmajor) return hipErrorInvalidValue;  // rejected on the host first
-  gemm_kernel<true, true, true><<<grid, THREADS, 0, s>>>(p);
+  gemm_kernel<true, true, true, kWaves><<<grid, kThreads, 0, s>>>(p);
   return finalize_if_split(p, s);
 }
 
