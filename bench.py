@@ -102,36 +102,33 @@ class Layer:
         # one workspace for all seq_chunk_gemm calls (stream-ordered): control
         # words plus the split-K scratch of the narrowest projections
         shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1)]
-        self.ws_g = torch.empty(max(tpm.workspace_bytes(tpm.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
+        self.ws_g = torch.zeros(max(tpm.workspace_bytes(tpm.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
                                 dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
+        self.counters = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.order = si.ring_chunk_order(T, self.C, rank)
         self.dest = si.dest_range_order(T, rank)
-        self.side = torch.cuda.Stream()
+        self.compute, self.side = tpm.masked_streams(producer_cus=8)
         self.gemm_events = []
         fl = lambda m, n, k: 2.0 * m * n * k
         self.flops = (3 * fl(M, Nq, D) + 3 * fl(M, Ft, D) + 3 * fl(M, D, Da) + 3 * fl(M, D, Ft))
 
-    # -- chunk arrival: side stream copies the remote chunks and signals flags.
-    # The boundary event is recorded on the compute stream before the
-    # chunk-fed GEMM is enqueued; the copies are enqueued after it (so the
-    # host-side launch cost of the copies overlaps the GEMM), but start at
-    # the boundary.
+    # -- chunk arrival: the producer stream writes the remote chunks in ring
+    # order (one tpm_write_chunks launch, which publishes each chunk's ready
+    # flag as soon as its rows are in place; the rank's own chunks are only
+    # flagged).  The boundary event is recorded on the compute stream before
+    # the chunk-fed GEMM is enqueued; the writer is enqueued after it (its
+    # host-side launch cost overlaps the GEMM) but starts at the boundary.
     def _boundary(self):
         ev = self.torch.cuda.Event()
         ev.record(self.torch.cuda.current_stream())
         return ev
 
     def _arrive(self, which, dst, src, epoch, boundary):
-        torch, tpm = self.torch, self.tpm
-        rows = self.M // self.C
         own = set(range(self.rank * (self.C // self.T), (self.rank + 1) * (self.C // self.T)))
         self.side.wait_event(boundary)            # communication starts at the layer boundary
-        with torch.cuda.stream(self.side):
-            for c in self.order:
-                if c not in own:
-                    dst[c * rows:(c + 1) * rows].copy_(src[c * rows:(c + 1) * rows])
-                tpm.signal_chunk(self.flags[which], c, epoch, stream=self.side)
+        self.tpm.write_chunks(dst, src, self.C, self.order, self.flags[which], epoch, self.counters[which],
+                              copy=[c not in own for c in range(self.C)], stream=self.side)
 
     def _timed(self, fn, record):
         if not record:
@@ -144,7 +141,15 @@ class Layer:
         b.record()
         self.gemm_events.append((a, b))
 
-    def step(self, epoch: int, arrive: bool = True, record: bool = False):
+    def _check(self, ws, check):
+        if not check:
+            return
+        self.torch.cuda.synchronize()
+        err = self.tpm.poll_device_error(ws)
+        if err != 0:
+            raise RuntimeError(f"device error {err} in a chunk-gated call (watchdog): the timing is invalid")
+
+    def step(self, epoch: int, arrive: bool = True, record: bool = False, check: bool = False):
         torch, tpm = self.torch, self.tpm
         T, r, C = self.T, self.rank, self.C
         ready = (lambda i: self.flags[i]) if arrive else (lambda i: None)
@@ -157,6 +162,7 @@ class Layer:
                                                workspace=wsg), record)
         if arrive:
             self._arrive(0, self.x_qkv, self.x_src, epoch, b)
+        self._check(wsg, check)
         self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
                                                chunk_order=self.dest, workspace=wsg), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
@@ -168,6 +174,7 @@ class Layer:
                                            workspace=self.ws_fwd), record)
         if arrive:
             self._arrive(1, self.x_mlp, self.x_src, epoch, b)
+        self._check(self.ws_fwd, check)
         tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
         # ---- backward, MLP
         b = self._boundary()
@@ -177,17 +184,27 @@ class Layer:
                                            dy_ready=ready(2), epoch=epoch, workspace=self.ws_bwd), record)
         if arrive:
             self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
+        self._check(self.ws_bwd, check)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
         # ---- backward, O projection: dA = dY_o W_o^T (chunk-fed), dW_o = A^T dY_o
         b = self._boundary()
 
-        def o_bwd():
+        def o_bwd_dgrad():
             tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
                                chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=wsg)
+
+        def o_bwd_wgrad():
             tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg)
-        self._timed(o_bwd, record)
-        if arrive:
-            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
+        if check:
+            o_bwd_dgrad()
+            if arrive:
+                self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
+            self._check(wsg, check)
+            o_bwd_wgrad()
+        else:
+            self._timed(lambda: (o_bwd_dgrad(), o_bwd_wgrad()), record)
+            if arrive:
+                self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
 
         # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T (partial)
         def qkv_bwd():
@@ -202,21 +219,56 @@ class Layer:
 
 
 def time_steps(torch, layer, steps, warmup, arrive, epoch0):
-    for i in range(warmup):
-        layer.step(epoch0 + i, arrive=arrive)
-    torch.cuda.synchronize()
-    layer.gemm_events = []
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        layer.step(epoch0 + warmup + i, arrive=arrive, record=True)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / steps
-    gemm_ms = sum(a.elapsed_time(b) for a, b in layer.gemm_events) / steps
+    """Warm-up, then `steps` timed steps on the compute stream (the CU-masked
+    one when chunks arrive from the producer stream, the default stream with
+    every CU when all chunks are resident)."""
+    stream = layer.compute if arrive else torch.cuda.default_stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            layer.step(epoch0 + i, arrive=arrive)
+        torch.cuda.synchronize()
+        layer.gemm_events = []
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            layer.step(epoch0 + warmup + i, arrive=arrive, record=True)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = start.elapsed_time(stop) / steps
+        gemm_ms = sum(a.elapsed_time(b) for a, b in layer.gemm_events) / steps
+        # one more step that synchronises after every chunk-gated call and
+        # reads its device error word: a wait that ran into the watchdog would
+        # have made the timed steps meaningless
+        if arrive:
+            layer.step(epoch0 + warmup + steps, arrive=arrive, check=True)
     return ms, gemm_ms, wall
+
+
+def arrival_step(torch, layer, args, ms_resident):
+    """The same step with the chunk-fed GEMMs (QKV, MLP up, dZ, dA) gated on
+    chunks that a producer stream writes in ring order while they run, the
+    producer confined to 8 CUs and the GEMMs to the others.  Reports the
+    writer's time alone (4 launches of 7 x 8 MB) and the overlap efficiency
+    (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
+    ms, gemm_ms, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    epoch = 5000
+    for rep in range(2):
+        a.record(layer.side)
+        for which, (dst, src) in enumerate(((layer.x_qkv, layer.x_src), (layer.x_mlp, layer.x_src),
+                                            (layer.dy_mlp, layer.dy_mlp_src), (layer.dy_o, layer.dy_o_src))):
+            layer._arrive(which, dst, src, epoch + rep, a)
+        b.record(layer.side)
+        torch.cuda.synchronize()
+    t_copy = a.elapsed_time(b)
+    eff = (ms_resident + t_copy - ms) / min(ms_resident, t_copy)
+    return {"ms": round(ms, 4), "TFLOPS": round(layer.flops / (ms * 1e-3) / 1e12, 2),
+            "gemm_TFLOPS": round(layer.flops / (gemm_ms * 1e-3) / 1e12, 2),
+            "writer_only_ms": round(t_copy, 4), "overlap_efficiency": round(eff, 3),
+            "producer_cus": 8}
 
 
 def bench_reduce(torch, tpm, si, iters=40):
@@ -375,7 +427,9 @@ def main():
         del src, dst
     layer = Layer(torch, tpm, si)
     torch.cuda.synchronize()
-    ms, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1)
+    # headline: the rank's step with every chunk already in place (flags
+    # not consulted), on the default stream with every CU
+    ms, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=0)
     flops = layer.flops
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (gemm_ms * 1e-3) / 1e12
@@ -385,8 +439,9 @@ def main():
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Llama3-70B-shaped TP=8 rank layer share fwd+bwd: QKV [8192,1280], O [1024,8192], "
-                               "MLP up [8192,3584] + GeLU, down [3584,8192]; 4096 tokens, 8 sequence chunks "
-                               "arriving on a side stream; 4 sequence-sharded reductions of 8 partials",
+                               "MLP up [8192,3584] + GeLU, down [3584,8192]; 4096 tokens; 4 sequence-sharded "
+                               "reductions of 8 partials; inputs resident in HBM (the step with the 8 sequence "
+                               "chunks arriving from a producer stream is extra.arrival_step)",
                    "tokens": 4096, "hidden": 8192, "ffn": 28672, "tp": 8, "chunks": 8,
                    "gflop_per_step": round(flops / 1e9, 1), "frac_mfma_peak": round(value / BF16_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -396,9 +451,7 @@ def main():
                      "gemm_ms_per_step": round(gemm_ms, 4)},
     }
     if not args.no_extra:
-        ms_r, gemm_ms_r, _ = time_steps(torch, layer, max(5, args.steps // 2), 2, arrive=False, epoch0=0)
-        extra = {"resident_step": {"ms": round(ms_r, 4), "TFLOPS": round(flops / (ms_r * 1e-3) / 1e12, 2),
-                                   "gemm_TFLOPS": round(flops / (gemm_ms_r * 1e-3) / 1e12, 2)}}
+        extra = {"arrival_step": arrival_step(torch, layer, args, ms)}
         del layer
         torch.cuda.empty_cache()
         extra["reduce_c3"] = bench_reduce(torch, tpm, si)

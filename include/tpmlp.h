@@ -191,9 +191,40 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
  * `flag` (marks a chunk as landed after the copies enqueued before it). */
 int tpm_signal_chunk(void* stream, uint32_t* flag, uint32_t value);
 
+/*
+ * tpm_write_chunks -- the side-stream writer of sequence-chunk arrival.  In
+ * tensor-sequence parallelism the input of a column-parallel GEMM reaches a
+ * rank as token chunks from its peers (the all-gather in front of the GEMM,
+ * "Collective GEMMs in Tensor Sequence Parallelism", section "Collective
+ * GEMMs (CGEMM)"); on one GPU a copy from a staging buffer stands in for the
+ * peers' writes.  One kernel launch writes, for i = 0 .. num_chunks-1 and
+ * chunk c = order[i], the bytes [c*chunk_bytes, (c+1)*chunk_bytes) of src
+ * into the same range of dst (skipped when copy != NULL and copy[c] == 0:
+ * a chunk already in place), and as soon as the whole chunk is written sets
+ * ready[c] = epoch with a release store, so a chunk-gated GEMM can start on
+ * chunk c while later chunks are still being written.
+ *   dst, src   device, 16-byte aligned; chunk_bytes a multiple of 16.
+ *   order      host, a permutation of 0 .. num_chunks-1 (<= TPM_MAX_CHUNKS).
+ *   copy       host, num_chunks bytes indexed by chunk id, or NULL (copy all).
+ *   ready      device, num_chunks words.
+ *   counters   device, num_chunks words, zero before the first call; every
+ *              call leaves them zero.  Calls that share counters must not
+ *              overlap.
+ * Work-groups: one per compute unit of the stream's CU mask (at most 64), or
+ * 8 on a stream that may use every CU.  Run it on a stream whose CU mask is
+ * disjoint from that of the consuming GEMM's stream: a writer work-group
+ * dispatched to a CU held by a waiting GEMM work-group cannot start, and the
+ * GEMM then ends with TPM_ETIMEOUT.
+ * Errors: TPM_EINVAL (arguments), TPM_EHIP (launch).
+ */
+int tpm_write_chunks(void* dst, const void* src, int64_t chunk_bytes, int num_chunks, const int32_t* order,
+                     const uint8_t* copy, uint32_t* ready, uint32_t epoch, uint32_t* counters, void* stream);
+
 /* After synchronising the stream: TPM_OK, or TPM_ETIMEOUT if a chunk wait
- * of the last chunk-gated call on this workspace gave up.  Blocking copy of
- * one device word. */
+ * of the last chunk-gated call on this workspace gave up.  Only chunk-gated
+ * (and fp8) calls reset the error word, so on a workspace that has seen none
+ * it reads whatever the memory held (zero-fill a new workspace).  Blocking
+ * copy of one device word. */
 int tpm_poll_device_error(const void* workspace, size_t workspace_bytes);
 
 /* Number of polls a device-side chunk wait makes before it gives up and

@@ -18,10 +18,11 @@ import torch
 from . import _abi
 from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, BF16, EPI_DACT, EPI_FWD, F32,  # noqa: F401
                    FP8_E4M3, OP_MLP_BWD, OP_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+from .streams import masked_streams  # noqa: F401
 
 __all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "partial_reduce_seqshard",
-           "workspace_bytes", "alloc_workspace", "signal_chunk", "poll_device_error",
-           "set_wait_limit", "dtype_code", "TpmError", "lib"]
+           "workspace_bytes", "alloc_workspace", "signal_chunk", "write_chunks", "poll_device_error",
+           "set_wait_limit", "dtype_code", "masked_streams", "TpmError", "lib"]
 
 
 def dtype_code(t: torch.dtype) -> int:
@@ -61,7 +62,8 @@ def workspace_bytes(op: int, M: int, N: int, K: int, T: int = 1, num_chunks: int
 
 def alloc_workspace(op: int, M: int, N: int, K: int, T: int = 1, num_chunks: int = 1, dtype: int = BF16,
                     device="cuda") -> torch.Tensor:
-    return torch.empty(max(workspace_bytes(op, M, N, K, T, num_chunks, dtype), 1), dtype=torch.uint8, device=device)
+    # zero-filled: the error word reads TPM_OK until a chunk-gated call sets it
+    return torch.zeros(max(workspace_bytes(op, M, N, K, T, num_chunks, dtype), 1), dtype=torch.uint8, device=device)
 
 
 def seq_chunk_gemm(A, B, Y, *, trans_a=False, trans_b=False, a_scale=None, b_scale=None,
@@ -140,6 +142,23 @@ def signal_chunk(flag_tensor, index: int, value: int, stream=None):
     """Release-store `value` into flag_tensor[index] (device uint32/int32) on `stream`."""
     ptr = flag_tensor.data_ptr() + 4 * index
     return check(lib.tpm_signal_chunk(_stream(stream), ptr, value))
+
+
+def write_chunks(dst, src, num_chunks: int, order, ready, epoch: int, counters, copy=None, stream=None):
+    """Side-stream chunk writer: for c in `order`, copy rows chunk c of `src`
+    into `dst` (skipped where copy[c] is false) and then set ready[c] = epoch.
+    dst/src: contiguous device tensors of equal size, split into num_chunks
+    equal chunks; ready/counters: device int32/uint32 tensors of num_chunks
+    words (counters zero before the first call)."""
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != nbytes or not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("write_chunks: dst and src must be contiguous and of equal size")
+    if nbytes % num_chunks != 0:
+        raise ValueError("write_chunks: size not divisible by num_chunks")
+    order_arr = (ctypes.c_int32 * num_chunks)(*[int(c) for c in order])
+    copy_arr = None if copy is None else (ctypes.c_uint8 * num_chunks)(*[1 if b else 0 for b in copy])
+    return check(lib.tpm_write_chunks(_ptr(dst), _ptr(src), nbytes // num_chunks, num_chunks, order_arr, copy_arr,
+                                      _ptr(ready), epoch, _ptr(counters), _stream(stream)))
 
 
 def poll_device_error(workspace) -> int:

@@ -62,6 +62,8 @@ lib.tpm_workspace_bytes.restype = _sz
 lib.tpm_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i32, _i32]
 lib.tpm_signal_chunk.restype = _i32
 lib.tpm_signal_chunk.argtypes = [_vp, _vp, _u32]
+lib.tpm_write_chunks.restype = _i32
+lib.tpm_write_chunks.argtypes = [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _u32, _vp, _vp]
 lib.tpm_poll_device_error.restype = _i32
 lib.tpm_poll_device_error.argtypes = [_vp, _sz]
 lib.tpm_set_wait_limit.restype = _i32
@@ -72,7 +74,7 @@ lib.tpm_version.restype = ctypes.c_char_p
 lib.tpm_version.argtypes = []
 
 EXPORTS = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "partial_reduce_seqshard",
-           "tpm_workspace_bytes", "tpm_signal_chunk", "tpm_poll_device_error",
+           "tpm_workspace_bytes", "tpm_signal_chunk", "tpm_write_chunks", "tpm_poll_device_error",
            "tpm_set_wait_limit", "tpm_last_error", "tpm_version"]
 
 

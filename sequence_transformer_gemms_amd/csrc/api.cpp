@@ -50,6 +50,22 @@ int num_cus() {
   return cached[dev];
 }
 
+// Compute units a kernel enqueued on stream s may use: the popcount of the
+// stream's CU mask (streams made with hipExtStreamCreateWithCUMask), else
+// the device's count.
+int stream_cus(hipStream_t s) {
+  const int dev_cus = num_cus();
+  uint32_t mask[32] = {0};
+  const uint32_t words = (uint32_t)std::min(32, (dev_cus + 31) / 32);
+  if (hipExtStreamGetCUMask(s, words, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return dev_cus;
+  }
+  int n = 0;
+  for (uint32_t i = 0; i < words; ++i) n += __builtin_popcount(mask[i]);
+  return (n > 0 && n <= dev_cus) ? n : dev_cus;
+}
+
 int esize(int dt) { return dt == TPM_F32 ? 4 : dt == TPM_BF16 ? 2 : 1; }
 bool valid_dt(int dt) { return dt == TPM_F32 || dt == TPM_BF16 || dt == TPM_FP8_E4M3; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -183,10 +199,13 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   p.tiles_per_group = p.mt_per_group * p.nt;
   p.total_tiles = p.tiles_per_group * p.num_groups;
   p.band_m = std::min(p.mt_per_group, 4);
-  // persistent grid: one work-group per CU; when chunks are gated on flags
-  // written by another stream, leave one CU per XCD free for the producer.
-  int cus = num_cus();
-  int grid = g.ready ? cus - 8 : cus;
+  // persistent grid: one work-group per CU the stream may use.  A
+  // chunk-gated GEMM on a stream that may use every CU leaves one CU per XCD
+  // to a producer that runs kernels on this device; a stream with a CU mask
+  // is taken to leave the producer its own CUs.
+  const int cus = num_cus();
+  const int avail = stream_cus(s);
+  int grid = (g.ready && avail == cus) ? cus - 8 : avail;
   grid = std::max(8, grid);
   grid = std::min(grid, p.total_tiles * p.splits);
   if (g.adt == TPM_BF16) e = launch_gemm_bf16(p, !g.ta, g.tb, grid, s);
@@ -246,6 +265,39 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
     }
     default: return 0;
   }
+}
+
+int tpm_write_chunks(void* dst, const void* src, int64_t chunk_bytes, int num_chunks, const int32_t* order,
+                     const uint8_t* copy, uint32_t* ready, uint32_t epoch, uint32_t* counters, void* stream) {
+  const char* who = "tpm_write_chunks";
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks out of range", who);
+  if (chunk_bytes < 0 || chunk_bytes % 16 != 0) return fail(TPM_EINVAL, "%s: chunk_bytes must be a multiple of 16", who);
+  if (!order || !ready || !counters) return fail(TPM_EINVAL, "%s: null order, ready or counters", who);
+  if (chunk_bytes > 0 && (!dst || !src)) return fail(TPM_EINVAL, "%s: null buffer", who);
+  if ((((uintptr_t)dst | (uintptr_t)src) & 15) != 0) return fail(TPM_EINVAL, "%s: buffers must be 16-byte aligned", who);
+  WriterParams p;
+  std::memset(&p, 0, sizeof(p));
+  std::vector<int> seen(num_chunks, 0);
+  for (int i = 0; i < num_chunks; ++i) {
+    const int c = order[i];
+    if (c < 0 || c >= num_chunks || seen[c]++) return fail(TPM_EINVAL, "%s: order is not a permutation", who);
+    p.order[i] = (int16_t)c;
+  }
+  for (int c = 0; c < num_chunks; ++c) p.copy[c] = (uint8_t)(copy ? (copy[c] != 0) : 1);
+  p.src = (const char*)src;
+  p.dst = (char*)dst;
+  p.chunk_bytes = chunk_bytes;
+  p.ready = ready;
+  p.counters = counters;
+  p.epoch = epoch;
+  p.n = num_chunks;
+  // one work-group per CU of the stream's mask (a producer stream confined
+  // to a few CUs), 8 on a stream that may use every CU
+  const hipStream_t s = (hipStream_t)stream;
+  const int avail = stream_cus(s);
+  const int groups = std::max(1, std::min(64, avail == num_cus() ? 8 : avail));
+  hipError_t e = launch_write_chunks(p, groups, s);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
 }
 
 int tpm_signal_chunk(void* stream, uint32_t* flag, uint32_t value) {

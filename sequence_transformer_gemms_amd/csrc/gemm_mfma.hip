@@ -46,10 +46,14 @@ struct Layout {
   static constexpr int NF = 4 * 2 / WAVES_N;          // 32-wide N fragments per wave (4 or 2)
   static constexpr int WN = 32 * NF;                  // wave tile width (128 or 64)
   static constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // loads per thread per operand tile
-  static constexpr int EPI_COLS = NW == 4 ? 64 : 32;  // columns staged per epilogue pass
-  static constexpr int EPI_LD = EPI_COLS + 4;         // padded staging row (floats)
-  static constexpr int EPI_WAVE_FLOATS = 128 * EPI_LD;
-  static constexpr int PASSES = WN / EPI_COLS;
+  // Epilogue staging: each pass moves EPI_ROWS x 64 fp32 of the wave tile
+  // through LDS, so every row segment a wave stores is 128 bytes of bf16.
+  static constexpr int EPI_COLS = 64;
+  static constexpr int EPI_ROWS = NW == 4 ? 128 : 64;  // 8 waves x 64 rows keeps the staging within 139 KB
+  static constexpr int EPI_LD = EPI_COLS + 4;          // padded staging row (floats)
+  static constexpr int EPI_WAVE_FLOATS = EPI_ROWS * EPI_LD;
+  static constexpr int COL_PASSES = WN / EPI_COLS;
+  static constexpr int PASSES = (128 / EPI_ROWS) * COL_PASSES;
   static constexpr int SMEM = (NSLOT * SLOT_BYTES > NW * EPI_WAVE_FLOATS * 4) ? NSLOT * SLOT_BYTES
                                                                                : NW * EPI_WAVE_FLOATS * 4;
 };
@@ -68,13 +72,6 @@ __device__ __forceinline__ uint32_t kmaj_offset(uint32_t row, uint32_t c) {
 // MN-major tile (bf16): 32 rows of K x 32 chunks; the four K rows read by one
 // transposed read land in distinct bank groups.
 __device__ __forceinline__ uint32_t swz_mn(uint32_t k) { return ((k & 3u) << 2) ^ ((k & 3u) << 1); }
-
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 struct Tile {
   int g, m0, m_end, n0;
@@ -346,21 +343,27 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-    auto slot = [&](int k) { return smem + (k % NSLOT) * SLOT_BYTES; };
-    auto load_one = [&](char* dst, int L, int k0) {
+    auto slot = [&](int k) { return smem + (k & (NSLOT - 1)) * SLOT_BYTES; };
+    // Load L (0 .. 2*LOADS-1) of K step k of this split into its slot.  Steps
+    // past the end of the split load zeros (out-of-range offsets) into a slot
+    // that no later step of this tile reads, so the issue pattern and the
+    // load counts are the same for every step.
+    auto load_one = [&](int L, int k) {
+      char* dst = slot(k);
+      const int k0 = k < nks ? (kbeg + k) * KSTEP : p.K;
       if (L < LOADS) issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
       else issue_one<BKM, ESZ, THREADS>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS);
     };
-    auto read_set = [&](const char* As, const char* Bs, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
+    auto read_set = [&](const char* __restrict__ st, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FP8) af[i] = read_frag_fp8(As, wm + 32 * i);
-        else af[i] = read_frag<AK>(As, wm + 32 * i, kk);
+        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i);
+        else af[i] = read_frag<AK>(st, wm + 32 * i, kk);
       }
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
-        if constexpr (FP8) bfr[j] = read_frag_fp8(Bs, wn + 32 * j);
-        else bfr[j] = read_frag<BKM>(Bs, wn + 32 * j, kk);
+        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j);
+        else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
       }
     };
     auto mfma_row = [&](const Frag& a, const Frag (&bfr)[NF], f32x16 (&accrow)[NF]) {
@@ -372,99 +375,125 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
           accrow[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], a, accrow[j], 0, 0, 0);
       }
     };
-    // One K step: the 2 * LOADS loads of step k + DIST are spread between
-    // the MFMA groups of this step, the fragments of substep kk+1 are read
-    // before the MFMAs of substep kk (sched_barrier keeps the scheduler from
-    // sinking them).  The restrict qualifiers tell the compiler that the slot
-    // being filled and the slot being read do not overlap.
-    constexpr int TOTAL_LOADS = 2 * LOADS, GROUPS = KSUB * 4;
-    auto iteration = [&](const char* __restrict__ cur, char* __restrict__ nxt, int k_next) {
-      Frag fa[2][4], fb[2][NF];
-      read_set(cur, cur + TILE_BYTES, 0, fa[0], fb[0]);
-      const bool more = k_next >= 0;
-      static_for<KSUB>([&](auto kkc) {
-        constexpr int kk = decltype(kkc)::value;
-        if constexpr (kk + 1 < KSUB) read_set(cur, cur + TILE_BYTES, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<4>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          mfma_row(fa[kk & 1][i], fb[kk & 1], acc[i]);
-          if (more) {
-            // load L goes out after MFMA group L * GROUPS / TOTAL_LOADS
-            static_for<TOTAL_LOADS>([&](auto lc) {
-              constexpr int L = decltype(lc)::value;
-              if constexpr (L * GROUPS / TOTAL_LOADS == kk * 4 + i) load_one(nxt, L, k_next);
-            });
-          }
-          __builtin_amdgcn_sched_barrier(0);
+    // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
+    // loads L0 .. L0+NL-1 of K step kl spread between the row groups.
+    constexpr int TOTAL_LOADS = 2 * LOADS, HALF_LOADS = TOTAL_LOADS / 2;
+    auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl) {
+      constexpr int I0 = decltype(i0c)::value, NI = decltype(nic)::value;
+      constexpr int L0 = decltype(l0c)::value, NL = decltype(nlc)::value;
+      static_for<NI>([&](auto ic) {
+        constexpr int ii = decltype(ic)::value;
+        mfma_row(fa[I0 + ii], fb, acc[I0 + ii]);
+        static_for<NL>([&](auto lc) {
+          constexpr int l = decltype(lc)::value;
+          if constexpr (l * NI / NL == ii) load_one(L0 + l, kl);
         });
+        __builtin_amdgcn_sched_barrier(0);
       });
     };
-
-    // Ring of NSLOT K steps.  Before computing step kt, this thread waits
-    // until its loads for step kt have landed: the loads still allowed in
-    // flight are those of the (at most DIST - 1) later steps already issued.
-    // The barrier then makes every thread's loads visible and guarantees
-    // that step kt-1's slot, which step kt+DIST refills, is no longer read.
-#pragma unroll
-    for (int k = 0; k < DIST; ++k)
-      if (k < nks)
-#pragma unroll
-        for (int L = 0; L < 2 * LOADS; ++L) load_one(slot(k), L, (kbeg + k) * KSTEP);
-    for (int kt = 0; kt < nks; ++kt) {
-      const int ahead = nks - 1 - kt;  // steps after kt already issued: min(DIST - 1, ahead)
-      if (ahead >= 2) wait_vmcnt<2 * 2 * LOADS>();
-      else if (ahead == 1) wait_vmcnt<2 * LOADS>();
-      else wait_vmcnt<0>();
-      // a bare s_barrier: __syncthreads() would also wait for the loads of
-      // the later steps.  The empty asm statements keep the compiler from
-      // moving LDS accesses across it.
+    // Wait until at most N of this thread's loads are in flight and all of
+    // its LDS reads are done, then synchronise the work-group with a bare
+    // s_barrier (__syncthreads() would also wait for every load in flight).
+    // The empty asm statements keep the compiler from moving LDS accesses
+    // across it.
+    auto step_barrier = [&]() {
+      constexpr int N = TOTAL_LOADS + HALF_LOADS;
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const int kn = kt + DIST;
-      iteration(slot(kt), slot(kn), kn < nks ? (kbeg + kn) * KSTEP : -1);
+    };
+
+    // Software pipeline over a ring of NSLOT K steps in LDS; loads run DIST
+    // steps ahead.  Step kt is computed in two halves (bf16: its two K
+    // substeps; fp8: accumulator rows 0-1, then 2-3).  Between the halves
+    // each thread waits for its loads of step kt+1 (the loads of steps kt+2
+    // and of the first half of kt+3 stay in flight) and the barrier makes
+    // every thread's loads visible; the fragments of step kt+1 are then read
+    // from LDS while the second half's MFMAs run, so no step starts with an
+    // LDS round trip.  The barrier also orders every read of step kt's slot
+    // (finished before it) before the loads of step kt+NSLOT into that slot
+    // (issued after the next one).
+    Frag fa[2][4], fb[2][NF];
+    static_for<DIST>([&](auto kc) {
+      static_for<TOTAL_LOADS>([&](auto lc) { load_one(decltype(lc)::value, decltype(kc)::value); });
+    });
+    {
+      constexpr int N = (DIST - 1) * TOTAL_LOADS;  // step 0 has landed
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
+    read_set(slot(0), 0, fa[0], fb[0]);
+    // P: fragment set that holds step kt (fp8 alternates sets between steps;
+    // bf16 always starts a step in set 0 and prefetches substep 1 into set 1)
+    auto compute_step = [&](auto pc, int kt) {
+      constexpr int P = decltype(pc)::value;
+      const char* cur = slot(kt);
+      const int kl = kt + DIST;
+      const bool has_next = kt + 1 < nks;
+      if constexpr (FP8) {
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<HALF_LOADS>{}, fa[P], fb[P], kl);
+        if (has_next) {
+          step_barrier();
+          read_set(slot(kt + 1), 0, fa[1 - P], fb[1 - P]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<2>{}, IC<2>{}, IC<HALF_LOADS>{}, IC<TOTAL_LOADS - HALF_LOADS>{}, fa[P], fb[P], kl);
+      } else {
+        read_set(cur, 1, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<HALF_LOADS>{}, fa[0], fb[0], kl);
+        if (has_next) {
+          step_barrier();
+          read_set(slot(kt + 1), 0, fa[0], fb[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<HALF_LOADS>{}, IC<TOTAL_LOADS - HALF_LOADS>{}, fa[1], fb[1], kl);
+      }
+    };
+    int kt = 0;
+    for (; kt + 1 < nks; kt += 2) {
+      compute_step(IC<0>{}, kt);
+      compute_step(IC<1>{}, kt + 1);
+    }
+    if (kt < nks) compute_step(IC<0>{}, kt);
     __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
 
     // ---- epilogue.  Lane l holds rows m0+wm+32i+l%32 and columns
     //      n0+wn+32j+8q+4*(l/32)+{0..3} in acc[i][j][4q..4q+3].  Each wave
-    //      stages its 128 x 128 fp32 block through a private LDS region, 64
-    //      columns at a time (rows padded to 68 floats against bank
+    //      stages its 128 x WN fp32 block through a private LDS region,
+    //      EPI_ROWS x 64 at a time (rows padded to 68 floats against bank
     //      conflicts), and reads it back as 8 consecutive columns per lane:
     //      the element-wise code then runs in one compact loop and every
-    //      global store is 16 bytes wide.
+    //      global store is 16 bytes wide, eight lanes covering 128 bytes.
     float lmax = 0.f;
     float* stage = reinterpret_cast<float*>(smem) + wave * LY::EPI_WAVE_FLOATS;
-    constexpr int EPI_LD = LY::EPI_LD, EPI_COLS = LY::EPI_COLS;
-    constexpr int FPP = EPI_COLS / 32;                 // fragments per pass
+    constexpr int EPI_LD = LY::EPI_LD, EPI_COLS = LY::EPI_COLS, EPI_ROWS = LY::EPI_ROWS;
+    constexpr int FPP = EPI_COLS / 32;                 // column fragments per pass
+    constexpr int IPP = EPI_ROWS / 32;                 // row fragments per pass
     static_for<LY::PASSES>([&](auto pc) {
       constexpr int pass = decltype(pc)::value;
-      static_for<4 * FPP * 4>([&](auto c) {
-        constexpr int i = decltype(c)::value / (FPP * 4);
+      constexpr int rp = pass / LY::COL_PASSES, cp = pass % LY::COL_PASSES;
+      static_for<IPP * FPP * 4>([&](auto c) {
+        constexpr int ii = decltype(c)::value / (FPP * 4);
         constexpr int jj = (decltype(c)::value / 4) % FPP;
         constexpr int q = decltype(c)::value % 4;
-        constexpr int j = FPP * pass + jj;
+        constexpr int i = IPP * rp + ii;
+        constexpr int j = FPP * cp + jj;
         const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        *(f32x4*)(stage + (32 * i + (lane & 31)) * EPI_LD + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
+        *(f32x4*)(stage + (32 * ii + (lane & 31)) * EPI_LD + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
       });
-      // read back 8 consecutive columns per lane
-      constexpr int LPR = EPI_COLS / 8;                // lanes per staged row
-      constexpr int RPI = 64 / LPR;                    // rows per iteration
+      // read back 8 consecutive columns per lane, 8 lanes per row
 #pragma unroll 1
-      for (int it = 0; it < 128 / RPI; ++it) {
-        int rl, cl;
-        if constexpr (NW == 4) {
-          rl = it * RPI + lane / LPR;
-          cl = (lane % LPR) * 8;
-        } else {
-          rl = it * RPI + (lane % RPI);  // consecutive lanes on consecutive rows: no bank conflicts
-          cl = (lane / RPI) * 8;
-        }
+      for (int it = 0; it < EPI_ROWS / 8; ++it) {
+        const int rl = it * 8 + (lane >> 3);
+        const int cl = (lane & 7) * 8;
         const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
         const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
-        const int row = tl.m0 + wm + rl;
-        const int col = tl.n0 + wn + EPI_COLS * pass + cl;
+        const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+        const int col = tl.n0 + wn + EPI_COLS * cp + cl;
         if (row < tl.m_end && col < p.N) {
           if (p.splits > 1) {
             // raw fp32 partial of this K range; splitk_finalize sums them
@@ -539,11 +568,17 @@ static hipError_t finalize_if_split(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef TPM_GEMM_WAVES
-#define TPM_GEMM_WAVES 8
+// bf16: 8 waves (two per SIMD, 128 x 64 each).  fp8: 4 waves (128 x 128
+// each): two fp8 fragment sets of a 128 x 64 wave do not fit next to its
+// accumulators in the registers of one of two waves per SIMD.
+#ifndef TPM_GEMM_WAVES_BF16
+#define TPM_GEMM_WAVES_BF16 8
 #endif
-constexpr int kWaves = TPM_GEMM_WAVES;
-constexpr int kThreads = 64 * kWaves;
+#ifndef TPM_GEMM_WAVES_FP8
+#define TPM_GEMM_WAVES_FP8 4
+#endif
+constexpr int kWaves = TPM_GEMM_WAVES_BF16, kWaves8 = TPM_GEMM_WAVES_FP8;
+constexpr int kThreads = 64 * kWaves, kThreads8 = 64 * kWaves8;
 
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (a_kmajor && !b_kmajor) gemm_kernel<false, true, false, kWaves><<<grid, kThreads, 0, s>>>(p);
@@ -555,7 +590,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
 
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (!a_kmajor || !b_kmajor) return hipErrorInvalidValue;  // rejected on the host first
-  gemm_kernel<true, true, true, kWaves><<<grid, kThreads, 0, s>>>(p);
+  gemm_kernel<true, true, true, kWaves8><<<grid, kThreads8, 0, s>>>(p);
   return finalize_if_split(p, s);
 }
 

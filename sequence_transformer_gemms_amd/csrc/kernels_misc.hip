@@ -93,6 +93,59 @@ __global__ void __launch_bounds__(256) quant_e4m3(const uint16_t* __restrict__ h
   }
 }
 
+// ------------------------------------------------------ chunk writer
+// Side-stream writer of sequence-chunk arrival: for each chunk of the list,
+// in list order, every work-group copies its share of the chunk (16-byte
+// vectors, kWriterDepth in flight per lane), makes it visible device-wide, and
+// counts itself in counters[c]; the last of the G work-groups to finish the
+// chunk publishes ready[c] = epoch with a release store and resets the
+// counter for the next call.
+#ifndef TPM_WRITER_THREADS
+#define TPM_WRITER_THREADS 1024
+#endif
+#ifndef TPM_WRITER_DEPTH
+#define TPM_WRITER_DEPTH 8
+#endif
+constexpr int kWriterThreads = TPM_WRITER_THREADS;  // per work-group
+constexpr int kWriterDepth = TPM_WRITER_DEPTH;      // 16-byte loads in flight per lane
+
+__global__ void __launch_bounds__(kWriterThreads) write_chunks(const WriterParams p) {
+  constexpr int NT = kWriterThreads, U = kWriterDepth;
+  const int G = gridDim.x;
+  const int64_t n16 = p.chunk_bytes / 16;
+  const int64_t share = (n16 + G - 1) / G;
+  const int64_t lo = (int64_t)blockIdx.x * share;
+  const int64_t hi = lo + share < n16 ? lo + share : n16;
+  for (int i = 0; i < p.n; ++i) {
+    const int c = p.order[i];
+    if (p.copy[c]) {
+      const i32x4* __restrict__ src = (const i32x4*)(p.src + (int64_t)c * p.chunk_bytes);
+      i32x4* __restrict__ dst = (i32x4*)(p.dst + (int64_t)c * p.chunk_bytes);
+      int64_t v = lo + threadIdx.x;
+      for (; v + (U - 1) * NT < hi; v += U * NT) {
+        i32x4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(src + v + u * NT);
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[v + u * NT] = w[u];
+      }
+      for (; v < hi; v += NT) dst[v] = src[v];
+    }
+    // every wave's stores of the share have completed (the barrier waits for
+    // them); one release by thread 0 then writes this XCD's L2 back, so
+    // the share is in memory before it is counted
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t prev = __hip_atomic_fetch_add(p.counters + c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == (uint32_t)G - 1u) {
+        __hip_atomic_store(p.counters + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ready + c, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
+
 __global__ void ctrl_init(uint32_t* w, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
 }
@@ -179,6 +232,11 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
                              int64_t ldq, float* s_out, hipStream_t s) {
   const int64_t work = M * (N / 8);
   quant_e4m3<<<grid_for(work, 256), 256, 0, s>>>(h, M, N / 8, ldh, amax, q, ldq, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_chunks(const WriterParams& p, int groups, hipStream_t s) {
+  write_chunks<<<groups, kWriterThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -39,6 +39,20 @@ struct GemmParams {
 
 enum { EPI_FWD = 0, EPI_DACT = 1 };
 
+// Side-stream chunk writer: chunks order[0..n-1] of chunk_bytes each, copied
+// src -> dst when copy[c] != 0, then ready[c] = epoch.
+struct WriterParams {
+  const char* src;
+  char* dst;
+  int64_t chunk_bytes;
+  uint32_t* ready;
+  uint32_t* counters;        // per chunk, zero between calls
+  uint32_t epoch;
+  int n;
+  int16_t order[kMaxGroups];
+  uint8_t copy[kMaxGroups];
+};
+
 // kernels' launchers (return hipError_t of the launch)
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
@@ -49,6 +63,7 @@ hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, i
 hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ldh, const float* amax,
                              uint8_t* q, int64_t ldq, float* s_out, hipStream_t s);
 hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
+hipError_t launch_write_chunks(const WriterParams& p, int groups, hipStream_t s);
 
 constexpr int kTileM = 256, kTileN = 256;
 constexpr int kStepBytes = 64;  // K bytes per staged step of the MFMA kernel

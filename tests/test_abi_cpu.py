@@ -104,3 +104,18 @@ def test_mlp_and_reduce_validation():
     assert L.partial_reduce_seqshard(8, 64, 64, 0, FAKE, 4096, 32, X.BF16, FAKE, 64, X.BF16, None) == X.EINVAL
     # empty input: nothing to do, nothing enqueued
     assert L.partial_reduce_seqshard(8, 0, 64, 0, None, 0, 64, X.BF16, None, 64, X.BF16, None) == X.OK
+
+
+def test_write_chunks_validation():
+    from sequence_transformer_gemms_amd import _abi
+    wc = _abi.lib.tpm_write_chunks
+    order = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    ok = order(0, 2, 1, 3)
+    assert wc(FAKE, FAKE, 4096, 4, order(0, 2, 2, 3), None, FAKE, 1, FAKE, None) == _abi.EINVAL   # not a permutation
+    assert wc(FAKE, FAKE, 4096, 4, order(0, 1, 2, 4), None, FAKE, 1, FAKE, None) == _abi.EINVAL   # id out of range
+    assert wc(FAKE, FAKE, 4100, 4, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL                  # not 16-byte chunks
+    assert wc(FAKE, FAKE, 4096, 4, ok, None, None, 1, FAKE, None) == _abi.EINVAL                  # no ready flags
+    assert wc(FAKE, FAKE, 4096, 4, ok, None, FAKE, 1, None, None) == _abi.EINVAL                  # no counters
+    assert wc(FAKE + 8, FAKE, 4096, 4, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL              # misaligned
+    assert wc(FAKE, FAKE, 4096, 0, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL                  # no chunks
+    assert wc(FAKE, FAKE, 4096, 257, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL                # too many

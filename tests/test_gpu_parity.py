@@ -353,6 +353,87 @@ def test_chunks_arrive_from_side_stream():
     assert torch.equal(Y, ref)
 
 
+def test_chunks_arrive_on_cu_masked_streams_full_chip():
+    # enough tiles for one waiting work-group on every CU of the compute
+    # stream; the producer's copy and signal kernels run on CUs of their own
+    M, N, K, C = 4096, 4096, 1024, 8
+    x = si.normal_f32((M, K), 63)
+    w = si.normal_f32((K, N), 64, 0.05)
+    Xsrc, W = dev_bf16(x), dev_bf16(w)
+    ref = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    tpm.seq_chunk_gemm(Xsrc, W, ref, act=_abi.ACT_RELU, num_chunks=C, workspace=ws)
+    sync()
+    compute, producer = tpm.masked_streams(producer_cus=8)
+    Xdst = torch.zeros_like(Xsrc)
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    Y = torch.empty_like(ref)
+    order = si.ring_chunk_order(8, C, 3)
+    rows = M // C
+    sync()
+    for epoch in (1, 2):
+        tpm.seq_chunk_gemm(Xdst, W, Y, act=_abi.ACT_RELU, num_chunks=C, chunk_order=order, chunk_ready=flags,
+                           epoch=epoch, workspace=ws, stream=compute)
+        with torch.cuda.stream(producer):
+            for c in order:
+                Xdst[c * rows:(c + 1) * rows].copy_(Xsrc[c * rows:(c + 1) * rows])
+                tpm.signal_chunk(flags, c, epoch, stream=producer)
+        sync()
+        assert tpm.poll_device_error(ws) == 0
+        assert torch.equal(Y, ref)
+        Xdst.zero_()
+        sync()
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_write_chunks_copies_in_order_and_flags(masked):
+    C, rows, cols = 8, 97, 1000          # 194000-byte chunks: 12125 vectors, a ragged share per work-group
+    g = torch.Generator().manual_seed(5)
+    src = torch.randint(-2**31, 2**31 - 1, (C * rows, cols // 2), generator=g, dtype=torch.int32).cuda()
+    dst = torch.zeros_like(src)
+    keep = torch.randint(-5, 5, (rows, cols // 2), generator=g, dtype=torch.int32).cuda()
+    dst[3 * rows:4 * rows] = keep                         # chunk 3 is already in place: not copied
+    ready = torch.zeros(C, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(C, dtype=torch.int32, device="cuda")
+    order = si.ring_chunk_order(4, C, 1)
+    copy = [c != 3 for c in range(C)]
+    stream = tpm.masked_streams(producer_cus=8)[1] if masked else torch.cuda.current_stream()
+    sync()
+    for epoch in (7, 8):
+        tpm.write_chunks(dst, src, C, order, ready, epoch, counters, copy=copy, stream=stream)
+        sync()
+        for c in range(C):
+            want = keep if c == 3 else src[c * rows:(c + 1) * rows]
+            assert torch.equal(dst[c * rows:(c + 1) * rows], want), c
+        assert torch.all(ready == epoch)
+        assert torch.count_nonzero(counters).item() == 0
+
+
+def test_write_chunks_feeds_gated_gemm_full_chip():
+    M, N, K, C = 4096, 4096, 1024, 8
+    Xsrc = dev_bf16(si.normal_f32((M, K), 65))
+    W = dev_bf16(si.normal_f32((K, N), 66, 0.05))
+    ref = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    tpm.seq_chunk_gemm(Xsrc, W, ref, act=_abi.ACT_GELU_TANH, num_chunks=C, workspace=ws)
+    compute, producer = tpm.masked_streams(producer_cus=8)
+    X = torch.zeros_like(Xsrc)
+    ready = torch.zeros(C, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(C, dtype=torch.int32, device="cuda")
+    Y = torch.empty_like(ref)
+    order = si.ring_chunk_order(8, C, 5)
+    sync()
+    for epoch in (1, 2):
+        tpm.seq_chunk_gemm(X, W, Y, act=_abi.ACT_GELU_TANH, num_chunks=C, chunk_order=order, chunk_ready=ready,
+                           epoch=epoch, workspace=ws, stream=compute)
+        tpm.write_chunks(X, Xsrc, C, order, ready, epoch, counters, stream=producer)
+        sync()
+        assert tpm.poll_device_error(ws) == 0
+        assert torch.equal(Y, ref)
+        X.zero_()
+        sync()
+
+
 def test_watchdog_reports_timeout_and_kernel_exits():
     M, N, K, C = 512, 256, 128, 2
     X = dev_bf16(si.normal_f32((M, K), 71))
