@@ -31,11 +31,11 @@ namespace tpm {
 namespace {
 
 constexpr int BM = kTileM, BN = kTileN;
-constexpr int ROW_BYTES = 64;                    // K bytes per staged row (32 bf16 / 64 fp8)
-constexpr int TILE_BYTES = 256 * ROW_BYTES;      // one operand tile of one K step: 16 KB
+constexpr int ROW_BYTES = 128;                   // K bytes per staged row (64 bf16 / 128 fp8)
+constexpr int TILE_BYTES = 256 * ROW_BYTES;      // one operand tile of one K step: 32 KB
 constexpr int SLOT_BYTES = 2 * TILE_BYTES;       // A + B
-constexpr int NSLOT = 4;                         // ring of K steps in LDS
-constexpr int DIST = NSLOT - 1;                  // K steps loaded ahead of the one computed
+constexpr int NSLOT = 2;                         // K steps held in LDS
+static_assert(ROW_BYTES == kStepBytes, "host-side K step");
 // Wave layouts of the 256 x 256 tile: NW = 4 waves as 2 x 2 (128 x 128 per
 // wave, one wave per SIMD) or NW = 8 waves as 2 x 4 (128 x 64 per wave, two
 // waves per SIMD so that one issues MFMAs while the other waits).
@@ -58,18 +58,17 @@ struct Layout {
                                                                                : NW * EPI_WAVE_FLOATS * 4;
 };
 
-// K-major tile: 256 rows x 64 bytes of K, stored as 128 LDS lines of 128
-// bytes; line L holds row L in its first half and row L + 128 in its second
-// half, so the 32 consecutive rows one ds_read_b128 touches are 128 bytes
-// apart.  Within a line the 16-byte chunk h*4 + c (h = row / 128, c = K
-// chunk) sits at position (h*4 + c) ^ swz_k(L), which spreads those rows over
-// distinct banks.
-__device__ __forceinline__ uint32_t swz_k(uint32_t line) { return (line ^ (line >> 3)) & 7u; }
+// K-major tile: 256 rows x 128 bytes of K, one 128-byte LDS line per row.
+// The 16-byte chunk c of row r sits at position c ^ swz_k(r): the 16
+// consecutive rows that one LDS cycle serves for a ds_read_b128 (same chunk)
+// then cover every bank once (odd and even rows fall in the two halves of the
+// 64 banks, and swz_k takes 8 distinct values over each half).  Global loads
+// fill whole rows, so every row segment fetched is 128 bytes.
+__device__ __forceinline__ uint32_t swz_k(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
 __device__ __forceinline__ uint32_t kmaj_offset(uint32_t row, uint32_t c) {
-  const uint32_t line = row & 127u;
-  return line * 128u + ((((row >> 7) << 2) | c) ^ swz_k(line)) * 16u;
+  return row * 128u + ((c ^ swz_k(row)) * 16u);
 }
-// MN-major tile (bf16): 32 rows of K x 32 chunks; the four K rows read by one
+// MN-major tile (bf16): 64 rows of K x 32 chunks; the four K rows read by one
 // transposed read land in distinct bank groups.
 __device__ __forceinline__ uint32_t swz_mn(uint32_t k) { return ((k & 3u) << 2) ^ ((k & 3u) << 1); }
 
@@ -124,8 +123,8 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
 
 // One of the sixteen-byte loads per thread that stage an operand tile of
 // one K step: thread t of the work-group fills LDS chunk P = j * THREADS + t.
-// kmajor: rows are the M (or N) index, 64 bytes of K each.  Otherwise: rows
-// are K (32 of them), 512 bytes (256 bf16) of M or N each.
+// kmajor: rows are the M (or N) index, 128 bytes of K each.  Otherwise: rows
+// are K (64 of them), 512 bytes (256 bf16) of M or N each.
 template <bool KMAJ, int ESZ, int THREADS>
 __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end, int k0,
                                           int K, char* lds_tile, int j) {
@@ -136,10 +135,8 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
   const uint32_t P = (uint32_t)(j * THREADS + tid);
   uint32_t voff;
   if (KMAJ) {
-    const uint32_t line = P >> 3;
-    const uint32_t hc = (P & 7u) ^ swz_k(line);   // inverse of kmaj_offset
-    const uint32_t row = ((hc >> 2) << 7) | line;
-    const uint32_t c = hc & 3u;
+    const uint32_t row = P >> 3;
+    const uint32_t c = (P & 7u) ^ swz_k(row);   // inverse of kmaj_offset
     const int k = k0 + (int)c * EPC;
     const bool ok = (mn0 + (int)row < mn_end) && (k < K);
     voff = ok ? (uint32_t)((int64_t)(mn0 + (int)row) * ld_bytes + (int64_t)k * ESZ) : kOOB;
@@ -154,7 +151,7 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
 }
 
 // One 32 (rows) x 16 (K) bf16 fragment for a 32x32x16 MFMA operand:
-// lane l holds row rb + l%32, K elements 8*(l/32) .. +7 of substep kk (0, 1).
+// lane l holds row rb + l%32, K elements 8*(l/32) .. +7 of substep kk (0..3).
 template <bool KMAJ>
 __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk) {
   const int lane = threadIdx.x & 63;
@@ -183,12 +180,12 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk
 }
 
 // One 32 (rows) x 64 (K) fp8 fragment for a 32x32x64 MFMA operand (K-major
-// tile only, one substep per K step): lane l holds row rb + l%32, K bytes
-// 32*(l/32) .. +31.
-__device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb) {
+// tile only): lane l holds row rb + l%32, K bytes 64*kk + 32*(l/32) .. +31 of
+// substep kk (0, 1).
+__device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb, int kk) {
   const int lane = threadIdx.x & 63;
   const uint32_t r = (uint32_t)(rb + (lane & 31));
-  const uint32_t c0 = (uint32_t)(2 * (lane >> 5));
+  const uint32_t c0 = (uint32_t)(4 * kk + 2 * (lane >> 5));
   const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0)));
   const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0 + 1u)));
   i32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -357,12 +354,12 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     auto read_set = [&](const char* __restrict__ st, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i);
+        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i, kk);
         else af[i] = read_frag<AK>(st, wm + 32 * i, kk);
       }
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
-        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j);
+        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j, kk);
         else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
       }
     };
@@ -375,9 +372,14 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
           accrow[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], a, accrow[j], 0, 0, 0);
       }
     };
+    // Loads of one K step are issued in three parts: part 0 right after the
+    // barrier that frees the slot (last phase of the step two before), parts
+    // 1 and 2 in the first two phases of the step before.  Each part's loads
+    // are spread between the MFMA row groups of its phase.
+    constexpr int TOTAL_LOADS = 2 * LOADS;
+    constexpr int P0 = TOTAL_LOADS / 3, P1 = (TOTAL_LOADS - P0) / 2, P2 = TOTAL_LOADS - P0 - P1;
     // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
     // loads L0 .. L0+NL-1 of K step kl spread between the row groups.
-    constexpr int TOTAL_LOADS = 2 * LOADS, HALF_LOADS = TOTAL_LOADS / 2;
     auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl) {
       constexpr int I0 = decltype(i0c)::value, NI = decltype(nic)::value;
       constexpr int L0 = decltype(l0c)::value, NL = decltype(nlc)::value;
@@ -391,74 +393,63 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // Wait until at most N of this thread's loads are in flight and all of
-    // its LDS reads are done, then synchronise the work-group with a bare
-    // s_barrier (__syncthreads() would also wait for every load in flight).
-    // The empty asm statements keep the compiler from moving LDS accesses
-    // across it.
+    // Wait until all of this thread's loads have landed and its LDS reads are
+    // done, then synchronise the work-group with a bare s_barrier
+    // (__syncthreads() would add a full fence).  The empty asm statements keep
+    // the compiler from moving LDS accesses across it.
     auto step_barrier = [&]() {
-      constexpr int N = TOTAL_LOADS + HALF_LOADS;
-      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
 
-    // Software pipeline over a ring of NSLOT K steps in LDS; loads run DIST
-    // steps ahead.  Step kt is computed in two halves (bf16: its two K
-    // substeps; fp8: accumulator rows 0-1, then 2-3).  Between the halves
-    // each thread waits for its loads of step kt+1 (the loads of steps kt+2
-    // and of the first half of kt+3 stay in flight) and the barrier makes
-    // every thread's loads visible; the fragments of step kt+1 are then read
-    // from LDS while the second half's MFMAs run, so no step starts with an
-    // LDS round trip.  The barrier also orders every read of step kt's slot
-    // (finished before it) before the loads of step kt+NSLOT into that slot
-    // (issued after the next one).
+    // Software pipeline over two K-step slots.  Step kt runs in four phases
+    // (bf16: its four K=16 substeps; fp8: its two K=64 substeps, accumulator
+    // rows 0-1 then 2-3).  The fragments of the next substep are read from
+    // LDS while the current one's MFMAs run.  Before the last phase every
+    // thread waits for its loads of step kt+1 and for its reads of step kt,
+    // and the barrier then (a) makes step kt+1 visible, whose first fragments
+    // are read during the last phase, and (b) frees step kt's slot, which the
+    // loads of step kt+2 start refilling in that same phase.
     Frag fa[2][4], fb[2][NF];
-    static_for<DIST>([&](auto kc) {
-      static_for<TOTAL_LOADS>([&](auto lc) { load_one(decltype(lc)::value, decltype(kc)::value); });
-    });
-    {
-      constexpr int N = (DIST - 1) * TOTAL_LOADS;  // step 0 has landed
-      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
+    static_for<TOTAL_LOADS>([&](auto lc) { load_one(decltype(lc)::value, 0); });
+    step_barrier();
     read_set(slot(0), 0, fa[0], fb[0]);
-    // P: fragment set that holds step kt (fp8 alternates sets between steps;
-    // bf16 always starts a step in set 0 and prefetches substep 1 into set 1)
-    auto compute_step = [&](auto pc, int kt) {
-      constexpr int P = decltype(pc)::value;
+    static_for<P0>([&](auto lc) { load_one(decltype(lc)::value, 1); });
+    for (int kt = 0; kt < nks; ++kt) {
       const char* cur = slot(kt);
-      const int kl = kt + DIST;
-      const bool has_next = kt + 1 < nks;
+      const int kn = kt + 1;
       if constexpr (FP8) {
-        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<HALF_LOADS>{}, fa[P], fb[P], kl);
-        if (has_next) {
-          step_barrier();
-          read_set(slot(kt + 1), 0, fa[1 - P], fb[1 - P]);
-        }
+        // phase 0: substep 0 rows 0-1; read substep 1
+        read_set(cur, 1, fa[1], fb[1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<2>{}, IC<2>{}, IC<HALF_LOADS>{}, IC<TOTAL_LOADS - HALF_LOADS>{}, fa[P], fb[P], kl);
+        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn);
+        // phase 1: substep 0 rows 2-3
+        mfma_rows(IC<2>{}, IC<2>{}, IC<P0 + P1>{}, IC<P2>{}, fa[0], fb[0], kn);
+        // phase 2: substep 1 rows 0-1
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn);
+        step_barrier();
+        // phase 3: read step kt+1 substep 0; loads of step kt+2 (part 0); substep 1 rows 2-3
+        read_set(slot(kn), 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2);
       } else {
         read_set(cur, 1, fa[1], fb[1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<HALF_LOADS>{}, fa[0], fb[0], kl);
-        if (has_next) {
-          step_barrier();
-          read_set(slot(kt + 1), 0, fa[0], fb[0]);
-        }
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn);
+        read_set(cur, 2, fa[0], fb[0]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<HALF_LOADS>{}, IC<TOTAL_LOADS - HALF_LOADS>{}, fa[1], fb[1], kl);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn);
+        read_set(cur, 3, fa[1], fb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn);
+        step_barrier();
+        read_set(slot(kn), 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2);
       }
-    };
-    int kt = 0;
-    for (; kt + 1 < nks; kt += 2) {
-      compute_step(IC<0>{}, kt);
-      compute_step(IC<1>{}, kt + 1);
     }
-    if (kt < nks) compute_step(IC<0>{}, kt);
     __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
 
     // ---- epilogue.  Lane l holds rows m0+wm+32i+l%32 and columns

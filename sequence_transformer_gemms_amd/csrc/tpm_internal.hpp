@@ -66,6 +66,6 @@ hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s);
 hipError_t launch_write_chunks(const WriterParams& p, int groups, hipStream_t s);
 
 constexpr int kTileM = 256, kTileN = 256;
-constexpr int kStepBytes = 64;  // K bytes per staged step of the MFMA kernel
+constexpr int kStepBytes = 128;  // K bytes per staged step of the MFMA kernel
 
 }  // namespace tpm
