@@ -363,6 +363,18 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
         else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
       }
     };
+    // fragment r of a set in the order the MFMAs first need them: A0, B0..B(NF-1), A1, A2, A3
+    auto read_one = [&](const char* __restrict__ st, int kk, int r, Frag (&af)[4], Frag (&bfr)[NF]) {
+      if (r == 0 || r > NF) {
+        const int i = r == 0 ? 0 : r - NF;
+        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i, kk);
+        else af[i] = read_frag<AK>(st, wm + 32 * i, kk);
+      } else {
+        const int j = r - 1;
+        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j, kk);
+        else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
+      }
+    };
     auto mfma_row = [&](const Frag& a, const Frag (&bfr)[NF], f32x16 (&accrow)[NF]) {
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
@@ -380,12 +392,28 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     constexpr int P0 = TOTAL_LOADS / 3, P1 = (TOTAL_LOADS - P0) / 2, P2 = TOTAL_LOADS - P0 - P1;
     // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
     // loads L0 .. L0+NL-1 of K step kl spread between the row groups.
-    auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl) {
+    auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl,
+                         auto r0c, auto nrc, const char* __restrict__ rst, int rkk, Frag (&rfa)[4], Frag (&rfb)[NF]) {
       constexpr int I0 = decltype(i0c)::value, NI = decltype(nic)::value;
       constexpr int L0 = decltype(l0c)::value, NL = decltype(nlc)::value;
+      constexpr int R0 = decltype(r0c)::value, NR = decltype(nrc)::value;
+      constexpr int NM = NI * NF;
       static_for<NI>([&](auto ic) {
         constexpr int ii = decltype(ic)::value;
-        mfma_row(fa[I0 + ii], fb, acc[I0 + ii]);
+        static_for<NF>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          constexpr int m = ii * NF + j;
+          if constexpr (FP8)
+            acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0,
+                                                                              0, 0, 0, 0);
+          else
+            acc[I0 + ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0, 0);
+          static_for<NR>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (r * NM / NR == m) read_one(rst, rkk, R0 + r, rfa, rfb);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
         static_for<NL>([&](auto lc) {
           constexpr int l = decltype(lc)::value;
           if constexpr (l * NI / NL == ii) load_one(L0 + l, kl);
@@ -407,7 +435,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     // Software pipeline over two K-step slots.  Step kt runs in four phases
     // (bf16: its four K=16 substeps; fp8: its two K=64 substeps, accumulator
     // rows 0-1 then 2-3).  The fragments of the next substep are read from
-    // LDS while the current one's MFMAs run.  Before the last phase every
+    // LDS while the current one's MFMAs run, one read after each MFMA in the
+    // order the next phase first needs them.  Before the last phase every
     // thread waits for its loads of step kt+1 and for its reads of step kt,
     // and the barrier then (a) makes step kt+1 visible, whose first fragments
     // are read during the last phase, and (b) frees step kt's slot, which the
@@ -417,37 +446,25 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     step_barrier();
     read_set(slot(0), 0, fa[0], fb[0]);
     static_for<P0>([&](auto lc) { load_one(decltype(lc)::value, 1); });
+    constexpr int NRD = 4 + NF;  // fragment reads per set
     for (int kt = 0; kt < nks; ++kt) {
       const char* cur = slot(kt);
+      const char* nx = slot(kt + 1);
       const int kn = kt + 1;
       if constexpr (FP8) {
-        // phase 0: substep 0 rows 0-1; read substep 1
-        read_set(cur, 1, fa[1], fb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn);
-        // phase 1: substep 0 rows 2-3
-        mfma_rows(IC<2>{}, IC<2>{}, IC<P0 + P1>{}, IC<P2>{}, fa[0], fb[0], kn);
-        // phase 2: substep 1 rows 0-1
-        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn);
+        // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0
+        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD / 2>{}, cur, 1, fa[1], fb[1]);
+        mfma_rows(IC<2>{}, IC<2>{}, IC<P0 + P1>{}, IC<P2>{}, fa[0], fb[0], kn, IC<NRD / 2>{}, IC<NRD - NRD / 2>{}, cur, 1,
+                  fa[1], fb[1]);
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn, IC<0>{}, IC<0>{}, cur, 0, fa[0], fb[0]);
         step_barrier();
-        // phase 3: read step kt+1 substep 0; loads of step kt+2 (part 0); substep 1 rows 2-3
-        read_set(slot(kn), 0, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2);
+        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0]);
       } else {
-        read_set(cur, 1, fa[1], fb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn);
-        read_set(cur, 2, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn);
-        read_set(cur, 3, fa[1], fb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 1, fa[1], fb[1]);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn, IC<0>{}, IC<NRD>{}, cur, 2, fa[0], fb[0]);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 3, fa[1], fb[1]);
         step_barrier();
-        read_set(slot(kn), 0, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0]);
       }
     }
     __syncthreads();  // every wave is done reading the ring before the epilogue stages into it

@@ -91,10 +91,13 @@ enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
 __device__ inline float act_fwd(float z, int act) {
   switch (act) {
     case ACT_RELU: return z > 0.f ? z : 0.f;
-    case ACT_GELU_ERF: return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+    // z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2: no cancellation in 1 + erf(.)
+    // for negative z, where the product is small
+    case ACT_GELU_ERF: return 0.5f * z * erfcf(-z * 0.70710678118654752f);
     case ACT_GELU_TANH: {
+      // 0.5 z (1 + tanh u) = z / (1 + exp(-2u)), free of the same cancellation
       float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-      return 0.5f * z * (1.f + tanhf(u));
+      return z / (1.f + expf(-2.f * u));
     }
     default: return z;
   }
@@ -104,15 +107,18 @@ __device__ inline float act_grad(float z, int act) {
   switch (act) {
     case ACT_RELU: return z > 0.f ? 1.f : 0.f;
     case ACT_GELU_ERF: {
-      float cdf = 0.5f * (1.f + erff(z * 0.70710678118654752f));
+      float cdf = 0.5f * erfcf(-z * 0.70710678118654752f);
       float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
       return cdf + z * pdf;
     }
     case ACT_GELU_TANH: {
+      // with s = (1 + tanh u) / 2 = 1 / (1 + e), e = exp(-2u):
+      // d/dz = s + 2 z s (1 - s) du/dz, and 1 - s = e s
       float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-      float t = tanhf(u);
+      float e = expf(-2.f * u);
+      float sg = 1.f / (1.f + e);
       float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
-      return 0.5f * (1.f + t) + 0.5f * z * (1.f - t * t) * du;
+      return sg + 2.f * z * sg * (e * sg) * du;
     }
     default: return 1.f;
   }

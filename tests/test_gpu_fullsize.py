@@ -1,0 +1,293 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+uses (same shapes, chunk counts and orders, dtypes and workspaces), checked
+on sampled outputs that the fp64 oracle computes one by one: a GEMM output
+row needs only the matching rows of its left operand, a column only the
+matching column of its right operand, so the oracle runs on those slices.
+Where a quantity depends on the whole tensor (the fp8 amax of H), the check
+at full size is a property that holds at any size, and a reduced-token run
+at the full hidden / FFN sizes is compared end to end."""
+import numpy as np
+import pytest
+import torch
+
+import sequence_transformer_gemms_amd as tpm
+from sequence_transformer_gemms_amd import _abi
+import synthetic_inputs as si
+from oracle import formats, ops
+from tests._util import TOL, f64, nerr
+
+pytestmark = pytest.mark.gpu
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def pick(n, k, seed):
+    """k distinct sorted indices in [0, n), always including the first and last."""
+    g = np.random.default_rng(seed)
+    idx = set(g.choice(n, size=k - 2, replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(idx))
+
+
+def bf16_either(v, rel=2.0 ** -16):
+    """(round_bf16(v), d): d is |other bf16 candidate - rounded| where v lies
+    within a relative distance `rel` of a rounding boundary (an fp32
+    evaluation may round it the other way), else 0."""
+    rb = formats.round_bf16(v)
+    lo, hi = formats.round_bf16(v * (1 - rel)), formats.round_bf16(v * (1 + rel))
+    other = np.where(lo != rb, lo, hi)
+    return rb, np.abs(other - rb)
+
+
+def host64(t):
+    """fp64 values of a (CPU or device) tensor's rows/cols already selected."""
+    return f64(t.cpu() if t.is_cuda else t)
+
+
+# ------------------------------------------------------------------ C2
+def test_c2_projection_full_size_resident_and_arriving():
+    """Single column-parallel projection: X [8192, 8192] bf16, rank shard
+    t = 0 of W [8192, 32768] (columns 0..8191), 4 chunks of 2048 tokens in
+    ring order [0, 3, 2, 1]; resident, then with the chunks written by the
+    side-stream writer on disjoint CUs (bitwise equal)."""
+    M, K, Nfull, T, C = 8192, 8192, 32768, 4, 4
+    N = Nfull // T
+    x = si.to_bf16(si.normal_f32((M, K), 1))
+    w = si.to_bf16(np.ascontiguousarray(si.normal_f32((K, Nfull), 2, 1.0 / np.sqrt(8192.0))[:, :N]))
+    X, W = x.cuda(), w.cuda()
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    order = si.ring_chunk_order(T, C, 0)
+    assert order == [0, 3, 2, 1]
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_order=order, workspace=ws)
+    sync()
+    rows, cols = pick(M, 48, 21), pick(N, 48, 22)
+    ref, _ = ops.seq_chunk_gemm(f64(x[rows]), f64(w[:, cols]))
+    got = host64(Y[rows][:, cols])
+    assert nerr(got, ref) <= TOL["bf16"]
+    # whole rows too (every column tile of the sampled token rows)
+    r2 = rows[:4]
+    ref_rows, _ = ops.seq_chunk_gemm(f64(x[r2]), f64(w))
+    assert nerr(host64(Y[r2]), ref_rows) <= TOL["bf16"]
+
+    compute, producer = tpm.masked_streams(producer_cus=8)
+    Xa = torch.zeros_like(X)
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(C, dtype=torch.int32, device="cuda")
+    Y2 = torch.empty_like(Y)
+    sync()
+    tpm.seq_chunk_gemm(Xa, W, Y2, num_chunks=C, chunk_order=order, chunk_ready=flags, epoch=1, workspace=ws,
+                       stream=compute)
+    tpm.write_chunks(Xa, X, C, order, flags, 1, counters, stream=producer)
+    sync()
+    assert tpm.poll_device_error(ws) == 0
+    assert torch.equal(Y2, Y)
+
+
+# ------------------------------------------------------------------ C3
+def test_c3_mlp_forward_full_size_and_reduction():
+    """Llama3-70B-shaped MLP share of rank 0 of TP = 8, bf16: 8192 tokens,
+    D = 8192, F = 28672 (F/T = 3584), GeLU, 8 chunks in ring order, the
+    second GEMM producing destination ranges in order r+1, ..., r; then the
+    sequence-sharded reduction of 8 seeded partials [8192, 8192]."""
+    M, D, F, T, C, r = 8192, 8192, 28672, 8, 8, 0
+    Ft = F // T
+    x = si.to_bf16(si.normal_f32((M, D), 1))
+    wu = si.to_bf16(si.normal_f32((D, Ft), 2, 0.02))
+    wd = si.to_bf16(si.normal_f32((Ft, D), 3, 0.02))
+    X, Wu, Wd = x.cuda(), wu.cuda(), wd.cuda()
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty_like(H)
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    done = torch.zeros(T, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_mlp_fwd(X, Wu, Wd, H, P, T=T, rank=r, act=_abi.ACT_GELU_ERF, Z_t=Z, num_chunks=C,
+                   chunk_order=si.ring_chunk_order(T, C, r), range_order=si.dest_range_order(T, r),
+                   range_done=done, epoch=3, workspace=ws)
+    sync()
+    assert torch.all(done == 3)
+    rows = pick(M, 24, 31)
+    ref = ops.tp_mlp_fwd(f64(x[rows]), f64(wu), f64(wd), ops.ACT_GELU_ERF, store="bf16")
+    assert nerr(host64(Z[rows]), ref["Z"]) <= TOL["bf16"]
+    assert nerr(host64(H[rows]), ref["H"]) <= TOL["bf16"]
+    assert nerr(host64(P[rows]), ref["P"]) <= TOL["bf16"]
+    del X, Wu, Wd, H, Z, P, ws
+    torch.cuda.empty_cache()
+
+    # reduction: partials [8, 8192, 8192] N(0,1) seeds 100..107 -> rank 5's [1024, 8192] slice
+    stack = torch.empty(T, M, D, dtype=torch.bfloat16, device="cuda")
+    host = []
+    for t in range(T):
+        pt = si.to_bf16(si.normal_f32((M, D), 100 + t))
+        host.append(pt)
+        stack[t] = pt.cuda()
+    out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+    rank = 5
+    tpm.partial_reduce_seqshard(stack, out, T=T, rank=rank)
+    sync()
+    lrows, cols = pick(M // T, 64, 32), pick(D, 64, 33)
+    grows = rank * (M // T) + lrows
+    parts = np.stack([f64(h[grows][:, cols]) for h in host])          # [T, rows, cols]
+    ref_red = ops.partial_reduce_seqshard(parts, -1)
+    got = host64(out[lrows][:, cols])
+    # one rounding of the fp32 sum to bf16: within half a bf16 ulp plus fp32 summation error
+    assert nerr(got, ref_red) <= TOL["bf16"]
+    assert np.array_equal(got, formats.round_bf16(ref_red)) or \
+        np.mean(got != formats.round_bf16(ref_red)) < 1e-3
+
+
+# ------------------------------------------------------------------ C4
+def _c4_inputs(M, D, F, T):
+    Ft = F // T
+    xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 1))
+    wu = si.normal_f32((D, Ft), 2, 0.02)
+    wd = si.normal_f32((Ft, D), 3, 0.02)
+    wuq, su = si.to_e4m3_current(np.ascontiguousarray(wu.T))    # K-major copies: [Ft, D]
+    wdq, sd = si.to_e4m3_current(np.ascontiguousarray(wd.T))    # [D, Ft]
+    return xq, sx, wuq, su, wdq, sd
+
+
+def _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C):
+    Ft = F // T
+    scales = torch.tensor([sx, su, sd], dtype=torch.float32, device="cuda")
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    sH = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.FP8_E4M3)
+    tpm.tp_mlp_fwd(xq.cuda(), wuq.cuda(), wdq.cuda(), H, P, T=T, rank=0, act=_abi.ACT_GELU_ERF, scales=scales,
+                   h_scale_out=sH, num_chunks=C, chunk_order=si.ring_chunk_order(T, C, 0), workspace=ws)
+    sync()
+    return H, P, sH, ws
+
+
+def test_c4_fp8_mlp_forward_full_size_sampled():
+    """Llama3-405B-shaped MLP share, fp8 e4m3 with per-tensor current scales:
+    8192 tokens, D = 16384, F/T = 6656, 16 chunks of 512.  H (bf16, before
+    its own quantisation) is checked on sampled rows against the oracle; the
+    scale of H must be max|H| / 448 of the H the kernel produced; P is
+    checked on sampled rows against the unquantised-H product within the
+    e4m3 rounding bound of H (relative 2^-4 per element, plus half the
+    smallest subnormal step times the scale)."""
+    M, D, F, T, C = 8192, 16384, 53248, 8, 16
+    Ft = F // T
+    xq, sx, wuq, su, wdq, sd = _c4_inputs(M, D, F, T)
+    H, P, sH, ws = _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C)
+    rows = pick(M, 12, 41)
+    x_r = f64(xq[rows]) * float(sx)                    # decoded operands
+    wu_d = f64(wuq).T * float(su)                      # [D, Ft]
+    wd_d = f64(wdq).T * float(sd)                      # [Ft, D]
+    h_ref, _ = ops.seq_chunk_gemm(x_r, wu_d, act=ops.ACT_GELU_ERF)
+    h_gpu = host64(H[rows])
+    assert nerr(h_gpu, h_ref) <= TOL["bf16"]
+    amax = float(torch.max(torch.abs(H.float())).item())
+    assert abs(sH.item() - np.float32(np.float32(amax) / np.float32(448.0))) <= 1e-6 * sH.item()
+    assert amax >= float(np.max(np.abs(formats.round_bf16(h_ref)))) * (1 - 2 ** -8)
+    hb = formats.round_bf16(h_ref)
+    p_ref, _ = ops.seq_chunk_gemm(hb, wd_d)
+    bound = (2.0 ** -4 * np.abs(hb) + 2.0 ** -10 * sH.item()) @ np.abs(wd_d)
+    p_gpu = host64(P[rows])
+    # bf16 rounding of P and fp32 accumulation on top of the quantisation bound
+    assert np.all(np.abs(p_gpu - p_ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(p_ref) + 1e-6)
+
+
+def test_c4_fp8_mlp_forward_full_width_end_to_end():
+    """The same hidden and FFN sizes and 16 chunks, 32 tokens: small enough
+    for the oracle to compute the whole H (hence its amax) and compare H,
+    the scale, the e4m3 codes of H and P end to end."""
+    M, D, F, T, C = 32, 16384, 53248, 8, 16
+    xq, sx, wuq, su, wdq, sd = _c4_inputs(M, D, F, T)
+    H, P, sH, ws = _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C)
+    ref = ops.tp_mlp_fwd_fp8(f64(xq), sx, f64(wuq).T, su, f64(wdq).T, sd, ops.ACT_GELU_ERF)
+    assert nerr(host64(H), ref["H"]) <= TOL["fp8"]
+    assert nerr(host64(P), ref["P"]) <= TOL["fp8"]
+    assert abs(sH.item() - ref["sH"]) <= 1e-2 * ref["sH"]
+    Ft = F // T
+    hq = ws[2048:2048 + M * Ft].cpu().numpy().reshape(M, Ft)
+    assert np.mean(hq != ref["Hq_codes"]) < 1e-2
+
+
+# ------------------------------------------------------------------ C5
+def test_c5_layer_step_full_size_sampled():
+    """The bench's Llama3-70B-shaped layer step of rank 0 (4096 tokens, bf16),
+    call by call with the bench's shapes, orders and workspaces: QKV and O
+    projections, MLP forward, MLP backward, O and QKV backward.  Row-indexed
+    outputs are checked on sampled token rows, weight gradients on sampled
+    rows or columns."""
+    M, D, F, T, C, r = 4096, 8192, 28672, 8, 8, 0
+    Ft, Nq, Da = F // T, 1280, 1024
+    bf = lambda a: si.to_bf16(a)
+    x = bf(si.normal_f32((M, D), 1))
+    wu = bf(si.normal_f32((D, Ft), 2, 0.02))
+    wd = bf(si.normal_f32((Ft, D), 3, 0.02))
+    dy = bf(si.normal_f32((M, D), 4))
+    wq = bf(si.normal_f32((D, Nq), 5, 0.02))
+    wo = bf(si.normal_f32((Da, D), 6, 0.02))
+    a = bf(si.normal_f32((M, Da), 7))
+    dq = bf(si.normal_f32((M, Nq), 8))
+    dyo = bf(si.normal_f32((M, D), 9))
+    dev = {k: v.cuda() for k, v in dict(x=x, wu=wu, wd=wd, dy=dy, wq=wq, wo=wo, a=a, dq=dq, dyo=dyo).items()}
+    e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+    shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1)]
+    wsg = torch.zeros(max(tpm.workspace_bytes(_abi.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
+                      dtype=torch.uint8, device="cuda")
+    order, dest = si.ring_chunk_order(T, C, r), si.dest_range_order(T, r)
+    qkv, o_part, z, h, p = e(M, Nq), e(M, D), e(M, Ft), e(M, Ft), e(M, D)
+    g_up, g_down, dx, d_attn, g_o, g_qkv, dx_q = e(D, Ft), e(Ft, D), e(M, D), e(M, Da), e(Da, D), e(D, Nq), e(M, D)
+    tpm.seq_chunk_gemm(dev["x"], dev["wq"], qkv, num_chunks=C, chunk_order=order, workspace=wsg)
+    tpm.seq_chunk_gemm(dev["a"], dev["wo"], o_part, num_chunks=T, chunk_order=dest, workspace=wsg)
+    ws_f = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_mlp_fwd(dev["x"], dev["wu"], dev["wd"], h, p, T=T, rank=r, act=_abi.ACT_GELU_ERF, Z_t=z, num_chunks=C,
+                   chunk_order=order, workspace=ws_f)
+    ws_b = tpm.alloc_workspace(_abi.OP_MLP_BWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_mlp_bwd(dev["x"], dev["wu"], dev["wd"], z, h, dev["dy"], g_up, g_down, dx, T=T, rank=r,
+                   act=_abi.ACT_GELU_ERF, num_chunks=C, dy_chunk_order=order, workspace=ws_b)
+    tpm.seq_chunk_gemm(dev["dyo"], dev["wo"], d_attn, trans_b=True, num_chunks=C, chunk_order=order, workspace=wsg)
+    tpm.seq_chunk_gemm(dev["a"], dev["dyo"], g_o, trans_a=True, workspace=wsg)
+    tpm.seq_chunk_gemm(dev["x"], dev["dq"], g_qkv, trans_a=True, workspace=wsg)
+    tpm.seq_chunk_gemm(dev["dq"], dev["wq"], dx_q, trans_b=True, workspace=wsg)
+    sync()
+    B = TOL["bf16"]
+    rows = pick(M, 16, 51)
+    X, WU, WD, DY = f64(x), f64(wu), f64(wd), f64(dy)
+    # projections, row samples
+    assert nerr(host64(qkv[rows]), ops.seq_chunk_gemm(X[rows], f64(wq))[0]) <= B
+    assert nerr(host64(o_part[rows]), ops.seq_chunk_gemm(f64(a[rows]), f64(wo))[0]) <= B
+    # MLP forward and backward, row samples (the backward reads Z and H as
+    # stored in bf16, and dZ as stored in bf16)
+    fw = ops.tp_mlp_fwd(X[rows], WU, WD, ops.ACT_GELU_ERF, store="bf16")
+    for name, t in (("Z", z), ("H", h), ("P", p)):
+        assert nerr(host64(t[rows]), fw[name]) <= B, name
+    zb, hb = formats.round_bf16(fw["Z"]), formats.round_bf16(fw["H"])
+    bw = ops.tp_mlp_bwd(X[rows], WU, WD, zb, hb, DY[rows], ops.ACT_GELU_ERF, store="bf16")
+    assert nerr(host64(dx[rows]), bw["dX"]) <= B
+    assert nerr(host64(d_attn[rows]), ops.seq_chunk_gemm(f64(dyo[rows]), f64(wo), trans_b=True)[0]) <= B
+    assert nerr(host64(dx_q[rows]), ops.seq_chunk_gemm(f64(dq[rows]), f64(wq), trans_b=True)[0]) <= B
+    # weight gradients: dW_down rows f need the H columns f over all tokens;
+    # dW_up columns f need the dZ columns f over all tokens.  Their inputs H,
+    # Z and dZ are bf16 intermediates that the GPU rounds from fp32 values:
+    # an element whose exact value lies within fp32 accumulation error of a
+    # bf16 rounding boundary may round either way, and over 4096 tokens one
+    # such flip of a large H (ulp 2^-6 at |H| ~ 3) moves a weight gradient
+    # by ~0.03, more than 2e-2 * (1 + |ref|) where the gradient is near 0.
+    # Either rounding is valid, so the bound adds, per token, the size of
+    # the other rounding where one exists, times the other operand.
+    fcols = pick(Ft, 8, 52)
+    zc = X @ WU[:, fcols]                                          # exact Z[:, f] over all tokens
+    zb, zamb = bf16_either(zc)
+    hb, hamb = bf16_either(ops.act_fwd(zc, ops.ACT_GELU_ERF))
+    ref = hb.T @ DY
+    tol = B * (1 + np.abs(ref)) + hamb.T @ np.abs(DY)
+    assert np.all(np.abs(host64(g_down[fcols]) - ref) <= tol)
+    dh = DY @ WD[fcols].T
+    dz_exact = dh * ops.act_grad(zb, ops.ACT_GELU_ERF)
+    dz_other = dh * ops.act_grad(zb + zamb * np.sign(zc - zb), ops.ACT_GELU_ERF)   # Z rounded the other way
+    dzb, dzamb = bf16_either(dz_exact)
+    amb = dzamb + np.where(zamb > 0, np.abs(dz_other - dz_exact), 0.0)
+    ref = X.T @ dzb
+    tol = B * (1 + np.abs(ref)) + np.abs(X).T @ amb
+    assert np.all(np.abs(host64(g_up[:, fcols]) - ref) <= tol)
+    orows = pick(Da, 8, 53)
+    assert nerr(host64(g_o[orows]), ops.seq_chunk_gemm(f64(a[:, orows]), f64(dyo), trans_a=True)[0]) <= B
+    qcols = pick(Nq, 8, 54)
+    assert nerr(host64(g_qkv[:, qcols]), ops.seq_chunk_gemm(X, f64(dq[:, qcols]), trans_a=True)[0]) <= B
