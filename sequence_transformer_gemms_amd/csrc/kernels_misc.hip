@@ -18,9 +18,12 @@ namespace {
 // ------------------------------------------------------------- reduction
 // out[i, :] = sum_{t=0}^{T-1} P_t[i, :] for i < rows, with the partials at
 // partials + t * pstride.  One lane owns 8 bf16 (16 bytes) of one row: T
-// sixteen-byte nontemporal loads, fp32 sum in ascending t, one rounding to
-// bf16, one 16-byte store.  Grid-stride over (row, 8-column group).
-__global__ void __launch_bounds__(256) reduce_bf16_vec(int T, int64_t rows, int64_t D8, const uint16_t* __restrict__ P,
+// sixteen-byte nontemporal loads, one in flight at a time (more per lane
+// measured slower: many waves each with one load keep HBM busier than few
+// waves with eight), fp32 sum in ascending t, one rounding to bf16, one
+// 16-byte store.  1024-thread blocks, grid-stride over (row, 8-column
+// group).
+__global__ void __launch_bounds__(1024) reduce_bf16_vec(int T, int64_t rows, int64_t D8, const uint16_t* __restrict__ P,
                                                        int64_t pstride, int64_t ld, uint16_t* __restrict__ out,
                                                        int64_t ldo) {
   const int64_t total = rows * D8;
@@ -220,8 +223,8 @@ hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, i
                    (((uintptr_t)partials & 15) == 0) && (((uintptr_t)out & 15) == 0);
   if (vec) {
     const int64_t work = rows * (D / 8);
-    reduce_bf16_vec<<<grid_for(work, 256), 256, 0, s>>>(T, rows, D / 8, (const uint16_t*)partials, pstride, ld,
-                                                        (uint16_t*)out, ldo);
+    reduce_bf16_vec<<<grid_for(work, 1024), 1024, 0, s>>>(T, rows, D / 8, (const uint16_t*)partials, pstride, ld,
+                                                          (uint16_t*)out, ldo);
   } else {
     reduce_scalar<<<grid_for(rows * D, 256), 256, 0, s>>>(T, rows, D, partials, pstride, ld, in_f32, out, ldo, out_f32);
   }
