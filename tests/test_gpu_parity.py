@@ -526,3 +526,63 @@ def test_chunk_gating_reads_fresh_data_after_stale_reads():
     sync()
     assert tpm.poll_device_error(ws) == 0
     assert torch.equal(Y, ref)
+
+
+# ------------------------------------------------ HIP graph capture / replay
+def test_graph_replays_match_eager():
+    # bf16 MLP forward, an fp8 forward (control-word init, amax, quantiser),
+    # a split-K GEMM (fp32 partials + finalisation) and a reduction, captured
+    # once and replayed three times with eager work and synchronisation in
+    # between; every replay must equal the eager result bit for bit
+    M, D, F, T = 512, 512, 2048, 4
+    Ft = F // T
+    X = dev_bf16(si.normal_f32((M, D), 111))
+    Wu = dev_bf16(si.normal_f32((D, Ft), 112, 0.05))
+    Wd = dev_bf16(si.normal_f32((Ft, D), 113, 0.05))
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    stack = dev_bf16(si.normal_f32((T, M, D), 114))
+    out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
+    ws_f = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, 4, _abi.BF16)
+    xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 115))
+    wuq, su = si.to_e4m3_current(si.normal_f32((Ft, D), 116, 0.05))
+    wdq, sd = si.to_e4m3_current(si.normal_f32((D, Ft), 117, 0.05))
+    xq, wuq, wdq = xq.cuda(), wuq.cuda(), wdq.cuda()
+    scales = dev_f32(np.array([sx, su, sd], dtype=np.float32))
+    H8 = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    P8 = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    sH = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws_8 = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, 4, _abi.FP8_E4M3)
+    a = dev_bf16(si.normal_f32((M, 4096), 118))
+    b = dev_bf16(si.normal_f32((4096, 264), 119, 0.02))
+    Yk = torch.empty(M, 264, dtype=torch.bfloat16, device="cuda")
+    ws_k = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, 264, 4096)
+    assert ws_k.numel() > 2048                                   # split-K planned
+
+    def run():
+        tpm.tp_mlp_fwd(X, Wu, Wd, H, stack[1], T=T, rank=1, act=_abi.ACT_GELU_TANH, num_chunks=4, workspace=ws_f)
+        tpm.partial_reduce_seqshard(stack, out, T=T, rank=1)
+        tpm.tp_mlp_fwd(xq, wuq, wdq, H8, P8, T=T, rank=0, act=_abi.ACT_RELU, scales=scales, h_scale_out=sH,
+                       num_chunks=4, workspace=ws_8)
+        tpm.seq_chunk_gemm(a, b, Yk, workspace=ws_k)
+
+    run()
+    sync()
+    ref = [t.clone() for t in (H, stack, out, H8, P8, sH, Yk)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in (H, out, H8, P8, sH, Yk):
+            t.zero_()
+        stack[1].zero_()
+        sync()
+        g.replay()
+        sync()
+        for got, want in zip((H, stack, out, H8, P8, sH, Yk), ref):
+            assert torch.equal(got, want), rep
