@@ -93,7 +93,10 @@ typedef enum { TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2
  *    (wrap-around compare); the flags are written by the producer of the
  *    chunk (tpm_signal_chunk).  The result does not depend on the order.
  * workspace: device, >= tpm_workspace_bytes(TPM_OP_SEQ_CHUNK_GEMM, ...);
- *    required when chunk_ready or amax_out is given, else may be NULL.
+ *    required when chunk_ready or amax_out is given, else may be NULL
+ *    (then no split-K: a GEMM with few output tiles runs on fewer CUs).
+ *    Its head holds control words and its tail the fp32 partial sums of
+ *    split-K; calls that share a workspace must not overlap in time.
  */
 int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
                    const void* A, int64_t lda, int trans_a, int a_dtype, const float* a_scale,

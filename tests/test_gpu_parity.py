@@ -495,6 +495,28 @@ def test_split_k_narrow_gemm():
     assert nerr(Yd, yd) <= TOL["bf16"]
 
 
+def test_split_k_sum_is_deterministic():
+    # The fp32 partial sums of the K splits are added in ascending split
+    # order, so repeated calls agree bit for bit; an ungated call does not
+    # read the control words at the head of the workspace (filled here with
+    # a byte pattern first).
+    M, N, K = 1000, 520, 8192             # ragged row and column tiles, 8 splits
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    assert ws.numel() > 2048
+    ws[:2048].fill_(0x13)
+    x = dev_bf16(si.normal_f32((M, K), 87))
+    w = dev_bf16(si.normal_f32((K, N), 88, 0.02))
+    outs = []
+    for _ in range(3):
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tpm.seq_chunk_gemm(x, w, Y, act=_abi.ACT_GELU_TANH, workspace=ws)
+        sync()
+        outs.append(Y.clone())
+    y, _ = ops.seq_chunk_gemm(f64(x), f64(w), act=_abi.ACT_GELU_TANH)
+    assert nerr(outs[0], y) <= TOL["bf16"]
+    assert all(torch.equal(o, outs[0]) for o in outs[1:])
+
+
 def test_chunk_gating_reads_fresh_data_after_stale_reads():
     # The consumer GEMM first reads X while it holds zeros (so caches may hold
     # those lines), then the chunks are rewritten with real data on a side

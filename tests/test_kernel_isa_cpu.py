@@ -1,0 +1,80 @@
+"""Code-generation guards for the GEMM kernel (no GPU needed).
+
+The GEMM's K loop overlaps LDS DMA (buffer_load ... lds, counted by vmcnt)
+with LDS fragment reads.  If the compiler cannot tell the two apart it
+inserts a full `s_waitcnt vmcnt(0)` before the reads, which serialises the
+loads with the MFMAs and roughly halves throughput without changing any
+result, so no parity test would notice.  These tests compile the kernel
+source for gfx950 with the library's own flags and read the AMD assembly.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "sequence_transformer_gemms_amd", "csrc", "gemm_mfma.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from sequence_transformer_gemms_amd import build
+    if not os.path.exists(build.HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "gemm_mfma.s"
+    cmd = [build.HIPCC, *build.COMMON, "--cuda-device-only", "-S", "-x", "hip", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out.read_text()
+
+
+def kernels(text):
+    """{mangled gemm_kernel name: (body lines, metadata dict)}"""
+    lines = text.split("\n")
+    bodies, cur = {}, None
+    for ln in lines:
+        m = re.match(r"^(_ZN\S*gemm_kernel\S*):", ln)
+        if m:
+            cur = m.group(1)
+            bodies[cur] = []
+            continue
+        if cur is not None:
+            if ln.strip().startswith("s_endpgm"):
+                cur = None
+            else:
+                bodies[cur].append(ln.strip())
+    meta = {}
+    for block in re.split(r"\n\s*- \.", text):
+        nm = re.search(r"\.name:\s+(\S*gemm_kernel\S*)", block)
+        if not nm:
+            continue
+        vals = {k: int(v) for k, v in re.findall(r"\.(vgpr_spill_count|sgpr_spill_count|group_segment_fixed_size"
+                                                 r"|private_segment_fixed_size):\s+(\d+)", block)}
+        meta[nm.group(1)] = vals
+    return bodies, meta
+
+
+def test_every_gemm_variant_is_compiled(asm):
+    bodies, meta = kernels(asm)
+    assert len(bodies) == 5          # 4 bf16 operand layouts + fp8
+    assert set(meta) == set(bodies)
+
+
+def test_no_full_vmcnt_wait_before_lds_reads(asm):
+    bodies, _ = kernels(asm)
+    for name, body in bodies.items():
+        code = [ln for ln in body if ln and not ln.startswith(";")]
+        bad = [i for i in range(len(code) - 1)
+               if re.match(r"s_waitcnt\s+vmcnt\(0\)", code[i]) and code[i + 1].startswith("ds_read")]
+        assert not bad, f"{name}: {len(bad)} x 's_waitcnt vmcnt(0)' right before an LDS read"
+
+
+def test_no_register_spills_and_lds_fits(asm):
+    # (scalar registers that overflow go to VGPR lanes, not memory: allowed)
+    _, meta = kernels(asm)
+    for name, m in meta.items():
+        assert m.get("vgpr_spill_count", 0) == 0, name
+        assert m.get("private_segment_fixed_size", 0) == 0, name
+        assert m["group_segment_fixed_size"] <= 160 * 1024, name
