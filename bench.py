@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: one line per (T, chunks) of the Llama3-70B MLP share "
+                         "(8192 tokens, D 8192, F 28672), T in 1, 2, 4, 8 and chunks in T, 2T, 4T")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 256 MiB device copy first (reference for HBM byte counters)")
     return ap.parse_args()
@@ -376,6 +379,59 @@ def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
                 frac_mfma_peak=tf / peak)
 
 
+def sweep_point(torch, tpm, si, M, D, F, T, C, iters=10):
+    """Rank 0's MLP share at tensor-parallel degree T with its X (and dY)
+    cut into C sequence chunks, chunk-gated with every flag already set:
+    forward (GEMM1 + GeLU, GEMM2) and backward (dZ, dW_down, dW_up, dX) timed
+    separately with events, bf16."""
+    Ft = F // T
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 * T + C)
+    rnd = lambda *shape, s=1.0: (torch.randn(*shape, generator=g, device=dev) * s).to(torch.bfloat16)
+    X, Wu, Wd, dY = rnd(M, D), rnd(D, Ft, s=0.02), rnd(Ft, D, s=0.02), rnd(M, D)
+    Z = torch.empty(M, Ft, dtype=torch.bfloat16, device=dev)
+    H, P, dX = torch.empty_like(Z), torch.empty(M, D, dtype=torch.bfloat16, device=dev), torch.empty_like(X)
+    dWu, dWd = torch.empty_like(Wu), torch.empty_like(Wd)
+    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
+    order = si.ring_chunk_order(T, C, 0)
+    wsf = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, C, tpm.BF16)
+    wsb = tpm.alloc_workspace(tpm.OP_MLP_BWD, M, D, F, T, C, tpm.BF16)
+    fwd = lambda: tpm.tp_mlp_fwd(X, Wu, Wd, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, Z_t=Z, num_chunks=C,
+                                 chunk_order=order, chunk_ready=flags, epoch=1, workspace=wsf)
+    bwd = lambda: tpm.tp_mlp_bwd(X, Wu, Wd, Z, H, dY, dWu, dWd, dX, T=T, rank=0, act=tpm.ACT_GELU_ERF,
+                                 num_chunks=C, dy_chunk_order=order, dy_ready=flags, epoch=1, workspace=wsb)
+    out = {}
+    for name, fn, gemms in (("fwd", fwd, 2), ("bwd", bwd, 4)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+        tf = gemms * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "TFLOPS": round(tf, 1), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
+    ms = out["fwd"]["ms"] + out["bwd"]["ms"]
+    return {"sweep": "tp_degree_and_chunks", "M": M, "D": D, "F": F, "T": T, "F_t": Ft, "chunks": C,
+            "chunk_rows": M // C, "dtype": "bf16", **out, "ms_fwd_bwd": round(ms, 4),
+            "TFLOPS_fwd_bwd": round(6 * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12, 1)}
+
+
+def run_sweep(torch, tpm, si):
+    M, D, F = 8192, 8192, 28672
+    for T in (1, 2, 4, 8):
+        for C in (T, 2 * T, 4 * T):
+            print(json.dumps(sweep_point(torch, tpm, si, M, D, F, T, C)), flush=True)
+            torch.cuda.empty_cache()
+
+
 def recorded_traffic():
     """HBM bytes per step of the GEMM launches, as measured with rocprofv3
     FETCH_SIZE / WRITE_SIZE (profiles/gemm_traffic.md), or None when the GEMM
@@ -455,6 +511,9 @@ def main():
     import sequence_transformer_gemms_amd as tpm
     import synthetic_inputs as si
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        run_sweep(torch, tpm, si)
+        return
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

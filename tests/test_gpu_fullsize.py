@@ -291,3 +291,46 @@ def test_c5_layer_step_full_size_sampled():
     assert nerr(host64(g_o[orows]), ops.seq_chunk_gemm(f64(a[:, orows]), f64(dyo), trans_a=True)[0]) <= B
     qcols = pick(Nq, 8, 54)
     assert nerr(host64(g_qkv[:, qcols]), ops.seq_chunk_gemm(X, f64(dq[:, qcols]), trans_a=True)[0]) <= B
+
+
+# ------------------------------------------------- tensor-parallel degree sweep
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_tp_degree_sweep_shapes_sampled_and_chunk_invariant(T):
+    """The Llama3-70B MLP share (8192 tokens, D = 8192, F = 28672) at the
+    other tensor-parallel degrees bench.py --sweep times (T = 8 is C3):
+    rank 0's F/T = 28672 / T columns, chunk-gated with the flags already set.
+    Sampled rows of Z, H and P against the oracle with C = T chunks in ring
+    order; then C = 4T chunks give bitwise the same forward and backward
+    results (the chunk count only changes the tile order)."""
+    M, D, F = 8192, 8192, 28672
+    Ft = F // T
+    x = si.to_bf16(si.normal_f32((M, D), 1))
+    wu = si.to_bf16(si.normal_f32((D, Ft), 2, 0.02))
+    wd = si.to_bf16(si.normal_f32((Ft, D), 3, 0.02))
+    X, Wu, Wd = x.cuda(), wu.cuda(), wd.cuda()
+    dY = si.to_bf16(si.normal_f32((M, D), 4)).cuda()
+    outs = []
+    for C in (T, 4 * T):
+        Z = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+        H, P = torch.empty_like(Z), torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+        dWu, dWd, dX = torch.empty_like(Wu), torch.empty_like(Wd), torch.empty_like(X)
+        flags = torch.full((C,), 2, dtype=torch.int32, device="cuda")
+        order = si.ring_chunk_order(T, C, 0)
+        ws = tpm.alloc_workspace(_abi.OP_MLP_FWD, M, D, F, T, C, _abi.BF16)
+        tpm.tp_mlp_fwd(X, Wu, Wd, H, P, T=T, rank=0, act=_abi.ACT_GELU_ERF, Z_t=Z, num_chunks=C,
+                       chunk_order=order, chunk_ready=flags, epoch=2, workspace=ws)
+        wsb = tpm.alloc_workspace(_abi.OP_MLP_BWD, M, D, F, T, C, _abi.BF16)
+        tpm.tp_mlp_bwd(X, Wu, Wd, Z, H, dY, dWu, dWd, dX, T=T, rank=0, act=_abi.ACT_GELU_ERF, num_chunks=C,
+                       dy_chunk_order=order, dy_ready=flags, epoch=2, workspace=wsb)
+        sync()
+        assert tpm.poll_device_error(ws) == 0 and tpm.poll_device_error(wsb) == 0
+        outs.append((Z, H, P, dWu, dWd, dX))
+        del ws, wsb
+    rows = pick(M, 12, 60 + T)
+    ref = ops.tp_mlp_fwd(f64(x[rows]), f64(wu), f64(wd), ops.ACT_GELU_ERF, store="bf16")
+    Z, H, P = outs[0][:3]
+    assert nerr(host64(Z[rows]), ref["Z"]) <= TOL["bf16"]
+    assert nerr(host64(H[rows]), ref["H"]) <= TOL["bf16"]
+    assert nerr(host64(P[rows]), ref["P"]) <= TOL["bf16"]
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
