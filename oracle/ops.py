@@ -15,6 +15,13 @@ Sources (page title, section):
          (CGEMM)" (sequence chunks give distinct output rows, no accumulation;
          the reduce-scatter delivers each rank its token range of the summed
          partial), "Supported quantization recipes" (FP8 current scaling).
+  [WE]   "Tensor and sequence parallelism", "Worked example: Partitioning an
+         MLP pair": an expansion weight and a gate weight, each column-
+         partitioned, a gated activation applied locally, and a row-
+         partitioned contraction producing a partial.  The page does not say
+         which gated activation; the functions below take the gated-linear-
+         unit form act(X W_gate) * (X W_up) (Shazeer, "GLU Variants Improve
+         Transformer") with the activation as an argument; SiLU gives SwiGLU.
 
 Matrices are row-major [rows, cols] as the pages write them: X[M,K], W[K,N].
 Every function takes float64 arrays holding exactly the values the GPU
@@ -29,7 +36,7 @@ from scipy.special import erf
 
 from . import formats
 
-ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
+ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
 _SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
 _GELU_TANH_C = 0.044715
 
@@ -72,6 +79,20 @@ def gelu_tanh_grad(z):
     return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * du
 
 
+def silu(z):
+    """SiLU (swish with unit slope): z * sigma(z), sigma the logistic function
+    1 / (1 + exp(-z))."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def silu_grad(z):
+    """d/dz [z sigma(z)] = sigma(z) + z sigma(z) (1 - sigma(z))."""
+    z = np.asarray(z, dtype=np.float64)
+    sig = 1.0 / (1.0 + np.exp(-z))
+    return sig + z * sig * (1.0 - sig)
+
+
 def act_fwd(z, act: int):
     if act == ACT_NONE:
         return np.array(z, dtype=np.float64, copy=True)
@@ -81,6 +102,8 @@ def act_fwd(z, act: int):
         return gelu_erf(z)
     if act == ACT_GELU_TANH:
         return gelu_tanh(z)
+    if act == ACT_SILU:
+        return silu(z)
     raise ValueError(f"unknown activation {act}")
 
 
@@ -93,6 +116,8 @@ def act_grad(z, act: int):
         return gelu_erf_grad(z)
     if act == ACT_GELU_TANH:
         return gelu_tanh_grad(z)
+    if act == ACT_SILU:
+        return silu_grad(z)
     raise ValueError(f"unknown activation {act}")
 
 
@@ -241,6 +266,45 @@ def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None):
     dw_up = gemm(np.asarray(x, dtype=np.float64).T, dzs)
     dx = gemm(dzs, np.asarray(w_up_t, dtype=np.float64).T)
     return dict(dH=dh, dZ=dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
+
+
+# ------------------------------------------------------- gated MLP share
+def gated_mlp_fwd(x, w_gate_t, w_up_t, w_down_t, act=ACT_SILU, store=None):
+    """One rank's share of the gated MLP of [WE]:
+        G_t = X . W_gate,t       (column-parallel, [M, F/T])
+        U_t = X . W_up,t         (column-parallel, [M, F/T])
+        H_t = act(G_t) * U_t     (gated activation, local, element-wise)
+        P_t = H_t . W_down,t     (row-parallel partial, [M, D])
+    store='bf16': the second GEMM reads H_t as stored in bf16."""
+    g = gemm(x, w_gate_t)
+    u = gemm(x, w_up_t)
+    h = act_fwd(g, act) * u
+    p = gemm(_stored(h, store), w_down_t)
+    return dict(G=g, U=u, H=h, P=p)
+
+
+def gated_mlp_bwd(x, w_gate_t, w_up_t, w_down_t, g, u, h, dy, act=ACT_SILU, store=None):
+    """Backward of gated_mlp_fwd by the chain rule, with the layouts of
+    [TSP] "Derive column-parallel linear algebra" / "Derive row-parallel
+    linear algebra" for the three projections:
+        dH_t      = dY . W_down,t^T
+        dG_t      = dH_t * U_t * act'(G_t)
+        dU_t      = dH_t * act(G_t)
+        dW_down,t = H_t^T . dY
+        dW_gate,t = X^T . dG_t,   dW_up,t = X^T . dU_t
+        dX_t      = dG_t . W_gate,t^T + dU_t . W_up,t^T   (full [M,D] partial)
+    G, U, H are the saved forward values.  store='bf16': the GEMMs that
+    consume dG_t and dU_t read them as stored in bf16."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    dh = gemm(dy, np.asarray(w_down_t, dtype=np.float64).T)
+    dg = dh * u * act_grad(g, act)
+    du = dh * act_fwd(g, act)
+    dw_down = gemm(np.asarray(h, dtype=np.float64).T, dy)
+    dgs, dus = _stored(dg, store), _stored(du, store)
+    xt = np.asarray(x, dtype=np.float64).T
+    dx = gemm(dgs, np.asarray(w_gate_t, dtype=np.float64).T) + gemm(dus, np.asarray(w_up_t, dtype=np.float64).T)
+    return dict(dH=dh, dG=dg, dU=du, dW_down=dw_down, dW_gate=gemm(xt, dgs), dW_up=gemm(xt, dus), dX=dx)
 
 
 def linear_bwd(x, w, dy):

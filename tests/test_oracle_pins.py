@@ -72,7 +72,7 @@ def test_bf16_matches_torch_and_ties():
 
 
 # -------------------------------------------------------------- activations
-@pytest.mark.parametrize("act", [ops.ACT_RELU, ops.ACT_GELU_ERF, ops.ACT_GELU_TANH, ops.ACT_NONE])
+@pytest.mark.parametrize("act", [ops.ACT_RELU, ops.ACT_GELU_ERF, ops.ACT_GELU_TANH, ops.ACT_NONE, ops.ACT_SILU])
 def test_activation_derivatives_by_central_differences(act):
     z = np.linspace(-6, 6, 2401) + 1e-3      # avoid the ReLU kink
     h = 1e-6
@@ -92,6 +92,126 @@ def test_activation_closed_forms():
     assert 1e-4 < diff < 5e-4
     # Phi(1) from the standard normal table
     assert abs(ops.gelu_erf(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+
+
+def test_silu_closed_forms():
+    from scipy.special import expit
+    z = np.linspace(-30, 30, 6001)
+    assert np.allclose(ops.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)      # z * logistic(z)
+    assert np.allclose(ops.silu(-z), ops.silu(z) - z, rtol=0, atol=1e-12)       # sigma(-z) = 1 - sigma(z)
+    assert ops.silu(np.array([0.0]))[0] == 0.0
+    assert ops.silu_grad(np.array([0.0]))[0] == 0.5
+    # logistic(1) = 1 / (1 + 1/e) = 0.7310585786300049
+    assert abs(ops.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    assert abs(ops.silu(np.array([40.0]))[0] - 40.0) < 1e-12 and abs(ops.silu(np.array([-40.0]))[0]) < 1e-15
+    assert np.allclose(ops.silu_grad(np.array([40.0, -40.0])), [1.0, 0.0], atol=1e-12)
+
+
+# --------------------------------------------------------------- gated MLP
+def _gated_brute(x, wg, wu, wd, act):
+    """Pure-Python gated MLP share: correctly rounded sums (math.fsum) and
+    the math module's erf / exp."""
+    M, D = len(x), len(x[0])
+    F = len(wg[0])
+    def a(z):
+        if act == ops.ACT_SILU:
+            return z / (1.0 + math.exp(-z))
+        if act == ops.ACT_GELU_ERF:
+            return 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+        assert act == ops.ACT_NONE
+        return z
+    h = [[a(math.fsum(x[i][k] * wg[k][j] for k in range(D))) * math.fsum(x[i][k] * wu[k][j] for k in range(D))
+          for j in range(F)] for i in range(M)]
+    return [[math.fsum(h[i][j] * wd[j][c] for j in range(F)) for c in range(D)] for i in range(M)]
+
+
+@pytest.mark.parametrize("act", [ops.ACT_SILU, ops.ACT_GELU_ERF, ops.ACT_NONE])
+def test_gated_mlp_fwd_vs_brute(act):
+    g = np.random.default_rng(71 + act)
+    M, D, F = 3, 5, 4
+    x, wg, wu, wd = g.standard_normal((M, D)), g.standard_normal((D, F)), g.standard_normal((D, F)), \
+        g.standard_normal((F, D))
+    ref = np.array(_gated_brute(x.tolist(), wg.tolist(), wu.tolist(), wd.tolist(), act))
+    got = ops.gated_mlp_fwd(x, wg, wu, wd, act)["P"]
+    assert np.max(np.abs(got - ref)) <= 1e-12 * (1 + np.max(np.abs(ref)))
+
+
+def test_gated_mlp_special_cases():
+    g = np.random.default_rng(73)
+    M, D, F = 6, 7, 5
+    x, wg, wd = g.standard_normal((M, D)), g.standard_normal((D, F)), g.standard_normal((F, D))
+    # U == 1 (X's column 0 is all ones, W_up selects it): the gated MLP is the
+    # plain MLP with the gate weight as its expansion, forward and backward
+    x[:, 0] = 1.0
+    wu = np.zeros((D, F))
+    wu[0, :] = 1.0
+    dy = g.standard_normal((M, D))
+    for act in (ops.ACT_SILU, ops.ACT_GELU_ERF, ops.ACT_RELU):
+        gf = ops.gated_mlp_fwd(x, wg, wu, wd, act)
+        pf = ops.tp_mlp_fwd(x, wg, wd, act)
+        assert np.array_equal(gf["U"], np.ones((M, F)))
+        assert np.allclose(gf["P"], pf["P"], rtol=0, atol=1e-13)
+        gb = ops.gated_mlp_bwd(x, wg, wu, wd, gf["G"], gf["U"], gf["H"], dy, act)
+        pb = ops.tp_mlp_bwd(x, wg, wd, pf["Z"], pf["H"], dy, act)
+        assert np.allclose(gb["dG"], pb["dZ"], rtol=0, atol=1e-13)
+        assert np.allclose(gb["dW_gate"], pb["dW_up"], rtol=0, atol=1e-12)
+        assert np.allclose(gb["dW_down"], pb["dW_down"], rtol=0, atol=1e-12)
+    # no activation and W_gate == W_up: H = G^2 exactly
+    f = ops.gated_mlp_fwd(x, wg, wg, wd, ops.ACT_NONE)
+    assert np.array_equal(f["H"], f["G"] * f["G"])
+
+
+def test_gated_sharded_equals_unsharded():
+    # [WE]: gate and expansion column-partitioned, contraction row-partitioned;
+    # the partials sum to the unsharded output, the shard gradients are the
+    # blocks of the unsharded ones and the dX partials sum to the unsharded dX
+    g = np.random.default_rng(75)
+    M, D, F, T = 8, 12, 16, 4
+    x, wg, wu, wd, dy = (g.standard_normal((M, D)), g.standard_normal((D, F)), g.standard_normal((D, F)),
+                         g.standard_normal((F, D)), g.standard_normal((M, D)))
+    full = ops.gated_mlp_fwd(x, wg, wu, wd, ops.ACT_SILU)
+    fullb = ops.gated_mlp_bwd(x, wg, wu, wd, full["G"], full["U"], full["H"], dy, ops.ACT_SILU)
+    P = np.zeros((M, D))
+    dX = np.zeros((M, D))
+    for t in range(T):
+        wgt, wut, wdt = ops.col_block(wg, T, t), ops.col_block(wu, T, t), ops.row_block(wd, T, t)
+        f = ops.gated_mlp_fwd(x, wgt, wut, wdt, ops.ACT_SILU)
+        b = ops.gated_mlp_bwd(x, wgt, wut, wdt, f["G"], f["U"], f["H"], dy, ops.ACT_SILU)
+        assert f["H"].shape == (M, F // T) and f["P"].shape == (M, D)
+        P += f["P"]
+        dX += b["dX"]
+        assert np.allclose(b["dW_gate"], ops.col_block(fullb["dW_gate"], T, t), rtol=0, atol=1e-12)
+        assert np.allclose(b["dW_up"], ops.col_block(fullb["dW_up"], T, t), rtol=0, atol=1e-12)
+        assert np.allclose(b["dW_down"], ops.row_block(fullb["dW_down"], T, t), rtol=0, atol=1e-12)
+    assert np.allclose(P, full["P"], rtol=0, atol=1e-12)
+    assert np.allclose(dX, fullb["dX"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", [ops.ACT_SILU, ops.ACT_GELU_ERF])
+def test_gated_gradients_by_finite_differences(act):
+    # L = <Gm, P>, dP = Gm
+    M, D, F = 4, 5, 3
+    g = np.random.default_rng(77 + act)
+    x, wg, wu, wd, Gm = (g.standard_normal((M, D)), g.standard_normal((D, F)) * 0.5,
+                         g.standard_normal((D, F)) * 0.5, g.standard_normal((F, D)) * 0.5,
+                         g.standard_normal((M, D)))
+    f = ops.gated_mlp_fwd(x, wg, wu, wd, act)
+    b = ops.gated_mlp_bwd(x, wg, wu, wd, f["G"], f["U"], f["H"], Gm, act)
+    args = [x, wg, wu, wd]
+
+    def loss(a):
+        return float(np.sum(Gm * ops.gated_mlp_fwd(*a, act)["P"]))
+
+    eps = 1e-6
+    for k, grad in enumerate((b["dX"], b["dW_gate"], b["dW_up"], b["dW_down"])):
+        fd = np.zeros_like(args[k])
+        for idx in np.ndindex(args[k].shape):
+            ap, am = list(args), list(args)
+            ap[k], am[k] = args[k].copy(), args[k].copy()
+            ap[k][idx] += eps
+            am[k][idx] -= eps
+            fd[idx] = (loss(ap) - loss(am)) / (2 * eps)
+        assert np.max(np.abs(fd - grad)) <= 1e-7 * (1 + np.max(np.abs(grad))), k
 
 
 # ------------------------------------------------------------- brute force
