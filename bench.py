@@ -432,6 +432,52 @@ def run_sweep(torch, tpm, si):
             torch.cuda.empty_cache()
 
 
+def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10):
+    """The worked example's gated MLP share (X [8192, 4096], F = 16384, T = 4:
+    gate and up shards [4096, 4096] each, contraction shard [4096, 4096]),
+    SwiGLU, bf16, rank 0, chunk-gated with the flags already set: forward and
+    backward timed separately with events."""
+    import numpy as np
+    Ft = F // T
+    dev = "cuda"
+    X = si.to_bf16(si.normal_f32((M, D), 1)).to(dev)
+    WGU = si.to_bf16(np.concatenate([si.normal_f32((D, Ft), 2, 0.02), si.normal_f32((D, Ft), 5, 0.02)],
+                                    axis=1)).to(dev)
+    WD = si.to_bf16(si.normal_f32((Ft, D), 3, 0.02)).to(dev)
+    dY = si.to_bf16(si.normal_f32((M, D), 4)).to(dev)
+    GU = torch.empty(M, 2 * Ft, dtype=torch.bfloat16, device=dev)
+    H, P = torch.empty(M, Ft, dtype=torch.bfloat16, device=dev), torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    dWgu, dWd, dX = torch.empty_like(WGU), torch.empty_like(WD), torch.empty_like(X)
+    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
+    order = si.ring_chunk_order(T, C, 0)
+    wsf = tpm.alloc_workspace(tpm.OP_GATED_MLP_FWD, M, D, F, T, C, tpm.BF16)
+    wsb = tpm.alloc_workspace(tpm.OP_GATED_MLP_BWD, M, D, F, T, C, tpm.BF16)
+    fwd = lambda: tpm.tp_gated_mlp_fwd(X, WGU, WD, H, P, T=T, rank=0, act=tpm.ACT_SILU, GU_t=GU, num_chunks=C,
+                                       chunk_order=order, chunk_ready=flags, epoch=1, workspace=wsf)
+    bwd = lambda: tpm.tp_gated_mlp_bwd(X, WGU, WD, GU, H, dY, dWgu, dWd, dX, T=T, rank=0, act=tpm.ACT_SILU,
+                                       num_chunks=C, dy_chunk_order=order, dy_ready=flags, epoch=1, workspace=wsb)
+    out = {"M": M, "D": D, "F": F, "T": T, "chunks": C, "act": "silu (SwiGLU)", "dtype": "bf16"}
+    for name, fn, units in (("fwd", fwd, 3), ("bwd", bwd, 6)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+        tf = units * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "TFLOPS": round(tf, 1), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
+    ms = out["fwd"]["ms"] + out["bwd"]["ms"]
+    out["TFLOPS_fwd_bwd"] = round(9 * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
 def recorded_traffic():
     """HBM bytes per step of the GEMM launches, as measured with rocprofv3
     FETCH_SIZE / WRITE_SIZE (profiles/gemm_traffic.md), or None when the GEMM
@@ -557,6 +603,8 @@ def main():
         extra["mlp_fwd_c3_bf16"] = bench_mlp_fwd(torch, tpm, si, 8192, 8192, 28672, 8, 8, False)
         torch.cuda.empty_cache()
         extra["mlp_fwd_c4_fp8"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
+        torch.cuda.empty_cache()
+        extra["gated_mlp_worked_example"] = bench_gated_mlp(torch, tpm, si)
         rec["extra"] = extra
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

@@ -39,13 +39,26 @@ typedef enum { TPM_F32 = 0, TPM_BF16 = 1, TPM_FP8_E4M3 = 2 } tpm_dtype;
 
 /* Activations.  GELU_ERF: 0.5 z (1 + erf(z / sqrt 2)); GELU_TANH: the tanh
  * approximation; RELU: max(z, 0) with derivative 1 only where z > 0
- * ("Tensor parallelism" algorithm page, section "Code"). */
-typedef enum { TPM_ACT_NONE = 0, TPM_ACT_RELU = 1, TPM_ACT_GELU_ERF = 2, TPM_ACT_GELU_TANH = 3 } tpm_act;
-
-/* Epilogue of seq_chunk_gemm. */
+ * ("Tensor parallelism" algorithm page, section "Code"); SILU: z sigma(z),
+ * sigma the logistic function (the gate of SwiGLU). */
 typedef enum {
-  TPM_EPI_FWD = 0,  /* Y = act(acc * sa * sb); aux (optional) receives the pre-activation */
-  TPM_EPI_DACT = 1  /* Y = acc * sa * sb * act'(aux): aux is the saved pre-activation Z */
+  TPM_ACT_NONE = 0, TPM_ACT_RELU = 1, TPM_ACT_GELU_ERF = 2, TPM_ACT_GELU_TANH = 3, TPM_ACT_SILU = 4
+} tpm_act;
+
+/* Epilogue of seq_chunk_gemm.  The gated forms serve the gated MLP of the
+ * worked example in "Tensor and sequence parallelism" ("Worked example:
+ * Partitioning an MLP pair"), H = act(X W_gate) * (X W_up), with the gate
+ * and up shards side by side: W_gu = [W_gate | W_up], [K, 2N]. */
+typedef enum {
+  TPM_EPI_FWD = 0,   /* Y = act(acc * sa * sb); aux (optional) receives the pre-activation */
+  TPM_EPI_DACT = 1,  /* Y = acc * sa * sb * act'(aux): aux is the saved pre-activation Z */
+  TPM_EPI_GATED = 2, /* B is W_gu [K, ldb >= 2N] (trans_b = 0): G = op(A) . B[:, 0:N],
+                        U = op(A) . B[:, N:2N]; Y[M,N] = act(G) * U; aux (optional,
+                        [M, ldaux >= 2N]) receives [G | U].  bf16 operands, trans_a = 0,
+                        no amax. */
+  TPM_EPI_DGATED = 3 /* acc is dH [M,N]; aux is the saved [G | U] ([M, ldaux >= 2N]);
+                        Y [M, ldy >= 2N] receives [dG | dU] with dG = dH * U * act'(G),
+                        dU = dH * act(G).  bf16 operands, no amax. */
 } tpm_epilogue;
 
 typedef enum {
@@ -58,7 +71,10 @@ typedef enum {
 } tpm_status;
 
 /* Operation ids for tpm_workspace_bytes(). */
-typedef enum { TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2 } tpm_op;
+typedef enum {
+  TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2,
+  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4
+} tpm_op;
 
 #define TPM_MAX_CHUNKS 256
 
@@ -82,7 +98,8 @@ typedef enum { TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2
  *    scale), or NULL for 1.
  * Y: [M, ldy >= N], y_dtype F32 or BF16 (round to nearest even).
  * epilogue/act/aux: see tpm_epilogue; aux is [M, ldaux >= N] of y_dtype
- *    (FWD: written if non-NULL; DACT: required, read).
+ *    (FWD: written if non-NULL; DACT: required, read; the gated forms use
+ *    [M, 2N] aux and, for DGATED, a [M, 2N] Y).
  * amax_out: device fp32 or NULL; set to max |Y| as stored (zeroed by the
  *    call first).
  * Chunks: the M rows of Y are cut into num_chunks equal chunks (M %
@@ -185,9 +202,55 @@ int partial_reduce_seqshard(int T, int64_t M, int64_t D, int rank,
                             const void* partials, int64_t partial_stride, int64_t ld, int in_dtype,
                             void* out, int64_t ldo, int out_dtype, void* stream);
 
+/*
+ * tp_gated_mlp_fwd -- rank `rank` of a T-way tensor-parallel gated MLP
+ * ("Tensor and sequence parallelism", "Worked example: Partitioning an MLP
+ * pair": the expansion and gate weights column-partitioned, the gated
+ * activation applied locally, the contraction row-partitioned):
+ *
+ *   G_t = X . W_gate,t,  U_t = X . W_up,t      [M, F/T] each
+ *   H_t = act(G_t) * U_t                        [M, F/T]  (act gates)
+ *   P_t = H_t . W_down,t                        [M, D] partial
+ *
+ * X [M, D] bf16; W_gu_t [D, 2F/T] bf16 = [W_gate,t | W_up,t] (the rank's two
+ * column shards side by side); W_down_t [F/T, D] bf16.  GU_t [M, 2F/T] bf16
+ * or NULL receives [G_t | U_t] (saved for the backward); H_t [M, F/T] and
+ * P_t [M, D] bf16.  Chunks, orders, flags and range_done as in tp_mlp_fwd.
+ * dtype must be TPM_BF16.  All leading dimensions are the row widths.
+ * workspace >= tpm_workspace_bytes(TPM_OP_GATED_MLP_FWD, M, D, F, T, ...)
+ * (may be NULL when no flags are given: then no split-K).
+ */
+int tp_gated_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+                     const void* X, const void* W_gu_t, const void* W_down_t, int dtype, int act,
+                     void* GU_t, void* H_t, void* P_t,
+                     int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                     const int32_t* range_order, uint32_t* range_done,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_gated_mlp_bwd -- backward of tp_gated_mlp_fwd (chain rule through the
+ * gate; column- and row-parallel layouts as in tp_mlp_bwd):
+ *
+ *   dH_t = dY . W_down,t^T;  dG_t = dH_t * U_t * act'(G_t);  dU_t = dH_t * act(G_t)
+ *   dW_down,t = H_t^T . dY                      [F/T, D]
+ *   dW_gu,t   = X^T . [dG_t | dU_t]             [D, 2F/T] = [dW_gate,t | dW_up,t]
+ *   dX_t      = [dG_t | dU_t] . W_gu,t^T        [M, D] partial
+ *
+ * GU_t and H_t are the forward's saved values; dY [M, D] arrives in chunks
+ * (dy_ready as in tp_mlp_bwd).  [dG_t | dU_t] is stored in bf16 in the
+ * workspace before the two GEMMs that read it.  dw_dtype BF16 or F32.
+ * workspace >= tpm_workspace_bytes(TPM_OP_GATED_MLP_BWD, M, D, F, T, ...).
+ */
+int tp_gated_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+                     const void* X, const void* W_gu_t, const void* W_down_t,
+                     const void* GU_t, const void* H_t, const void* dY, int dtype, int act,
+                     void* dW_gu_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                     int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
- * TPM_OP_MLP_BWD pass (M, N = D, K = F, T); for TPM_OP_SEQ_CHUNK_GEMM the
- * sizes are (M, N, K) and T is ignored. */
+ * TPM_OP_MLP_BWD and the gated forms pass (M, N = D, K = F, T); for
+ * TPM_OP_SEQ_CHUNK_GEMM the sizes are (M, N, K) and T is ignored. */
 size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int num_chunks, int dtype);
 
 /* Enqueue on `stream` a release store of `value` into the device word

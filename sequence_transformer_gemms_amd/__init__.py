@@ -7,6 +7,8 @@ Arguments are marshalled to the C ABI; nothing is computed here.
     seq_chunk_gemm          chunk-fed local GEMM with fused epilogue
     tp_mlp_fwd              Z = X W_up,t; H = act(Z); P = H W_down,t (partial)
     tp_mlp_bwd              dZ, dW_down,t, dW_up,t, dX_t (partial)
+    tp_gated_mlp_fwd        G, U = X [W_gate,t | W_up,t]; H = act(G) * U; P = H W_down,t
+    tp_gated_mlp_bwd        [dG | dU], dW_down,t, [dW_gate,t | dW_up,t], dX_t (partial)
     partial_reduce_seqshard sum of T partials over this rank's token slice
 """
 from __future__ import annotations
@@ -16,11 +18,13 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, BF16, EPI_DACT, EPI_FWD, F32,  # noqa: F401
-                   FP8_E4M3, OP_MLP_BWD, OP_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF16, EPI_DACT,  # noqa: F401
+                   EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD,
+                   OP_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
-__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "partial_reduce_seqshard",
+__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+           "partial_reduce_seqshard",
            "workspace_bytes", "alloc_workspace", "signal_chunk", "write_chunks", "poll_device_error",
            "set_wait_limit", "dtype_code", "masked_streams", "TpmError", "lib"]
 
@@ -70,13 +74,16 @@ def seq_chunk_gemm(A, B, Y, *, trans_a=False, trans_b=False, a_scale=None, b_sca
                    epilogue=EPI_FWD, act=ACT_NONE, aux=None, amax_out=None, num_chunks=1,
                    chunk_order=None, chunk_ready=None, epoch=0, workspace=None, stream=None,
                    M=None, N=None, K=None):
-    """Y = epilogue(op(A) . op(B)); shapes are taken from the tensors."""
+    """Y = epilogue(op(A) . op(B)); shapes are taken from the tensors (with
+    EPI_GATED, B is [W_gate | W_up] and N is half its width)."""
     if M is None:
         M = A.shape[1] if trans_a else A.shape[0]
     if K is None:
         K = A.shape[0] if trans_a else A.shape[1]
     if N is None:
         N = B.shape[0] if trans_b else B.shape[1]
+        if epilogue == EPI_GATED:
+            N //= 2
     order = _abi.int_array(chunk_order)
     rc = lib.seq_chunk_gemm(M, N, K,
                             _ptr(A), _ld(A), int(trans_a), dtype_code(A.dtype), _ptr(a_scale),
@@ -122,6 +129,36 @@ def tp_mlp_bwd(X, W_up_t, W_down_t, Z_t, H_t, dY, dW_up_t, dW_down_t, dX_t, *, T
                         num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch,
                         _ptr(workspace), workspace.numel() if workspace is not None else 0,
                         _stream(stream))
+    return check(rc)
+
+
+def tp_gated_mlp_fwd(X, W_gu_t, W_down_t, H_t, P_t, *, T, rank, act=ACT_SILU, GU_t=None, num_chunks=1,
+                     chunk_order=None, chunk_ready=None, epoch=0, range_order=None, range_done=None,
+                     workspace=None, stream=None):
+    """One rank's gated-MLP forward (bf16).  X [M,D], W_gu_t [D, 2F/T] =
+    [W_gate,t | W_up,t], W_down_t [F/T, D], H_t [M, F/T], P_t [M, D], GU_t
+    [M, 2F/T] or None."""
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_gated_mlp_fwd(M, D, Ft * T, T, rank, _ptr(X), _ptr(W_gu_t), _ptr(W_down_t),
+                              dtype_code(X.dtype), act, _ptr(GU_t), _ptr(H_t), _ptr(P_t),
+                              num_chunks, _abi.int_array(chunk_order), _ptr(chunk_ready), epoch,
+                              _abi.int_array(range_order), _ptr(range_done),
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                              _stream(stream))
+    return check(rc)
+
+
+def tp_gated_mlp_bwd(X, W_gu_t, W_down_t, GU_t, H_t, dY, dW_gu_t, dW_down_t, dX_t, *, T, rank, act=ACT_SILU,
+                     num_chunks=1, dy_chunk_order=None, dy_ready=None, epoch=0, workspace=None, stream=None):
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_gated_mlp_bwd(M, D, Ft * T, T, rank, _ptr(X), _ptr(W_gu_t), _ptr(W_down_t),
+                              _ptr(GU_t), _ptr(H_t), _ptr(dY), dtype_code(X.dtype), act,
+                              _ptr(dW_gu_t), _ptr(dW_down_t), _ptr(dX_t), dtype_code(dW_gu_t.dtype),
+                              num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch,
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                              _stream(stream))
     return check(rc)
 
 

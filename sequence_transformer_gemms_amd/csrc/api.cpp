@@ -117,8 +117,20 @@ int check_gemm(const GemmDesc& g, const char* who) {
   if (g.M > INT32_MAX || g.N > INT32_MAX || g.K > INT32_MAX) return fail(TPM_EUNSUPPORTED, "%s: size >= 2^31", who);
   if (!valid_dt(g.adt) || g.adt != g.bdt) return fail(TPM_EINVAL, "%s: operand dtypes must match", who);
   if (g.ydt != TPM_F32 && g.ydt != TPM_BF16) return fail(TPM_EINVAL, "%s: output dtype must be F32 or BF16", who);
-  if (g.epi != TPM_EPI_FWD && g.epi != TPM_EPI_DACT) return fail(TPM_EINVAL, "%s: bad epilogue", who);
-  if (g.act < TPM_ACT_NONE || g.act > TPM_ACT_GELU_TANH) return fail(TPM_EINVAL, "%s: bad activation", who);
+  if (g.epi < TPM_EPI_FWD || g.epi > TPM_EPI_DGATED) return fail(TPM_EINVAL, "%s: bad epilogue", who);
+  if (g.act < TPM_ACT_NONE || g.act > TPM_ACT_SILU) return fail(TPM_EINVAL, "%s: bad activation", who);
+  const bool gated = g.epi == TPM_EPI_GATED || g.epi == TPM_EPI_DGATED;
+  if (gated) {
+    if (g.adt != TPM_BF16) return fail(TPM_EUNSUPPORTED, "%s: gated epilogues take bf16 operands", who);
+    if (g.amax) return fail(TPM_EUNSUPPORTED, "%s: no amax with a gated epilogue", who);
+    if (g.epi == TPM_EPI_GATED && (g.ta || g.tb))
+      return fail(TPM_EUNSUPPORTED, "%s: EPI_GATED needs trans_a = 0 and trans_b = 0", who);
+    if (g.epi == TPM_EPI_DGATED && !g.aux) return fail(TPM_EINVAL, "%s: DGATED epilogue needs aux ([G | U])", who);
+    if (g.aux && g.ldaux < 2 * g.N) return fail(TPM_EINVAL, "%s: gated aux needs ldaux >= 2N", who);
+    if (g.epi == TPM_EPI_DGATED && g.ldy < 2 * g.N) return fail(TPM_EINVAL, "%s: DGATED needs ldy >= 2N", who);
+    if (g.epi == TPM_EPI_GATED && g.K > 0 && g.ldb < 2 * g.N)
+      return fail(TPM_EINVAL, "%s: EPI_GATED needs ldb >= 2N ([W_gate | W_up])", who);
+  }
   if (g.groups < 1 || g.groups > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks must be in [1, %d]", who, TPM_MAX_CHUNKS);
   if (g.M % g.groups != 0) return fail(TPM_EINVAL, "%s: M (%lld) %% num_chunks (%d) != 0", who, (long long)g.M, g.groups);
   if (g.order) {
@@ -136,7 +148,7 @@ int check_gemm(const GemmDesc& g, const char* who) {
   if (g.ldy < g.N || (g.K > 0 && (g.lda < a_cols || g.ldb < b_cols)))
     return fail(TPM_EINVAL, "%s: leading dimension smaller than the row width", who);
   if (g.epi == TPM_EPI_DACT && !g.aux) return fail(TPM_EINVAL, "%s: DACT epilogue needs aux (Z)", who);
-  if (g.aux && g.ldaux < g.N) return fail(TPM_EINVAL, "%s: ldaux < N", who);
+  if (g.aux && g.ldaux < (gated ? 2 * g.N : g.N)) return fail(TPM_EINVAL, "%s: ldaux < N", who);
   if ((g.ready || g.amax || g.done) && !g.ctrl) return fail(TPM_EWORKSPACE, "%s: workspace required", who);
   if (g.adt == TPM_F32) {
     if (g.ydt != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 operands give fp32 output", who);
@@ -185,7 +197,8 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   }
   // split-K when the plan asks for it and the scratch is there (chunk-gated
   // GEMMs split too; range-done signalling needs whole tiles)
-  int S = g.done ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+  // (the gated forward pairs gate and up columns inside one tile: no split-K)
+  int S = (g.done || g.epi == TPM_EPI_GATED) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
   if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
   const int64_t nk = (g.K * esize(g.adt) + kStepBytes - 1) / kStepBytes;
   p.splits = S;
@@ -194,8 +207,10 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
   p.a_bytes = g.K == 0 ? 0u : (uint32_t)(a_rows * g.lda * esize(g.adt));
   p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
+  p.gu_off = (g.epi == TPM_EPI_GATED || g.epi == TPM_EPI_DGATED) ? (int)g.N : 0;
+  p.bn_out = g.epi == TPM_EPI_GATED ? kTileN / 2 : kTileN;
   p.mt_per_group = (p.group_rows + kTileM - 1) / kTileM;
-  p.nt = (p.N + kTileN - 1) / kTileN;
+  p.nt = (p.N + p.bn_out - 1) / p.bn_out;
   p.tiles_per_group = p.mt_per_group * p.nt;
   p.total_tiles = p.tiles_per_group * p.num_groups;
   p.band_m = std::min(p.mt_per_group, 4);
@@ -262,6 +277,21 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       part = std::max(part, partial_bytes(D, Ft, plan_splits(D, Ft, M, 1, dtype)));
       part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, dtype)));
       return kCtrlBytes + dz + part;
+    }
+    case TPM_OP_GATED_MLP_FWD: {
+      if (T <= 0) return 0;
+      const int64_t D = N, Ft = K / T;
+      return kCtrlBytes + partial_bytes(M, D, plan_splits(M, D, Ft, T, dtype));
+    }
+    case TPM_OP_GATED_MLP_BWD: {
+      if (T <= 0) return 0;
+      const int64_t D = N, Ft = K / T;
+      const size_t dgu = round_up((size_t)M * (size_t)(2 * Ft) * 2, 256);
+      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype));
+      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, dtype)));
+      part = std::max(part, partial_bytes(D, 2 * Ft, plan_splits(D, 2 * Ft, M, 1, dtype)));
+      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, 2 * Ft, 1, dtype)));
+      return kCtrlBytes + dgu + part;
     }
     default: return 0;
   }
@@ -476,6 +506,120 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
     if (e != hipSuccess) return hip_fail(e, who);
   }
   for (const GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
+    int rc = run_gemm(*g, s, who);
+    if (rc != TPM_OK) return rc;
+  }
+  return TPM_OK;
+}
+
+int tp_gated_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+                     const void* X, const void* W_gu_t, const void* W_down_t, int dtype, int act,
+                     void* GU_t, void* H_t, void* P_t,
+                     int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                     const int32_t* range_order, uint32_t* range_done,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_gated_mlp_fwd";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0 || M % T != 0) return fail(TPM_EINVAL, "%s: F %% T or M %% T != 0", who);
+  if (dtype != TPM_BF16) return fail(TPM_EUNSUPPORTED, "%s: the gated MLP runs in bf16", who);
+  if (!H_t || !P_t) return fail(TPM_EINVAL, "%s: null H_t or P_t", who);
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
+  const int64_t Ft = F / T;
+  const size_t need = tpm_workspace_bytes(TPM_OP_GATED_MLP_FWD, M, D, F, T, num_chunks, dtype);
+  const bool need_ctrl = chunk_ready || range_done;
+  if (need_ctrl && (!workspace || workspace_bytes < need))
+    return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  uint32_t* ctrl = (workspace && workspace_bytes >= kCtrlBytes) ? (uint32_t*)workspace : nullptr;
+  int32_t corder[TPM_MAX_CHUNKS], rorder[TPM_MAX_CHUNKS];
+  if (chunk_order) std::memcpy(corder, chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  if (range_order) std::memcpy(rorder, range_order, sizeof(int32_t) * T);
+  else for (int i = 0; i < T; ++i) rorder[i] = (rank + 1 + i) % T;
+  // GEMM1: H = act(X W_gate) * (X W_up), chunk-fed; W_gu_t = [W_gate,t | W_up,t] [D, 2Ft]
+  GemmDesc g1{M, Ft, D, X, D, false, TPM_BF16, nullptr, W_gu_t, 2 * Ft, false, TPM_BF16, nullptr,
+              H_t, Ft, TPM_BF16, TPM_EPI_GATED, act, GU_t, 2 * Ft, nullptr,
+              num_chunks, corder, chunk_ready, nullptr, epoch, ctrl};
+  // GEMM2: row-parallel partial P = H W_down, destination ranges in order
+  GemmDesc g2{M, D, Ft, H_t, Ft, false, TPM_BF16, nullptr, W_down_t, D, false, TPM_BF16, nullptr,
+              P_t, D, TPM_BF16, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+              T, rorder, nullptr, range_done, epoch, ctrl};
+  for (const GemmDesc* g : {&g1, &g2}) {
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  if (workspace && workspace_bytes >= need) {
+    g1.part = g2.part = (float*)((char*)workspace + kCtrlBytes);
+    g1.part_bytes = g2.part_bytes = workspace_bytes - kCtrlBytes;
+  }
+  if (M == 0 || D == 0) return TPM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (need_ctrl) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  int rc = run_gemm(g1, s, who);
+  if (rc != TPM_OK) return rc;
+  return run_gemm(g2, s, who);
+}
+
+int tp_gated_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
+                     const void* X, const void* W_gu_t, const void* W_down_t,
+                     const void* GU_t, const void* H_t, const void* dY, int dtype, int act,
+                     void* dW_gu_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                     int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_gated_mlp_bwd";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0 || M % T != 0) return fail(TPM_EINVAL, "%s: F %% T or M %% T != 0", who);
+  if (dtype != TPM_BF16) return fail(TPM_EUNSUPPORTED, "%s: the gated MLP runs in bf16", who);
+  if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
+  if (!GU_t || !H_t || !dY || !dW_gu_t || !dW_down_t || !dX_t || !X || !W_gu_t || !W_down_t)
+    return fail(TPM_EINVAL, "%s: null pointer", who);
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
+  const int64_t Ft = F / T;
+  const size_t need = tpm_workspace_bytes(TPM_OP_GATED_MLP_BWD, M, D, F, T, num_chunks, dtype);
+  if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  uint32_t* ctrl = (uint32_t*)workspace;
+  void* dGU = (char*)workspace + kCtrlBytes;
+  int32_t corder[TPM_MAX_CHUNKS];
+  if (dy_chunk_order) std::memcpy(corder, dy_chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  const int bf = TPM_BF16;
+  // [dG | dU] from dH = dY . W_down^T       W_down_t [Ft, D]: op(B) = W_down^T, stored [N=Ft, K=D]
+  GemmDesc g_dh{M, Ft, D, dY, D, false, bf, nullptr, W_down_t, D, true, bf, nullptr,
+                dGU, 2 * Ft, bf, TPM_EPI_DGATED, act, const_cast<void*>(GU_t), 2 * Ft, nullptr,
+                num_chunks, corder, dy_ready, nullptr, epoch, ctrl};
+  // dW_down = H^T . dY
+  GemmDesc g_wd{Ft, D, M, H_t, Ft, true, bf, nullptr, dY, D, false, bf, nullptr,
+                dW_down_t, D, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, epoch, ctrl};
+  // [dW_gate | dW_up] = X^T . [dG | dU]
+  GemmDesc g_wgu{D, 2 * Ft, M, X, D, true, bf, nullptr, dGU, 2 * Ft, false, bf, nullptr,
+                 dW_gu_t, 2 * Ft, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                 1, nullptr, nullptr, nullptr, epoch, ctrl};
+  // dX = [dG | dU] . [W_gate | W_up]^T       W_gu_t [D, 2Ft]: op(B) = W_gu^T, stored [N=D, K=2Ft]
+  GemmDesc g_dx{M, D, 2 * Ft, dGU, 2 * Ft, false, bf, nullptr, W_gu_t, 2 * Ft, true, bf, nullptr,
+                dX_t, D, bf, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, epoch, ctrl};
+  {
+    const size_t dgu_bytes = round_up((size_t)M * (size_t)(2 * Ft) * 2, 256);
+    for (GemmDesc* g : {&g_dh, &g_wd, &g_wgu, &g_dx}) {
+      g->part = (float*)((char*)workspace + kCtrlBytes + dgu_bytes);
+      g->part_bytes = workspace_bytes - kCtrlBytes - dgu_bytes;
+    }
+  }
+  for (const GemmDesc* g : {&g_dh, &g_wd, &g_wgu, &g_dx}) {
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (dy_ready) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  for (const GemmDesc* g : {&g_dh, &g_wd, &g_wgu, &g_dx}) {
     int rc = run_gemm(*g, s, who);
     if (rc != TPM_OK) return rc;
   }

@@ -117,7 +117,7 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
   tl.m0 = gstart + mt * BM;
   const int gend = gstart + p.group_rows;
   tl.m_end = (tl.m0 + BM < gend) ? tl.m0 + BM : gend;
-  tl.n0 = ntile * BN;
+  tl.n0 = ntile * p.bn_out;
   return un;
 }
 
@@ -125,10 +125,16 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
 // one K step: thread t of the work-group fills LDS chunk P = j * THREADS + t.
 // kmajor: rows are the M (or N) index, 128 bytes of K each.  Otherwise: rows
 // are K (64 of them), 512 bytes (256 bf16) of M or N each.
-template <bool KMAJ, int ESZ, int THREADS>
+// GATED (MN-major B only): the 256 tile columns are 32-column blocks taken
+// alternately from the gate half and the up half of B = [W_gate | W_up]
+// (up half at column up_off), both for output columns mn0 + 32 b' .. +31 of
+// block pair b', so that the two N fragments of a wave (64 columns) hold the
+// gate and up products of the same 32 output columns.
+template <bool KMAJ, int ESZ, int THREADS, bool GATED = false>
 __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end, int k0,
-                                          int K, char* lds_tile, int j) {
+                                          int K, char* lds_tile, int j, int up_off = 0) {
   static_assert(KMAJ || ESZ == 2, "MN-major staging is bf16 only");
+  static_assert(!(GATED && KMAJ), "gated staging is MN-major");
   constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,9 +149,16 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
   } else {
     const uint32_t row = P >> 5;
     const uint32_t c = (P & 31u) ^ swz_mn(row);
-    const int mn = mn0 + (int)c * 8;
+    int mn, src;
+    if constexpr (GATED) {
+      mn = mn0 + (int)(c >> 3) * 32 + (int)(c & 3u) * 8;   // output column of chunk c
+      src = mn + (((c >> 2) & 1u) ? up_off : 0);
+    } else {
+      mn = mn0 + (int)c * 8;
+      src = mn;
+    }
     const bool ok = (k0 + (int)row < K) && (mn < mn_end);
-    voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)mn * 2) : kOOB;
+    voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)src * 2) : kOOB;
   }
   load16_to_lds(rs, voff, lds_tile + (j * THREADS + wave * 64) * 16);
 }
@@ -234,8 +247,63 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Epilogue of eight consecutive output columns (row, col..col+7) of one lane.
+// 8 consecutive values of a row-major bf16 or fp32 matrix
+__device__ __forceinline__ void load_oct(const void* base, int64_t ld, bool f32, int row, int col, float (&v)[8]) {
+  if (f32) {
+    const f32x4* src = (const f32x4*)((const float*)base + (int64_t)row * ld + col);
+    const f32x4 a = src[0], b = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+  } else {
+    const i32x4 zz = *(const i32x4*)((const uint16_t*)base + (int64_t)row * ld + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_to_f32((uint16_t)((uint32_t)zz[e] & 0xFFFFu));
+      v[2 * e + 1] = bf16_to_f32((uint16_t)((uint32_t)zz[e] >> 16));
+    }
+  }
+}
+__device__ __forceinline__ void store_oct(void* base, int64_t ld, bool f32, int row, int col, const float (&v)[8]) {
+  if (f32) {
+    f32x4* dst = (f32x4*)((float*)base + (int64_t)row * ld + col);
+    dst[0] = (f32x4){v[0], v[1], v[2], v[3]};
+    dst[1] = (f32x4){v[4], v[5], v[6], v[7]};
+  } else {
+    i32x4 yy;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      yy[e] = (int)((uint32_t)f32_to_bf16_rne(v[2 * e]) | ((uint32_t)f32_to_bf16_rne(v[2 * e + 1]) << 16));
+    *(i32x4*)((uint16_t*)base + (int64_t)row * ld + col) = yy;
+  }
+}
+
+// Gated forward epilogue of 8 output columns: g, u are the gate and up
+// products; aux (optional) keeps [G | U], Y = act(G) * U.
+__device__ __forceinline__ void epi_gated_oct(const GemmParams& p, const float (&g)[8], const float (&u)[8], int row,
+                                              int col) {
+  if (p.aux) {
+    store_oct(p.aux, p.ldaux, p.aux_f32, row, col, g);
+    store_oct(p.aux, p.ldaux, p.aux_f32, row, p.gu_off + col, u);
+  }
+  float h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = act_fwd(g[e], p.act) * u[e];
+  store_oct(p.Y, p.ldy, p.y_f32, row, col, h);
+}
+
 __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax) {
-  if (p.epi == EPI_DACT) {
+  if (p.epi == EPI_DGATED) {
+    // v = dH; aux = [G | U]: Y[:, col] = dG = dH U act'(G), Y[:, N + col] = dU = dH act(G)
+    float g[8], u[8], du[8];
+    load_oct(p.aux, p.ldaux, p.aux_f32, row, col, g);
+    load_oct(p.aux, p.ldaux, p.aux_f32, row, p.gu_off + col, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      du[e] = v[e] * act_fwd(g[e], p.act);
+      v[e] = v[e] * u[e] * act_grad(g[e], p.act);
+    }
+    store_oct(p.Y, p.ldy, p.y_f32, row, p.gu_off + col, du);
+  } else if (p.epi == EPI_DACT) {
     float z[8];
     if (p.aux_f32) {
       const f32x4* src = (const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
@@ -291,8 +359,9 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
   }
 }
 
-template <bool FP8, bool AK, bool BKM, int NW>
+template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
+  static_assert(!GATED || (!FP8 && !BKM && NW == 8), "gated: bf16, MN-major B, 8 waves (two N fragments)");
   using LY = Layout<NW>;
   constexpr int THREADS = LY::THREADS, LOADS = LY::LOADS, NF = LY::NF;
   constexpr int ESZ = FP8 ? 1 : 2;
@@ -349,7 +418,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
       char* dst = slot(k);
       const int k0 = k < nks ? (kbeg + k) * KSTEP : p.K;
       if (L < LOADS) issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
-      else issue_one<BKM, ESZ, THREADS>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS);
+      else issue_one<BKM, ESZ, THREADS, GATED>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS, p.gu_off);
     };
     auto read_set = [&](const char* __restrict__ st, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
 #pragma unroll
@@ -493,6 +562,29 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
         const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         *(f32x4*)(stage + (32 * ii + (lane & 31)) * EPI_LD + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
       });
+      if constexpr (GATED) {
+        // staged columns 0..31 are the gate products and 32..63 the up
+        // products of the wave's 32 output columns: 8 of each per lane, 4
+        // lanes per row
+#pragma unroll 1
+        for (int it = 0; it < EPI_ROWS / 16; ++it) {
+          const int rl = it * 16 + (lane >> 2);
+          const int cl = (lane & 3) * 8;
+          const f32x4 g0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
+          const f32x4 g1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+          const f32x4 u0 = *(const f32x4*)(stage + rl * EPI_LD + 32 + cl);
+          const f32x4 u1 = *(const f32x4*)(stage + rl * EPI_LD + 36 + cl);
+          const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+          const int col = tl.n0 + wn / 2 + cl;
+          if (row < tl.m_end && col < p.N) {
+            const float g[8] = {g0[0] * scale, g0[1] * scale, g0[2] * scale, g0[3] * scale,
+                                g1[0] * scale, g1[1] * scale, g1[2] * scale, g1[3] * scale};
+            const float u[8] = {u0[0] * scale, u0[1] * scale, u0[2] * scale, u0[3] * scale,
+                                u1[0] * scale, u1[1] * scale, u1[2] * scale, u1[3] * scale};
+            epi_gated_oct(p, g, u, row, col);
+          }
+        }
+      } else {
       // read back 8 consecutive columns per lane, 8 lanes per row
 #pragma unroll 1
       for (int it = 0; it < EPI_ROWS / 8; ++it) {
@@ -514,6 +606,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
             epi_oct(p, v, row, col, lmax);
           }
         }
+      }
       }
     });
     if (p.amax) {
@@ -589,6 +682,11 @@ constexpr int kWaves = TPM_GEMM_WAVES_BF16, kWaves8 = TPM_GEMM_WAVES_FP8;
 constexpr int kThreads = 64 * kWaves, kThreads8 = 64 * kWaves8;
 
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
+  if (p.epi == EPI_GATED) {
+    if (!a_kmajor || b_kmajor || p.splits != 1) return hipErrorInvalidValue;  // rejected on the host first
+    gemm_kernel<false, true, false, 8, true><<<grid, 512, 0, s>>>(p);
+    return hipGetLastError();
+  }
   if (a_kmajor && !b_kmajor) gemm_kernel<false, true, false, kWaves><<<grid, kThreads, 0, s>>>(p);
   else if (a_kmajor && b_kmajor) gemm_kernel<false, true, true, kWaves><<<grid, kThreads, 0, s>>>(p);
   else if (!a_kmajor && !b_kmajor) gemm_kernel<false, false, false, kWaves><<<grid, kThreads, 0, s>>>(p);

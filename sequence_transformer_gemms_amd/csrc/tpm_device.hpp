@@ -86,7 +86,7 @@ __device__ inline uint8_t f32_to_e4m3_rne_sat(float f) {
 }
 
 // ------------------------------------------------------------ activations
-enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
 
 __device__ inline float act_fwd(float z, int act) {
   switch (act) {
@@ -99,6 +99,7 @@ __device__ inline float act_fwd(float z, int act) {
       float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
       return z / (1.f + expf(-2.f * u));
     }
+    case ACT_SILU: return z / (1.f + expf(-z));  // z sigma(z); -0 once expf overflows
     default: return z;
   }
 }
@@ -119,6 +120,12 @@ __device__ inline float act_grad(float z, int act) {
       float sg = 1.f / (1.f + e);
       float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
       return sg + 2.f * z * sg * (e * sg) * du;
+    }
+    case ACT_SILU: {
+      // sigma(z) (1 + z sigma(-z)), both logistic values taken directly so
+      // that neither 1 - sigma nor inf * 0 appears at large |z|
+      const float sp = 1.f / (1.f + expf(-z)), sn = 1.f / (1.f + expf(z));
+      return sp * (1.f + z * sn);
     }
     default: return 1.f;
   }

@@ -34,10 +34,12 @@ struct GemmParams {
   int splits;                // K-range splits (1: none); > 1 needs `partial`
   int ksteps_per_split;      // K steps (of 32 bf16 / 64 fp8) per split
   float* partial;            // device fp32 [splits][M][N] partial sums
+  int gu_off;                // gated epilogues: column offset of the up half in B / aux / Y (= N)
+  int bn_out;                // output columns per tile (256; 128 for EPI_GATED)
   int16_t order[kMaxGroups];
 };
 
-enum { EPI_FWD = 0, EPI_DACT = 1 };
+enum { EPI_FWD = 0, EPI_DACT = 1, EPI_GATED = 2, EPI_DGATED = 3 };
 
 // Side-stream chunk writer: chunks order[0..n-1] of chunk_bytes each, copied
 // src -> dst when copy[c] != 0, then ready[c] = epoch.

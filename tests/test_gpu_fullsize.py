@@ -334,3 +334,67 @@ def test_tp_degree_sweep_shapes_sampled_and_chunk_invariant(T):
     assert nerr(host64(P[rows]), ref["P"]) <= TOL["bf16"]
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------ gated MLP (worked example)
+def test_gated_mlp_worked_example_full_size_sampled():
+    """The worked example's MLP pair ("Tensor and sequence parallelism",
+    "Worked example: Partitioning an MLP pair") at its full size, rank 0 of
+    T = 4: X [8192, 4096], gate and up shards [4096, 4096] each (side by side
+    in one [4096, 8192] buffer), SwiGLU, contraction shard [4096, 4096], 4
+    chunks in ring order; forward and backward as bench.py runs them.  Rows
+    of G, U, H, P and dX; columns of dW_gate, dW_up and rows of dW_down, with
+    the bf16-rounding ambiguity of the stored intermediates added to the bound
+    (as for the layer step's weight gradients)."""
+    M, D, F, T, C, r = 8192, 4096, 16384, 4, 4, 0
+    Ft, act = F // T, ops.ACT_SILU
+    x = si.to_bf16(si.normal_f32((M, D), 1))
+    wg, wu = si.to_bf16(si.normal_f32((D, Ft), 2, 0.02)), si.to_bf16(si.normal_f32((D, Ft), 5, 0.02))
+    wd = si.to_bf16(si.normal_f32((Ft, D), 3, 0.02))
+    dy = si.to_bf16(si.normal_f32((M, D), 4))
+    X, WGU, WD, DYd = x.cuda(), torch.cat([wg, wu], dim=1).cuda(), wd.cuda(), dy.cuda()
+    e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+    GU, H, P = e(M, 2 * Ft), e(M, Ft), e(M, D)
+    dWgu, dWd, dX = e(D, 2 * Ft), e(Ft, D), e(M, D)
+    flags = torch.full((C,), 1, dtype=torch.int32, device="cuda")
+    order = si.ring_chunk_order(T, C, r)
+    wsf = tpm.alloc_workspace(_abi.OP_GATED_MLP_FWD, M, D, F, T, C, _abi.BF16)
+    wsb = tpm.alloc_workspace(_abi.OP_GATED_MLP_BWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_gated_mlp_fwd(X, WGU, WD, H, P, T=T, rank=r, act=act, GU_t=GU, num_chunks=C, chunk_order=order,
+                         chunk_ready=flags, epoch=1, workspace=wsf)
+    tpm.tp_gated_mlp_bwd(X, WGU, WD, GU, H, DYd, dWgu, dWd, dX, T=T, rank=r, act=act, num_chunks=C,
+                         dy_chunk_order=order, dy_ready=flags, epoch=1, workspace=wsb)
+    sync()
+    assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
+    B = TOL["bf16"]
+    Xf, WG, WU, WDf, DY = f64(x), f64(wg), f64(wu), f64(wd), f64(dy)
+    rows = pick(M, 12, 61)
+    fw = ops.gated_mlp_fwd(Xf[rows], WG, WU, WDf, act, store="bf16")
+    assert nerr(host64(GU[rows][:, :Ft]), fw["G"]) <= B and nerr(host64(GU[rows][:, Ft:]), fw["U"]) <= B
+    assert nerr(host64(H[rows]), fw["H"]) <= B
+    assert nerr(host64(P[rows]), fw["P"]) <= B
+    gb, ub, hb = (formats.round_bf16(fw[k]) for k in ("G", "U", "H"))
+    bw = ops.gated_mlp_bwd(Xf[rows], WG, WU, WDf, gb, ub, hb, DY[rows], act, store="bf16")
+    assert nerr(host64(dX[rows]), bw["dX"]) <= B
+    # weight gradients on sampled columns over all tokens
+    fcols = pick(Ft, 6, 62)
+    g_ex, u_ex = Xf @ WG[:, fcols], Xf @ WU[:, fcols]                 # exact G, U columns
+    gb, gamb = bf16_either(g_ex)
+    ub, uamb = bf16_either(u_ex)
+    hb, hamb = bf16_either(ops.act_fwd(g_ex, act) * u_ex)
+    ref = hb.T @ DY                                                    # rows fcols of dW_down
+    tol = B * (1 + np.abs(ref)) + hamb.T @ np.abs(DY)
+    assert np.all(np.abs(host64(dWd[fcols]) - ref) <= tol)
+    dh = DY @ WDf[fcols].T                                             # dH columns, exact
+    g_o = gb + gamb * np.sign(g_ex - gb)                               # G saved the other way
+    u_o = ub + uamb * np.sign(u_ex - ub)
+    dg = dh * ub * ops.act_grad(gb, act)
+    du = dh * ops.act_fwd(gb, act)
+    dg_in = np.where(gamb > 0, np.abs(dh * ub * ops.act_grad(g_o, act) - dg), 0.0) + \
+        np.where(uamb > 0, np.abs(dh * u_o * ops.act_grad(gb, act) - dg), 0.0)
+    du_in = np.where(gamb > 0, np.abs(dh * ops.act_fwd(g_o, act) - du), 0.0)
+    for got, val, amb_in in ((dWgu[:, fcols], dg, dg_in), (dWgu[:, Ft + fcols], du, du_in)):
+        vb, vamb = bf16_either(val)
+        ref = Xf.T @ vb
+        tol = B * (1 + np.abs(ref)) + np.abs(Xf).T @ (vamb + amb_in)
+        assert np.all(np.abs(host64(got) - ref) <= tol)

@@ -286,15 +286,151 @@ def test_mlp_fwd_bwd_bf16_small(act):
     gd = torch.empty(Ft, D, dtype=torch.bfloat16, device="cuda")
     dX = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
     wsb = tpm.alloc_workspace(_abi.OP_MLP_BWD, M, D, F, T, C, _abi.BF16)
-    tpm.tp_mlp_bwd(X, WU, WD, Z, H, dY, gu, gd, dX, T=T, rank=1, act=act, num_chunks=C, workspace=wsb)
+    # the backward takes the oracle's forward values as stored in bf16, on both sides
+    zb, hb = formats.round_bf16(ref["Z"]), formats.round_bf16(ref["H"])
+    tpm.tp_mlp_bwd(X, WU, WD, si.to_bf16(zb).cuda(), si.to_bf16(hb).cuda(), dY, gu, gd, dX, T=T, rank=1, act=act,
+                   num_chunks=C, workspace=wsb)
     sync()
-    rb = ops.tp_mlp_bwd(f64(X), f64(WU), f64(WD), f64(Z), f64(H), f64(dY), act, store="bf16")
+    rb = ops.tp_mlp_bwd(f64(X), f64(WU), f64(WD), zb, hb, f64(dY), act, store="bf16")
     assert nerr(gu, rb["dW_up"]) <= TOL["bf16"]
     assert nerr(gd, rb["dW_down"]) <= TOL["bf16"]
     assert nerr(dX, rb["dX"]) <= TOL["bf16"]
     # the workspace holds dZ after the call
     dZ = wsb[2048:2048 + M * Ft * 2].view(torch.bfloat16).view(M, Ft)
     assert nerr(dZ, rb["dZ"]) <= TOL["bf16"]
+
+
+# --------------------------------------------------------------- gated MLP
+ACTS_GATED = [_abi.ACT_SILU, _abi.ACT_GELU_ERF] if torch.cuda.is_available() else []
+
+
+@pytest.mark.parametrize("act", [0, 1])      # none, ReLU: integer results
+def test_gated_gemm_integer_exact(act):
+    # EPI_GATED with integer inputs: G and U are exact integers, act(G) * U
+    # too, so fp32 outputs equal the oracle bit for bit and bf16 outputs its
+    # one rounding.  This pins the pairing of gate and up columns (32-column
+    # blocks taken alternately from the two halves of [W_gate | W_up]), the
+    # output column of every block and the ragged tails (304 = 256 + 48
+    # rows, 136 = 128 + 8 output columns), chunked and unchunked.
+    M, K, N = 304, 200, 136
+    a = si.small_ints((M, K), 91)
+    wg, wu = si.small_ints((K, N), 92), si.small_ints((K, N), 93)
+    A, B = dev_bf16(a), dev_bf16(np.concatenate([wg, wu], axis=1))
+    g, u = a.astype(np.float64) @ wg, a.astype(np.float64) @ wu
+    h = ops.act_fwd(g, act) * u
+    for C in (1, 4):
+        Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        aux = torch.empty(M, 2 * N, dtype=torch.float32, device="cuda")
+        tpm.seq_chunk_gemm(A, B, Y, epilogue=_abi.EPI_GATED, act=act, aux=aux, num_chunks=C,
+                           chunk_order=list(range(C))[::-1])
+        Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tpm.seq_chunk_gemm(A, B, Yb, epilogue=_abi.EPI_GATED, act=act, num_chunks=C)
+        sync()
+        assert np.array_equal(f64(aux[:, :N]), g) and np.array_equal(f64(aux[:, N:]), u)
+        assert np.array_equal(f64(Y), h)
+        assert np.array_equal(f64(Yb), formats.round_bf16(h))
+
+
+@pytest.mark.parametrize("act", ACTS_GATED)
+def test_gated_gemm_float(act):
+    M, K, N = 304, 512, 264
+    x = si.normal_f32((M, K), 94)
+    wg, wu = si.normal_f32((K, N), 95, 0.05), si.normal_f32((K, N), 96, 0.05)
+    X, B = dev_bf16(x), dev_bf16(np.concatenate([wg, wu], axis=1))
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    aux = torch.empty(M, 2 * N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(X, B, Y, epilogue=_abi.EPI_GATED, act=act, aux=aux)
+    sync()
+    Bf = f64(B)
+    g, u = f64(X) @ Bf[:, :N], f64(X) @ Bf[:, N:]
+    assert nerr(aux[:, :N], g) <= TOL["bf16"] and nerr(aux[:, N:], u) <= TOL["bf16"]
+    assert nerr(Y, ops.act_fwd(g, act) * u) <= TOL["bf16"]
+
+
+def test_dgated_epilogue_integer_exact_and_split_k():
+    # EPI_DGATED, no activation: dG = dH U and dU = dH G are exact integers.
+    # Second shape: 4 output tiles and K = 4096, so the plan splits K and the
+    # split-K finalisation runs the same epilogue.
+    for (M, N, K, ws) in ((304, 136, 200, False), (512, 264, 4096, True)):
+        dy = si.small_ints((M, K), 97)
+        wd = si.small_ints((N, K), 98)              # W_down [F/T, D] as stored: op(B) = W_down^T
+        gu = si.small_ints((M, 2 * N), 99)
+        Y = torch.empty(M, 2 * N, dtype=torch.float32, device="cuda")
+        aux = dev_f32(gu)
+        w = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K) if ws else None
+        if ws:
+            assert w.numel() > 2048                  # split-K planned
+        tpm.seq_chunk_gemm(dev_bf16(dy), dev_bf16(wd), Y, trans_b=True, epilogue=_abi.EPI_DGATED,
+                           act=_abi.ACT_NONE, aux=aux, workspace=w)
+        sync()
+        dh = dy.astype(np.float64) @ wd.astype(np.float64).T
+        assert np.array_equal(f64(Y[:, :N]), dh * gu[:, N:])
+        assert np.array_equal(f64(Y[:, N:]), dh * gu[:, :N])
+
+
+@pytest.mark.parametrize("act", ACTS_GATED)
+def test_dgated_epilogue_float(act):
+    M, N, K = 512, 264, 4096
+    dy = si.normal_f32((M, K), 100)
+    wd = si.normal_f32((N, K), 101, 0.02)
+    gu = si.normal_f32((M, 2 * N), 102)
+    w = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    Y = torch.empty(M, 2 * N, dtype=torch.bfloat16, device="cuda")
+    GU = dev_bf16(gu)
+    tpm.seq_chunk_gemm(dev_bf16(dy), dev_bf16(wd), Y, trans_b=True, epilogue=_abi.EPI_DGATED, act=act, aux=GU,
+                       workspace=w)
+    sync()
+    dh = f64(dev_bf16(dy)) @ f64(dev_bf16(wd)).T
+    g, u = f64(GU)[:, :N], f64(GU)[:, N:]
+    assert nerr(Y[:, :N], dh * u * ops.act_grad(g, act)) <= TOL["bf16"]
+    assert nerr(Y[:, N:], dh * ops.act_fwd(g, act)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("act", ACTS_GATED)
+def test_gated_mlp_fwd_bwd_small(act):
+    """The gated MLP share through tp_gated_mlp_fwd / _bwd: 512 tokens,
+    D = 256, F = 1024, T = 4, 8 chunks, rank 1.  The backward is fed the
+    oracle's forward values rounded to bf16 (the same values on both sides)."""
+    M, D, F, T, C, r = 512, 256, 1024, 4, 8, 1
+    Ft = F // T
+    x = si.normal_f32((M, D), 1)
+    wg, wu = si.normal_f32((D, Ft), 2, 0.05), si.normal_f32((D, Ft), 5, 0.05)
+    wd = si.normal_f32((Ft, D), 3, 0.05)
+    X, WGU, WD = dev_bf16(x), dev_bf16(np.concatenate([wg, wu], axis=1)), dev_bf16(wd)
+    Xf, WGUf, WDf = f64(X), f64(WGU), f64(WD)
+    GU = torch.empty(M, 2 * Ft, dtype=torch.bfloat16, device="cuda")
+    H = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    flags = torch.full((C,), 4, dtype=torch.int32, device="cuda")
+    done = torch.zeros(T, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_GATED_MLP_FWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_gated_mlp_fwd(X, WGU, WD, H, P, T=T, rank=r, act=act, GU_t=GU, num_chunks=C,
+                         chunk_order=si.ring_chunk_order(T, C, r), chunk_ready=flags, epoch=4, range_done=done,
+                         workspace=ws)
+    sync()
+    assert tpm.poll_device_error(ws) == 0 and done.tolist() == [4] * T
+    ref = ops.gated_mlp_fwd(Xf, WGUf[:, :Ft], WGUf[:, Ft:], WDf, act, store="bf16")
+    assert nerr(GU[:, :Ft], ref["G"]) <= TOL["bf16"] and nerr(GU[:, Ft:], ref["U"]) <= TOL["bf16"]
+    assert nerr(H, ref["H"]) <= TOL["bf16"]
+    assert nerr(P, ref["P"]) <= TOL["bf16"]
+    # backward on the oracle's stored forward values
+    gb, ub, hb = (formats.round_bf16(ref[k]) for k in ("G", "U", "H"))
+    GUin, Hin = si.to_bf16(np.concatenate([gb, ub], axis=1)).cuda(), si.to_bf16(hb).cuda()
+    dY = dev_bf16(si.normal_f32((M, D), 4))
+    dWgu = torch.empty(D, 2 * Ft, dtype=torch.bfloat16, device="cuda")
+    dWd = torch.empty(Ft, D, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    wsb = tpm.alloc_workspace(_abi.OP_GATED_MLP_BWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_gated_mlp_bwd(X, WGU, WD, GUin, Hin, dY, dWgu, dWd, dX, T=T, rank=r, act=act, num_chunks=C,
+                         dy_chunk_order=si.ring_chunk_order(T, C, r), dy_ready=flags, epoch=4, workspace=wsb)
+    sync()
+    assert tpm.poll_device_error(wsb) == 0
+    rb = ops.gated_mlp_bwd(Xf, WGUf[:, :Ft], WGUf[:, Ft:], WDf, gb, ub, hb, f64(dY), act, store="bf16")
+    dGU = wsb[2048:2048 + M * 2 * Ft * 2].view(torch.bfloat16).view(M, 2 * Ft)   # [dG | dU] left in the workspace
+    assert nerr(dGU[:, :Ft], rb["dG"]) <= TOL["bf16"] and nerr(dGU[:, Ft:], rb["dU"]) <= TOL["bf16"]
+    assert nerr(dWgu[:, :Ft], rb["dW_gate"]) <= TOL["bf16"] and nerr(dWgu[:, Ft:], rb["dW_up"]) <= TOL["bf16"]
+    assert nerr(dWd, rb["dW_down"]) <= TOL["bf16"]
+    assert nerr(dX, rb["dX"]) <= TOL["bf16"]
 
 
 def test_mlp_fwd_fp8_small():
