@@ -9,6 +9,17 @@ finite magnitude is 1.75 * 2^8 = 448.
 
 Encoders round to the nearest representable value, ties to the even code,
 and (e4m3fn) saturate finite overflow to +-448 ("satfinite").
+
+MXFP8 (the "MXFP8 block scaling" recipe of "Collective GEMMs in Tensor
+Sequence Parallelism", section "Supported quantization recipes"; the format
+is the OCP Microscaling (MX) specification v1.0): blocks of 32 consecutive
+elements share one scale X = 2^(E - 127) stored as an 8-bit exponent E
+(E8M0, 255 = NaN); each element is an e4m3fn code P_i and the block holds
+the values X * P_i.  Quantising a block V: E = floor(log2 max|V_i|) - 8 + 127
+(8 being the exponent of e4m3fn's largest normal, 448 = 1.75 * 2^8), clamped
+to [0, 254] (E = 0 for an all-zero block, a choice the spec leaves free), and
+P_i = e4m3fn(V_i / X), nearest-even and saturating, since max|V_i| / X lies
+in [256, 512).
 """
 from __future__ import annotations
 
@@ -98,3 +109,44 @@ def f32_to_bf16_bits(x) -> np.ndarray:
 def round_bf16(x) -> np.ndarray:
     """float64 -> fp32 (nearest) -> bf16 (nearest even) -> float64."""
     return bf16_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32)))
+
+
+# ------------------------------------------------------------------- MX
+MX_BLOCK = 32
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """Scale value 2^(E - 127) of E8M0 codes (255, NaN, is not produced here)."""
+    e = np.asarray(codes, dtype=np.int64)
+    return np.ldexp(1.0, e - 127)
+
+
+def mx_e4m3_quantize(v) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 (e4m3 elements) of V [rows, K], K % 32 == 0, blocks along the
+    last axis.  Returns (codes uint8 [rows, K], scale exponents uint8
+    [rows, K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    rows, k = v.shape
+    assert k % MX_BLOCK == 0
+    blocks = v.reshape(rows, k // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.floor(np.log2(amax[nz])).astype(np.int64) - 8 + 127
+    # floor(log2) of a value just under a power of two can come out one high
+    # in float64 log2; fix it against the definition 2^f <= amax < 2^(f+1)
+    f = e - 127 + 8
+    hi = nz & (np.ldexp(1.0, f) > amax)
+    e[hi] -= 1
+    e = np.clip(e, 0, 254)
+    scale = np.ldexp(1.0, e - 127)
+    codes = e4m3_encode(blocks / scale[:, :, None]).reshape(rows, k)
+    return codes, e.astype(np.uint8)
+
+
+def mx_e4m3_decode(codes, scales) -> np.ndarray:
+    """Values X * P of MXFP8 codes [rows, K] with scale exponents [rows, K/32]."""
+    c = e4m3_to_f64(codes)
+    rows, k = c.shape
+    x = e8m0_to_f64(scales)
+    return (c.reshape(rows, k // MX_BLOCK, MX_BLOCK) * x[:, :, None]).reshape(rows, k)

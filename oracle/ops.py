@@ -232,6 +232,23 @@ def tp_mlp_fwd_fp8(xq, sx, wq_up, s_up, wq_down, s_down, act=ACT_GELU_ERF):
 
 
 # ------------------------------------------------- partial_reduce_seqshard
+def tp_mlp_fwd_mx(xq, xs, wuq_t, wus_t, wdq_t, wds_t, act=ACT_GELU_ERF):
+    """MXFP8 block-scaling variant ([CG] "Supported quantization recipes",
+    MXFP8 block scaling; format in oracle.formats) with the rounding points
+    of the GPU path.  Every operand is MXFP8 with its blocks along the
+    contraction dimension, so the weights come K-major (transposed):
+        Z  = dec(Xq, Xs) . dec(Wq_up^T, Ws_up^T)^T          [M, F/T]
+        H  = act(Z)
+        Hq, Hs = MXFP8(H)   (blocks of 32 along F/T, no bf16 step)
+        P  = dec(Hq, Hs) . dec(Wq_down^T, Ws_down^T)^T      [M, D]
+    Inputs: e4m3 codes and E8M0 scale exponents (row-major [rows, K/32])."""
+    z = gemm(formats.mx_e4m3_decode(xq, xs), formats.mx_e4m3_decode(wuq_t, wus_t).T)
+    h = act_fwd(z, act)
+    hq, hs = formats.mx_e4m3_quantize(h)
+    p = gemm(formats.mx_e4m3_decode(hq, hs), formats.mx_e4m3_decode(wdq_t, wds_t).T)
+    return dict(Z=z, H=h, Hq_codes=hq, Hq_scales=hs, P=p)
+
+
 def partial_reduce_seqshard(partials, rank: int):
     """Local arithmetic of the reduce-scatter that follows a row-parallel GEMM
     ([CG] "Collective GEMMs (CGEMM)", GEMM + reduce-scatter; [TSP] "Derive

@@ -75,6 +75,25 @@ def to_e4m3_current(x: np.ndarray):
     return q.view(torch.uint8), scale
 
 
+def to_mxfp8(x: np.ndarray):
+    """MXFP8 inputs (OCP Microscaling: 32-element blocks along the last axis,
+    one power-of-two scale per block, e4m3fn elements) for a [rows, K] fp32
+    array, K % 32 == 0.  Returns (codes uint8 torch [rows, K], scale
+    exponents uint8 torch [rows, K/32], row-major).  The block exponent is
+    floor(log2 amax) from torch.frexp, minus 8, biased by 127 and clamped to
+    [0, 254] (0 for an all-zero block); elements are cast with PyTorch's
+    float8_e4m3fn conversion after clamping to +-448."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    rows, k = t.shape
+    b = t.reshape(rows, k // 32, 32)
+    amax = b.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                        # amax = m * 2^ex, m in [0.5, 1)
+    e = torch.where(amax > 0, ex - 1 - 8 + 127, torch.zeros_like(ex)).clamp(0, 254)
+    scaled = torch.ldexp(b, (127 - e).unsqueeze(2).to(torch.float32))
+    codes = scaled.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows, k)
+    return codes.contiguous(), e.to(torch.uint8).contiguous()
+
+
 def to_e4m3_exact(x: np.ndarray) -> torch.Tensor:
     """Cast values that are exactly representable in e4m3fn (e.g. small ints)."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)

@@ -107,6 +107,89 @@ def test_silu_closed_forms():
     assert np.allclose(ops.silu_grad(np.array([40.0, -40.0])), [1.0, 0.0], atol=1e-12)
 
 
+# ------------------------------------------------------------------ MXFP8
+def test_mx_quantizer_against_definition_brute_force():
+    # OCP MX: per 32-block a power-of-two scale X with max|V| / X in [256, 512)
+    # (e4m3's largest normal exponent is 8), each element the nearest e4m3
+    # value of V / X (ties to the even code), saturated at 448
+    g = np.random.default_rng(81)
+    v = g.standard_normal((6, 128)) * np.exp(g.uniform(-12, 12, size=(6, 1)))
+    v[2, 32:64] = 0.0                                   # an all-zero block
+    v[3, :32] = g.choice([-1.0, 1.0], 32) * 2.0 ** 5    # amax exactly a power of two
+    v[4, 64:96] *= 1e-38                                # tiny block: scale exponent clamps at 0
+    codes, e = formats.mx_e4m3_quantize(v)
+    x = formats.e8m0_to_f64(e)
+    grid = formats.E4M3_TABLE[:0x7F]                    # non-negative finite e4m3 values
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[r, 32 * b:32 * (b + 1)]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                assert e[r, b] == 0
+            elif e[r, b] > 0:
+                assert 256 <= amax / x[r, b] < 512
+            for i, val in enumerate(blk):
+                t = abs(val) / x[r, b]
+                d = np.abs(grid - t)
+                best = np.flatnonzero(d == d.min())
+                want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+                if t >= 448:
+                    want = 0x7E
+                got = int(codes[r, 32 * b + i]) & 0x7F
+                assert got == want, (r, b, i)
+    assert e[3, 0] == 5 - 8 + 127
+    dec = formats.mx_e4m3_decode(codes, e)
+    assert np.array_equal(dec[2, 32:64], np.zeros(32))
+
+
+def test_mx_roundtrip_and_relation_to_scaling():
+    g = np.random.default_rng(82)
+    # values already on an MX grid come back unchanged
+    c0 = g.integers(0, 0x7F, size=(4, 64)).astype(np.uint8) | (g.integers(0, 2, size=(4, 64)) << 7).astype(np.uint8)
+    c0[:, ::32] = 0x78                                    # 256 (2^8): the block maximum sets the scale
+    e0 = g.integers(100, 150, size=(4, 2)).astype(np.uint8)
+    v = formats.mx_e4m3_decode(c0, e0)
+    c, e = formats.mx_e4m3_quantize(v)
+    assert np.array_equal(e, e0) and np.array_equal(formats.mx_e4m3_decode(c, e), v)
+    # scaling a block by a power of two moves only its exponent
+    w = g.standard_normal((3, 96))
+    c1, e1 = formats.mx_e4m3_quantize(w)
+    c2, e2 = formats.mx_e4m3_quantize(w * 2.0 ** 7)
+    assert np.array_equal(c1, c2) and np.array_equal(e2.astype(int), e1.astype(int) + 7)
+
+
+def test_mx_input_quantizer_agrees_with_oracle():
+    # the seeded-input MXFP8 cast (torch frexp / ldexp / float8 cast) and the
+    # oracle's quantiser are written independently and must agree
+    x = si.normal_f32((96, 512), 83) * np.float32(3.0)
+    x[5, 64:96] = 0
+    c, e = si.to_mxfp8(x)
+    c2, e2 = formats.mx_e4m3_quantize(x.astype(np.float64))
+    assert np.array_equal(c.numpy(), c2) and np.array_equal(e.numpy(), e2)
+
+
+def test_mx_mlp_forward_composes_the_steps():
+    g = np.random.default_rng(84)
+    M, D, Ft = 8, 64, 96
+    xq, xs = formats.mx_e4m3_quantize(g.standard_normal((M, D)))
+    wu_q, wu_s = formats.mx_e4m3_quantize(g.standard_normal((Ft, D)) * 0.1)
+    wd_q, wd_s = formats.mx_e4m3_quantize(g.standard_normal((D, Ft)) * 0.1)
+    r = ops.tp_mlp_fwd_mx(xq, xs, wu_q, wu_s, wd_q, wd_s, ops.ACT_GELU_ERF)
+    z = formats.mx_e4m3_decode(xq, xs) @ formats.mx_e4m3_decode(wu_q, wu_s).T
+    assert np.allclose(r["Z"], z, rtol=0, atol=1e-12)
+    assert np.array_equal(r["Hq_codes"], formats.mx_e4m3_quantize(ops.gelu_erf(z))[0])
+    h_dec = formats.mx_e4m3_decode(r["Hq_codes"], r["Hq_scales"])
+    # within e4m3's normal range (2^-6 .. 448 times the block scale) the
+    # rounding error is at most half a step, 2^-4 of the value; above 448
+    # the element saturates
+    X = formats.e8m0_to_f64(np.repeat(r["Hq_scales"], 32, axis=1))
+    t = np.abs(r["H"]) / X
+    normal = (t >= 2.0 ** -6) & (t <= 448)
+    assert np.all(np.abs(h_dec - r["H"])[normal] <= 2.0 ** -4 * np.abs(r["H"])[normal])
+    assert np.all(np.abs(h_dec)[t > 448] == 448 * X[t > 448])
+    assert np.allclose(r["P"], h_dec @ formats.mx_e4m3_decode(wd_q, wd_s).T, rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------- gated MLP
 def _gated_brute(x, wg, wu, wd, act):
     """Pure-Python gated MLP share: correctly rounded sums (math.fsum) and
