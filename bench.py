@@ -432,6 +432,44 @@ def run_sweep(torch, tpm, si):
             torch.cuda.empty_cache()
 
 
+def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
+    """The fp8 configuration's MLP forward under MXFP8 block scaling (inputs
+    and weights MXFP8 along their contraction axes, H requantised to MXFP8 in
+    GEMM1's epilogue), chunk-gated with the flags already set; events."""
+    Ft = F // T
+    dev = "cuda"
+    def mx(x, k):
+        c, e = si.to_mxfp8(x)
+        return c.to(dev), tpm.mx_swizzle_scales(e.to(dev), k)
+    X, Xs = mx(si.normal_f32((M, D), 1), D)
+    WU, WUs = mx(si.normal_f32((Ft, D), 2, 0.02), D)
+    WD, WDs = mx(si.normal_f32((D, Ft), 3, 0.02), Ft)
+    H = torch.empty(M, Ft, dtype=torch.uint8, device=dev)
+    Hs = torch.zeros(tpm.mx_scales_bytes(M, Ft), dtype=torch.uint8, device=dev)
+    P = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
+    ws = tpm.alloc_workspace(tpm.OP_MX_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
+    order = si.ring_chunk_order(T, C, 0)
+    call = lambda: tpm.tp_mlp_fwd_mx(X, Xs, WU, WUs, WD, WDs, H, Hs, P, T=T, rank=0, act=tpm.ACT_GELU_ERF,
+                                     num_chunks=C, chunk_order=order, chunk_ready=flags, epoch=1, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    assert tpm.poll_device_error(ws) == 0
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    tf = 2.0 * M * Ft * D * 2 / (ms * 1e-3) / 1e12
+    return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="mxfp8 (e4m3, 32-element E8M0 blocks)", ms=ms, TFLOPS=tf,
+                frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
+
+
 def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10):
     """The worked example's gated MLP share (X [8192, 4096], F = 16384, T = 4:
     gate and up shards [4096, 4096] each, contraction shard [4096, 4096]),
@@ -603,6 +641,8 @@ def main():
         extra["mlp_fwd_c3_bf16"] = bench_mlp_fwd(torch, tpm, si, 8192, 8192, 28672, 8, 8, False)
         torch.cuda.empty_cache()
         extra["mlp_fwd_c4_fp8"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
+        torch.cuda.empty_cache()
+        extra["mlp_fwd_c4_mxfp8"] = bench_mlp_fwd_mx(torch, tpm, si)
         torch.cuda.empty_cache()
         extra["gated_mlp_worked_example"] = bench_gated_mlp(torch, tpm, si)
         rec["extra"] = extra

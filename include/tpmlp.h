@@ -73,7 +73,7 @@ typedef enum {
 /* Operation ids for tpm_workspace_bytes(). */
 typedef enum {
   TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2,
-  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4
+  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5
 } tpm_op;
 
 #define TPM_MAX_CHUNKS 256
@@ -247,6 +247,61 @@ int tp_gated_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
                      void* dW_gu_t, void* dW_down_t, void* dX_t, int dw_dtype,
                      int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MXFP8 block scaling ("Collective GEMMs in Tensor Sequence Parallelism",
+ * section "Supported quantization recipes", MXFP8; the format is the OCP
+ * Microscaling v1.0 one): an operand stored K-major ([rows, K], K contiguous)
+ * as e4m3fn codes, each 32-element block of a row along K with one E8M0
+ * scale 2^(E - 127).  The scales are passed in the layout gfx950's scaled
+ * MFMA reads them: rows in groups of 32, each group one 128-byte record per
+ * 128 elements of K holding 4 bytes (blocks 4s .. 4s+3) for each of its 32
+ * rows.  tpm_mx_scales_bytes(rows, K) is the size of such an array (rows
+ * padded to a multiple of 32); tpm_mx_swizzle_scales converts row-major
+ * [rows, ld >= K/32] E8M0 bytes into it (padding rows get E = 0).  K must
+ * be a multiple of 128.
+ */
+size_t tpm_mx_scales_bytes(int64_t rows, int64_t k);
+int tpm_mx_swizzle_scales(int64_t rows, int64_t k, const uint8_t* src, int64_t ld, uint8_t* dst, void* stream);
+
+/*
+ * seq_chunk_gemm_mx -- seq_chunk_gemm with MXFP8 operands: A [M, lda >= K]
+ * and B stored [N, ldb >= K] (op(B) = B^T), both e4m3 codes with their
+ * block scales (layout above); fp32 accumulation on the scaled MFMA.
+ * y_dtype BF16 or F32: Y = act(A . B^T); y_dtype FP8_E4M3: Y is written as
+ * MXFP8 (codes [M, ldy >= N], y_scales in the layout above for K = N, blocks
+ * of 32 output columns; N % 128 == 0), each block's scale exponent the
+ * exponent field of its fp32 amax minus 8 (0 for a zero block) and each code
+ * e4m3(v * 2^(127 - E)), nearest-even, saturating.  aux (optional, bf16
+ * [M, ldaux >= N]) receives the pre-activation.  Chunks as seq_chunk_gemm.
+ */
+int seq_chunk_gemm_mx(int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda, const uint8_t* a_scales,
+                      const void* B, int64_t ldb, const uint8_t* b_scales,
+                      void* Y, int64_t ldy, int y_dtype, uint8_t* y_scales,
+                      int act, void* aux, int64_t ldaux,
+                      int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_fwd_mx -- tp_mlp_fwd under MXFP8 block scaling: X [M, D] codes with
+ * x_scales; W_up,t stored K-major [F/T, D] with w_up_scales; W_down,t stored
+ * K-major [D, F/T] with w_down_scales.  GEMM1's epilogue writes H straight
+ * to MXFP8 (H_t codes [M, F/T], h_scales of tpm_mx_scales_bytes(M, F/T)
+ * bytes) from its fp32 result: the blocks are local, so there is no
+ * tensor-wide amax and no separate quantisation pass.  Z_t (bf16, optional)
+ * receives the pre-activation; P_t [M, D] bf16.  D and F/T multiples of 128.
+ * Chunks, orders, flags and range_done as in tp_mlp_fwd.  workspace >=
+ * tpm_workspace_bytes(TPM_OP_MX_MLP_FWD, M, D, F, T, ...) when flags are
+ * given (else may be NULL).
+ */
+int tp_mlp_fwd_mx(int64_t M, int64_t D, int64_t F, int T, int rank,
+                  const void* X, const uint8_t* x_scales, const void* W_up_t, const uint8_t* w_up_scales,
+                  const void* W_down_t, const uint8_t* w_down_scales, int act,
+                  void* Z_t, void* H_t, uint8_t* h_scales, void* P_t,
+                  int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                  const int32_t* range_order, uint32_t* range_done,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
  * TPM_OP_MLP_BWD and the gated forms pass (M, N = D, K = F, T); for

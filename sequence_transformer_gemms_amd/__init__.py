@@ -9,6 +9,8 @@ Arguments are marshalled to the C ABI; nothing is computed here.
     tp_mlp_bwd              dZ, dW_down,t, dW_up,t, dX_t (partial)
     tp_gated_mlp_fwd        G, U = X [W_gate,t | W_up,t]; H = act(G) * U; P = H W_down,t
     tp_gated_mlp_bwd        [dG | dU], dW_down,t, [dW_gate,t | dW_up,t], dX_t (partial)
+    seq_chunk_gemm_mx       the local GEMM with MXFP8 operands (and optionally output)
+    tp_mlp_fwd_mx           the MLP forward under MXFP8 block scaling
     partial_reduce_seqshard sum of T partials over this rank's token slice
 """
 from __future__ import annotations
@@ -20,10 +22,11 @@ import torch
 from . import _abi
 from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF16, EPI_DACT,  # noqa: F401
                    EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD,
-                   OP_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+                   OP_MLP_FWD, OP_MX_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
 __all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+           "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "mx_scales_bytes", "mx_swizzle_scales",
            "partial_reduce_seqshard",
            "workspace_bytes", "alloc_workspace", "signal_chunk", "write_chunks", "poll_device_error",
            "set_wait_limit", "dtype_code", "masked_streams", "TpmError", "lib"]
@@ -159,6 +162,51 @@ def tp_gated_mlp_bwd(X, W_gu_t, W_down_t, GU_t, H_t, dY, dW_gu_t, dW_down_t, dX_
                               num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch,
                               _ptr(workspace), workspace.numel() if workspace is not None else 0,
                               _stream(stream))
+    return check(rc)
+
+
+def mx_scales_bytes(rows: int, k: int) -> int:
+    return int(lib.tpm_mx_scales_bytes(rows, k))
+
+
+def mx_swizzle_scales(scales, k: int, out=None, stream=None):
+    """Row-major E8M0 scales [rows, K/32] (uint8, device) -> a new (or the
+    given) uint8 device tensor in the scaled-MFMA layout."""
+    rows = scales.shape[0]
+    if out is None:
+        out = torch.empty(max(mx_scales_bytes(rows, k), 1), dtype=torch.uint8, device=scales.device)
+    check(lib.tpm_mx_swizzle_scales(rows, k, _ptr(scales), _ld(scales), _ptr(out), _stream(stream)))
+    return out
+
+
+def seq_chunk_gemm_mx(A, a_scales, B, b_scales, Y, *, y_scales=None, act=ACT_NONE, aux=None, num_chunks=1,
+                      chunk_order=None, chunk_ready=None, epoch=0, workspace=None, stream=None):
+    """Y = act(A . B^T) with MXFP8 operands: A [M, K], B stored [N, K] (codes,
+    uint8) and their swizzled scales; Y bf16 / fp32, or uint8 codes with
+    y_scales (MXFP8 output)."""
+    M, K = A.shape
+    N = B.shape[0]
+    ydt = FP8_E4M3 if Y.dtype == torch.uint8 else dtype_code(Y.dtype)
+    rc = lib.seq_chunk_gemm_mx(M, N, K, _ptr(A), _ld(A), _ptr(a_scales), _ptr(B), _ld(B), _ptr(b_scales),
+                               _ptr(Y), _ld(Y), ydt, _ptr(y_scales), act, _ptr(aux), _ld(aux) if aux is not None else 0,
+                               num_chunks, _abi.int_array(chunk_order), _ptr(chunk_ready), epoch,
+                               _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+    return check(rc)
+
+
+def tp_mlp_fwd_mx(X, x_scales, W_up_t, w_up_scales, W_down_t, w_down_scales, H_t, h_scales, P_t, *, T, rank,
+                  act=ACT_GELU_ERF, Z_t=None, num_chunks=1, chunk_order=None, chunk_ready=None, epoch=0,
+                  range_order=None, range_done=None, workspace=None, stream=None):
+    """MXFP8 forward: X [M,D] codes; W_up_t [F/T, D] and W_down_t [D, F/T]
+    codes stored K-major; all scales swizzled; H_t [M, F/T] uint8 codes with
+    h_scales; P_t [M, D] bf16."""
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_mlp_fwd_mx(M, D, Ft * T, T, rank, _ptr(X), _ptr(x_scales), _ptr(W_up_t), _ptr(w_up_scales),
+                           _ptr(W_down_t), _ptr(w_down_scales), act, _ptr(Z_t), _ptr(H_t), _ptr(h_scales), _ptr(P_t),
+                           num_chunks, _abi.int_array(chunk_order), _ptr(chunk_ready), epoch,
+                           _abi.int_array(range_order), _ptr(range_done),
+                           _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     return check(rc)
 
 

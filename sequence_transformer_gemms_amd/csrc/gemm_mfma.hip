@@ -193,14 +193,19 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int rb, int kk
 }
 
 // One 32 (rows) x 64 (K) fp8 fragment for a 32x32x64 MFMA operand (K-major
-// tile only): lane l holds row rb + l%32, K bytes 64*kk + 32*(l/32) .. +31 of
-// substep kk (0, 1).
+// tile only): lane l holds row rb + l%32 and, of substep kk's 64 K bytes
+// (64*kk ..), bytes 16*h .. +15 in its first 16 bytes and 32 + 16*h .. +15
+// in its last 16, h = l/32.  That is the order the matrix core takes K in
+// (measured with block scales: bytes 0-15 of both lane halves form the
+// first 32-element block, scaled by lane l%32's scale, bytes 16-31 the
+// second, scaled by lane 32 + l%32's), so the MX blocks of 32 consecutive
+// K elements in memory are the MFMA's blocks.
 __device__ __forceinline__ i32x8 read_frag_fp8(const char* lds_tile, int rb, int kk) {
   const int lane = threadIdx.x & 63;
   const uint32_t r = (uint32_t)(rb + (lane & 31));
-  const uint32_t c0 = (uint32_t)(4 * kk + 2 * (lane >> 5));
+  const uint32_t c0 = (uint32_t)(4 * kk + (lane >> 5));
   const i32x4 lo = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0)));
-  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0 + 1u)));
+  const i32x4 hi = *(const lds_i32x4*)((lds_void*)(lds_tile + kmaj_offset(r, c0 + 2u)));
   i32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return v;
 }
@@ -359,9 +364,10 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
   }
 }
 
-template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false>
+template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
   static_assert(!GATED || (!FP8 && !BKM && NW == 8), "gated: bf16, MN-major B, 8 waves (two N fragments)");
+  static_assert(!MX || (FP8 && AK && BKM), "MXFP8: fp8 operands stored K-major");
   using LY = Layout<NW>;
   constexpr int THREADS = LY::THREADS, LOADS = LY::LOADS, NF = LY::NF;
   constexpr int ESZ = FP8 ? 1 : 2;
@@ -376,6 +382,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
+  // MXFP8 block scales (reads past the end of a scale array return zeros,
+  // which only happens for rows or K steps whose operand data are zeros too)
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(MX ? (const void*)p.a_mx : p.A, MX ? p.a_mx_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(MX ? (const void*)p.b_mx : p.B, MX ? p.b_mx_bytes : 0u);
   const int64_t lda_b = p.lda * ESZ, ldb_b = p.ldb * ESZ;
   const int nk = (p.K + KSTEP - 1) / KSTEP;
   float scale = 1.f;
@@ -461,8 +471,39 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     constexpr int P0 = TOTAL_LOADS / 3, P1 = (TOTAL_LOADS - P0) / 2, P2 = TOTAL_LOADS - P0 - P1;
     // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
     // loads L0 .. L0+NL-1 of K step kl spread between the row groups.
+    // MXFP8: the scale dwords of K step s for this lane's fragments (4 rows
+    // of A, NF of B; bytes = the step's four 32-element blocks), and the same
+    // shifted right by 8 bytes for lanes 32-63, which hold the second 32 K
+    // elements of each 64-element MFMA: byte 0 then scales substep 0 and
+    // byte 2 substep 1 for every lane (op_sel 0 / 2).
+    int sa_next[4] = {0, 0, 0, 0}, sb_next[NF] = {}, sa_cur[4] = {0, 0, 0, 0}, sb_cur[NF] = {};
+    auto load_scales = [&](int s) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sa_next[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+              rsa, mx_scale_offset((uint32_t)(tl.m0 + wm + 32 * i + (lane & 31)), 4u * (uint32_t)s, (uint32_t)p.mx_steps),
+              0, 0);
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+          sb_next[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+              rsb, mx_scale_offset((uint32_t)(tl.n0 + wn + 32 * j + (lane & 31)), 4u * (uint32_t)s, (uint32_t)p.mx_steps),
+              0, 0);
+      }
+    };
+    auto take_scales = [&]() {
+      if constexpr (MX) {
+        const uint32_t h8 = 8u * (uint32_t)(lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa_cur[i] = (int)((uint32_t)sa_next[i] >> h8);
+#pragma unroll
+        for (int j = 0; j < NF; ++j) sb_cur[j] = (int)((uint32_t)sb_next[j] >> h8);
+      }
+    };
     auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl,
-                         auto r0c, auto nrc, const char* __restrict__ rst, int rkk, Frag (&rfa)[4], Frag (&rfb)[NF]) {
+                         auto r0c, auto nrc, const char* __restrict__ rst, int rkk, Frag (&rfa)[4], Frag (&rfb)[NF],
+                         auto opc) {
+      constexpr int OPS = decltype(opc)::value;  // MX: byte of the scale dwords (0: substep 0, 2: substep 1)
       constexpr int I0 = decltype(i0c)::value, NI = decltype(nic)::value;
       constexpr int L0 = decltype(l0c)::value, NL = decltype(nlc)::value;
       constexpr int R0 = decltype(r0c)::value, NR = decltype(nrc)::value;
@@ -472,7 +513,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
         static_for<NF>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           constexpr int m = ii * NF + j;
-          if constexpr (FP8)
+          if constexpr (MX)
+            acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0,
+                                                                              OPS, sb_cur[j], OPS, sa_cur[I0 + ii]);
+          else if constexpr (FP8)
             acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0,
                                                                               0, 0, 0, 0);
           else
@@ -511,6 +555,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
     // are read during the last phase, and (b) frees step kt's slot, which the
     // loads of step kt+2 start refilling in that same phase.
     Frag fa[2][4], fb[2][NF];
+    load_scales(kbeg);
     static_for<TOTAL_LOADS>([&](auto lc) { load_one(decltype(lc)::value, 0); });
     step_barrier();
     read_set(slot(0), 0, fa[0], fb[0]);
@@ -521,19 +566,29 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
       const char* nx = slot(kt + 1);
       const int kn = kt + 1;
       if constexpr (FP8) {
-        // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0
-        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD / 2>{}, cur, 1, fa[1], fb[1]);
+        // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0.
+        // MX: the scales of step kt+1 load during phase 0 and land by the
+        // barrier (which waits for every load of this thread).
+        take_scales();
+        load_scales(kbeg + kn);
+        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD / 2>{}, cur, 1, fa[1], fb[1],
+                  IC<0>{});
         mfma_rows(IC<2>{}, IC<2>{}, IC<P0 + P1>{}, IC<P2>{}, fa[0], fb[0], kn, IC<NRD / 2>{}, IC<NRD - NRD / 2>{}, cur, 1,
-                  fa[1], fb[1]);
-        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn, IC<0>{}, IC<0>{}, cur, 0, fa[0], fb[0]);
+                  fa[1], fb[1], IC<0>{});
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn, IC<0>{}, IC<0>{}, cur, 0, fa[0], fb[0], IC<2>{});
         step_barrier();
-        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0]);
+        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0],
+                  IC<2>{});
       } else {
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 1, fa[1], fb[1]);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn, IC<0>{}, IC<NRD>{}, cur, 2, fa[0], fb[0]);
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 3, fa[1], fb[1]);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 1, fa[1], fb[1],
+                  IC<0>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn, IC<0>{}, IC<NRD>{}, cur, 2, fa[0], fb[0],
+                  IC<0>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 3, fa[1], fb[1],
+                  IC<0>{});
         step_barrier();
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0]);
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0],
+                  IC<0>{});
       }
     }
     __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
@@ -582,6 +637,46 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
             const float u[8] = {u0[0] * scale, u0[1] * scale, u0[2] * scale, u0[3] * scale,
                                 u1[0] * scale, u1[1] * scale, u1[2] * scale, u1[3] * scale};
             epi_gated_oct(p, g, u, row, col);
+          }
+        }
+      } else if (FP8 && p.y_mx) {
+        // MXFP8 output: each 32-column block of a row (4 lanes) shares one
+        // scale 2^(E-127), E = exponent field of the block's amax - 8 (0 for
+        // a zero block); codes are e4m3(v * 2^(127-E)), nearest-even,
+        // saturating.  The four lanes of a block always share their row and
+        // validity (N % 32 == 0), so the shuffles stay inside live groups.
+#pragma unroll 1
+        for (int it = 0; it < EPI_ROWS / 8; ++it) {
+          const int rl = it * 8 + (lane >> 3);
+          const int cl = (lane & 7) * 8;
+          const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
+          const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+          const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+          const int col = tl.n0 + wn + EPI_COLS * cp + cl;
+          const bool ok = row < tl.m_end && col < p.N;
+          float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                        v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+          if (ok && p.aux) store_oct(p.aux, p.ldaux, false, row, col, v);  // pre-activation, bf16
+          float m = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] = act_fwd(v[e], p.act);
+            m = fmaxf(m, fabsf(v[e]));
+          }
+          m = fmaxf(m, __shfl_xor(m, 1, 64));
+          m = fmaxf(m, __shfl_xor(m, 2, 64));
+          if (ok) {
+            const int E = max((int)((__float_as_uint(m) >> 23) & 0xFFu) - 8, 0);
+            const float inv = __uint_as_float((uint32_t)(254 - E) << 23);   // 2^(127 - E)
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lo |= (uint32_t)f32_to_e4m3_rne_sat(v[e] * inv) << (8 * e);
+              hi |= (uint32_t)f32_to_e4m3_rne_sat(v[4 + e] * inv) << (8 * e);
+            }
+            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+            if ((lane & 3) == 0)
+              p.y_mx[mx_scale_offset((uint32_t)row, (uint32_t)col >> 5, (uint32_t)p.y_mx_steps)] = (uint8_t)E;
           }
         }
       } else {
@@ -696,7 +791,8 @@ hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
 
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (!a_kmajor || !b_kmajor) return hipErrorInvalidValue;  // rejected on the host first
-  gemm_kernel<true, true, true, kWaves8><<<grid, kThreads8, 0, s>>>(p);
+  if (p.a_mx) gemm_kernel<true, true, true, kWaves8, false, true><<<grid, kThreads8, 0, s>>>(p);
+  else gemm_kernel<true, true, true, kWaves8><<<grid, kThreads8, 0, s>>>(p);
   return finalize_if_split(p, s);
 }
 

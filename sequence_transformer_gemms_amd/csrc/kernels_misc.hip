@@ -149,6 +149,18 @@ __global__ void __launch_bounds__(kWriterThreads) write_chunks(const WriterParam
   }
 }
 
+// MXFP8 scales: row-major [rows, kblocks] E8M0 bytes -> the layout the
+// scaled MFMA reads (mx_scale_offset); rows padded to a multiple of 32 get
+// exponent 0.  One thread per destination byte.
+__global__ void __launch_bounds__(256) mx_swizzle(const uint8_t* __restrict__ src, int64_t ld, int rows, int kblocks,
+                                                  int64_t total, uint8_t* __restrict__ dst) {
+  const int ksteps = kblocks / 4;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(t / kblocks), kb = (int)(t - (int64_t)row * kblocks);
+    dst[mx_scale_offset((uint32_t)row, (uint32_t)kb, (uint32_t)ksteps)] = row < rows ? src[(int64_t)row * ld + kb] : 0;
+  }
+}
+
 __global__ void ctrl_init(uint32_t* w, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
 }
@@ -235,6 +247,12 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
                              int64_t ldq, float* s_out, hipStream_t s) {
   const int64_t work = M * (N / 8);
   quant_e4m3<<<grid_for(work, 256), 256, 0, s>>>(h, M, N / 8, ldh, amax, q, ldq, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_swizzle(const uint8_t* src, int64_t ld, int rows, int kblocks, uint8_t* dst, hipStream_t s) {
+  const int64_t total = (int64_t)((rows + 31) / 32) * 32 * kblocks;
+  mx_swizzle<<<grid_for(total, 256), 256, 0, s>>>(src, ld, rows, kblocks, total, dst);
   return hipGetLastError();
 }
 

@@ -34,12 +34,30 @@ struct GemmParams {
   int splits;                // K-range splits (1: none); > 1 needs `partial`
   int ksteps_per_split;      // K steps (of 32 bf16 / 64 fp8) per split
   float* partial;            // device fp32 [splits][M][N] partial sums
+  // MXFP8 (fp8 kernel only): E8M0 block scales of A and B in the MFMA
+  // layout (mx_scale_offset), K / 128 records per 32-row group; y_mx: Y is
+  // written as MXFP8 codes with its scales there (N / 128 records per group)
+  const uint8_t* a_mx;
+  const uint8_t* b_mx;
+  uint32_t a_mx_bytes, b_mx_bytes;
+  int mx_steps;
+  uint8_t* y_mx;
+  int y_mx_steps;
   int gu_off;                // gated epilogues: column offset of the up half in B / aux / Y (= N)
   int bn_out;                // output columns per tile (256; 128 for EPI_GATED)
   int16_t order[kMaxGroups];
 };
 
 enum { EPI_FWD = 0, EPI_DACT = 1, EPI_GATED = 2, EPI_DGATED = 3 };
+
+// Byte offset of the E8M0 scale of (row, 32-element block kb) of an MXFP8
+// operand in the layout the scaled MFMA reads: rows in groups of 32, each
+// group a run of 128-byte records, one per K step of 128 elements, holding
+// 4 bytes (blocks 4s .. 4s+3) for each of its 32 rows.  One fragment's 32
+// lanes then read one 128-byte line per K step.
+__host__ __device__ inline uint32_t mx_scale_offset(uint32_t row, uint32_t kb, uint32_t ksteps) {
+  return (((row >> 5) * ksteps + (kb >> 2)) * 32u + (row & 31u)) * 4u + (kb & 3u);
+}
 
 // Side-stream chunk writer: chunks order[0..n-1] of chunk_bytes each, copied
 // src -> dst when copy[c] != 0, then ready[c] = epoch.
@@ -58,6 +76,7 @@ struct WriterParams {
 // kernels' launchers (return hipError_t of the launch)
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
+hipError_t launch_mx_swizzle(const uint8_t* src, int64_t ld, int rows, int kblocks, uint8_t* dst, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
 hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s);
 hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, int64_t pstride,

@@ -25,3 +25,39 @@ def nerr(gpu, ref) -> float:
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def assert_mx_close(codes, e, h, delta, frac=1e-2):
+    """An MXFP8 tensor produced on the GPU from fp32 values against the
+    exact values h (float64), where delta bounds the error of the GPU's fp32
+    evaluation of each value (accumulation and activation).  MX quantisation
+    is monotone, so each block exponent must be that of some amax within
+    delta of the exact block amax, and each code that of some value within
+    delta of h at the GPU's block scale; and at most a fraction `frac` of
+    the blocks / codes may differ from the quantisation of h itself."""
+    e_ref = formats.mx_e4m3_quantize(h)[1]
+    rows, k = h.shape
+    hb = np.abs(h).reshape(rows, k // 32, 32)
+    db = np.asarray(delta).reshape(rows, k // 32, 32)
+    amax_lo = np.max(np.maximum(hb - db, 0), axis=2)
+    amax_hi = np.max(hb + db, axis=2)
+
+    def exp_of(a):
+        out = np.zeros(a.shape, dtype=np.int64)
+        nz = a > 0
+        f = np.floor(np.log2(a[nz])).astype(np.int64)
+        f -= (np.ldexp(1.0, f) > a[nz]).astype(np.int64)
+        out[nz] = np.clip(f - 8 + 127, 0, 254)
+        return out
+
+    eg = e.astype(np.int64)
+    assert np.all((eg >= exp_of(amax_lo)) & (eg <= exp_of(amax_hi)))
+    assert np.mean(eg != e_ref) < frac
+    X = formats.e8m0_to_f64(np.repeat(e, 32, axis=1))
+    lo = formats.e4m3_to_f64(formats.e4m3_encode((h - delta) / X))
+    hi = formats.e4m3_to_f64(formats.e4m3_encode((h + delta) / X))
+    got = formats.e4m3_to_f64(codes)
+    assert np.all((got >= lo) & (got <= hi))
+    same = np.repeat(e == e_ref, 32, axis=1)
+    ref_codes = formats.e4m3_encode(h / X)
+    assert np.mean(same & (codes != ref_codes)) < frac

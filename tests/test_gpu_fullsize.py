@@ -14,7 +14,7 @@ import sequence_transformer_gemms_amd as tpm
 from sequence_transformer_gemms_amd import _abi
 import synthetic_inputs as si
 from oracle import formats, ops
-from tests._util import TOL, f64, nerr
+from tests._util import TOL, assert_mx_close, f64, nerr
 
 pytestmark = pytest.mark.gpu
 
@@ -398,3 +398,46 @@ def test_gated_mlp_worked_example_full_size_sampled():
         ref = Xf.T @ vb
         tol = B * (1 + np.abs(ref)) + np.abs(Xf).T @ (vamb + amb_in)
         assert np.all(np.abs(host64(got) - ref) <= tol)
+
+
+# ------------------------------------------------------------ MXFP8 (C4 shape)
+def test_c4_mxfp8_mlp_forward_full_size_sampled():
+    """The fp8 configuration's shapes (8192 tokens, D = 16384, F = 53248,
+    T = 8, 16 chunks in ring order) under MXFP8 block scaling: every operand
+    in 32-element blocks along its contraction axis, H requantised to MXFP8
+    in GEMM1's epilogue.  MX blocks are local to a row, so the oracle
+    computes sampled token rows of Z, H (codes and block exponents) and P
+    exactly; H is compared under the fp32-evaluation bound of its values."""
+    M, D, F, T, C = 8192, 16384, 53248, 8, 16
+    Ft = F // T
+    xc, xe = (t.numpy() for t in si.to_mxfp8(si.normal_f32((M, D), 1)))
+    uc, ue = (t.numpy() for t in si.to_mxfp8(si.normal_f32((Ft, D), 2, 0.02)))   # W_up,t K-major [Ft, D]
+    dc, de = (t.numpy() for t in si.to_mxfp8(si.normal_f32((D, Ft), 3, 0.02)))   # W_down,t K-major [D, Ft]
+    dev = lambda c, e, k: (torch.from_numpy(c).cuda(), tpm.mx_swizzle_scales(torch.from_numpy(e).cuda(), k))
+    X, Xs = dev(xc, xe, D)
+    WU, WUs = dev(uc, ue, D)
+    WD, WDs = dev(dc, de, Ft)
+    H = torch.empty(M, Ft, dtype=torch.uint8, device="cuda")
+    Hs = torch.zeros(tpm.mx_scales_bytes(M, Ft), dtype=torch.uint8, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    flags = torch.full((C,), 1, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MX_MLP_FWD, M, D, F, T, C, _abi.FP8_E4M3)
+    tpm.tp_mlp_fwd_mx(X, Xs, WU, WUs, WD, WDs, H, Hs, P, T=T, rank=0, act=_abi.ACT_GELU_ERF, num_chunks=C,
+                      chunk_order=si.ring_chunk_order(T, C, 0), chunk_ready=flags, epoch=1, workspace=ws)
+    sync()
+    assert tpm.poll_device_error(ws) == 0
+    rows = pick(M, 10, 71)
+    Xd = formats.mx_e4m3_decode(xc[rows], xe[rows])
+    Ud = formats.mx_e4m3_decode(uc, ue)
+    z = Xd @ Ud.T
+    h = ops.act_fwd(z, ops.ACT_GELU_ERF)
+    off = (((rows[:, None] // 32) * (Ft // 128) + np.arange(Ft // 32)[None, :] // 4) * 32 + rows[:, None] % 32) * 4 + \
+        np.arange(Ft // 32)[None, :] % 4
+    hc, he = H[rows].cpu().numpy(), Hs.cpu().numpy()[off]
+    delta = D * 2.0 ** -24 * (np.abs(Xd) @ np.abs(Ud).T) * np.abs(ops.act_grad(z, ops.ACT_GELU_ERF)) + \
+        2.0 ** -20 * np.abs(h) + 1e-30
+    assert_mx_close(hc, he, h, delta)
+    del Ud
+    hq, hs = formats.mx_e4m3_quantize(h)
+    p_ref = formats.mx_e4m3_decode(hq, hs) @ formats.mx_e4m3_decode(dc, de).T
+    assert nerr(host64(P[rows]), p_ref) <= TOL["fp8"]

@@ -8,7 +8,7 @@ import torch
 
 import synthetic_inputs as si
 from oracle import formats, ops
-from tests._util import TOL, f64, nerr
+from tests._util import TOL, assert_mx_close, f64, nerr
 
 pytestmark = pytest.mark.gpu
 
@@ -431,6 +431,139 @@ def test_gated_mlp_fwd_bwd_small(act):
     assert nerr(dWgu[:, :Ft], rb["dW_gate"]) <= TOL["bf16"] and nerr(dWgu[:, Ft:], rb["dW_up"]) <= TOL["bf16"]
     assert nerr(dWd, rb["dW_down"]) <= TOL["bf16"]
     assert nerr(dX, rb["dX"]) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ MXFP8
+def _mx_offsets(rows, kblocks):
+    """Byte offset of scale (row, kb) in the scaled-MFMA layout, from its
+    definition: 32-row groups, one 128-byte record per 4 blocks (128 K
+    elements), 4 bytes per row inside a record."""
+    r = np.arange(rows)[:, None]
+    kb = np.arange(kblocks)[None, :]
+    ks = kblocks // 4
+    return (((r // 32) * ks + kb // 4) * 32 + r % 32) * 4 + kb % 4
+
+
+def _mx_dev(codes, e):
+    """Device codes + swizzled scales from row-major host arrays."""
+    rows, k = codes.shape
+    sw = tpm.mx_swizzle_scales(torch.from_numpy(np.ascontiguousarray(e, dtype=np.uint8)).cuda(), k)
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).cuda(), sw
+
+
+def _mx_unswizzle(sw, rows, k):
+    return sw.cpu().numpy()[_mx_offsets(rows, k // 32)]
+
+
+def test_mx_swizzle_layout():
+    rows, k = 70, 384
+    e = np.random.default_rng(111).integers(0, 255, size=(rows, k // 32)).astype(np.uint8)
+    sw = tpm.mx_swizzle_scales(torch.from_numpy(e).cuda(), k)
+    sync()
+    assert sw.numel() == tpm.mx_scales_bytes(rows, k) == 96 * (k // 32)
+    host = sw.cpu().numpy()
+    assert np.array_equal(host[_mx_offsets(rows, k // 32)], e)
+    pad = np.ones(host.size, bool)
+    pad[_mx_offsets(rows, k // 32).ravel()] = False
+    assert np.all(host[pad] == 0)                       # rows 70..95 of the last group
+
+
+def _mx_int_operand(rows, k, seed):
+    """Integer e4m3 codes (|v| <= 3) with block exponents 125..129: every
+    product of the GEMM is a multiple of 2^-4 below 2^8, so fp32 sums of a
+    few hundred of them are exact."""
+    g = np.random.default_rng(seed)
+    codes = si.to_e4m3_exact(si.small_ints((rows, k), seed)).numpy()
+    e = g.integers(125, 130, size=(rows, k // 32)).astype(np.uint8)
+    return codes, e
+
+
+def test_mx_gemm_integer_exact():
+    # pins the scaled MFMA's use of the block scales: which byte, which lane,
+    # which operand; ragged rows (300) and columns (136)
+    M, N, K = 300, 136, 512
+    ac, ae = _mx_int_operand(M, K, 112)
+    bc, be = _mx_int_operand(N, K, 113)
+    A, As = _mx_dev(ac, ae)
+    B, Bs = _mx_dev(bc, be)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm_mx(A, As, B, Bs, Y)
+    sync()
+    ref = formats.mx_e4m3_decode(ac, ae) @ formats.mx_e4m3_decode(bc, be).T
+    assert np.array_equal(f64(Y), ref)
+    # chunked, with a split-K workspace (4 output tiles: the plan splits K)
+    M2, N2, K2 = 512, 264, 4096
+    ac, ae = _mx_int_operand(M2, K2, 114)
+    bc, be = _mx_int_operand(N2, K2, 115)
+    A, As = _mx_dev(ac, ae)
+    B, Bs = _mx_dev(bc, be)
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M2, N2, K2, 1, 4, _abi.FP8_E4M3)
+    assert ws.numel() > 2048
+    Y2 = torch.empty(M2, N2, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm_mx(A, As, B, Bs, Y2, num_chunks=4, chunk_order=[3, 1, 0, 2], workspace=ws)
+    sync()
+    ref2 = formats.mx_e4m3_decode(ac, ae) @ formats.mx_e4m3_decode(bc, be).T
+    assert np.array_equal(f64(Y2), ref2)
+
+
+def test_mx_output_quantisation_exact():
+    # no activation, exact fp32 products: the MXFP8 output (codes and block
+    # exponents) must equal the oracle's quantisation of the exact values
+    M, N, K = 260, 256, 384
+    ac, ae = _mx_int_operand(M, K, 116)
+    bc, be = _mx_int_operand(N, K, 117)
+    A, As = _mx_dev(ac, ae)
+    B, Bs = _mx_dev(bc, be)
+    Yq = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+    Ys = torch.zeros(tpm.mx_scales_bytes(M, N), dtype=torch.uint8, device="cuda")
+    Z = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm_mx(A, As, B, Bs, Yq, y_scales=Ys, aux=Z)
+    sync()
+    z = formats.mx_e4m3_decode(ac, ae) @ formats.mx_e4m3_decode(bc, be).T
+    qc, qe = formats.mx_e4m3_quantize(z)
+    assert np.array_equal(Yq.cpu().numpy(), qc)
+    assert np.array_equal(_mx_unswizzle(Ys, M, N), qe)
+    assert np.array_equal(f64(Z), formats.round_bf16(z))
+
+
+def _mx_float_operand(rows, k, seed, sigma):
+    c, e = si.to_mxfp8(si.normal_f32((rows, k), seed, sigma))
+    return c.numpy(), e.numpy()
+
+
+def test_mlp_fwd_mx_small():
+    M, D, F, T, C = 512, 512, 2048, 4, 8
+    Ft = F // T
+    xc, xe = _mx_float_operand(M, D, 1, 1.0)
+    uc, ue = _mx_float_operand(Ft, D, 2, 0.02)           # W_up,t stored K-major [F/T, D]
+    dc, de = _mx_float_operand(D, Ft, 3, 0.02)           # W_down,t stored K-major [D, F/T]
+    X, Xs = _mx_dev(xc, xe)
+    WU, WUs = _mx_dev(uc, ue)
+    WD, WDs = _mx_dev(dc, de)
+    H = torch.empty(M, Ft, dtype=torch.uint8, device="cuda")
+    Hs = torch.zeros(tpm.mx_scales_bytes(M, Ft), dtype=torch.uint8, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, Ft, dtype=torch.bfloat16, device="cuda")
+    flags = torch.full((C,), 6, dtype=torch.int32, device="cuda")
+    done = torch.zeros(T, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MX_MLP_FWD, M, D, F, T, C, _abi.FP8_E4M3)
+    tpm.tp_mlp_fwd_mx(X, Xs, WU, WUs, WD, WDs, H, Hs, P, T=T, rank=2, act=_abi.ACT_GELU_ERF, Z_t=Z, num_chunks=C,
+                      chunk_order=si.ring_chunk_order(T, C, 2), chunk_ready=flags, epoch=6, range_done=done,
+                      workspace=ws)
+    sync()
+    assert tpm.poll_device_error(ws) == 0 and done.tolist() == [6] * T
+    ref = ops.tp_mlp_fwd_mx(xc, xe, uc, ue, dc, de, ops.ACT_GELU_ERF)
+    assert nerr(Z, ref["Z"]) <= TOL["bf16"]
+    hc, he = H.cpu().numpy(), _mx_unswizzle(Hs, M, Ft)
+    # block exponents and codes: equal but for values the fp32 evaluation puts
+    # on the other side of a rounding (or power-of-two) boundary
+    # fp32 evaluation error of H: the accumulation of D products (at most D
+    # ulps of their absolute sum) through act', plus the activation's own
+    Xd, Ud = formats.mx_e4m3_decode(xc, xe), formats.mx_e4m3_decode(uc, ue)
+    dz = D * 2.0 ** -24 * (np.abs(Xd) @ np.abs(Ud).T)
+    delta = dz * np.abs(ops.act_grad(ref["Z"], ops.ACT_GELU_ERF)) + 2.0 ** -20 * np.abs(ref["H"]) + 1e-30
+    assert_mx_close(hc, he, ref["H"], delta)
+    assert nerr(P, ref["P"]) <= TOL["fp8"]
 
 
 def test_mlp_fwd_fp8_small():
