@@ -232,6 +232,38 @@ def tp_mlp_fwd_fp8(xq, sx, wq_up, s_up, wq_down, s_down, act=ACT_GELU_ERF):
 
 
 # ------------------------------------------------- partial_reduce_seqshard
+def fp8_delayed_scale(amax_history):
+    """Dequantisation factor of a tensor under delayed scaling ([CG]
+    "Supported quantization recipes", FP8 with delayed scaling; the page
+    names the recipe only): the largest amax recorded over the history
+    window, divided by 448 in fp32 (1 when every entry is 0)."""
+    a = float(np.max(np.asarray(amax_history, dtype=np.float64))) if len(amax_history) else 0.0
+    a32 = np.float32(a)
+    return float(np.float32(a32 / np.float32(448.0))) if a32 > 0 else 1.0
+
+
+def tp_mlp_fwd_fp8_delayed(xq, sx, wq_up, s_up, wq_down, s_down, s_h, act=ACT_GELU_ERF):
+    """fp8 forward under delayed scaling: H is quantised with a scale s_H
+    fixed before the step (from earlier steps' amax), so GEMM1 can write it
+    as e4m3 directly; the step's own amax of H is recorded for later steps.
+        Z   = (Xq . Wq_up) * sX * sWup
+        H   = act(Z)
+        inv = fp32(1 / s_H)
+        Hq  = e4m3(fp32(H * inv))                 (nearest even, saturating)
+        P   = (Hq . Wq_down) * s_H * sWdown
+        amax = max |H|
+    Inputs are decoded values (float64) of the e4m3 codes and fp32 scales."""
+    z = gemm(xq, wq_up) * (float(np.float32(sx)) * float(np.float32(s_up)))
+    h = act_fwd(z, act)
+    inv32 = np.float32(np.float32(1.0) / np.float32(s_h))
+    prod32 = (h * float(inv32)).astype(np.float32)
+    hq_codes = formats.e4m3_encode(prod32.astype(np.float64))
+    hq = formats.e4m3_to_f64(hq_codes)
+    p = gemm(hq, wq_down) * (float(np.float32(s_h)) * float(np.float32(s_down)))
+    amax = float(np.max(np.abs(h))) if h.size else 0.0
+    return dict(Z=z, H=h, inv=float(inv32), Hq_codes=hq_codes, P=p, amax=amax)
+
+
 def tp_mlp_fwd_mx(xq, xs, wuq_t, wus_t, wdq_t, wds_t, act=ACT_GELU_ERF):
     """MXFP8 block-scaling variant ([CG] "Supported quantization recipes",
     MXFP8 block scaling; format in oracle.formats) with the rounding points

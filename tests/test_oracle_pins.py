@@ -107,6 +107,39 @@ def test_silu_closed_forms():
     assert np.allclose(ops.silu_grad(np.array([40.0, -40.0])), [1.0, 0.0], atol=1e-12)
 
 
+# ---------------------------------------------------------- delayed scaling
+def test_delayed_scale_from_history():
+    assert ops.fp8_delayed_scale([0.0, 0.0]) == 1.0
+    assert ops.fp8_delayed_scale([1.0, 448.0, 3.0]) == 1.0
+    assert ops.fp8_delayed_scale([2.0, 896.0]) == 2.0
+    assert ops.fp8_delayed_scale([7.0]) == float(np.float32(np.float32(7.0) / np.float32(448.0)))
+
+
+def test_fp8_delayed_forward_rounding_and_saturation():
+    g = np.random.default_rng(85)
+    M, D, Ft = 16, 64, 48
+    xq = formats.e4m3_to_f64(formats.e4m3_encode(g.standard_normal((M, D))))
+    wu = formats.e4m3_to_f64(formats.e4m3_encode(g.standard_normal((D, Ft)) * 4))
+    wd = formats.e4m3_to_f64(formats.e4m3_encode(g.standard_normal((Ft, D)) * 4))
+    sx, su, sd = 0.5, 0.03125, 0.0625
+    h = ops.act_fwd(ops.gemm(xq, wu) * sx * su, ops.ACT_GELU_ERF)
+    amax = float(np.max(np.abs(h)))
+    # a fresh scale (amax of this very H): no element saturates, each within
+    # half an e4m3 step of its value; P is the GEMM of the decoded codes
+    s_h = ops.fp8_delayed_scale([amax])
+    r = ops.tp_mlp_fwd_fp8_delayed(xq, sx, wu, su, wd, sd, s_h, ops.ACT_GELU_ERF)
+    assert r["amax"] == amax
+    dec = formats.e4m3_to_f64(r["Hq_codes"]) * s_h
+    normal = np.abs(h) >= 2.0 ** -6 * s_h
+    assert np.all(np.abs(dec - h)[normal] <= 2.0 ** -4 * np.abs(h)[normal] * (1 + 1e-6))
+    assert np.allclose(r["P"], ops.gemm(formats.e4m3_to_f64(r["Hq_codes"]), wd) * s_h * sd, rtol=0, atol=1e-12)
+    # a stale scale half as large: the largest elements saturate at +-448 s_h
+    r2 = ops.tp_mlp_fwd_fp8_delayed(xq, sx, wu, su, wd, sd, s_h / 2, ops.ACT_GELU_ERF)
+    big = np.abs(h) >= 448 * s_h / 2 * (1 + 2.0 ** -4)
+    assert big.any()
+    assert np.all(np.abs(formats.e4m3_to_f64(r2["Hq_codes"]))[big] == 448.0)
+
+
 # ------------------------------------------------------------------ MXFP8
 def test_mx_quantizer_against_definition_brute_force():
     # OCP MX: per 32-block a power-of-two scale X with max|V| / X in [256, 512)
