@@ -432,6 +432,52 @@ def run_sweep(torch, tpm, si):
             torch.cuda.empty_cache()
 
 
+def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
+    """The fp8 configuration's MLP forward under delayed scaling: H's scale
+    comes from the amax history (updated on the device after each call), so
+    GEMM1 writes e4m3 H directly; chunk-gated with the flags already set."""
+    import numpy as np
+    Ft = F // T
+    dev = "cuda"
+    xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 1))
+    wuq, su = si.to_e4m3_current(np.ascontiguousarray(si.normal_f32((D, Ft), 2, 0.02).T))
+    wdq, sd = si.to_e4m3_current(np.ascontiguousarray(si.normal_f32((Ft, D), 3, 0.02).T))
+    X, WU, WD = xq.to(dev), wuq.to(dev), wdq.to(dev)
+    scales = torch.tensor([sx, su, sd], dtype=torch.float32, device=dev)
+    hist = torch.zeros(16, dtype=torch.float32, device=dev)
+    hs = torch.ones(1, dtype=torch.float32, device=dev)
+    H = torch.empty(M, Ft, dtype=torch.uint8, device=dev)
+    P = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
+    ws = tpm.alloc_workspace(tpm.OP_FP8_DELAYED_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
+    order = si.ring_chunk_order(T, C, 0)
+    step = [0]
+
+    def call():
+        k = step[0] % hist.numel()
+        tpm.tp_mlp_fwd_delayed(X, WU, WD, H, P, T=T, rank=0, scales=scales, h_scale=hs,
+                               h_amax_out=hist[k:k + 1], act=tpm.ACT_GELU_ERF, num_chunks=C, chunk_order=order,
+                               chunk_ready=flags, epoch=1, workspace=ws)
+        tpm.fp8_delayed_scale(hist, hs)
+        step[0] += 1
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    assert tpm.poll_device_error(ws) == 0
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    tf = 2.0 * M * Ft * D * 2 / (ms * 1e-3) / 1e12
+    return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="fp8_e4m3 (delayed scaling, history 16)", ms=ms, TFLOPS=tf,
+                frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
+
+
 def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
     """The fp8 configuration's MLP forward under MXFP8 block scaling (inputs
     and weights MXFP8 along their contraction axes, H requantised to MXFP8 in
@@ -643,6 +689,8 @@ def main():
         extra["mlp_fwd_c4_fp8"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
         torch.cuda.empty_cache()
         extra["mlp_fwd_c4_mxfp8"] = bench_mlp_fwd_mx(torch, tpm, si)
+        torch.cuda.empty_cache()
+        extra["mlp_fwd_c4_fp8_delayed"] = bench_mlp_fwd_delayed(torch, tpm, si)
         torch.cuda.empty_cache()
         extra["gated_mlp_worked_example"] = bench_gated_mlp(torch, tpm, si)
         rec["extra"] = extra

@@ -73,7 +73,7 @@ typedef enum {
 /* Operation ids for tpm_workspace_bytes(). */
 typedef enum {
   TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2,
-  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5
+  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5, TPM_OP_FP8_DELAYED_MLP_FWD = 6
 } tpm_op;
 
 #define TPM_MAX_CHUNKS 256
@@ -302,6 +302,35 @@ int tp_mlp_fwd_mx(int64_t M, int64_t D, int64_t F, int T, int rank,
                   int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
                   const int32_t* range_order, uint32_t* range_done,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_fwd_delayed -- the fp8 MLP forward under delayed scaling
+ * ("Collective GEMMs in Tensor Sequence Parallelism", section "Supported
+ * quantization recipes", FP8 with delayed scaling): X, W_up,t, W_down,t as
+ * in tp_mlp_fwd's fp8 form (codes, weights stored K-major, scales =
+ * device {sX, sWup, sWdown}); h_scale (device fp32) is H's dequantisation
+ * factor fixed before the step.  GEMM1's epilogue writes H_t [M, F/T] as
+ * e4m3 codes e4m3(act(Z) * fp32(1 / h_scale)), nearest-even, saturating, and
+ * records max|act(Z)| (fp32 values) into h_amax_out (device, zeroed by the
+ * call; NULL to skip); GEMM2 reads the codes with h_scale.  Z_t (bf16,
+ * optional) receives the pre-activation.  Chunks, orders, flags and
+ * range_done as in tp_mlp_fwd.  workspace >= tpm_workspace_bytes(
+ * TPM_OP_FP8_DELAYED_MLP_FWD, M, D, F, T, ...) when flags or h_amax_out are
+ * given.
+ */
+int tp_mlp_fwd_delayed(int64_t M, int64_t D, int64_t F, int T, int rank,
+                       const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
+                       const float* h_scale, float* h_amax_out, int act,
+                       void* Z_t, void* H_t, void* P_t,
+                       int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                       const int32_t* range_order, uint32_t* range_done,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Delayed scaling's scale update: *scale_out = fp32(max(amax_history[0..n)) /
+ * 448), or 1 when every entry is 0 (device pointers, one small kernel on
+ * `stream`).  With h_amax_out of step k pointing at history[k % n], this
+ * gives the h_scale of step k + 1. */
+int tpm_fp8_delayed_scale(const float* amax_history, int n, float* scale_out, void* stream);
 
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
  * TPM_OP_MLP_BWD and the gated forms pass (M, N = D, K = F, T); for

@@ -11,6 +11,7 @@ Arguments are marshalled to the C ABI; nothing is computed here.
     tp_gated_mlp_bwd        [dG | dU], dW_down,t, [dW_gate,t | dW_up,t], dX_t (partial)
     seq_chunk_gemm_mx       the local GEMM with MXFP8 operands (and optionally output)
     tp_mlp_fwd_mx           the MLP forward under MXFP8 block scaling
+    tp_mlp_fwd_delayed      the fp8 MLP forward under delayed scaling (+ fp8_delayed_scale)
     partial_reduce_seqshard sum of T partials over this rank's token slice
 """
 from __future__ import annotations
@@ -22,11 +23,12 @@ import torch
 from . import _abi
 from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF16, EPI_DACT,  # noqa: F401
                    EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD,
-                   OP_MLP_FWD, OP_MX_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+                   OP_FP8_DELAYED_MLP_FWD, OP_MLP_FWD, OP_MX_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
 __all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "mx_scales_bytes", "mx_swizzle_scales",
+           "tp_mlp_fwd_delayed", "fp8_delayed_scale",
            "partial_reduce_seqshard",
            "workspace_bytes", "alloc_workspace", "signal_chunk", "write_chunks", "poll_device_error",
            "set_wait_limit", "dtype_code", "masked_streams", "TpmError", "lib"]
@@ -208,6 +210,30 @@ def tp_mlp_fwd_mx(X, x_scales, W_up_t, w_up_scales, W_down_t, w_down_scales, H_t
                            _abi.int_array(range_order), _ptr(range_done),
                            _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
     return check(rc)
+
+
+def tp_mlp_fwd_delayed(X, W_up_t, W_down_t, H_t, P_t, *, T, rank, scales, h_scale, h_amax_out=None,
+                       act=ACT_GELU_ERF, Z_t=None, num_chunks=1, chunk_order=None, chunk_ready=None, epoch=0,
+                       range_order=None, range_done=None, workspace=None, stream=None):
+    """fp8 forward under delayed scaling: X [M,D] codes, W_up_t [F/T, D] and
+    W_down_t [D, F/T] codes stored K-major, scales = device fp32 {sX, sWup,
+    sWdown}, h_scale = device fp32 scale of H fixed before the step; H_t
+    [M, F/T] uint8 codes, P_t [M, D] bf16; h_amax_out (device fp32) gets
+    max|H|."""
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_mlp_fwd_delayed(M, D, Ft * T, T, rank, _ptr(X), _ptr(W_up_t), _ptr(W_down_t), _ptr(scales),
+                                _ptr(h_scale), _ptr(h_amax_out), act, _ptr(Z_t), _ptr(H_t), _ptr(P_t),
+                                num_chunks, _abi.int_array(chunk_order), _ptr(chunk_ready), epoch,
+                                _abi.int_array(range_order), _ptr(range_done),
+                                _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+    return check(rc)
+
+
+def fp8_delayed_scale(amax_history, scale_out, stream=None):
+    """scale_out[0] = max(amax_history) / 448 (1 when all are 0), on the device."""
+    return check(lib.tpm_fp8_delayed_scale(_ptr(amax_history), amax_history.numel(), _ptr(scale_out),
+                                           _stream(stream)))
 
 
 def partial_reduce_seqshard(partials, out, *, T, rank, M=None, stream=None):

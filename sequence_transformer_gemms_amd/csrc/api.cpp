@@ -113,6 +113,7 @@ struct GemmDesc {
   const uint8_t* a_mx = nullptr;
   const uint8_t* b_mx = nullptr;
   uint8_t* y_mx = nullptr;
+  const float* y_qs = nullptr;   // fp8 per-tensor output scale (dequant factor), delayed scaling
 };
 
 size_t mx_scales_bytes(int64_t rows, int64_t k) { return (size_t)((rows + 31) / 32) * 32 * (size_t)(k / 32); }
@@ -122,7 +123,7 @@ int check_gemm(const GemmDesc& g, const char* who) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return fail(TPM_EINVAL, "%s: negative size", who);
   if (g.M > INT32_MAX || g.N > INT32_MAX || g.K > INT32_MAX) return fail(TPM_EUNSUPPORTED, "%s: size >= 2^31", who);
   if (!valid_dt(g.adt) || g.adt != g.bdt) return fail(TPM_EINVAL, "%s: operand dtypes must match", who);
-  if (g.ydt != TPM_F32 && g.ydt != TPM_BF16 && !(g.ydt == TPM_FP8_E4M3 && g.y_mx))
+  if (g.ydt != TPM_F32 && g.ydt != TPM_BF16 && !(g.ydt == TPM_FP8_E4M3 && (g.y_mx || g.y_qs)))
     return fail(TPM_EINVAL, "%s: output dtype must be F32 or BF16 (or MXFP8)", who);
   if (g.epi < TPM_EPI_FWD || g.epi > TPM_EPI_DGATED) return fail(TPM_EINVAL, "%s: bad epilogue", who);
   if (g.act < TPM_ACT_NONE || g.act > TPM_ACT_SILU) return fail(TPM_EINVAL, "%s: bad activation", who);
@@ -156,8 +157,12 @@ int check_gemm(const GemmDesc& g, const char* who) {
     if (g.asc || g.bsc || g.amax) return fail(TPM_EINVAL, "%s: MXFP8 takes no per-tensor scales or amax", who);
     if (g.epi != TPM_EPI_FWD) return fail(TPM_EUNSUPPORTED, "%s: MXFP8 with the FWD epilogue only", who);
   }
-  if (g.ydt == TPM_FP8_E4M3 && (!g.y_mx || g.N % 128 != 0))
+  if (g.ydt == TPM_FP8_E4M3 && g.y_qs) {
+    if (g.y_mx || g.adt != TPM_FP8_E4M3 || g.epi != TPM_EPI_FWD)
+      return fail(TPM_EUNSUPPORTED, "%s: a per-tensor fp8 output needs fp8 operands and the FWD epilogue", who);
+  } else if (g.ydt == TPM_FP8_E4M3 && (!g.y_mx || g.N % 128 != 0)) {
     return fail(TPM_EUNSUPPORTED, "%s: an fp8 output is MXFP8 (scales required, N %% 128 == 0)", who);
+  }
   if (g.y_mx && g.ydt != TPM_FP8_E4M3) return fail(TPM_EINVAL, "%s: output scales given for a non-fp8 output", who);
   if (g.M == 0 || g.N == 0) return TPM_OK;
   if (!g.Y) return fail(TPM_EINVAL, "%s: null output", who);
@@ -178,7 +183,7 @@ int check_gemm(const GemmDesc& g, const char* who) {
     return fail(TPM_EUNSUPPORTED, "%s: fp8 operands must be stored K-major (trans_a=0, trans_b=1)", who);
   if (g.N % 8 != 0 || g.K % q != 0) return fail(TPM_EUNSUPPORTED, "%s: N %% 8 and K %% %d must be 0", who, q);
   if (g.ldy % 4 != 0 || (g.aux && g.ldaux % 4 != 0)) return fail(TPM_EUNSUPPORTED, "%s: ldy/ldaux %% 4 != 0", who);
-  if (g.y_mx && g.ldy % 8 != 0) return fail(TPM_EUNSUPPORTED, "%s: MXFP8 output needs ldy %% 8 == 0", who);
+  if ((g.y_mx || g.y_qs) && g.ldy % 8 != 0) return fail(TPM_EUNSUPPORTED, "%s: an fp8 output needs ldy %% 8 == 0", who);
   if (((uintptr_t)g.Y & 15) || (g.aux && ((uintptr_t)g.aux & 15)))
     return fail(TPM_EUNSUPPORTED, "%s: device pointers must be 16-byte aligned", who);
   if (g.K == 0) return TPM_OK;  // Y = epilogue(0): the operands are never read
@@ -217,7 +222,7 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   // split-K when the plan asks for it and the scratch is there (chunk-gated
   // GEMMs split too; range-done signalling needs whole tiles)
   // (the gated forward pairs gate and up columns inside one tile: no split-K)
-  int S = (g.done || g.epi == TPM_EPI_GATED || g.y_mx) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+  int S = (g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
   if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
   const int64_t nk = (g.K * esize(g.adt) + kStepBytes - 1) / kStepBytes;
   p.splits = S;
@@ -226,7 +231,7 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
   p.a_bytes = g.K == 0 ? 0u : (uint32_t)(a_rows * g.lda * esize(g.adt));
   p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
-  p.a_mx = g.a_mx; p.b_mx = g.b_mx; p.y_mx = g.y_mx;
+  p.a_mx = g.a_mx; p.b_mx = g.b_mx; p.y_mx = g.y_mx; p.y_q_scale = g.y_qs;
   p.mx_steps = (int)(g.K / 128);
   p.y_mx_steps = (int)(g.N / 128);
   p.a_mx_bytes = g.a_mx ? (uint32_t)mx_scales_bytes(g.M, g.K) : 0u;
@@ -302,7 +307,8 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, dtype)));
       return kCtrlBytes + dz + part;
     }
-    case TPM_OP_MX_MLP_FWD: {
+    case TPM_OP_MX_MLP_FWD:
+    case TPM_OP_FP8_DELAYED_MLP_FWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       return kCtrlBytes + partial_bytes(M, D, plan_splits(M, D, Ft, T, TPM_FP8_E4M3));
@@ -554,6 +560,70 @@ int tpm_mx_swizzle_scales(int64_t rows, int64_t k, const uint8_t* src, int64_t l
   if (!src || !dst || ld < k / 32) return fail(TPM_EINVAL, "%s: null pointer or ld < k/32", who);
   hipError_t e = launch_mx_swizzle(src, ld, (int)rows, (int)(k / 32), dst, (hipStream_t)stream);
   return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+int tpm_fp8_delayed_scale(const float* amax_history, int n, float* scale_out, void* stream) {
+  const char* who = "tpm_fp8_delayed_scale";
+  if (n < 1 || !amax_history || !scale_out) return fail(TPM_EINVAL, "%s: n >= 1 and non-null pointers", who);
+  hipError_t e = launch_delayed_scale(amax_history, n, scale_out, (hipStream_t)stream);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+int tp_mlp_fwd_delayed(int64_t M, int64_t D, int64_t F, int T, int rank,
+                       const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
+                       const float* h_scale, float* h_amax_out, int act,
+                       void* Z_t, void* H_t, void* P_t,
+                       int num_chunks, const int32_t* chunk_order, const uint32_t* chunk_ready, uint32_t epoch,
+                       const int32_t* range_order, uint32_t* range_done,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_mlp_fwd_delayed";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0 || M % T != 0) return fail(TPM_EINVAL, "%s: F %% T or M %% T != 0", who);
+  if (!scales || !h_scale || !H_t || !P_t) return fail(TPM_EINVAL, "%s: null pointer", who);
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
+  const int64_t Ft = F / T;
+  const size_t need = tpm_workspace_bytes(TPM_OP_FP8_DELAYED_MLP_FWD, M, D, F, T, num_chunks, TPM_FP8_E4M3);
+  const bool need_ctrl = chunk_ready || range_done || h_amax_out;
+  if (need_ctrl && (!workspace || workspace_bytes < need))
+    return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  uint32_t* ctrl = (workspace && workspace_bytes >= kCtrlBytes) ? (uint32_t*)workspace : nullptr;
+  int32_t corder[TPM_MAX_CHUNKS], rorder[TPM_MAX_CHUNKS];
+  if (chunk_order) std::memcpy(corder, chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  if (range_order) std::memcpy(rorder, range_order, sizeof(int32_t) * T);
+  else for (int i = 0; i < T; ++i) rorder[i] = (rank + 1 + i) % T;
+  const int f8 = TPM_FP8_E4M3;
+  // GEMM1: H = e4m3(act(X W_up) / s_H), chunk-fed; amax of act(.) recorded
+  GemmDesc g1{M, Ft, D, X, D, false, f8, scales + 0, W_up_t, D, true, f8, scales + 1,
+              H_t, Ft, f8, TPM_EPI_FWD, act, Z_t, Ft, h_amax_out,
+              num_chunks, corder, chunk_ready, nullptr, epoch, ctrl};
+  g1.y_qs = h_scale;
+  // GEMM2: P = (Hq W_down) s_H s_Wdown
+  GemmDesc g2{M, D, Ft, H_t, Ft, false, f8, h_scale, W_down_t, Ft, true, f8, scales + 2,
+              P_t, D, TPM_BF16, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+              T, rorder, nullptr, range_done, epoch, ctrl};
+  for (const GemmDesc* g : {&g1, &g2}) {
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  if (workspace && workspace_bytes >= need) {
+    g1.part = g2.part = (float*)((char*)workspace + kCtrlBytes);
+    g1.part_bytes = g2.part_bytes = workspace_bytes - kCtrlBytes;
+  }
+  if (M == 0 || D == 0) return TPM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (need_ctrl) {
+    hipError_t e = launch_ctrl_init(ctrl, kCtrlWords, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  if (h_amax_out) {
+    hipError_t e = launch_ctrl_init((uint32_t*)h_amax_out, 1, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  int rc = run_gemm(g1, s, who);
+  if (rc != TPM_OK) return rc;
+  return run_gemm(g2, s, who);
 }
 
 int seq_chunk_gemm_mx(int64_t M, int64_t N, int64_t K,

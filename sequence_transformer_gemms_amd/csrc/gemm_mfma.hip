@@ -639,6 +639,35 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
             epi_gated_oct(p, g, u, row, col);
           }
         }
+      } else if (FP8 && p.y_q_scale) {
+        // fp8 output with a scale fixed before the call (delayed scaling):
+        // codes e4m3(v * fp32(1 / s)), nearest-even, saturating; amax of the
+        // fp32 values quantised
+        const float inv = 1.0f / *p.y_q_scale;
+#pragma unroll 1
+        for (int it = 0; it < EPI_ROWS / 8; ++it) {
+          const int rl = it * 8 + (lane >> 3);
+          const int cl = (lane & 7) * 8;
+          const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
+          const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+          const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+          const int col = tl.n0 + wn + EPI_COLS * cp + cl;
+          if (row < tl.m_end && col < p.N) {
+            float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                          v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+            if (p.aux) store_oct(p.aux, p.ldaux, false, row, col, v);  // pre-activation, bf16
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float h = act_fwd(v[e], p.act);
+              lmax = fmaxf(lmax, fabsf(h));
+              const uint32_t q = f32_to_e4m3_rne_sat(h * inv);
+              if (e < 4) lo |= q << (8 * e);
+              else hi |= q << (8 * (e - 4));
+            }
+            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+          }
+        }
       } else if (FP8 && p.y_mx) {
         // MXFP8 output: each 32-column block of a row (4 lanes) shares one
         // scale 2^(E-127), E = exponent field of the block's amax - 8 (0 for

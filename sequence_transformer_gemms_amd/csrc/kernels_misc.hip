@@ -161,6 +161,20 @@ __global__ void __launch_bounds__(256) mx_swizzle(const uint8_t* __restrict__ sr
   }
 }
 
+// Delayed scaling: scale = fp32(max(history) / 448), 1 when all are 0.
+__global__ void __launch_bounds__(256) delayed_scale(const float* __restrict__ hist, int n, float* out) {
+  __shared__ float red[256];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, hist[i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0] > 0.f ? red[0] / 448.0f : 1.0f;
+}
+
 __global__ void ctrl_init(uint32_t* w, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
 }
@@ -247,6 +261,11 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
                              int64_t ldq, float* s_out, hipStream_t s) {
   const int64_t work = M * (N / 8);
   quant_e4m3<<<grid_for(work, 256), 256, 0, s>>>(h, M, N / 8, ldh, amax, q, ldq, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_delayed_scale(const float* history, int n, float* scale_out, hipStream_t s) {
+  delayed_scale<<<1, 256, 0, s>>>(history, n, scale_out);
   return hipGetLastError();
 }
 

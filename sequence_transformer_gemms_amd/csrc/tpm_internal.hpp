@@ -43,6 +43,7 @@ struct GemmParams {
   int mx_steps;
   uint8_t* y_mx;
   int y_mx_steps;
+  const float* y_q_scale;    // fp8 per-tensor output: Y = e4m3(v / *y_q_scale) (or null)
   int gu_off;                // gated epilogues: column offset of the up half in B / aux / Y (= N)
   int bn_out;                // output columns per tile (256; 128 for EPI_GATED)
   int16_t order[kMaxGroups];
@@ -76,6 +77,7 @@ struct WriterParams {
 // kernels' launchers (return hipError_t of the launch)
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
+hipError_t launch_delayed_scale(const float* history, int n, float* scale_out, hipStream_t s);
 hipError_t launch_mx_swizzle(const uint8_t* src, int64_t ld, int rows, int kblocks, uint8_t* dst, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
 hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s);

@@ -566,6 +566,84 @@ def test_mlp_fwd_mx_small():
     assert nerr(P, ref["P"]) <= TOL["fp8"]
 
 
+# -------------------------------------------------------- fp8 delayed scaling
+def test_mlp_fwd_fp8_delayed_integer_exact():
+    # integer operands, ReLU: H is exact, H * fp32(1 / s_H) exact for s_H =
+    # 1/16, so the e4m3 codes (saturating above 448) and the amax are bit-exact
+    M, D, F, T = 256, 64, 512, 2
+    Ft = F // T
+    x, wu, wd = si.small_ints((M, D), 121), si.small_ints((D, Ft), 122), si.small_ints((Ft, D), 123)
+    X = si.to_e4m3_exact(x).cuda()
+    WU = si.to_e4m3_exact(np.ascontiguousarray(wu.T)).cuda()        # K-major [Ft, D]
+    WD = si.to_e4m3_exact(np.ascontiguousarray(wd.T)).cuda()        # K-major [D, Ft]
+    scales = dev_f32(np.array([1.0, 1.0, 1.0], np.float32))
+    hs = dev_f32(np.array([0.0625], np.float32))
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    H = torch.empty(M, Ft, dtype=torch.uint8, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_FP8_DELAYED_MLP_FWD, M, D, F, T, 1, _abi.FP8_E4M3)
+    tpm.tp_mlp_fwd_delayed(X, WU, WD, H, P, T=T, rank=0, scales=scales, h_scale=hs, h_amax_out=amax,
+                           act=_abi.ACT_RELU, workspace=ws)
+    sync()
+    ref = ops.tp_mlp_fwd_fp8_delayed(x.astype(np.float64), 1.0, wu.astype(np.float64), 1.0, wd.astype(np.float64),
+                                     1.0, 0.0625, ops.ACT_RELU)
+    assert np.any(np.abs(ref["H"]) * 16 > 464)                  # some codes saturate
+    assert np.array_equal(H.cpu().numpy(), ref["Hq_codes"])
+    assert amax.item() == ref["amax"]
+    assert nerr(P, ref["P"]) <= TOL["bf16"]
+
+
+def test_mlp_fwd_fp8_delayed_steps():
+    """Two steps of delayed scaling on float inputs: step 1 with the initial
+    scale 1, then the scale from the amax history (the oracle's, given to
+    both sides); the library's scale update of the history is checked
+    against the same rule."""
+    M, D, F, T, C = 512, 512, 2048, 4, 8
+    Ft = F // T
+    x = si.normal_f32((M, D), 1)
+    wu = si.normal_f32((D, Ft), 2, 0.02)
+    wd = si.normal_f32((Ft, D), 3, 0.02)
+    xq, sx = si.to_e4m3_current(x)
+    wuq, su = si.to_e4m3_current(np.ascontiguousarray(wu.T))
+    wdq, sd = si.to_e4m3_current(np.ascontiguousarray(wd.T))
+    X, WU, WD = xq.cuda(), wuq.cuda(), wdq.cuda()
+    scales = dev_f32(np.array([sx, su, sd], np.float32))
+    hist = torch.zeros(4, dtype=torch.float32, device="cuda")
+    H = torch.empty(M, Ft, dtype=torch.uint8, device="cuda")
+    P = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    flags = torch.full((C,), 2, dtype=torch.int32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_FP8_DELAYED_MLP_FWD, M, D, F, T, C, _abi.FP8_E4M3)
+    xd, wud, wdd = f64(xq), f64(wuq).T, f64(wdq).T
+    s_h = 1.0
+    for step in range(2):
+        hs = dev_f32(np.array([s_h], np.float32))
+        tpm.tp_mlp_fwd_delayed(X, WU, WD, H, P, T=T, rank=1, scales=scales, h_scale=hs, h_amax_out=hist[step:step + 1],
+                               act=_abi.ACT_GELU_ERF, num_chunks=C, chunk_ready=flags, epoch=2, workspace=ws)
+        sync()
+        assert tpm.poll_device_error(ws) == 0
+        ref = ops.tp_mlp_fwd_fp8_delayed(xd, sx, wud, su, wdd, sd, s_h, ops.ACT_GELU_ERF)
+        hc = H.cpu().numpy().astype(int)
+        rc = ref["Hq_codes"].astype(int)
+        diff = hc != rc
+        assert np.mean(diff) < 1e-2
+        # a differing code is a neighbour (fp32 vs fp64 evaluation across a rounding boundary)
+        assert np.all(((hc[diff] & 0x80) == (rc[diff] & 0x80)) & (np.abs((hc[diff] & 0x7F) - (rc[diff] & 0x7F)) == 1)
+                      | (((hc[diff] & 0x7F) <= 1) & ((rc[diff] & 0x7F) <= 1)))
+        assert abs(hist[step].item() - ref["amax"]) <= 1e-5 * ref["amax"]
+        assert nerr(P, ref["P"]) <= TOL["fp8"]
+        s_next = ops.fp8_delayed_scale([ref["amax"]] + ([] if step == 0 else [amax_prev]))
+        amax_prev = ref["amax"]
+        out = torch.empty(1, dtype=torch.float32, device="cuda")
+        tpm.fp8_delayed_scale(hist, out)
+        sync()
+        # the update is fp32(max(history) / 448) of the history it read, and
+        # that history holds amaxes within fp32 evaluation error of the oracle's
+        h32 = hist.cpu().numpy()
+        assert out.item() == float(np.float32(np.max(h32) / np.float32(448.0)))
+        assert abs(out.item() - s_next) <= 1e-5 * s_next
+        s_h = s_next
+
+
 def test_mlp_fwd_fp8_small():
     M, D, F, T, C = 512, 512, 2048, 4, 8
     Ft = F // T
