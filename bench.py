@@ -435,7 +435,7 @@ def run_sweep(torch, tpm, si):
 def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
     """The fp8 configuration's MLP forward under delayed scaling: H's scale
     comes from the amax history (updated on the device after each call), so
-    GEMM1 writes e4m3 H directly; chunk-gated with the flags already set."""
+    GEMM1 writes e4m3 H directly; inputs resident (no chunk flags, every CU)."""
     import numpy as np
     Ft = F // T
     dev = "cuda"
@@ -448,7 +448,6 @@ def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, i
     hs = torch.ones(1, dtype=torch.float32, device=dev)
     H = torch.empty(M, Ft, dtype=torch.uint8, device=dev)
     P = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
-    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
     ws = tpm.alloc_workspace(tpm.OP_FP8_DELAYED_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
     order = si.ring_chunk_order(T, C, 0)
     step = [0]
@@ -457,7 +456,7 @@ def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, i
         k = step[0] % hist.numel()
         tpm.tp_mlp_fwd_delayed(X, WU, WD, H, P, T=T, rank=0, scales=scales, h_scale=hs,
                                h_amax_out=hist[k:k + 1], act=tpm.ACT_GELU_ERF, num_chunks=C, chunk_order=order,
-                               chunk_ready=flags, epoch=1, workspace=ws)
+                               workspace=ws)
         tpm.fp8_delayed_scale(hist, hs)
         step[0] += 1
     for _ in range(3):
@@ -481,7 +480,7 @@ def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, i
 def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
     """The fp8 configuration's MLP forward under MXFP8 block scaling (inputs
     and weights MXFP8 along their contraction axes, H requantised to MXFP8 in
-    GEMM1's epilogue), chunk-gated with the flags already set; events."""
+    GEMM1's epilogue), inputs resident (no chunk flags, every CU); events."""
     Ft = F // T
     dev = "cuda"
     def mx(x, k):
@@ -493,11 +492,10 @@ def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=
     H = torch.empty(M, Ft, dtype=torch.uint8, device=dev)
     Hs = torch.zeros(tpm.mx_scales_bytes(M, Ft), dtype=torch.uint8, device=dev)
     P = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
-    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
     ws = tpm.alloc_workspace(tpm.OP_MX_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
     order = si.ring_chunk_order(T, C, 0)
     call = lambda: tpm.tp_mlp_fwd_mx(X, Xs, WU, WUs, WD, WDs, H, Hs, P, T=T, rank=0, act=tpm.ACT_GELU_ERF,
-                                     num_chunks=C, chunk_order=order, chunk_ready=flags, epoch=1, workspace=ws)
+                                     num_chunks=C, chunk_order=order, workspace=ws)
     for _ in range(3):
         call()
     torch.cuda.synchronize()
@@ -519,8 +517,8 @@ def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=
 def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10):
     """The worked example's gated MLP share (X [8192, 4096], F = 16384, T = 4:
     gate and up shards [4096, 4096] each, contraction shard [4096, 4096]),
-    SwiGLU, bf16, rank 0, chunk-gated with the flags already set: forward and
-    backward timed separately with events."""
+    SwiGLU, bf16, rank 0, inputs resident (no chunk flags, every CU): forward
+    and backward timed separately with events."""
     import numpy as np
     Ft = F // T
     dev = "cuda"
@@ -532,14 +530,13 @@ def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10)
     GU = torch.empty(M, 2 * Ft, dtype=torch.bfloat16, device=dev)
     H, P = torch.empty(M, Ft, dtype=torch.bfloat16, device=dev), torch.empty(M, D, dtype=torch.bfloat16, device=dev)
     dWgu, dWd, dX = torch.empty_like(WGU), torch.empty_like(WD), torch.empty_like(X)
-    flags = torch.full((C,), 1, dtype=torch.int32, device=dev)
     order = si.ring_chunk_order(T, C, 0)
     wsf = tpm.alloc_workspace(tpm.OP_GATED_MLP_FWD, M, D, F, T, C, tpm.BF16)
     wsb = tpm.alloc_workspace(tpm.OP_GATED_MLP_BWD, M, D, F, T, C, tpm.BF16)
     fwd = lambda: tpm.tp_gated_mlp_fwd(X, WGU, WD, H, P, T=T, rank=0, act=tpm.ACT_SILU, GU_t=GU, num_chunks=C,
-                                       chunk_order=order, chunk_ready=flags, epoch=1, workspace=wsf)
+                                       chunk_order=order, workspace=wsf)
     bwd = lambda: tpm.tp_gated_mlp_bwd(X, WGU, WD, GU, H, dY, dWgu, dWd, dX, T=T, rank=0, act=tpm.ACT_SILU,
-                                       num_chunks=C, dy_chunk_order=order, dy_ready=flags, epoch=1, workspace=wsb)
+                                       num_chunks=C, dy_chunk_order=order, workspace=wsb)
     out = {"M": M, "D": D, "F": F, "T": T, "chunks": C, "act": "silu (SwiGLU)", "dtype": "bf16"}
     for name, fn, units in (("fwd", fwd, 3), ("bwd", bwd, 6)):
         for _ in range(3):
