@@ -87,7 +87,10 @@ struct Unit {
 // (chunks / destination ranges) in the caller's order, each group in bands
 // of band_m row tiles, so the 32 tiles an XCD works on at once share few
 // A row panels and B column panels in its L2.  Splits of the K range are the
-// outermost index.
+// outermost index, except in a chunk-gated GEMM, where they come right
+// after the group: every unit of a chunk precedes the next chunk's, so the
+// work-groups' first units are the earliest chunks' and later chunks are
+// only waited for by units of a later round.
 __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
   const int G = gridDim.x;
   const int total = p.total_tiles * p.splits;
@@ -100,10 +103,19 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
     }
   }
   Unit un;
-  un.split = L / p.total_tiles;
-  L -= un.split * p.total_tiles;
-  const int pos = L / p.tiles_per_group;
-  const int q = L - pos * p.tiles_per_group;
+  int pos, q;
+  if (p.ready) {
+    const int per_group = p.tiles_per_group * p.splits;
+    pos = L / per_group;
+    const int rem = L - pos * per_group;
+    un.split = rem / p.tiles_per_group;
+    q = rem - un.split * p.tiles_per_group;
+  } else {
+    un.split = L / p.total_tiles;
+    L -= un.split * p.total_tiles;
+    pos = L / p.tiles_per_group;
+    q = L - pos * p.tiles_per_group;
+  }
   const int g = p.order[pos];
   const int band = q / (p.band_m * p.nt);
   const int rem_m = p.mt_per_group - band * p.band_m;
