@@ -111,6 +111,53 @@ def round_bf16(x) -> np.ndarray:
     return bf16_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32)))
 
 
+# ----------------------------------------------------------------- e5m2
+# OCP e5m2 (the gradient format of the hybrid fp8 recipes): 1 sign, 5
+# exponent (bias 15), 2 mantissa bits; exponent field 0 is subnormal
+# (m/4 * 2^-14); field 31 is inf (m = 0) or NaN; the largest finite
+# magnitude is 1.75 * 2^15 = 57344.  The encoder saturates finite overflow
+# to +-57344 (like e4m3fn's satfinite).
+E5M2_MAX = 57344.0
+
+
+def _e5m2_value(code: int) -> float:
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        return s * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return s * (m / 4.0) * 2.0 ** -14
+    return s * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+
+
+E5M2_TABLE = np.array([_e5m2_value(c) for c in range(256)], dtype=np.float64)
+_E5M2_POS = E5M2_TABLE[:0x7C].copy()          # 0x00 .. 0x7B: non-negative finite values, ascending
+
+
+def e5m2_to_f64(codes) -> np.ndarray:
+    return E5M2_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e5m2_encode(x) -> np.ndarray:
+    """Nearest e5m2 code to each value (float64 compare), ties to the even
+    code, saturating to +-57344; NaN -> 0x7F; the sign is kept for zero."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    idx = np.searchsorted(_E5M2_POS, a, side="left")
+    idx = np.clip(idx, 1, len(_E5M2_POS) - 1)
+    lo, hi = idx - 1, idx
+    dlo = a - _E5M2_POS[lo]
+    dhi = _E5M2_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a <= 0.0, 0, code)
+    code = np.where(a >= E5M2_MAX, 0x7B, code)
+    code = code.astype(np.uint8)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
 # ------------------------------------------------------------------- MX
 MX_BLOCK = 32
 

@@ -232,6 +232,44 @@ def tp_mlp_fwd_fp8(xq, sx, wq_up, s_up, wq_down, s_down, act=ACT_GELU_ERF):
 
 
 # ------------------------------------------------- partial_reduce_seqshard
+def _current_scale(v, fmax):
+    """Per-tensor current scaling of v to a format with largest value fmax:
+    (inv, s) = (fp32(fmax / amax), fp32(amax / fmax)), both 1 when amax = 0."""
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0.0)
+    if amax == 0:
+        return np.float32(1.0), np.float32(1.0), 0.0
+    return np.float32(np.float32(fmax) / amax), np.float32(amax / np.float32(fmax)), float(amax)
+
+
+def tp_mlp_bwd_fp8(x8, sx, wu8, su, wd8, sd, z, h8, sh, dy, act=ACT_GELU_ERF):
+    """fp8 backward of one rank's MLP share (the backward the fp8 recipes of
+    [CG] "Supported quantization recipes" imply; the pages do not spell it
+    out): activations and weights in e4m3 with their forward scales,
+    gradients in e5m2 with current scaling, the chain of tp_mlp_bwd:
+        dYq = e5m2(fp32(dY * fp32(57344 / amax dY))),  s_dY = fp32(amax dY / 57344)
+        dH  = (dYq . W_down,t^T) * s_dY * s_Wd
+        dZ  = bf16(dH * act'(Z))                       (stored intermediate)
+        dZq = e5m2(fp32(dZ * fp32(57344 / amax dZ))),  s_dZ
+        dW_down,t = (Hq^T . dYq) * s_H * s_dY
+        dW_up,t   = (Xq^T . dZq) * s_X * s_dZ
+        dX_t      = (dZq . W_up,t^T) * s_dZ * s_Wu
+    Inputs: decoded e4m3 values of X [M, D], W_up,t [D, F/T], W_down,t
+    [F/T, D], H [M, F/T] with their fp32 scales; Z and dY as bf16 values."""
+    f = lambda v: float(np.float32(v))
+    dy = np.asarray(dy, dtype=np.float64)
+    inv_dy, s_dy, amax_dy = _current_scale(dy, formats.E5M2_MAX)
+    dyq = formats.e5m2_to_f64(formats.e5m2_encode((dy * float(inv_dy)).astype(np.float32).astype(np.float64)))
+    dh = gemm(dyq, np.asarray(wd8, dtype=np.float64).T) * (float(s_dy) * f(sd))
+    dz = formats.round_bf16(dh * act_grad(np.asarray(z, dtype=np.float64), act))
+    inv_dz, s_dz, amax_dz = _current_scale(dz, formats.E5M2_MAX)
+    dzq = formats.e5m2_to_f64(formats.e5m2_encode((dz * float(inv_dz)).astype(np.float32).astype(np.float64)))
+    dw_down = gemm(np.asarray(h8, dtype=np.float64).T, dyq) * (f(sh) * float(s_dy))
+    dw_up = gemm(np.asarray(x8, dtype=np.float64).T, dzq) * (f(sx) * float(s_dz))
+    dx = gemm(dzq, np.asarray(wu8, dtype=np.float64).T) * (float(s_dz) * f(su))
+    return dict(dYq=dyq, s_dY=float(s_dy), amax_dY=amax_dy, dH=dh, dZ=dz, dZq=dzq, s_dZ=float(s_dz),
+                amax_dZ=amax_dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
+
+
 def fp8_delayed_scale(amax_history):
     """Dequantisation factor of a tensor under delayed scaling ([CG]
     "Supported quantization recipes", FP8 with delayed scaling; the page

@@ -107,6 +107,52 @@ def test_silu_closed_forms():
     assert np.allclose(ops.silu_grad(np.array([40.0, -40.0])), [1.0, 0.0], atol=1e-12)
 
 
+# --------------------------------------------------------------- e5m2
+def test_e5m2_table_from_definition():
+    t = formats.E5M2_TABLE
+    assert t[0x7B] == 57344.0 and t[0x01] == 2.0 ** -16 and t[0x04] == 2.0 ** -14
+    assert np.isinf(t[0x7C]) and np.isnan(t[0x7D]) and t[0x3C] == 1.0
+    assert np.all(np.diff(t[:0x7C]) > 0)                  # ascending magnitudes
+    assert np.array_equal(t[0x80:0xFC], -t[:0x7C])
+
+
+def test_e5m2_encoder_against_torch_and_saturation():
+    g = np.random.default_rng(86)
+    v = np.concatenate([g.standard_normal(200000) * np.exp(g.uniform(-20, 11, 200000)),
+                        formats.E5M2_TABLE[:0x7C], (formats.E5M2_TABLE[1:0x7C] + formats.E5M2_TABLE[:0x7B]) / 2])
+    v = v[np.abs(v) < 57344].astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(formats.e5m2_encode(v.astype(np.float64)), want)   # includes every tie
+    assert np.array_equal(formats.e5m2_encode(np.array([60000.0, -1e9, 57344.0])), [0x7B, 0xFB, 0x7B])
+
+
+def test_fp8_backward_mirror_composes_and_bounds():
+    g = np.random.default_rng(87)
+    M, D, Ft = 32, 64, 48
+    q4 = lambda a: formats.e4m3_to_f64(formats.e4m3_encode(a))
+    x8, wu8, wd8, h8 = q4(g.standard_normal((M, D)) * 8), q4(g.standard_normal((D, Ft)) * 8), \
+        q4(g.standard_normal((Ft, D)) * 8), q4(np.abs(g.standard_normal((M, Ft))) * 8)
+    sx, su, sd, sh = 0.125, 0.0078125, 0.0078125, 0.03125
+    z = formats.round_bf16(g.standard_normal((M, Ft)))
+    dy = formats.round_bf16(g.standard_normal((M, D)))
+    r = ops.tp_mlp_bwd_fp8(x8, sx, wu8, su, wd8, sd, z, h8, sh, dy, ops.ACT_GELU_ERF)
+    # quantised gradients: within half an e5m2 step (2^-3 relative in the normal range)
+    for q, v, s in ((r["dYq"], dy, r["s_dY"]), (r["dZq"], r["dZ"], r["s_dZ"])):
+        normal = np.abs(v) >= 2.0 ** -14 * s
+        assert np.all(np.abs(q * s - v)[normal] <= 2.0 ** -3 * np.abs(v)[normal] * (1 + 1e-6))
+        assert np.max(np.abs(q)) == 57344.0                 # current scaling maps amax to the top code
+    # the chain, step by step
+    assert np.allclose(r["dH"], r["dYq"] @ wd8.T * r["s_dY"] * sd, rtol=1e-12)
+    assert np.array_equal(r["dZ"], formats.round_bf16(r["dH"] * ops.gelu_erf_grad(z)))
+    assert np.allclose(r["dW_down"], h8.T @ r["dYq"] * sh * r["s_dY"], rtol=1e-12)
+    assert np.allclose(r["dW_up"], x8.T @ r["dZq"] * sx * r["s_dZ"], rtol=1e-12)
+    assert np.allclose(r["dX"], r["dZq"] @ wu8.T * r["s_dZ"] * su, rtol=1e-12)
+    # and close to the unquantised backward
+    ref = ops.tp_mlp_bwd(x8 * sx, wu8 * su, wd8 * sd, z, h8 * sh, dy, ops.ACT_GELU_ERF)
+    for k in ("dW_down", "dW_up", "dX"):
+        assert ops.normalized_error(r[k], ref[k]) < 0.25 * np.max(np.abs(ref[k]))
+
+
 # ---------------------------------------------------------- delayed scaling
 def test_delayed_scale_from_history():
     assert ops.fp8_delayed_scale([0.0, 0.0]) == 1.0
