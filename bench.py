@@ -477,6 +477,51 @@ def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, i
                 frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
 
 
+def bench_mlp_bwd_fp8(torch, tpm, M=8192, D=16384, F=53248, T=8, iters=10):
+    """The fp8 configuration's MLP backward in fp8 (e5m2 gradients with
+    current scaling, e4m3 activations and weights): the casts of dY, H and X
+    and the four GEMMs, timed with events.  Inputs drawn on the device (N(0,1)
+    activations and gradients, N(0, 0.02) weights) and cast with the
+    library's own current-scaling cast."""
+    Ft = F // T
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    rnd = lambda r, c, s=1.0: (torch.randn(r, c, generator=g, device=dev) * s).to(torch.bfloat16)
+
+    def fp8(x):
+        q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        sc = torch.empty(1, dtype=torch.float32, device=dev)
+        tpm.cast_fp8(x, tpm.FP8_E4M3, q=q, scale_out=sc)
+        return q, sc
+    X, sx = fp8(rnd(M, D))
+    WU, su = fp8(rnd(D, Ft, 0.02))
+    WD, sd = fp8(rnd(Ft, D, 0.02))
+    scales = torch.cat([sx, su, sd])
+    Z, H, dY = rnd(M, Ft), rnd(M, Ft).abs(), rnd(M, D)
+    dWu = torch.empty(D, Ft, dtype=torch.bfloat16, device=dev)
+    dWd = torch.empty(Ft, D, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    ws = tpm.alloc_workspace(tpm.OP_MLP_BWD_FP8, M, D, F, T, 1, tpm.FP8_E4M3)
+    call = lambda: tpm.tp_mlp_bwd_fp8(X, WU, WD, Z, H, dY, dWu, dWd, dX, T=T, rank=0, scales=scales,
+                                      act=tpm.ACT_GELU_ERF, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    tf = 4 * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
+    return dict(M=M, D=D, F=F, T=T, dtype="fp8 (e4m3 activations / weights, e5m2 gradients)", ms=ms, TFLOPS=tf,
+                frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
+
+
 def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=10):
     """The fp8 configuration's MLP forward under MXFP8 block scaling (inputs
     and weights MXFP8 along their contraction axes, H requantised to MXFP8 in
@@ -688,6 +733,8 @@ def main():
         extra["mlp_fwd_c4_mxfp8"] = bench_mlp_fwd_mx(torch, tpm, si)
         torch.cuda.empty_cache()
         extra["mlp_fwd_c4_fp8_delayed"] = bench_mlp_fwd_delayed(torch, tpm, si)
+        torch.cuda.empty_cache()
+        extra["mlp_bwd_c4_fp8"] = bench_mlp_bwd_fp8(torch, tpm)
         torch.cuda.empty_cache()
         extra["gated_mlp_worked_example"] = bench_gated_mlp(torch, tpm, si)
         rec["extra"] = extra

@@ -34,8 +34,10 @@
 extern "C" {
 #endif
 
-/* Element types.  TPM_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf). */
-typedef enum { TPM_F32 = 0, TPM_BF16 = 1, TPM_FP8_E4M3 = 2 } tpm_dtype;
+/* Element types.  TPM_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf);
+ * TPM_FP8_E5M2 is OCP e5m2 (bias 15, max 57344; the gradient format of the
+ * hybrid fp8 recipe).  An fp8 GEMM may mix the two (not e5m2 x e5m2). */
+typedef enum { TPM_F32 = 0, TPM_BF16 = 1, TPM_FP8_E4M3 = 2, TPM_FP8_E5M2 = 3 } tpm_dtype;
 
 /* Activations.  GELU_ERF: 0.5 z (1 + erf(z / sqrt 2)); GELU_TANH: the tanh
  * approximation; RELU: max(z, 0) with derivative 1 only where z > 0
@@ -73,7 +75,8 @@ typedef enum {
 /* Operation ids for tpm_workspace_bytes(). */
 typedef enum {
   TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2,
-  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5, TPM_OP_FP8_DELAYED_MLP_FWD = 6
+  TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5, TPM_OP_FP8_DELAYED_MLP_FWD = 6,
+  TPM_OP_MLP_BWD_FP8 = 7, TPM_OP_CAST_FP8 = 8
 } tpm_op;
 
 #define TPM_MAX_CHUNKS 256
@@ -331,6 +334,42 @@ int tp_mlp_fwd_delayed(int64_t M, int64_t D, int64_t F, int T, int rank,
  * `stream`).  With h_amax_out of step k pointing at history[k % n], this
  * gives the h_scale of step k + 1. */
 int tpm_fp8_delayed_scale(const float* amax_history, int n, float* scale_out, void* stream);
+
+/*
+ * tpm_cast_fp8 -- current-scaling cast of a bf16 matrix x [rows, ld >= cols]
+ * to fp8 (dtype TPM_FP8_E4M3 or TPM_FP8_E5M2, largest value fmax 448 or
+ * 57344): amax = max|x|, inv = fp32(fmax / amax), code = fp8(fp32(x * inv)),
+ * nearest-even and saturating; *scale_out = fp32(amax / fmax) (device; both
+ * factors 1 when amax = 0).  q [rows, ldq] and / or qt [cols, ldqt] (the
+ * transpose) receive the codes (either may be NULL).  rows and cols
+ * multiples of 16, ld % 8, ldq and ldqt % 16 == 0.  workspace >=
+ * tpm_workspace_bytes(TPM_OP_CAST_FP8, ...) holds the amax.
+ */
+int tpm_cast_fp8(int64_t rows, int64_t cols, const void* x, int64_t ld, int dtype,
+                 void* q, int64_t ldq, void* qt, int64_t ldqt, float* scale_out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_bwd_fp8 -- tp_mlp_bwd in fp8 (hybrid recipe: activations and
+ * weights e4m3 with their forward scales, gradients e5m2 with current
+ * scaling):
+ *   dY [M, D] bf16 -> e5m2 (current scaling) and its transpose;
+ *   H_t [M, F/T] bf16 (the forward's) -> e4m3 transposed (current scaling,
+ *     the codes the forward's GEMM2 read);
+ *   dZ_t = (dY . W_down,t^T) * act'(Z_t), stored bf16, -> e5m2 and transpose;
+ *   dW_down,t = H_t^T . dY,  dW_up,t = X^T . dZ_t,  dX_t = dZ_t . W_up,t^T.
+ * X [M, D] e4m3 codes; W_up_t [D, F/T] and W_down_t [F/T, D] e4m3 codes in
+ * the pages' layouts (the transposes of the forward's K-major copies);
+ * scales = device fp32 {sX, sWup, sWdown}; Z_t bf16 (pre-activation).
+ * dW_up_t [D, F/T], dW_down_t [F/T, D] in dw_dtype (BF16 or F32), dX_t
+ * [M, D] bf16.  M, D and F/T multiples of 16.  workspace >=
+ * tpm_workspace_bytes(TPM_OP_MLP_BWD_FP8, M, D, F, T, ...) holds the casts.
+ */
+int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
+                   const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
+                   const void* Z_t, const void* H_t, const void* dY, int act,
+                   void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
  * TPM_OP_MLP_BWD and the gated forms pass (M, N = D, K = F, T); for

@@ -12,6 +12,7 @@ Arguments are marshalled to the C ABI; nothing is computed here.
     seq_chunk_gemm_mx       the local GEMM with MXFP8 operands (and optionally output)
     tp_mlp_fwd_mx           the MLP forward under MXFP8 block scaling
     tp_mlp_fwd_delayed      the fp8 MLP forward under delayed scaling (+ fp8_delayed_scale)
+    tp_mlp_bwd_fp8          the MLP backward in fp8 (e5m2 gradients); cast_fp8 the current-scaling cast
     partial_reduce_seqshard sum of T partials over this rank's token slice
 """
 from __future__ import annotations
@@ -22,13 +23,14 @@ import torch
 
 from . import _abi
 from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF16, EPI_DACT,  # noqa: F401
-                   EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD,
-                   OP_FP8_DELAYED_MLP_FWD, OP_MLP_FWD, OP_MX_MLP_FWD, OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
+                   EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, FP8_E5M2, OP_CAST_FP8, OP_FP8_DELAYED_MLP_FWD,
+                   OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD, OP_MLP_BWD_FP8, OP_MLP_FWD, OP_MX_MLP_FWD,
+                   OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
 __all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "mx_scales_bytes", "mx_swizzle_scales",
-           "tp_mlp_fwd_delayed", "fp8_delayed_scale",
+           "tp_mlp_fwd_delayed", "fp8_delayed_scale", "cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",
            "workspace_bytes", "alloc_workspace", "signal_chunk", "write_chunks", "poll_device_error",
            "set_wait_limit", "dtype_code", "masked_streams", "TpmError", "lib"]
@@ -41,6 +43,8 @@ def dtype_code(t: torch.dtype) -> int:
         return BF16
     if t in (torch.uint8, torch.float8_e4m3fn):
         return FP8_E4M3
+    if t == torch.float8_e5m2:
+        return FP8_E5M2
     raise TypeError(f"unsupported dtype {t}")
 
 
@@ -234,6 +238,34 @@ def fp8_delayed_scale(amax_history, scale_out, stream=None):
     """scale_out[0] = max(amax_history) / 448 (1 when all are 0), on the device."""
     return check(lib.tpm_fp8_delayed_scale(_ptr(amax_history), amax_history.numel(), _ptr(scale_out),
                                            _stream(stream)))
+
+
+def cast_fp8(x, dtype, q=None, qt=None, scale_out=None, workspace=None, stream=None):
+    """Current-scaling cast of a bf16 [rows, cols] tensor to fp8 codes (dtype
+    FP8_E4M3 or FP8_E5M2): q [rows, cols] and / or qt [cols, rows] (uint8),
+    scale_out (device fp32) = amax / fmax."""
+    rows, cols = x.shape
+    if workspace is None:
+        workspace = torch.zeros(max(workspace_bytes(OP_CAST_FP8, 0, 0, 0), 1), dtype=torch.uint8, device=x.device)
+    rc = lib.tpm_cast_fp8(rows, cols, _ptr(x), _ld(x), dtype, _ptr(q), _ld(q) if q is not None else 0,
+                          _ptr(qt), _ld(qt) if qt is not None else 0, _ptr(scale_out),
+                          _ptr(workspace), workspace.numel(), _stream(stream))
+    return check(rc)
+
+
+def tp_mlp_bwd_fp8(X, W_up_t, W_down_t, Z_t, H_t, dY, dW_up_t, dW_down_t, dX_t, *, T, rank, scales,
+                   act=ACT_GELU_ERF, workspace=None, stream=None):
+    """fp8 backward: X [M, D] e4m3 codes, W_up_t [D, F/T] and W_down_t [F/T, D]
+    e4m3 codes (the pages' layouts), scales = device fp32 {sX, sWup, sWdown};
+    Z_t, H_t [M, F/T] bf16, dY [M, D] bf16; dW_up_t, dW_down_t (bf16 / fp32),
+    dX_t bf16."""
+    M, D = X.shape
+    Ft = H_t.shape[1]
+    rc = lib.tp_mlp_bwd_fp8(M, D, Ft * T, T, rank, _ptr(X), _ptr(W_up_t), _ptr(W_down_t), _ptr(scales),
+                            _ptr(Z_t), _ptr(H_t), _ptr(dY), act, _ptr(dW_up_t), _ptr(dW_down_t), _ptr(dX_t),
+                            dtype_code(dW_up_t.dtype), _ptr(workspace),
+                            workspace.numel() if workspace is not None else 0, _stream(stream))
+    return check(rc)
 
 
 def partial_reduce_seqshard(partials, out, *, T, rank, M=None, stream=None):

@@ -21,12 +21,12 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 # ---- enums (mirror include/tpmlp.h)
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
 ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
 EPI_FWD, EPI_DACT, EPI_GATED, EPI_DGATED = 0, 1, 2, 3
 OK, EINVAL, EUNSUPPORTED, EHIP, ETIMEOUT, EWORKSPACE = 0, -1, -2, -3, -4, -5
 (OP_SEQ_CHUNK_GEMM, OP_MLP_FWD, OP_MLP_BWD, OP_GATED_MLP_FWD, OP_GATED_MLP_BWD, OP_MX_MLP_FWD,
- OP_FP8_DELAYED_MLP_FWD) = 0, 1, 2, 3, 4, 5, 6
+ OP_FP8_DELAYED_MLP_FWD, OP_MLP_BWD_FP8, OP_CAST_FP8) = 0, 1, 2, 3, 4, 5, 6, 7, 8
 MAX_CHUNKS = 256
 
 _i64, _i32, _u32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
@@ -99,6 +99,14 @@ lib.tp_mlp_fwd_delayed.argtypes = [_i64, _i64, _i64, _i32, _i32,
                                    _vp, _sz, _vp]
 lib.tpm_fp8_delayed_scale.restype = _i32
 lib.tpm_fp8_delayed_scale.argtypes = [_vp, _i32, _vp, _vp]
+lib.tpm_cast_fp8.restype = _i32
+lib.tpm_cast_fp8.argtypes = [_i64, _i64, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp]
+lib.tp_mlp_bwd_fp8.restype = _i32
+lib.tp_mlp_bwd_fp8.argtypes = [_i64, _i64, _i64, _i32, _i32,
+                               _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _i32,
+                               _vp, _vp, _vp, _i32,
+                               _vp, _sz, _vp]
 lib.partial_reduce_seqshard.restype = _i32
 lib.partial_reduce_seqshard.argtypes = [_i32, _i64, _i64, _i32,
                                         _vp, _i64, _i64, _i32,
@@ -120,7 +128,7 @@ lib.tpm_version.argtypes = []
 
 EXPORTS = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "tpm_mx_scales_bytes", "tpm_mx_swizzle_scales",
-           "tp_mlp_fwd_delayed", "tpm_fp8_delayed_scale",
+           "tp_mlp_fwd_delayed", "tpm_fp8_delayed_scale", "tpm_cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",
            "tpm_workspace_bytes", "tpm_signal_chunk", "tpm_write_chunks", "tpm_poll_device_error",
            "tpm_set_wait_limit", "tpm_last_error", "tpm_version"]

@@ -67,7 +67,8 @@ int stream_cus(hipStream_t s) {
 }
 
 int esize(int dt) { return dt == TPM_F32 ? 4 : dt == TPM_BF16 ? 2 : 1; }
-bool valid_dt(int dt) { return dt == TPM_F32 || dt == TPM_BF16 || dt == TPM_FP8_E4M3; }
+bool valid_dt(int dt) { return dt == TPM_F32 || dt == TPM_BF16 || dt == TPM_FP8_E4M3 || dt == TPM_FP8_E5M2; }
+bool is_fp8(int dt) { return dt == TPM_FP8_E4M3 || dt == TPM_FP8_E5M2; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Split-K plan.  A GEMM with fewer output tiles than about three quarters of
@@ -122,7 +123,10 @@ size_t mx_scales_bytes(int64_t rows, int64_t k) { return (size_t)((rows + 31) / 
 int check_gemm(const GemmDesc& g, const char* who) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return fail(TPM_EINVAL, "%s: negative size", who);
   if (g.M > INT32_MAX || g.N > INT32_MAX || g.K > INT32_MAX) return fail(TPM_EUNSUPPORTED, "%s: size >= 2^31", who);
-  if (!valid_dt(g.adt) || g.adt != g.bdt) return fail(TPM_EINVAL, "%s: operand dtypes must match", who);
+  if (!valid_dt(g.adt) || !valid_dt(g.bdt) || (g.adt != g.bdt && !(is_fp8(g.adt) && is_fp8(g.bdt))))
+    return fail(TPM_EINVAL, "%s: operand dtypes must match (or both be fp8)", who);
+  if (g.adt == TPM_FP8_E5M2 && g.bdt == TPM_FP8_E5M2)
+    return fail(TPM_EUNSUPPORTED, "%s: e5m2 x e5m2 is not implemented", who);
   if (g.ydt != TPM_F32 && g.ydt != TPM_BF16 && !(g.ydt == TPM_FP8_E4M3 && (g.y_mx || g.y_qs)))
     return fail(TPM_EINVAL, "%s: output dtype must be F32 or BF16 (or MXFP8)", who);
   if (g.epi < TPM_EPI_FWD || g.epi > TPM_EPI_DGATED) return fail(TPM_EINVAL, "%s: bad epilogue", who);
@@ -179,7 +183,7 @@ int check_gemm(const GemmDesc& g, const char* who) {
     return TPM_OK;
   }
   const int q = g.adt == TPM_BF16 ? 8 : 16;
-  if (g.adt == TPM_FP8_E4M3 && (g.ta || !g.tb))
+  if (is_fp8(g.adt) && (g.ta || !g.tb))
     return fail(TPM_EUNSUPPORTED, "%s: fp8 operands must be stored K-major (trans_a=0, trans_b=1)", who);
   if (g.N % 8 != 0 || g.K % q != 0) return fail(TPM_EUNSUPPORTED, "%s: N %% 8 and K %% %d must be 0", who, q);
   if (g.ldy % 4 != 0 || (g.aux && g.ldaux % 4 != 0)) return fail(TPM_EUNSUPPORTED, "%s: ldy/ldaux %% 4 != 0", who);
@@ -232,6 +236,7 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   p.a_bytes = g.K == 0 ? 0u : (uint32_t)(a_rows * g.lda * esize(g.adt));
   p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
   p.a_mx = g.a_mx; p.b_mx = g.b_mx; p.y_mx = g.y_mx; p.y_q_scale = g.y_qs;
+  p.f8fmt = (g.adt == TPM_FP8_E5M2 ? 1 : 0) | (g.bdt == TPM_FP8_E5M2 ? 2 : 0);
   p.mx_steps = (int)(g.K / 128);
   p.y_mx_steps = (int)(g.N / 128);
   p.a_mx_bytes = g.a_mx ? (uint32_t)mx_scales_bytes(g.M, g.K) : 0u;
@@ -312,6 +317,19 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       return kCtrlBytes + partial_bytes(M, D, plan_splits(M, D, Ft, T, TPM_FP8_E4M3));
+    }
+    case TPM_OP_CAST_FP8:
+      return kCtrlBytes;
+    case TPM_OP_MLP_BWD_FP8: {
+      if (T <= 0) return 0;
+      const int64_t D = N, Ft = K / T;
+      const int f8 = TPM_FP8_E4M3;
+      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, 1, f8));
+      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, f8)));
+      part = std::max(part, partial_bytes(D, Ft, plan_splits(D, Ft, M, 1, f8)));
+      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, f8)));
+      const size_t md = round_up((size_t)M * (size_t)D, 256), mf = round_up((size_t)M * (size_t)Ft, 256);
+      return kCtrlBytes + 3 * md + 2 * mf + 3 * mf + part;   // dY8, dY8^T, X8^T; dZ (bf16); dZ8, dZ8^T, H8^T
     }
     case TPM_OP_GATED_MLP_FWD: {
       if (T <= 0) return 0;
@@ -560,6 +578,106 @@ int tpm_mx_swizzle_scales(int64_t rows, int64_t k, const uint8_t* src, int64_t l
   if (!src || !dst || ld < k / 32) return fail(TPM_EINVAL, "%s: null pointer or ld < k/32", who);
   hipError_t e = launch_mx_swizzle(src, ld, (int)rows, (int)(k / 32), dst, (hipStream_t)stream);
   return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+// control words of the fp8 backward (after the per-group counters)
+constexpr int kCtrlF8 = kCtrlWords + 4;
+static_assert((kCtrlF8 + 8) * 4 <= (int)kCtrlBytes, "control block");
+
+int tpm_cast_fp8(int64_t rows, int64_t cols, const void* x, int64_t ld, int dtype,
+                 void* q, int64_t ldq, void* qt, int64_t ldqt, float* scale_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tpm_cast_fp8";
+  if (dtype != TPM_FP8_E4M3 && dtype != TPM_FP8_E5M2) return fail(TPM_EINVAL, "%s: dtype must be fp8", who);
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0)
+    return fail(TPM_EUNSUPPORTED, "%s: rows and cols must be multiples of 16", who);
+  if (!workspace || workspace_bytes < kCtrlBytes) return fail(TPM_EWORKSPACE, "%s: workspace required", who);
+  if (rows == 0 || cols == 0) return TPM_OK;
+  if (!x || ld < cols || ld % 8 != 0 || !aligned16(x)) return fail(TPM_EINVAL, "%s: x, ld", who);
+  if ((q && (ldq < cols || ldq % 16 != 0 || !aligned16(q))) || (qt && (ldqt < rows || ldqt % 16 != 0 || !aligned16(qt))))
+    return fail(TPM_EINVAL, "%s: output leading dimensions / alignment", who);
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* amax = (uint32_t*)workspace + kCtrlF8;
+  hipError_t e = launch_ctrl_init(amax, 1, s);
+  if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)x, rows, cols, ld, amax, s);
+  if (e == hipSuccess)
+    e = launch_cast_fp8_t((const uint16_t*)x, rows, cols, ld, (const float*)amax, dtype == TPM_FP8_E5M2,
+                          (uint8_t*)q, ldq, (uint8_t*)qt, ldqt, scale_out, s);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+}
+
+int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
+                   const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
+                   const void* Z_t, const void* H_t, const void* dY, int act,
+                   void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_mlp_bwd_fp8";
+  if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
+  if (M < 0 || D < 0 || F < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (F % T != 0 || M % T != 0) return fail(TPM_EINVAL, "%s: F %% T or M %% T != 0", who);
+  const int64_t Ft = F / T;
+  if (M % 16 != 0 || D % 16 != 0 || Ft % 16 != 0) return fail(TPM_EUNSUPPORTED, "%s: M, D, F/T multiples of 16", who);
+  if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
+  if (!X || !W_up_t || !W_down_t || !scales || !Z_t || !H_t || !dY || !dW_up_t || !dW_down_t || !dX_t)
+    return fail(TPM_EINVAL, "%s: null pointer", who);
+  const size_t need = tpm_workspace_bytes(TPM_OP_MLP_BWD_FP8, M, D, F, T, 1, TPM_FP8_E4M3);
+  if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  if (!aligned16(dY) || !aligned16(H_t)) return fail(TPM_EUNSUPPORTED, "%s: dY, H_t must be 16-byte aligned", who);
+  uint32_t* ctrl = (uint32_t*)workspace;
+  float* cw = (float*)(ctrl + kCtrlF8);   // amax dY, s dY, amax dZ, s dZ, amax H, s H
+  const size_t md = round_up((size_t)M * (size_t)D, 256), mf = round_up((size_t)M * (size_t)Ft, 256);
+  char* w = (char*)workspace + kCtrlBytes;
+  uint8_t* dy8 = (uint8_t*)w;              w += md;
+  uint8_t* dy8t = (uint8_t*)w;             w += md;
+  uint8_t* x8t = (uint8_t*)w;              w += md;
+  uint16_t* dz = (uint16_t*)w;             w += 2 * mf;
+  uint8_t* dz8 = (uint8_t*)w;              w += mf;
+  uint8_t* dz8t = (uint8_t*)w;             w += mf;
+  uint8_t* h8t = (uint8_t*)w;              w += mf;
+  float* part = (float*)w;
+  const size_t part_bytes = workspace_bytes - (size_t)(w - (char*)workspace);
+  const int e4 = TPM_FP8_E4M3, e5 = TPM_FP8_E5M2;
+  // dZ = (dY8 . W_down^T) * act'(Z), bf16, amax   W_down_t [Ft, D]: stored [N=Ft, K=D]
+  GemmDesc g_dz{M, Ft, D, dy8, D, false, e5, cw + 1, W_down_t, D, true, e4, scales + 2,
+                dz, Ft, TPM_BF16, TPM_EPI_DACT, act, const_cast<void*>(Z_t), Ft, cw + 2,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  // dW_down = H^T . dY:  A = H8^T [Ft, M], B stored [N=D, K=M] = dY8^T
+  GemmDesc g_wd{Ft, D, M, h8t, M, false, e4, cw + 5, dy8t, M, true, e5, cw + 1,
+                dW_down_t, D, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  // dW_up = X^T . dZ:  A = X8^T [D, M], B stored [N=Ft, K=M] = dZ8^T
+  GemmDesc g_wu{D, Ft, M, x8t, M, false, e4, scales + 0, dz8t, M, true, e5, cw + 3,
+                dW_up_t, Ft, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  // dX = dZ . W_up^T:  A = dZ8 [M, Ft], B stored [N=D, K=Ft] = W_up_t [D, Ft]
+  GemmDesc g_dx{M, D, Ft, dz8, Ft, false, e5, cw + 3, W_up_t, Ft, true, e4, scales + 1,
+                dX_t, D, TPM_BF16, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  for (GemmDesc* g : {&g_dz, &g_wd, &g_wu, &g_dx}) {
+    g->part = part;
+    g->part_bytes = part_bytes;
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  if (M == 0 || D == 0 || Ft == 0) return TPM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_ctrl_init(ctrl, kCtrlF8 + 8, s);
+  // gradient and activation casts: dY -> e5m2 (+ transpose), H -> e4m3 transposed, X transposed
+  if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)dY, M, D, D, (uint32_t*)(cw + 0), s);
+  if (e == hipSuccess) e = launch_cast_fp8_t((const uint16_t*)dY, M, D, D, cw + 0, true, dy8, D, dy8t, M, cw + 1, s);
+  if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)H_t, M, Ft, Ft, (uint32_t*)(cw + 4), s);
+  if (e == hipSuccess) e = launch_cast_fp8_t((const uint16_t*)H_t, M, Ft, Ft, cw + 4, false, nullptr, 0, h8t, M, cw + 5, s);
+  if (e == hipSuccess) e = launch_transpose_u8((const uint8_t*)X, M, D, D, x8t, M, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  int rc = run_gemm(g_dz, s, who);
+  if (rc != TPM_OK) return rc;
+  e = launch_cast_fp8_t(dz, M, Ft, Ft, cw + 2, true, dz8, Ft, dz8t, M, cw + 3, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  for (const GemmDesc* g : {&g_wd, &g_wu, &g_dx}) {
+    rc = run_gemm(*g, s, who);
+    if (rc != TPM_OK) return rc;
+  }
+  return TPM_OK;
 }
 
 int tpm_fp8_delayed_scale(const float* amax_history, int n, float* scale_out, void* stream) {

@@ -376,8 +376,11 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
   }
 }
 
-template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false>
+template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false, int F8F = 0>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
+  // fp8 formats of the MFMA operands (0 e4m3, 1 e5m2): the first operand
+  // is the B fragment, the second the A fragment
+  constexpr int FMT0 = (F8F >> 1) & 1, FMT1 = F8F & 1;
   static_assert(!GATED || (!FP8 && !BKM && NW == 8), "gated: bf16, MN-major B, 8 waves (two N fragments)");
   static_assert(!MX || (FP8 && AK && BKM), "MXFP8: fp8 operands stored K-major");
   using LY = Layout<NW>;
@@ -529,8 +532,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
             acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0,
                                                                               OPS, sb_cur[j], OPS, sa_cur[I0 + ii]);
           else if constexpr (FP8)
-            acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0,
-                                                                              0, 0, 0, 0);
+            acc[I0 + ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[I0 + ii], acc[I0 + ii][j], FMT0,
+                                                                              FMT1, 0, 0, 0, 0);
           else
             acc[I0 + ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0, 0);
           static_for<NR>([&](auto rc) {
@@ -833,7 +836,10 @@ hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {
   if (!a_kmajor || !b_kmajor) return hipErrorInvalidValue;  // rejected on the host first
   if (p.a_mx) gemm_kernel<true, true, true, kWaves8, false, true><<<grid, kThreads8, 0, s>>>(p);
-  else gemm_kernel<true, true, true, kWaves8><<<grid, kThreads8, 0, s>>>(p);
+  else if (p.f8fmt == 1) gemm_kernel<true, true, true, kWaves8, false, false, 1><<<grid, kThreads8, 0, s>>>(p);
+  else if (p.f8fmt == 2) gemm_kernel<true, true, true, kWaves8, false, false, 2><<<grid, kThreads8, 0, s>>>(p);
+  else if (p.f8fmt == 0) gemm_kernel<true, true, true, kWaves8><<<grid, kThreads8, 0, s>>>(p);
+  else return hipErrorInvalidValue;  // both operands e5m2: rejected on the host first
   return finalize_if_split(p, s);
 }
 

@@ -96,6 +96,102 @@ __global__ void __launch_bounds__(256) quant_e4m3(const uint16_t* __restrict__ h
   }
 }
 
+// ------------------------------------------- fp8 backward: amax, casts
+// max |x| of a bf16 [rows, cols] matrix into *out (fp32 bits as uint32,
+// non-negative floats order as integers; *out zeroed beforehand)
+__global__ void __launch_bounds__(256) amax_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t c8, int64_t ld,
+                                                 uint32_t* out) {
+  float m = 0.f;
+  const int64_t total = rows * c8;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / c8, c = (v - r * c8) * 8;
+    const i32x4 w = *(const i32x4*)(x + r * ld + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] & 0xFFFFu))));
+      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] >> 16))));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+}
+
+// Current-scaling cast of a bf16 [rows, cols] matrix to fp8 (e4m3 or e5m2,
+// largest value fmax): inv = fp32(fmax / amax), s = fp32(amax / fmax) (both 1
+// when amax = 0), code = fp8(fp32(x * inv)).  Writes the codes row-major (q)
+// and / or transposed (qt, [cols, rows]), 64 x 64 tiles through LDS.
+template <bool E5M2>
+__global__ void __launch_bounds__(256) cast_fp8_t(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                  const float* __restrict__ amax_p, float fmax, uint8_t* __restrict__ q,
+                                                  int64_t ldq, uint8_t* __restrict__ qt, int64_t ldqt, float* s_out) {
+  __shared__ uint8_t tile[64][64 + 16];
+  const float amax = *amax_p;
+  const float inv = amax > 0.f ? fmax / amax : 1.0f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && s_out) *s_out = amax > 0.f ? amax / fmax : 1.0f;
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  {
+    const int r = t >> 2, cg = (t & 3) * 16;
+    const int64_t row = r0 + r, col = c0 + cg;
+    if (row < rows && col < cols) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const i32x4 v = *(const i32x4*)(x + row * ld + col + 8 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u = (uint32_t)v[e];
+          const float a = bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv, b = bf16_to_f32((uint16_t)(u >> 16)) * inv;
+          const uint32_t ca = E5M2 ? f32_to_e5m2_rne_sat(a) : f32_to_e4m3_rne_sat(a);
+          const uint32_t cb = E5M2 ? f32_to_e5m2_rne_sat(b) : f32_to_e4m3_rne_sat(b);
+          const int k = 4 * h + e;  // pair index 0..7 -> bytes 2k, 2k+1
+          if (k % 2 == 0) w[k / 2] = ca | (cb << 8);
+          else w[k / 2] |= (ca << 16) | (cb << 24);
+        }
+      }
+      if (q) *(uint4*)(q + row * ldq + col) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[r][cg + i] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
+    }
+  }
+  if (!qt) return;
+  __syncthreads();
+  const int oc = t >> 2, rg = (t & 3) * 16;      // source column oc, source rows rg .. rg+15
+  const int64_t col = c0 + oc, row = r0 + rg;
+  if (col < cols && row < rows) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i / 4] |= (uint32_t)tile[rg + i][oc] << (8 * (i % 4));
+    *(uint4*)(qt + col * ldqt + row) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Byte transpose [rows, cols] -> [cols, rows] (fp8 codes), 64 x 64 tiles.
+__global__ void __launch_bounds__(256) transpose_u8(const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+                                                    uint8_t* __restrict__ y, int64_t ldy) {
+  __shared__ uint8_t tile[64][64 + 16];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  {
+    const int r = t >> 2, cg = (t & 3) * 16;
+    if (r0 + r < rows && c0 + cg < cols) {
+      const uint4 v = *(const uint4*)(x + (r0 + r) * ld + c0 + cg);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[r][cg + i] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
+    }
+  }
+  __syncthreads();
+  const int oc = t >> 2, rg = (t & 3) * 16;
+  if (c0 + oc < cols && r0 + rg < rows) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i / 4] |= (uint32_t)tile[rg + i][oc] << (8 * (i % 4));
+    *(uint4*)(y + (c0 + oc) * ldy + r0 + rg) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ------------------------------------------------------ chunk writer
 // Side-stream writer of sequence-chunk arrival: for each chunk of the list,
 // in list order, every work-group copies its share of the chunk (16-byte
@@ -261,6 +357,27 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
                              int64_t ldq, float* s_out, hipStream_t s) {
   const int64_t work = M * (N / 8);
   quant_e4m3<<<grid_for(work, 256), 256, 0, s>>>(h, M, N / 8, ldh, amax, q, ldq, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* out, hipStream_t s) {
+  const int64_t work = rows * (cols / 8);
+  amax_bf16<<<grid_for(work, 256), 256, 0, s>>>(x, rows, cols / 8, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_fp8_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* amax, bool e5m2,
+                             uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s_out, hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (e5m2) cast_fp8_t<true><<<grid, 256, 0, s>>>(x, rows, cols, ld, amax, 57344.0f, q, ldq, qt, ldqt, s_out);
+  else cast_fp8_t<false><<<grid, 256, 0, s>>>(x, rows, cols, ld, amax, 448.0f, q, ldq, qt, ldqt, s_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_u8(const uint8_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* y, int64_t ldy,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  transpose_u8<<<grid, 256, 0, s>>>(x, rows, cols, ld, y, ldy);
   return hipGetLastError();
 }
 

@@ -85,6 +85,42 @@ __device__ inline uint8_t f32_to_e4m3_rne_sat(float f) {
   return (uint8_t)(sign | code);
 }
 
+// OCP e5m2 encode of an fp32 value: nearest, ties to even, saturating to
+// +-57344 (1.75 * 2^15, fp32 bits 0x47600000: every larger finite value,
+// and inf, rounds past it), NaN -> 0x7F, sign kept for zero.
+__device__ inline uint8_t f32_to_e5m2_rne_sat(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7F;
+  if (a >= 0x47600000u) return (uint8_t)(sign | 0x7B);
+  int e = (int)(a >> 23) - 127;
+  uint8_t code;
+  if (e >= -14) {
+    // normal e5m2: keep 2 mantissa bits, round the 21 dropped bits
+    uint32_t mant = a & 0x7FFFFFu;
+    uint32_t keep = mant >> 21;
+    uint32_t rest = mant & 0x1FFFFFu;
+    uint32_t half = 0x100000u;
+    uint32_t q = ((uint32_t)(e + 15) << 2) | keep;
+    if (rest > half || (rest == half && (keep & 1u))) q += 1;  // may carry into exponent
+    if (q > 0x7B) q = 0x7B;
+    code = (uint8_t)q;
+  } else {
+    // subnormal e5m2: value = m * 2^-16, m in 0..3 (m = 4 is the smallest
+    // normal, code 0x04).  x / 2^-16 = significand * 2^(e + 16 - 23).
+    if (e < -17) return (uint8_t)sign;           // below half the smallest subnormal
+    uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;
+    int shift = 7 - e;                           // 22 .. 24
+    uint32_t m = sig >> shift;
+    uint32_t rest = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rest > half || (rest == half && (m & 1u))) m += 1;
+    code = (uint8_t)m;
+  }
+  return (uint8_t)(sign | code);
+}
+
 // ------------------------------------------------------------ activations
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
 

@@ -44,6 +44,7 @@ struct GemmParams {
   uint8_t* y_mx;
   int y_mx_steps;
   const float* y_q_scale;    // fp8 per-tensor output: Y = e4m3(v / *y_q_scale) (or null)
+  int f8fmt;                 // fp8 operand formats: bit 0 A is e5m2, bit 1 B is e5m2 (else e4m3)
   int gu_off;                // gated epilogues: column offset of the up half in B / aux / Y (= N)
   int bn_out;                // output columns per tile (256; 128 for EPI_GATED)
   int16_t order[kMaxGroups];
@@ -78,6 +79,11 @@ struct WriterParams {
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_delayed_scale(const float* history, int n, float* scale_out, hipStream_t s);
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* out, hipStream_t s);
+hipError_t launch_cast_fp8_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* amax, bool e5m2,
+                             uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* s_out, hipStream_t s);
+hipError_t launch_transpose_u8(const uint8_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* y, int64_t ldy,
+                               hipStream_t s);
 hipError_t launch_mx_swizzle(const uint8_t* src, int64_t ld, int rows, int kblocks, uint8_t* dst, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
 hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s);

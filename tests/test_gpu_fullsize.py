@@ -14,7 +14,7 @@ import sequence_transformer_gemms_amd as tpm
 from sequence_transformer_gemms_amd import _abi
 import synthetic_inputs as si
 from oracle import formats, ops
-from tests._util import TOL, assert_mx_close, f64, nerr
+from tests._util import TOL, assert_mx_close, bf16_either, f64, nerr
 
 pytestmark = pytest.mark.gpu
 
@@ -28,16 +28,6 @@ def pick(n, k, seed):
     g = np.random.default_rng(seed)
     idx = set(g.choice(n, size=k - 2, replace=False).tolist()) | {0, n - 1}
     return np.array(sorted(idx))
-
-
-def bf16_either(v, rel=2.0 ** -16):
-    """(round_bf16(v), d): d is |other bf16 candidate - rounded| where v lies
-    within a relative distance `rel` of a rounding boundary (an fp32
-    evaluation may round it the other way), else 0."""
-    rb = formats.round_bf16(v)
-    lo, hi = formats.round_bf16(v * (1 - rel)), formats.round_bf16(v * (1 + rel))
-    other = np.where(lo != rb, lo, hi)
-    return rb, np.abs(other - rb)
 
 
 def host64(t):

@@ -8,6 +8,7 @@ import torch
 
 import synthetic_inputs as si
 from oracle import formats, ops
+from tests import _util
 from tests._util import TOL, assert_mx_close, f64, nerr
 
 pytestmark = pytest.mark.gpu
@@ -564,6 +565,97 @@ def test_mlp_fwd_mx_small():
     delta = dz * np.abs(ops.act_grad(ref["Z"], ops.ACT_GELU_ERF)) + 2.0 ** -20 * np.abs(ref["H"]) + 1e-30
     assert_mx_close(hc, he, ref["H"], delta)
     assert nerr(P, ref["P"]) <= TOL["fp8"]
+
+
+# --------------------------------------------------------------- fp8 backward
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_cast_fp8_bit_exact(dt):
+    # current-scaling cast, row-major and transposed codes: ragged 64x64 tiles
+    rows, cols = 96, 160
+    x = si.to_bf16(si.normal_f32((rows, cols), 131) * np.float32(7.0))
+    X = x.cuda()
+    code = _abi.FP8_E5M2 if dt == "e5m2" else _abi.FP8_E4M3
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.cast_fp8(X, code, q=q, qt=qt, scale_out=sc)
+    sync()
+    xv = f64(x)
+    fmax = np.float32(57344.0 if dt == "e5m2" else 448.0)
+    amax = np.float32(np.max(np.abs(xv)))
+    inv = np.float32(fmax / amax)
+    prod = (xv * float(inv)).astype(np.float32).astype(np.float64)
+    want = formats.e5m2_encode(prod) if dt == "e5m2" else formats.e4m3_encode(prod)
+    assert np.array_equal(q.cpu().numpy(), want)
+    assert np.array_equal(qt.cpu().numpy(), want.T)
+    assert sc.item() == float(np.float32(amax / fmax))
+
+
+def test_fp8_mixed_format_gemm_integer_exact():
+    # e5m2 x e4m3 and e4m3 x e5m2 through seq_chunk_gemm: integers in [-3, 3]
+    # are exact in both formats, so the fp32 products are exact
+    M, N, K = 200, 136, 512
+    a, b = si.small_ints((M, K), 132), si.small_ints((N, K), 133)
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    e5 = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e5m2).cuda()
+    e4 = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn).cuda()
+    for A, B in ((e5(a), e4(b)), (e4(a), e5(b))):
+        Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        tpm.seq_chunk_gemm(A, B, Y, trans_b=True)
+        sync()
+        assert np.array_equal(f64(Y), ref)
+
+
+def test_mlp_bwd_fp8_small():
+    M, D, F, T = 512, 512, 2048, 4
+    Ft = F // T
+    xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 1))
+    wuq, su = si.to_e4m3_current(si.normal_f32((D, Ft), 2, 0.02))      # the pages' layouts
+    wdq, sd = si.to_e4m3_current(si.normal_f32((Ft, D), 3, 0.02))
+    z = si.to_bf16(si.normal_f32((M, Ft), 134))
+    h = si.to_bf16(np.abs(si.normal_f32((M, Ft), 135)))
+    dy = si.to_bf16(si.normal_f32((M, D), 136))
+    scales = dev_f32(np.array([sx, su, sd], np.float32))
+    dWu = torch.empty(D, Ft, dtype=torch.bfloat16, device="cuda")
+    dWd = torch.empty(Ft, D, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_MLP_BWD_FP8, M, D, F, T, 1, _abi.FP8_E4M3)
+    tpm.tp_mlp_bwd_fp8(xq.cuda(), wuq.cuda(), wdq.cuda(), z.cuda(), h.cuda(), dy.cuda(), dWu, dWd, dX, T=T, rank=0,
+                       scales=scales, act=_abi.ACT_GELU_ERF, workspace=ws)
+    sync()
+    # the oracle's H codes: the forward's current-scaling cast of the same bf16 H
+    hv = f64(h)
+    amax_h = np.float32(np.max(np.abs(hv)))
+    h8 = formats.e4m3_to_f64(formats.e4m3_encode((hv * float(np.float32(np.float32(448) / amax_h))).astype(np.float32)))
+    sh = float(np.float32(amax_h / np.float32(448)))
+    r = ops.tp_mlp_bwd_fp8(f64(xq), sx, f64(wuq), su, f64(wdq), sd, f64(z), h8, sh, f64(dy), ops.ACT_GELU_ERF)
+    # dY's e5m2 codes are bit-exact (the same fp32 arithmetic on the same bf16 values)
+    dy8 = ws[2048:2048 + M * D].cpu().numpy().reshape(M, D)
+    assert np.array_equal(formats.e5m2_to_f64(dy8), r["dYq"])
+    off = 2048 + 3 * ((M * D + 255) // 256 * 256)
+    dz = ws[off:off + 2 * M * Ft].view(torch.bfloat16).view(M, Ft)
+    assert nerr(dz, r["dZ"]) <= TOL["bf16"]
+    assert nerr(dWd, r["dW_down"]) <= TOL["fp8"]
+    # dZ's e5m2 codes step by 2^-2 of a value: where the oracle's fp64 dZ
+    # lies within fp32 evaluation error of a bf16 or e5m2 rounding boundary
+    # the GPU's code may be the neighbour, and one such code moves a
+    # 512-token weight gradient by more than the fp8 tolerance.  The bound
+    # adds that code step, times the other operand, where it can occur.
+    inv = np.float32(np.float32(57344.0) / np.float32(r["amax_dZ"]))
+    g = ops.act_grad(f64(z), ops.ACT_GELU_ERF)
+    v = r["dH"] * g
+    # fp32 evaluation error of dZ: D products accumulated (D ulps of their
+    # absolute sum at most), then act' and one product
+    ddh = D * 2.0 ** -24 * (np.abs(r["dYq"]) @ np.abs(f64(wdq)).T) * r["s_dY"] * float(np.float32(sd))
+    q, amb = _util.e5m2_cast_ambiguity(v, ddh * np.abs(g) + 2.0 ** -20 * np.abs(v), inv)
+    assert np.array_equal(q, r["dZq"])
+    s_dz = r["s_dZ"]
+    Xd, Wud = f64(xq) * float(np.float32(sx)), f64(wuq) * float(np.float32(su))
+    tol_u = TOL["fp8"] * (1 + np.abs(r["dW_up"])) + np.abs(Xd).T @ amb * s_dz
+    assert np.all(np.abs(f64(dWu) - r["dW_up"]) <= tol_u)
+    tol_x = TOL["fp8"] * (1 + np.abs(r["dX"])) + amb @ np.abs(Wud).T * s_dz
+    assert np.all(np.abs(f64(dX) - r["dX"]) <= tol_x)
+    assert np.mean(amb > 0) < 0.05
 
 
 # -------------------------------------------------------- fp8 delayed scaling

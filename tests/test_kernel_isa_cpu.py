@@ -58,7 +58,7 @@ def kernels(text):
 
 def test_every_gemm_variant_is_compiled(asm):
     bodies, meta = kernels(asm)
-    assert len(bodies) == 7          # 4 bf16 operand layouts + gated + fp8 + MXFP8
+    assert len(bodies) == 9          # 4 bf16 operand layouts + gated + fp8 (3 format pairs) + MXFP8
     assert set(meta) == set(bodies)
 
 
