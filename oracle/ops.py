@@ -355,6 +355,23 @@ def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None):
     return dict(dH=dh, dZ=dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
 
 
+def linear_bwd(x, w, dy):
+    """Backward of one sharded linear layer Y = X . W ([TSP] "Derive
+    column-parallel linear algebra" and "Derive row-parallel linear
+    algebra"; the attention projections of [TSP] "Pair adjacent transformer
+    projections" are such layers):
+        dW = X^T . dY      (same shape as W, [K, N])
+        dX = dY . W^T      ([M, K]; for a column-parallel W it is a full
+                            partial summed across ranks, for a row-parallel
+                            W the rank's shard of the input gradient)
+    The two products read the same dY and are independent of each other."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    assert x.shape[1] == w.shape[0] and dy.shape == (x.shape[0], w.shape[1]), (x.shape, w.shape, dy.shape)
+    return dict(dW=gemm(x.T, dy), dX=gemm(dy, w.T))
+
+
 # ------------------------------------------------------- gated MLP share
 def gated_mlp_fwd(x, w_gate_t, w_up_t, w_down_t, act=ACT_SILU, store=None):
     """One rank's share of the gated MLP of [WE]:

@@ -605,3 +605,54 @@ def test_store_bf16_rounds_only_the_consumed_intermediate():
     r = ops.tp_mlp_bwd(x, wu, wd, a["Z"], a["H"], dy, ops.ACT_GELU_ERF, store="bf16")
     assert np.array_equal(r["dW_up"], x.T @ formats.round_bf16(r["dZ"]))
     assert np.array_equal(r["dW_down"], a["H"].T @ dy)
+
+
+def test_linear_bwd_by_finite_differences_and_brute_force():
+    # O8 pinned: the gradients of L = <G, X.W> (forward by correctly rounded
+    # brute force) in X and W, and the two products against brute force
+    M, K, N = 5, 7, 3
+    g = np.random.default_rng(31)
+    x, w, G = g.standard_normal((M, K)), g.standard_normal((K, N)), g.standard_normal((M, N))
+    bw = ops.linear_bwd(x, w, G)
+    assert bw["dW"].shape == w.shape and bw["dX"].shape == x.shape                   # I7
+
+    def loss(x_, w_):
+        y = np.array(brute.matmul(brute.to_lists(x_), brute.to_lists(w_)))
+        return float(np.sum(G * y))
+
+    eps = 1e-6
+    for name, arr, grad in (("X", x, bw["dX"]), ("W", w, bw["dW"])):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            fd[idx] = ((loss(ap, w) - loss(am, w)) if name == "X" else (loss(x, ap) - loss(x, am))) / (2 * eps)
+        assert np.max(np.abs(fd - grad)) <= 1e-7 * (1 + np.max(np.abs(grad))), name
+    tl = brute.to_lists
+    assert np.allclose(bw["dW"], brute.matmul(brute.transpose(tl(x)), tl(G)), rtol=1e-13, atol=1e-13)
+    assert np.allclose(bw["dX"], brute.matmul(tl(G), brute.transpose(tl(w))), rtol=1e-13, atol=1e-13)
+
+
+def test_linear_bwd_shard_invariants():
+    # I4/I5 for a column-parallel layer (W split by columns, dY_t its columns):
+    # dW_t is column block t of the unsharded dW, and the dX_t sum to the
+    # unsharded dX; I6 for a row-parallel layer (W split by rows, X_t the
+    # matching columns of X, dY whole): dW_t is row block t and dX_t is
+    # column block t of the unsharded gradients.  Integer inputs: exact.
+    M, K, N, T = 6, 8, 12, 4
+    g = np.random.default_rng(32)
+    x = g.integers(-3, 4, (M, K)).astype(np.float64)
+    w = g.integers(-3, 4, (K, N)).astype(np.float64)
+    dy = g.integers(-3, 4, (M, N)).astype(np.float64)
+    un = ops.linear_bwd(x, w, dy)
+    dx_sum = np.zeros_like(x)
+    for t in range(T):
+        b = ops.linear_bwd(x, ops.col_block(w, T, t), ops.col_block(dy, T, t))
+        assert np.array_equal(b["dW"], ops.col_block(un["dW"], T, t))
+        dx_sum += b["dX"]
+    assert np.array_equal(dx_sum, un["dX"])
+    for t in range(T):
+        b = ops.linear_bwd(ops.col_block(x, T, t), ops.row_block(w, T, t), dy)
+        assert np.array_equal(b["dW"], ops.row_block(un["dW"], T, t))
+        assert np.array_equal(b["dX"], ops.col_block(un["dX"], T, t))
