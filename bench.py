@@ -107,6 +107,9 @@ class Layer:
         shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1)]
         self.ws_g = torch.zeros(max(tpm.workspace_bytes(tpm.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
                                 dtype=torch.uint8, device=dev)
+        # and one for the paired backward launches of the two projections
+        self.ws_l = torch.zeros(max(tpm.workspace_bytes(tpm.OP_LINEAR_BWD, M, n, k) for n, k in ((D, Da), (Nq, D))),
+                                dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.counters = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.order = si.ring_chunk_order(T, self.C, rank)
@@ -189,8 +192,13 @@ class Layer:
             self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
         self._check(self.ws_bwd, check)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
-        # ---- backward, O projection: dA = dY_o W_o^T (chunk-fed), dW_o = A^T dY_o
-        b = self._boundary()
+        # ---- backward, O projection: dA = dY_o W_o^T, dW_o = A^T dY_o.  All of
+        # dY_o resident: one paired launch (tp_linear_bwd); with dY_o's rows
+        # arriving: dA chunk-fed, then dW_o (which needs every row)
+        if not arrive:
+            self._timed(lambda: tpm.tp_linear_bwd(self.attn, self.w_o, self.dy_o, self.g_o, self.d_attn,
+                                                  workspace=self.ws_l), record)
+        b = self._boundary() if arrive else None
 
         def o_bwd_dgrad():
             tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
@@ -198,22 +206,19 @@ class Layer:
 
         def o_bwd_wgrad():
             tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg)
-        if check:
+        if arrive and check:
             o_bwd_dgrad()
-            if arrive:
-                self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
+            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
             self._check(wsg, check)
             o_bwd_wgrad()
-        else:
+        elif arrive:
             self._timed(lambda: (o_bwd_dgrad(), o_bwd_wgrad()), record)
-            if arrive:
-                self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
+            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
 
-        # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T (partial)
-        def qkv_bwd():
-            tpm.seq_chunk_gemm(self.x_qkv, self.dy_qkv, self.g_qkv, trans_a=True, workspace=wsg)
-            tpm.seq_chunk_gemm(self.dy_qkv, self.w_qkv, own_slot, trans_b=True, workspace=wsg)
-        self._timed(qkv_bwd, record)
+        # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T
+        # (partial), one paired launch
+        self._timed(lambda: tpm.tp_linear_bwd(self.x_qkv, self.w_qkv, self.dy_qkv, self.g_qkv, own_slot,
+                                              workspace=self.ws_l), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
         if arrive:
             done = torch.cuda.Event()

@@ -76,7 +76,7 @@ typedef enum {
 typedef enum {
   TPM_OP_SEQ_CHUNK_GEMM = 0, TPM_OP_MLP_FWD = 1, TPM_OP_MLP_BWD = 2,
   TPM_OP_GATED_MLP_FWD = 3, TPM_OP_GATED_MLP_BWD = 4, TPM_OP_MX_MLP_FWD = 5, TPM_OP_FP8_DELAYED_MLP_FWD = 6,
-  TPM_OP_MLP_BWD_FP8 = 7, TPM_OP_CAST_FP8 = 8
+  TPM_OP_MLP_BWD_FP8 = 7, TPM_OP_CAST_FP8 = 8, TPM_OP_LINEAR_BWD = 9
 } tpm_op;
 
 #define TPM_MAX_CHUNKS 256
@@ -186,6 +186,39 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
                void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
                int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_linear_bwd -- backward of one sharded linear layer Y = X . W ("Tensor
+ * and sequence parallelism", sections "Derive column-parallel linear
+ * algebra" and "Derive row-parallel linear algebra"; the attention
+ * projections of section "Pair adjacent transformer projections" are such
+ * layers: W_qkv,t column-parallel, W_o,t row-parallel):
+ *
+ *   dW = X^T . dY     [K, N]   (the rank's weight gradient, W's shape)
+ *   dX = dY . W^T     [M, K]   (column-parallel W: a full partial summed
+ *                              across ranks; row-parallel W: the rank's
+ *                              shard of the input gradient)
+ *
+ * X [M, K], W [K, N] (the shard as the rank stores it), dY [M, N]: dense
+ * row-major device arrays, 16-byte aligned, dtype BF16 (M, N, K multiples
+ * of 8: every operand row is whole 16-byte chunks) or F32.  dW in
+ * dw_dtype (BF16 or F32; F32 only with dtype F32), dX in dtype.  The two
+ * products read the same dY and are independent; for BF16 they run as one
+ * launch whose work-groups take tiles of either product from per-XCD
+ * queues, so that narrow shards (few output tiles each) fill the chip
+ * together, and split-K is used only where one product's tiles are much
+ * longer than the other's.  Results do not depend on which work-group
+ * computes a tile.  Caller-owned device workspace of
+ * >= tpm_workspace_bytes(TPM_OP_LINEAR_BWD, M, N, K, 1, 1, dtype) bytes
+ * (control words and split-K partial sums).  Errors: TPM_EINVAL (null
+ * pointer, negative size, bad dtype), TPM_EWORKSPACE (workspace too small),
+ * TPM_EUNSUPPORTED (misaligned operand or size, operand >= 4 GiB); nothing is
+ * enqueued on error.  Asynchronous on `stream`.
+ */
+int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
+                  const void* X, const void* W, const void* dY, int dtype,
+                  void* dW, void* dX, int dw_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * partial_reduce_seqshard -- the arithmetic a rank performs in the
@@ -373,7 +406,8 @@ int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
 
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
  * TPM_OP_MLP_BWD and the gated forms pass (M, N = D, K = F, T); for
- * TPM_OP_SEQ_CHUNK_GEMM the sizes are (M, N, K) and T is ignored. */
+ * TPM_OP_SEQ_CHUNK_GEMM and TPM_OP_LINEAR_BWD the sizes are (M, N, K)
+ * and T is ignored. */
 size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int num_chunks, int dtype);
 
 /* Enqueue on `stream` a release store of `value` into the device word

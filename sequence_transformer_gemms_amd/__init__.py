@@ -23,12 +23,12 @@ import torch
 
 from . import _abi
 from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF16, EPI_DACT,  # noqa: F401
-                   EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, FP8_E5M2, OP_CAST_FP8, OP_FP8_DELAYED_MLP_FWD,
+                   EPI_DGATED, EPI_FWD, EPI_GATED, F32, FP8_E4M3, FP8_E5M2, OP_CAST_FP8, OP_FP8_DELAYED_MLP_FWD, OP_LINEAR_BWD,
                    OP_GATED_MLP_BWD, OP_GATED_MLP_FWD, OP_MLP_BWD, OP_MLP_BWD_FP8, OP_MLP_FWD, OP_MX_MLP_FWD,
                    OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
-__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "mx_scales_bytes", "mx_swizzle_scales",
            "tp_mlp_fwd_delayed", "fp8_delayed_scale", "cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",
@@ -138,6 +138,28 @@ def tp_mlp_bwd(X, W_up_t, W_down_t, Z_t, H_t, dY, dW_up_t, dW_down_t, dX_t, *, T
                         num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch,
                         _ptr(workspace), workspace.numel() if workspace is not None else 0,
                         _stream(stream))
+    return check(rc)
+
+
+def tp_linear_bwd(X, W, dY, dW, dX, *, workspace=None, stream=None):
+    """dW = X^T . dY and dX = dY . W^T of a linear layer Y = X . W (X [M, K],
+    W [K, N], dY [M, N]) in one call; the workspace defaults to a fresh one."""
+    M, K = X.shape
+    N = W.shape[1]
+    if tuple(W.shape) != (K, N) or tuple(dY.shape) != (M, N) or tuple(dW.shape) != (K, N) or tuple(dX.shape) != (M, K):
+        raise ValueError(f"tp_linear_bwd: shapes X {tuple(X.shape)}, W {tuple(W.shape)}, dY {tuple(dY.shape)}, "
+                         f"dW {tuple(dW.shape)}, dX {tuple(dX.shape)}")
+    if not (W.dtype == dY.dtype == dX.dtype == X.dtype):
+        raise ValueError("tp_linear_bwd: X, W, dY and dX share one dtype (dW may be fp32)")
+    for t in (X, W, dY, dW, dX):
+        _ld(t)
+        if t.stride(0) != t.shape[1]:
+            raise ValueError("tp_linear_bwd: dense row-major tensors")
+    if workspace is None:
+        workspace = alloc_workspace(OP_LINEAR_BWD, M, N, K, 1, 1, dtype_code(X.dtype), device=X.device)
+    rc = lib.tp_linear_bwd(M, N, K, _ptr(X), _ptr(W), _ptr(dY), dtype_code(X.dtype),
+                           _ptr(dW), _ptr(dX), dtype_code(dW.dtype),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
     return check(rc)
 
 

@@ -26,7 +26,7 @@ ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU = 0, 1, 2, 3, 4
 EPI_FWD, EPI_DACT, EPI_GATED, EPI_DGATED = 0, 1, 2, 3
 OK, EINVAL, EUNSUPPORTED, EHIP, ETIMEOUT, EWORKSPACE = 0, -1, -2, -3, -4, -5
 (OP_SEQ_CHUNK_GEMM, OP_MLP_FWD, OP_MLP_BWD, OP_GATED_MLP_FWD, OP_GATED_MLP_BWD, OP_MX_MLP_FWD,
- OP_FP8_DELAYED_MLP_FWD, OP_MLP_BWD_FP8, OP_CAST_FP8) = 0, 1, 2, 3, 4, 5, 6, 7, 8
+ OP_FP8_DELAYED_MLP_FWD, OP_MLP_BWD_FP8, OP_CAST_FP8, OP_LINEAR_BWD) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 MAX_CHUNKS = 256
 
 _i64, _i32, _u32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
@@ -55,6 +55,11 @@ lib.tp_mlp_bwd.argtypes = [_i64, _i64, _i64, _i32, _i32,
                            _vp, _vp, _vp, _i32,
                            _i32, _vp, _vp, _u32,
                            _vp, _sz, _vp]
+lib.tp_linear_bwd.restype = _i32
+lib.tp_linear_bwd.argtypes = [_i64, _i64, _i64,
+                              _vp, _vp, _vp, _i32,
+                              _vp, _vp, _i32,
+                              _vp, _sz, _vp]
 lib.tp_gated_mlp_fwd.restype = _i32
 lib.tp_gated_mlp_fwd.argtypes = [_i64, _i64, _i64, _i32, _i32,
                                  _vp, _vp, _vp, _i32, _i32,
@@ -126,7 +131,7 @@ lib.tpm_last_error.argtypes = []
 lib.tpm_version.restype = ctypes.c_char_p
 lib.tpm_version.argtypes = []
 
-EXPORTS = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+EXPORTS = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "tpm_mx_scales_bytes", "tpm_mx_swizzle_scales",
            "tp_mlp_fwd_delayed", "tpm_fp8_delayed_scale", "tpm_cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",

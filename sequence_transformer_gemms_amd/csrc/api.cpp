@@ -32,7 +32,8 @@ int hip_fail(hipError_t e, const char* what) {
 
 // control words at the head of every workspace
 constexpr int kCtrlErr = 0, kCtrlAmax = 1, kCtrlScale = 2, kCtrlCnt = 4;
-constexpr int kCtrlWords = kCtrlCnt + kMaxGroups;
+constexpr int kCtrlQueue = kCtrlCnt + kMaxGroups;   // 8 per-XCD ticket counters of paired launches
+constexpr int kCtrlWords = kCtrlQueue + 8;
 constexpr size_t kCtrlBytes = 2048;
 static_assert(kCtrlWords * 4 <= (int)kCtrlBytes, "control block");
 
@@ -98,6 +99,28 @@ int plan_splits(int64_t M, int64_t N, int64_t K, int groups, int dt) {
 
 size_t partial_bytes(int64_t M, int64_t N, int S) {
   return S > 1 ? round_up((size_t)S * (size_t)M * (size_t)N * 4, 256) : 0;
+}
+
+// Split plan of the paired launch of a linear layer's backward (dW = X^T dY:
+// [K, N] over M; dX = dY W^T: [M, K] over N; S[0], S[1]).  The launch
+// shares the two GEMMs' K steps over kPlanCUs work-groups; a GEMM whose
+// whole-tile units are longer than that per-CU share is cut into
+// ceil(steps / share) K ranges (at most 8, each of at least 8 steps), so
+// that no unit outlasts the balanced finish by much.  BF16 only; else 1.
+void plan_linear_bwd(int64_t M, int64_t N, int64_t K, int dt, int (&S)[2]) {
+  S[0] = S[1] = 1;
+  if (dt != TPM_BF16 || M <= 0 || N <= 0 || K <= 0) return;
+  const int64_t tiles[2] = {((K + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN),
+                            ((M + kTileM - 1) / kTileM) * ((K + kTileN - 1) / kTileN)};
+  const int64_t nk[2] = {(M * esize(dt) + kStepBytes - 1) / kStepBytes, (N * esize(dt) + kStepBytes - 1) / kStepBytes};
+  const int64_t work = tiles[0] * nk[0] + tiles[1] * nk[1];
+  const int64_t share = std::max<int64_t>(1, (work + kPlanCUs - 1) / kPlanCUs);
+  for (int i = 0; i < 2; ++i) {
+    int64_t s = (nk[i] + share - 1) / share;
+    s = std::min<int64_t>(s, 8);
+    while (s > 1 && nk[i] / s < 8) --s;
+    S[i] = (int)std::max<int64_t>(s, 1);
+  }
 }
 
 struct GemmDesc {
@@ -201,9 +224,9 @@ int check_gemm(const GemmDesc& g, const char* who) {
   return TPM_OK;
 }
 
-int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
-  if (g.M == 0 || g.N == 0) return TPM_OK;
-  GemmParams p;
+// Kernel parameters of one checked GEMM with S K-range splits (the caller
+// has made sure the partial-sum scratch holds S > 1 splits).
+void make_params(const GemmDesc& g, int S, GemmParams& p) {
   std::memset(&p, 0, sizeof(p));
   p.A = g.A; p.B = g.B; p.Y = g.Y; p.aux = g.aux;
   p.a_scale = g.asc; p.b_scale = g.bsc; p.amax = g.amax;
@@ -218,16 +241,6 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   p.wait_limit = g_wait_limit;
   p.act = g.act; p.epi = g.epi; p.y_f32 = g.ydt == TPM_F32; p.aux_f32 = p.y_f32;
   for (int i = 0; i < g.groups; ++i) p.order[i] = (int16_t)(g.order ? g.order[i] : i);
-  hipError_t e;
-  if (g.adt == TPM_F32) {
-    e = launch_gemm_f32(p, g.ta, g.tb, s);
-    return e == hipSuccess ? TPM_OK : hip_fail(e, who);
-  }
-  // split-K when the plan asks for it and the scratch is there (chunk-gated
-  // GEMMs split too; range-done signalling needs whole tiles)
-  // (the gated forward pairs gate and up columns inside one tile: no split-K)
-  int S = (g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
-  if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
   const int64_t nk = (g.K * esize(g.adt) + kStepBytes - 1) / kStepBytes;
   p.splits = S;
   p.ksteps_per_split = (int)((nk + S - 1) / S);
@@ -248,6 +261,23 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   p.tiles_per_group = p.mt_per_group * p.nt;
   p.total_tiles = p.tiles_per_group * p.num_groups;
   p.band_m = std::min(p.mt_per_group, 4);
+}
+
+int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
+  if (g.M == 0 || g.N == 0) return TPM_OK;
+  GemmParams p;
+  hipError_t e;
+  if (g.adt == TPM_F32) {
+    make_params(g, 1, p);
+    e = launch_gemm_f32(p, g.ta, g.tb, s);
+    return e == hipSuccess ? TPM_OK : hip_fail(e, who);
+  }
+  // split-K when the plan asks for it and the scratch is there (chunk-gated
+  // GEMMs split too; range-done signalling needs whole tiles)
+  // (the gated forward pairs gate and up columns inside one tile: no split-K)
+  int S = (g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+  if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
+  make_params(g, S, p);
   // persistent grid: one work-group per CU the stream may use.  A
   // chunk-gated GEMM on a stream that may use every CU leaves one CU per XCD
   // to a producer that runs kernels on this device; a stream with a CU mask
@@ -294,6 +324,11 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
   switch (op) {
     case TPM_OP_SEQ_CHUNK_GEMM:
       return kCtrlBytes + partial_bytes(M, N, plan_splits(M, N, K, num_chunks, dtype));
+    case TPM_OP_LINEAR_BWD: {
+      int S[2];
+      plan_linear_bwd(M, N, K, dtype, S);
+      return kCtrlBytes + partial_bytes(K, N, S[0]) + partial_bytes(M, K, S[1]);
+    }
     case TPM_OP_MLP_FWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
@@ -498,6 +533,60 @@ int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
     if (e != hipSuccess) return hip_fail(e, who);
   }
   return run_gemm(g2, s, who);
+}
+
+int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
+                  const void* X, const void* W, const void* dY, int dtype,
+                  void* dW, void* dX, int dw_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "tp_linear_bwd";
+  if (M < 0 || N < 0 || K < 0) return fail(TPM_EINVAL, "%s: negative size", who);
+  if (dtype != TPM_BF16 && dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dtype BF16 or F32", who);
+  if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
+  if (dtype == TPM_F32 && dw_dtype != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 inputs give fp32 dW", who);
+  if (!X || !W || !dY || !dW || !dX) return fail(TPM_EINVAL, "%s: null pointer", who);
+  if (dtype == TPM_BF16 && (M % 8 || N % 8 || K % 8))
+    return fail(TPM_EUNSUPPORTED, "%s: bf16 M, N and K must be multiples of 8 (16-byte rows)", who);
+  const size_t need = tpm_workspace_bytes(TPM_OP_LINEAR_BWD, M, N, K, 1, 1, dtype);
+  if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
+  uint32_t* ctrl = (uint32_t*)workspace;
+  // dW = X^T . dY    [K, N], contraction over M; X [M, K] stored: op(A) = X^T
+  GemmDesc g_dw{K, N, M, X, K, true, dtype, nullptr, dY, N, false, dtype, nullptr,
+                dW, N, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  // dX = dY . W^T    [M, K], contraction over N; W [K, N] stored: op(B) = W^T
+  GemmDesc g_dx{M, K, N, dY, N, false, dtype, nullptr, W, N, true, dtype, nullptr,
+                dX, K, dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
+                1, nullptr, nullptr, nullptr, 0, ctrl};
+  int S[2];
+  plan_linear_bwd(M, N, K, dtype, S);
+  g_dw.part = (float*)((char*)workspace + kCtrlBytes);
+  g_dw.part_bytes = partial_bytes(K, N, S[0]);
+  g_dx.part = (float*)((char*)workspace + kCtrlBytes + g_dw.part_bytes);
+  g_dx.part_bytes = partial_bytes(M, K, S[1]);
+  for (const GemmDesc* g : {&g_dw, &g_dx}) {
+    int rc = check_gemm(*g, who);
+    if (rc != TPM_OK) return rc;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype != TPM_BF16 || K == 0 || N == 0 || M == 0) {
+    // fp32 (the small exact-arithmetic path), or one product empty
+    for (const GemmDesc* g : {&g_dw, &g_dx}) {
+      int rc = run_gemm(*g, s, who);
+      if (rc != TPM_OK) return rc;
+    }
+    return TPM_OK;
+  }
+  GemmParams p_dw, p_dx;
+  make_params(g_dw, S[0], p_dw);
+  make_params(g_dx, S[1], p_dx);
+  const int units = p_dw.total_tiles * p_dw.splits + p_dx.total_tiles * p_dx.splits;
+  // at least one work-group per XCD queue, at most one per CU the stream may use
+  const int grid = std::max(8, std::min(stream_cus(s), units));
+  const int first = p_dx.ksteps_per_split > p_dw.ksteps_per_split ? 1 : 0;
+  hipError_t e = launch_ctrl_init(ctrl + kCtrlQueue, 8, s);
+  if (e == hipSuccess) e = launch_gemm_pair_bf16(p_dw, false, false, p_dx, true, true, first, ctrl + kCtrlQueue, grid, s);
+  return e == hipSuccess ? TPM_OK : hip_fail(e, who);
 }
 
 int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,

@@ -91,7 +91,7 @@ struct Unit {
 // after the group: every unit of a chunk precedes the next chunk's, so the
 // work-groups' first units are the earliest chunks' and later chunks are
 // only waited for by units of a later round.
-__device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
+__device__ __forceinline__ int xcd_logical(const GemmParams& p, int u) {
   const int G = gridDim.x;
   const int total = p.total_tiles * p.splits;
   int L = u;
@@ -102,6 +102,11 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
       L = r * G + (s & 7) * (G >> 3) + (s >> 3);
     }
   }
+  return L;
+}
+
+// Logical unit L (0 .. total_tiles * splits - 1) -> (split, tile).
+__device__ __forceinline__ Unit logical_unit(const GemmParams& p, int L) {
   Unit un;
   int pos, q;
   if (p.ready) {
@@ -132,6 +137,8 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) {
   tl.n0 = ntile * p.bn_out;
   return un;
 }
+
+__device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) { return logical_unit(p, xcd_logical(p, u)); }
 
 // One of the sixteen-byte loads per thread that stage an operand tile of
 // one K step: thread t of the work-group fills LDS chunk P = j * THREADS + t.
@@ -376,8 +383,10 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
   }
 }
 
+// One work unit (a K range of one output tile) of the GEMM p, staged
+// through the work-group's LDS block `smem` (Layout<NW>::SMEM bytes).
 template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false, int F8F = 0>
-__global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
+__device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, char* __restrict__ smem) {
   // fp8 formats of the MFMA operands (0 e4m3, 1 e5m2): the first operand
   // is the B fragment, the second the A fragment
   constexpr int FMT0 = (F8F >> 1) & 1, FMT1 = F8F & 1;
@@ -388,7 +397,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int KSTEP = ROW_BYTES / ESZ;  // K elements per staged step
   constexpr int KSUB = FP8 ? 1 : 2;        // MFMA substeps per K step
-  __shared__ __attribute__((aligned(1024))) char smem[LY::SMEM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -407,16 +415,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
   if (p.a_scale) scale *= *p.a_scale;
   if (p.b_scale) scale *= *p.b_scale;
 
-  // Chunk-gated GEMM: invalidate this XCD's caches once, before any
-  // operand is loaded.  A row of chunk c is only ever loaded after
-  // ready[c] has been seen set, and the producer publishes the data before
-  // the flag (release), so no cache can hold a stale copy of it afterwards:
-  // the per-chunk wait needs no further invalidation (which would throw away
-  // every tile's cached operands on each chunk arrival).
-  if (p.ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int total_units = p.total_tiles * p.splits;
-  for (int u = blockIdx.x; u < total_units; u += gridDim.x) {
-    const Unit un = map_unit(p, u);
+  {
     const Tile& tl = un.tl;
     // K steps [kbeg, kend) of this split
     const int kbeg = un.split * p.ksteps_per_split;
@@ -764,6 +763,61 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
   }
 }
 
+template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false, int F8F = 0>
+__global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[Layout<NW>::SMEM];
+  // Chunk-gated GEMM: invalidate this XCD's caches once, before any
+  // operand is loaded.  A row of chunk c is only ever loaded after
+  // ready[c] has been seen set, and the producer publishes the data before
+  // the flag (release), so no cache can hold a stale copy of it afterwards:
+  // the per-chunk wait needs no further invalidation (which would throw away
+  // every tile's cached operands on each chunk arrival).
+  if (p.ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int total_units = p.total_tiles * p.splits;
+  for (int u = blockIdx.x; u < total_units; u += gridDim.x)
+    run_unit<FP8, AK, BKM, NW, GATED, MX, F8F>(p, map_unit(p, u), smem);
+}
+
+// Two independent bf16 GEMMs in one persistent launch (the weight and the
+// input gradient of a linear layer, which read the same dY): each XCD
+// (work-groups congruent mod 8) owns a contiguous eighth of each GEMM's
+// logical units, those of GEMM FIRST listed first, and its work-groups take
+// units from that list through a per-XCD ticket counter (queue[x], zero at
+// launch), so that the longer units start first and the shorter ones fill
+// in behind them.  Every unit is computed whole by the work-group that
+// takes it, so results do not depend on which one does.  A work-group
+// leaves the first GEMM's loop for good once its ticket passes that GEMM's
+// units, so the two loops (and their loop-invariant registers) never
+// overlap.
+template <int NW, bool AK0, bool BK0, bool AK1, bool BK1, int FIRST>
+__global__ void __launch_bounds__(64 * NW, 1) gemm_pair_kernel(const GemmParams p0, const GemmParams p1,
+                                                              uint32_t* queue) {
+  // the ticket word sits just past the tile's LDS block, inside the same
+  // array: a __shared__ variable of its own makes the compiler wait for all
+  // LDS DMA before every LDS read of the K loop
+  __shared__ __attribute__((aligned(1024))) char smem[Layout<NW>::SMEM + 16];
+  volatile int* ticket_word = reinterpret_cast<volatile int*>(smem + Layout<NW>::SMEM);
+  const int x = blockIdx.x & 7;
+  const int n0 = p0.total_tiles * p0.splits, n1 = p1.total_tiles * p1.splits;
+  const int b0 = (int)((int64_t)x * n0 / 8), c0 = (int)((int64_t)(x + 1) * n0 / 8) - b0;
+  const int b1 = (int)((int64_t)x * n1 / 8), c1 = (int)((int64_t)(x + 1) * n1 / 8) - b1;
+  // (every thread reads a ticket before thread 0 can take the next one:
+  // the unit's body passes several work-group barriers)
+  auto take = [&]() {
+    if (threadIdx.x == 0) *ticket_word = (int)atomicAdd(queue + x, 1u);
+    __syncthreads();
+    return *ticket_word;
+  };
+  int i = take();
+  if constexpr (FIRST == 0) {
+    for (; i < c0; i = take()) run_unit<false, AK0, BK0, NW>(p0, logical_unit(p0, b0 + i), smem);
+    for (; i < c0 + c1; i = take()) run_unit<false, AK1, BK1, NW>(p1, logical_unit(p1, b1 + i - c0), smem);
+  } else {
+    for (; i < c1; i = take()) run_unit<false, AK1, BK1, NW>(p1, logical_unit(p1, b1 + i), smem);
+    for (; i < c0 + c1; i = take()) run_unit<false, AK0, BK0, NW>(p0, logical_unit(p0, b0 + i - c1), smem);
+  }
+}
+
 
 // Split-K finalisation: Y = epilogue(scale * sum_{s=0}^{S-1} partial_s),
 // summed in ascending s (deterministic), 8 consecutive columns per lane.
@@ -831,6 +885,18 @@ hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
   else if (!a_kmajor && !b_kmajor) gemm_kernel<false, false, false, kWaves><<<grid, kThreads, 0, s>>>(p);
   else gemm_kernel<false, false, true, kWaves><<<grid, kThreads, 0, s>>>(p);
   return finalize_if_split(p, s);
+}
+
+hipError_t launch_gemm_pair_bf16(const GemmParams& p0, bool a0_kmajor, bool b0_kmajor, const GemmParams& p1,
+                                 bool a1_kmajor, bool b1_kmajor, int first, uint32_t* queue, int grid, hipStream_t s) {
+  // instantiated for a linear layer's backward: dW = X^T dY (both operands
+  // MN-major) and dX = dY W^T (both K-major)
+  if (a0_kmajor || b0_kmajor || !a1_kmajor || !b1_kmajor) return hipErrorInvalidValue;  // rejected on the host first
+  if (first == 0) gemm_pair_kernel<kWaves, false, false, true, true, 0><<<grid, kThreads, 0, s>>>(p0, p1, queue);
+  else gemm_pair_kernel<kWaves, false, false, true, true, 1><<<grid, kThreads, 0, s>>>(p0, p1, queue);
+  hipError_t e = finalize_if_split(p0, s);
+  if (e != hipSuccess) return e;
+  return finalize_if_split(p1, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s) {

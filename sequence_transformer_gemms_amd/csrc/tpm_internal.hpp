@@ -77,6 +77,11 @@ struct WriterParams {
 
 // kernels' launchers (return hipError_t of the launch)
 hipError_t launch_gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
+// Two bf16 GEMMs in one persistent launch (p0: both operands MN-major, p1:
+// both K-major), units taken from per-XCD ticket counters queue[0..7]
+// (zero at launch); `first` (0 or 1) names the GEMM whose units go first.
+hipError_t launch_gemm_pair_bf16(const GemmParams& p0, bool a0_kmajor, bool b0_kmajor, const GemmParams& p1,
+                                 bool a1_kmajor, bool b1_kmajor, int first, uint32_t* queue, int grid, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmParams& p, bool a_kmajor, bool b_kmajor, int grid, hipStream_t s);
 hipError_t launch_delayed_scale(const float* history, int n, float* scale_out, hipStream_t s);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* out, hipStream_t s);

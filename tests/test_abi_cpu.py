@@ -119,3 +119,29 @@ def test_write_chunks_validation():
     assert wc(FAKE + 8, FAKE, 4096, 4, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL              # misaligned
     assert wc(FAKE, FAKE, 4096, 0, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL                  # no chunks
     assert wc(FAKE, FAKE, 4096, 257, ok, None, FAKE, 1, FAKE, None) == _abi.EINVAL                # too many
+
+
+def test_linear_bwd_workspace_and_split_plan():
+    from sequence_transformer_gemms_amd import _abi
+    ws = _abi.lib.tpm_workspace_bytes
+    # O projection of one TP=8 rank (A [4096, 1024], W_o [1024, 8192]): dW_o's
+    # 128 tiles of 64 K steps and dA's 64 tiles of 128 share 256 CUs at 64
+    # steps each, so dA's contraction is cut in 2: fp32 partials [2, 4096, 1024]
+    assert ws(_abi.OP_LINEAR_BWD, 4096, 8192, 1024, 1, 1, _abi.BF16) == 2048 + 2 * 4096 * 1024 * 4
+    # QKV projection (X [4096, 8192], W_qkv [8192, 1280]): 160 tiles of 64
+    # steps and 512 of 20 -> 80 steps per CU, no unit longer: no split
+    assert ws(_abi.OP_LINEAR_BWD, 4096, 1280, 8192, 1, 1, _abi.BF16) == 2048
+    # fp32: no split
+    assert ws(_abi.OP_LINEAR_BWD, 4096, 256, 1024, 1, 1, _abi.F32) == 2048
+
+
+def test_linear_bwd_host_errors_without_device():
+    # argument checks run on the host before anything touches a device
+    from sequence_transformer_gemms_amd import _abi
+    f = _abi.lib.tp_linear_bwd
+    assert f(-1, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EINVAL
+    assert f(8, 8, 8, None, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EINVAL
+    assert f(8, 8, 8, 16, 16, 16, _abi.FP8_E4M3, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EINVAL
+    assert f(8, 8, 8, 16, 16, 16, _abi.F32, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EUNSUPPORTED
+    assert f(8, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 4, None) == _abi.EWORKSPACE
+    assert f(300, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 1 << 30, None) == _abi.EUNSUPPORTED

@@ -201,7 +201,8 @@ def test_c4_fp8_mlp_forward_full_width_end_to_end():
 def test_c5_layer_step_full_size_sampled():
     """The bench's Llama3-70B-shaped layer step of rank 0 (4096 tokens, bf16),
     call by call with the bench's shapes, orders and workspaces: QKV and O
-    projections, MLP forward, MLP backward, O and QKV backward.  Row-indexed
+    projections, MLP forward, MLP backward, O and QKV backward (as separate
+    GEMMs, and as the paired tp_linear_bwd launches of the resident step).  Row-indexed
     outputs are checked on sampled token rows, weight gradients on sampled
     rows or columns."""
     M, D, F, T, C, r = 4096, 8192, 28672, 8, 8, 0
@@ -236,6 +237,12 @@ def test_c5_layer_step_full_size_sampled():
     tpm.seq_chunk_gemm(dev["a"], dev["dyo"], g_o, trans_a=True, workspace=wsg)
     tpm.seq_chunk_gemm(dev["x"], dev["dq"], g_qkv, trans_a=True, workspace=wsg)
     tpm.seq_chunk_gemm(dev["dq"], dev["wq"], dx_q, trans_b=True, workspace=wsg)
+    # the same two backward pairs as the resident step runs them: one launch each
+    ws_l = torch.zeros(max(tpm.workspace_bytes(_abi.OP_LINEAR_BWD, M, n, k) for n, k in ((D, Da), (Nq, D))),
+                       dtype=torch.uint8, device="cuda")
+    g_o2, d_attn2, g_qkv2, dx_q2 = e(Da, D), e(M, Da), e(D, Nq), e(M, D)
+    tpm.tp_linear_bwd(dev["a"], dev["wo"], dev["dyo"], g_o2, d_attn2, workspace=ws_l)
+    tpm.tp_linear_bwd(dev["x"], dev["wq"], dev["dq"], g_qkv2, dx_q2, workspace=ws_l)
     sync()
     B = TOL["bf16"]
     rows = pick(M, 16, 51)
@@ -253,6 +260,8 @@ def test_c5_layer_step_full_size_sampled():
     assert nerr(host64(dx[rows]), bw["dX"]) <= B
     assert nerr(host64(d_attn[rows]), ops.seq_chunk_gemm(f64(dyo[rows]), f64(wo), trans_b=True)[0]) <= B
     assert nerr(host64(dx_q[rows]), ops.seq_chunk_gemm(f64(dq[rows]), f64(wq), trans_b=True)[0]) <= B
+    assert nerr(host64(d_attn2[rows]), ops.linear_bwd(f64(a[rows]), f64(wo), f64(dyo[rows]))["dX"]) <= B
+    assert nerr(host64(dx_q2[rows]), ops.linear_bwd(X[rows], f64(wq), f64(dq[rows]))["dX"]) <= B
     # weight gradients: dW_down rows f need the H columns f over all tokens;
     # dW_up columns f need the dZ columns f over all tokens.  Their inputs H,
     # Z and dZ are bf16 intermediates that the GPU rounds from fp32 values:
@@ -281,6 +290,11 @@ def test_c5_layer_step_full_size_sampled():
     assert nerr(host64(g_o[orows]), ops.seq_chunk_gemm(f64(a[:, orows]), f64(dyo), trans_a=True)[0]) <= B
     qcols = pick(Nq, 8, 54)
     assert nerr(host64(g_qkv[:, qcols]), ops.seq_chunk_gemm(X, f64(dq[:, qcols]), trans_a=True)[0]) <= B
+    # dW_o rows i need A's column i; dW_qkv columns j need dQKV's column j
+    ref_o = ops.linear_bwd(f64(a[:, orows]), f64(wo)[orows], f64(dyo))["dW"]
+    assert nerr(host64(g_o2[orows]), ref_o) <= B
+    ref_q = ops.linear_bwd(X, f64(wq)[:, qcols], f64(dq[:, qcols]))["dW"]
+    assert nerr(host64(g_qkv2[:, qcols]), ref_q) <= B
 
 
 # ------------------------------------------------- tensor-parallel degree sweep

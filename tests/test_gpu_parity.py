@@ -1047,3 +1047,74 @@ def test_graph_replays_match_eager():
         sync()
         for got, want in zip((H, stack, out, H8, P8, sH, Yk), ref):
             assert torch.equal(got, want), rep
+
+
+# ------------------------------------------------------- linear backward pair
+LINEAR_SHAPES = [(296, 264, 520),     # ragged tiles, no split
+                 (4096, 256, 1024),   # dW's contraction (4096 tokens) split 8 ways
+                 (520, 4096, 264)]    # dX's contraction (4096) split 8 ways, dW first
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
+def test_linear_bwd_integer_exact(M, N, K):
+    # dW = X^T dY and dX = dY W^T in one launch; small integers make every
+    # fp32 sum exact, so dW (fp32) must equal the oracle bit for bit and dX
+    # (bf16) its single rounding, whatever split or work-group took a tile
+    x = si.small_ints((M, K), 91)
+    w = si.small_ints((K, N), 92)
+    dy = si.small_ints((M, N), 93)
+    dW = torch.empty(K, N, dtype=torch.float32, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_LINEAR_BWD, M, N, K)
+    tpm.tp_linear_bwd(dev_bf16(x), dev_bf16(w), dev_bf16(dy), dW, dX, workspace=ws)
+    sync()
+    ref = ops.linear_bwd(x, w, dy)
+    assert np.array_equal(f64(dW), ref["dW"])
+    assert np.array_equal(f64(dX), formats.round_bf16(ref["dX"]))
+
+
+def test_linear_bwd_float_repeatable_and_fp32():
+    # float inputs: both products within the bf16 bound of the oracle, and
+    # three calls bit-identical (which work-group takes which tile varies)
+    M, N, K = 1000, 1280, 2056
+    x = dev_bf16(si.normal_f32((M, K), 94))
+    w = dev_bf16(si.normal_f32((K, N), 95, 0.02))
+    dy = dev_bf16(si.normal_f32((M, N), 96))
+    ws = tpm.alloc_workspace(_abi.OP_LINEAR_BWD, M, N, K)
+    outs = []
+    for _ in range(3):
+        dW = torch.empty(K, N, dtype=torch.bfloat16, device="cuda")
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        tpm.tp_linear_bwd(x, w, dy, dW, dX, workspace=ws)
+        sync()
+        outs.append((dW.clone(), dX.clone()))
+    ref = ops.linear_bwd(f64(x), f64(w), f64(dy))
+    assert nerr(outs[0][0], ref["dW"]) <= TOL["bf16"] and nerr(outs[0][1], ref["dX"]) <= TOL["bf16"]
+    assert all(torch.equal(a, outs[0][0]) and torch.equal(b, outs[0][1]) for a, b in outs[1:])
+    # fp32 inputs take the fp32 kernel for both products (1e-4 bound)
+    xs, ws_, dys = (torch.from_numpy(si.uniform_f32(s, seed)).cuda()
+                    for s, seed in (((40, 24), 97), ((24, 36), 98), ((40, 36), 99)))
+    dW32 = torch.empty(24, 36, dtype=torch.float32, device="cuda")
+    dX32 = torch.empty(40, 24, dtype=torch.float32, device="cuda")
+    tpm.tp_linear_bwd(xs, ws_, dys, dW32, dX32)
+    sync()
+    r32 = ops.linear_bwd(f64(xs), f64(ws_), f64(dys))
+    assert nerr(dW32, r32["dW"]) <= TOL["f32"] and nerr(dX32, r32["dX"]) <= TOL["f32"]
+
+
+def test_linear_bwd_rejects_bad_arguments():
+    x = torch.zeros(64, 32, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(32, 48, dtype=torch.bfloat16, device="cuda")
+    dy = torch.zeros(64, 48, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(32, 48, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(64, 32, dtype=torch.bfloat16, device="cuda")
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tpm.TpmError):
+        tpm.tp_linear_bwd(x, w, dy, dW, dX, workspace=small)        # workspace too small
+    xm = torch.zeros(64 * 32 + 1, dtype=torch.bfloat16, device="cuda")[1:].view(64, 32)
+    with pytest.raises(tpm.TpmError):
+        tpm.tp_linear_bwd(xm, w, dy, dW, dX)                        # operand not 16-byte aligned
+    with pytest.raises(ValueError):
+        tpm.tp_linear_bwd(x, w, dy, dW, dX.float())                 # dX is written in the inputs' dtype
+    with pytest.raises(ValueError):
+        tpm.tp_linear_bwd(x, w, dy[:, :40].contiguous(), dW, dX)    # dY is [M, N]

@@ -31,11 +31,11 @@ def asm(tmp_path_factory):
 
 
 def kernels(text):
-    """{mangled gemm_kernel name: (body lines, metadata dict)}"""
+    """{mangled gemm_kernel / gemm_pair_kernel name: (body lines, metadata dict)}"""
     lines = text.split("\n")
     bodies, cur = {}, None
     for ln in lines:
-        m = re.match(r"^(_ZN\S*gemm_kernel\S*):", ln)
+        m = re.match(r"^(_ZN\S*gemm_(?:pair_)?kernel\S*):", ln)
         if m:
             cur = m.group(1)
             bodies[cur] = []
@@ -47,7 +47,7 @@ def kernels(text):
                 bodies[cur].append(ln.strip())
     meta = {}
     for block in re.split(r"\n\s*- \.", text):
-        nm = re.search(r"\.name:\s+(\S*gemm_kernel\S*)", block)
+        nm = re.search(r"\.name:\s+(\S*gemm_(?:pair_)?kernel\S*)", block)
         if not nm:
             continue
         vals = {k: int(v) for k, v in re.findall(r"\.(vgpr_spill_count|sgpr_spill_count|group_segment_fixed_size"
@@ -58,7 +58,9 @@ def kernels(text):
 
 def test_every_gemm_variant_is_compiled(asm):
     bodies, meta = kernels(asm)
-    assert len(bodies) == 9          # 4 bf16 operand layouts + gated + fp8 (3 format pairs) + MXFP8
+    # 4 bf16 operand layouts + gated + fp8 (3 format pairs) + MXFP8, and the
+    # paired linear-backward launch (either GEMM first)
+    assert len(bodies) == 11
     assert set(meta) == set(bodies)
 
 
