@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--yardstick", action="store_true",
+                    help="bf16 GEMM 8192^3 in three layouts, ours next to torch.matmul (hipBLASLt), and ours on "
+                         "256 / 128 / 64 CUs (CU-masked streams); one JSON line")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: one line per (T, chunks) of the Llama3-70B MLP share "
                          "(8192 tokens, D 8192, F 28672), T in 1, 2, 4, 8 and chunks in T, 2T, 4T")
@@ -429,6 +432,51 @@ def sweep_point(torch, tpm, si, M, D, F, T, C, iters=10):
             "TFLOPS_fwd_bwd": round(6 * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12, 1)}
 
 
+def run_yardstick(torch, tpm):
+    """Yardsticks for the GEMM kernel on one square bf16 product (M = N = K =
+    8192, random normal operands): ours and torch.matmul (hipBLASLt) in the
+    three operand layouts (A and B row-major; B stored [N, K]; A stored
+    [K, M]), then ours on streams restricted to 128 and 64 CUs, which shows
+    how the per-CU rate depends on how many CUs share the L2s and the
+    fabric.  Median of 10 calls each, HIP events; prints one JSON line."""
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    at, bt = a.t().contiguous(), b.t().contiguous()
+    y = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    fl = 2.0 * n ** 3
+
+    def med(fn, reps=10, stream=None):
+        stream = stream or torch.cuda.current_stream()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[reps // 2]
+
+    out = {"shape": [n, n, n], "dtype": "bf16", "unit": "TFLOP/s"}
+    layouts = {"NN": (lambda: tpm.seq_chunk_gemm(a, b, y), lambda: torch.matmul(a, b, out=y)),
+               "NT": (lambda: tpm.seq_chunk_gemm(a, bt, y, trans_b=True), lambda: torch.matmul(a, bt.t(), out=y)),
+               "TN": (lambda: tpm.seq_chunk_gemm(at, b, y, trans_a=True), lambda: torch.matmul(at.t(), b, out=y))}
+    for name, (ours, blas) in layouts.items():
+        out[f"ours_{name}"] = round(fl / (med(ours) * 1e-3) / 1e12, 1)
+        out[f"hipblaslt_{name}"] = round(fl / (med(blas) * 1e-3) / 1e12, 1)
+    for keep in (128, 64):
+        comp, _ = tpm.masked_streams(producer_cus=256 - keep)
+        with torch.cuda.stream(comp):
+            t = med(lambda: tpm.seq_chunk_gemm(a, b, y), reps=6, stream=comp)
+        out[f"ours_NN_{keep}cus"] = round(fl / (t * 1e-3) / 1e12, 1)
+        out[f"ours_NN_{keep}cus_per_cu_as_256"] = round(fl / (t * 1e-3) / 1e12 * 256 / keep, 1)
+    print(json.dumps({"yardstick": out}), flush=True)
+
+
 def run_sweep(torch, tpm, si):
     M, D, F = 8192, 8192, 28672
     for T in (1, 2, 4, 8):
@@ -691,6 +739,9 @@ def main():
     if args.sweep:
         run_sweep(torch, tpm, si)
         return
+    if args.yardstick:
+        run_yardstick(torch, tpm)
+        return
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -721,8 +772,9 @@ def main():
                    "launch": "hip_graph", "ms_per_step_eager": round(ms_eager, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(),
-                     "traffic_unit": "bytes per step (12 GEMM launches + split-K finalisation)",
-                     "kernel": "gemm_kernel (bf16 MFMA), all 12 GEMM launches of the step",
+                     "traffic_unit": "bytes per step (the 12 GEMMs in 10 launches + split-K finalisation)",
+                     "kernel": "gemm_kernel / gemm_pair_kernel (bf16 MFMA): the step's 12 GEMMs in 10 launches "
+                               "(each projection backward's dW and dX paired in one)",
                      "gemm_ms_per_step": round(gemm_ms, 4)},
     }
     if not args.no_extra:
