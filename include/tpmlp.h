@@ -210,8 +210,9 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
  * longer than the other's.  Results do not depend on which work-group
  * computes a tile.  Caller-owned device workspace of
  * >= tpm_workspace_bytes(TPM_OP_LINEAR_BWD, M, N, K, 1, 1, dtype) bytes
- * (control words and split-K partial sums).  Errors: TPM_EINVAL (null
- * pointer, negative size, bad dtype), TPM_EWORKSPACE (workspace too small),
+ * (control words and split-K partial sums).  M == 0 writes zeros to dW,
+ * N == 0 zeros to dX (empty arrays may be null).  Errors: TPM_EINVAL (null
+ * pointer to a non-empty array, negative size, bad dtype), TPM_EWORKSPACE (workspace too small),
  * TPM_EUNSUPPORTED (misaligned operand or size, operand >= 4 GiB); nothing is
  * enqueued on error.  Asynchronous on `stream`.
  */

@@ -152,8 +152,7 @@ def tp_linear_bwd(X, W, dY, dW, dX, *, workspace=None, stream=None):
     if not (W.dtype == dY.dtype == dX.dtype == X.dtype):
         raise ValueError("tp_linear_bwd: X, W, dY and dX share one dtype (dW may be fp32)")
     for t in (X, W, dY, dW, dX):
-        _ld(t)
-        if t.stride(0) != t.shape[1]:
+        if t.numel() and (t.stride(1) != 1 or t.stride(0) != t.shape[1]):
             raise ValueError("tp_linear_bwd: dense row-major tensors")
     if workspace is None:
         workspace = alloc_workspace(OP_LINEAR_BWD, M, N, K, 1, 1, dtype_code(X.dtype), device=X.device)

@@ -544,7 +544,10 @@ int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
   if (dtype != TPM_BF16 && dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dtype BF16 or F32", who);
   if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
   if (dtype == TPM_F32 && dw_dtype != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 inputs give fp32 dW", who);
-  if (!X || !W || !dY || !dW || !dX) return fail(TPM_EINVAL, "%s: null pointer", who);
+  // every array with elements needs a pointer (empty ones may be null)
+  auto given = [](const void* p, int64_t rows, int64_t cols) { return p != nullptr || rows == 0 || cols == 0; };
+  if (!given(X, M, K) || !given(W, K, N) || !given(dY, M, N) || !given(dW, K, N) || !given(dX, M, K))
+    return fail(TPM_EINVAL, "%s: null pointer", who);
   if (dtype == TPM_BF16 && (M % 8 || N % 8 || K % 8))
     return fail(TPM_EUNSUPPORTED, "%s: bf16 M, N and K must be multiples of 8 (16-byte rows)", who);
   const size_t need = tpm_workspace_bytes(TPM_OP_LINEAR_BWD, M, N, K, 1, 1, dtype);

@@ -1118,3 +1118,18 @@ def test_linear_bwd_rejects_bad_arguments():
         tpm.tp_linear_bwd(x, w, dy, dW, dX.float())                 # dX is written in the inputs' dtype
     with pytest.raises(ValueError):
         tpm.tp_linear_bwd(x, w, dy[:, :40].contiguous(), dW, dX)    # dY is [M, N]
+
+
+def test_linear_bwd_empty_contractions():
+    # M = 0 tokens: dW = X^T dY contracts over nothing and must be zeros, dX
+    # is empty; N = 0: dX contracts over nothing (zeros), dW is empty
+    ws = tpm.alloc_workspace(_abi.OP_LINEAR_BWD, 0, 64, 40)
+    e = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device="cuda")
+    dW = torch.full((40, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    tpm.tp_linear_bwd(e(0, 40), e(40, 64), e(0, 64), dW, e(0, 40), workspace=ws)
+    dX = torch.full((48, 40), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws2 = tpm.alloc_workspace(_abi.OP_LINEAR_BWD, 48, 0, 40)
+    tpm.tp_linear_bwd(e(48, 40), e(40, 0), e(48, 0), e(40, 0), dX, workspace=ws2)
+    sync()
+    assert torch.count_nonzero(dW).item() == 0
+    assert torch.count_nonzero(dX).item() == 0
