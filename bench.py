@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--producer-cus", type=int, default=32,
+                    help="CUs of the stream that writes arriving chunks in the arrival step (the others run the GEMMs)")
     ap.add_argument("--yardstick", action="store_true",
                     help="bf16 GEMM 8192^3 in three layouts, ours next to torch.matmul (hipBLASLt), and ours on "
                          "256 / 128 / 64 CUs (CU-masked streams); one JSON line")
@@ -62,7 +64,8 @@ def parse():
 class Layer:
     """Device buffers and the step of the C5 workload (one TP=8 rank)."""
 
-    def __init__(self, torch, tpm, si, M=4096, D=8192, F=28672, T=8, rank=0, heads=8, kv=1, hd=128):
+    def __init__(self, torch, tpm, si, M=4096, D=8192, F=28672, T=8, rank=0, heads=8, kv=1, hd=128,
+                 producer_cus=32):
         self.torch, self.tpm = torch, tpm
         self.M, self.D, self.T, self.rank = M, D, T, rank
         self.Ft = F // T
@@ -117,7 +120,8 @@ class Layer:
         self.counters = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.order = si.ring_chunk_order(T, self.C, rank)
         self.dest = si.dest_range_order(T, rank)
-        self.compute, self.side = tpm.masked_streams(producer_cus=8)
+        self.producer_cus = producer_cus
+        self.compute, self.side = tpm.masked_streams(producer_cus=producer_cus)
         self.gemm_events = []
         fl = lambda m, n, k: 2.0 * m * n * k
         self.flops = (3 * fl(M, Nq, D) + 3 * fl(M, Ft, D) + 3 * fl(M, D, Da) + 3 * fl(M, D, Ft))
@@ -285,8 +289,10 @@ def time_steps_graph(torch, layer, steps, warmup):
 def arrival_step(torch, layer, args, ms_resident):
     """The same step with the chunk-fed GEMMs (QKV, MLP up, dZ, dA) gated on
     chunks that a producer stream writes in ring order while they run, the
-    producer confined to 8 CUs and the GEMMs to the others.  Reports the
-    writer's time alone (4 launches of 7 x 8 MB) and the overlap efficiency
+    producer confined to `producer_cus` CUs (32 by default: about 0.67 TB/s
+    of chunk writes, the order of a rank's ingress over 7 xGMI links) and
+    the GEMMs to the others.  Reports the writer's time alone (4 launches of
+    7 x 8 MB) and the overlap efficiency
     (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
     ms, gemm_ms, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000)
     torch.cuda.synchronize()
@@ -304,7 +310,7 @@ def arrival_step(torch, layer, args, ms_resident):
     return {"ms": round(ms, 4), "TFLOPS": round(layer.flops / (ms * 1e-3) / 1e12, 2),
             "gemm_TFLOPS": round(layer.flops / (gemm_ms * 1e-3) / 1e12, 2),
             "writer_only_ms": round(t_copy, 4), "overlap_efficiency": round(eff, 3),
-            "producer_cus": 8}
+            "producer_cus": layer.producer_cus}
 
 
 def bench_reduce(torch, tpm, si, iters=40):
@@ -748,7 +754,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    layer = Layer(torch, tpm, si)
+    layer = Layer(torch, tpm, si, producer_cus=args.producer_cus)
     torch.cuda.synchronize()
     # headline: the rank's step with every chunk already in place (flags
     # not consulted), on the default stream with every CU
