@@ -992,7 +992,8 @@ def test_chunk_gating_reads_fresh_data_after_stale_reads():
 # ------------------------------------------------ HIP graph capture / replay
 def test_graph_replays_match_eager():
     # bf16 MLP forward, an fp8 forward (control-word init, amax, quantiser),
-    # a split-K GEMM (fp32 partials + finalisation) and a reduction, captured
+    # a split-K GEMM (fp32 partials + finalisation), a reduction and a paired
+    # linear backward (ticket counters zeroed by a kernel), captured
     # once and replayed three times with eager work and synchronisation in
     # between; every replay must equal the eager result bit for bit
     M, D, F, T = 512, 512, 2048, 4
@@ -1018,6 +1019,14 @@ def test_graph_replays_match_eager():
     Yk = torch.empty(M, 264, dtype=torch.bfloat16, device="cuda")
     ws_k = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, 264, 4096)
     assert ws_k.numel() > 2048                                   # split-K planned
+    # a paired linear backward (ticket counters zeroed by a kernel, dW split)
+    lx = dev_bf16(si.normal_f32((2048, 512), 120))
+    lw = dev_bf16(si.normal_f32((512, 256), 121, 0.05))
+    ldy = dev_bf16(si.normal_f32((2048, 256), 122))
+    ldW = torch.empty(512, 256, dtype=torch.bfloat16, device="cuda")
+    ldX = torch.empty(2048, 512, dtype=torch.bfloat16, device="cuda")
+    ws_l = tpm.alloc_workspace(_abi.OP_LINEAR_BWD, 2048, 256, 512)
+    assert ws_l.numel() > 2048                                   # dW's contraction split
 
     def run():
         tpm.tp_mlp_fwd(X, Wu, Wd, H, stack[1], T=T, rank=1, act=_abi.ACT_GELU_TANH, num_chunks=4, workspace=ws_f)
@@ -1025,10 +1034,11 @@ def test_graph_replays_match_eager():
         tpm.tp_mlp_fwd(xq, wuq, wdq, H8, P8, T=T, rank=0, act=_abi.ACT_RELU, scales=scales, h_scale_out=sH,
                        num_chunks=4, workspace=ws_8)
         tpm.seq_chunk_gemm(a, b, Yk, workspace=ws_k)
+        tpm.tp_linear_bwd(lx, lw, ldy, ldW, ldX, workspace=ws_l)
 
     run()
     sync()
-    ref = [t.clone() for t in (H, stack, out, H8, P8, sH, Yk)]
+    ref = [t.clone() for t in (H, stack, out, H8, P8, sH, Yk, ldW, ldX)]
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -1039,13 +1049,13 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(g):
         run()
     for rep in range(3):
-        for t in (H, out, H8, P8, sH, Yk):
+        for t in (H, out, H8, P8, sH, Yk, ldW, ldX):
             t.zero_()
         stack[1].zero_()
         sync()
         g.replay()
         sync()
-        for got, want in zip((H, stack, out, H8, P8, sH, Yk), ref):
+        for got, want in zip((H, stack, out, H8, P8, sH, Yk, ldW, ldX), ref):
             assert torch.equal(got, want), rep
 
 
