@@ -303,6 +303,7 @@ __device__ __forceinline__ void store_oct(void* base, int64_t ld, bool f32, int 
 
 // Gated forward epilogue of 8 output columns: g, u are the gate and up
 // products; aux (optional) keeps [G | U], Y = act(G) * U.
+template <int ACT>
 __device__ __forceinline__ void epi_gated_oct(const GemmParams& p, const float (&g)[8], const float (&u)[8], int row,
                                               int col) {
   if (p.aux) {
@@ -311,10 +312,12 @@ __device__ __forceinline__ void epi_gated_oct(const GemmParams& p, const float (
   }
   float h[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = act_fwd(g[e], p.act) * u[e];
+  for (int e = 0; e < 8; ++e) h[e] = act_fwd_c<ACT>(g[e]) * u[e];
   store_oct(p.Y, p.ldy, p.y_f32, row, col, h);
 }
 
+// (ACT: the activation p.act, fixed at compile time by with_act)
+template <int ACT>
 __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax) {
   if (p.epi == EPI_DGATED) {
     // v = dH; aux = [G | U]: Y[:, col] = dG = dH U act'(G), Y[:, N + col] = dU = dH act(G)
@@ -323,8 +326,8 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
     load_oct(p.aux, p.ldaux, p.aux_f32, row, p.gu_off + col, u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      du[e] = v[e] * act_fwd(g[e], p.act);
-      v[e] = v[e] * u[e] * act_grad(g[e], p.act);
+      du[e] = v[e] * act_fwd_c<ACT>(g[e]);
+      v[e] = v[e] * u[e] * act_grad_c<ACT>(g[e]);
     }
     store_oct(p.Y, p.ldy, p.y_f32, row, p.gu_off + col, du);
   } else if (p.epi == EPI_DACT) {
@@ -343,7 +346,7 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= act_grad(z[e], p.act);
+    for (int e = 0; e < 8; ++e) v[e] *= act_grad_c<ACT>(z[e]);
   } else {
     if (p.aux) {
       if (p.aux_f32) {
@@ -358,9 +361,9 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
         *(i32x4*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
       }
     }
-    if (p.act != ACT_NONE) {
+    if constexpr (ACT != ACT_NONE) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = act_fwd(v[e], p.act);
+      for (int e = 0; e < 8; ++e) v[e] = act_fwd_c<ACT>(v[e]);
     }
   }
   if (p.y_f32) {
@@ -635,6 +638,8 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         // staged columns 0..31 are the gate products and 32..63 the up
         // products of the wave's 32 output columns: 8 of each per lane, 4
         // lanes per row
+        with_act(p.act, [&](auto ac) {
+        constexpr int ACT = decltype(ac)::value;
 #pragma unroll 1
         for (int it = 0; it < EPI_ROWS / 16; ++it) {
           const int rl = it * 16 + (lane >> 2);
@@ -650,14 +655,17 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
                                 g1[0] * scale, g1[1] * scale, g1[2] * scale, g1[3] * scale};
             const float u[8] = {u0[0] * scale, u0[1] * scale, u0[2] * scale, u0[3] * scale,
                                 u1[0] * scale, u1[1] * scale, u1[2] * scale, u1[3] * scale};
-            epi_gated_oct(p, g, u, row, col);
+            epi_gated_oct<ACT>(p, g, u, row, col);
           }
         }
+        });
       } else if (FP8 && p.y_q_scale) {
         // fp8 output with a scale fixed before the call (delayed scaling):
         // codes e4m3(v * fp32(1 / s)), nearest-even, saturating; amax of the
         // fp32 values quantised
         const float inv = 1.0f / *p.y_q_scale;
+        with_act(p.act, [&](auto ac) {
+        constexpr int ACT = decltype(ac)::value;
 #pragma unroll 1
         for (int it = 0; it < EPI_ROWS / 8; ++it) {
           const int rl = it * 8 + (lane >> 3);
@@ -673,7 +681,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float h = act_fwd(v[e], p.act);
+              const float h = act_fwd_c<ACT>(v[e]);
               lmax = fmaxf(lmax, fabsf(h));
               const uint32_t q = f32_to_e4m3_rne_sat(h * inv);
               if (e < 4) lo |= q << (8 * e);
@@ -682,12 +690,15 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
           }
         }
+        });
       } else if (FP8 && p.y_mx) {
         // MXFP8 output: each 32-column block of a row (4 lanes) shares one
         // scale 2^(E-127), E = exponent field of the block's amax - 8 (0 for
         // a zero block); codes are e4m3(v * 2^(127-E)), nearest-even,
         // saturating.  The four lanes of a block always share their row and
         // validity (N % 32 == 0), so the shuffles stay inside live groups.
+        with_act(p.act, [&](auto ac) {
+        constexpr int ACT = decltype(ac)::value;
 #pragma unroll 1
         for (int it = 0; it < EPI_ROWS / 8; ++it) {
           const int rl = it * 8 + (lane >> 3);
@@ -703,7 +714,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           float m = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            v[e] = act_fwd(v[e], p.act);
+            v[e] = act_fwd_c<ACT>(v[e]);
             m = fmaxf(m, fabsf(v[e]));
           }
           m = fmaxf(m, __shfl_xor(m, 1, 64));
@@ -722,8 +733,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
               p.y_mx[mx_scale_offset((uint32_t)row, (uint32_t)col >> 5, (uint32_t)p.y_mx_steps)] = (uint8_t)E;
           }
         }
+        });
       } else {
       // read back 8 consecutive columns per lane, 8 lanes per row
+      with_act(p.act, [&](auto ac) {
+      constexpr int ACT = decltype(ac)::value;
 #pragma unroll 1
       for (int it = 0; it < EPI_ROWS / 8; ++it) {
         const int rl = it * 8 + (lane >> 3);
@@ -741,10 +755,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           } else {
             float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
                           v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
-            epi_oct(p, v, row, col, lmax);
+            epi_oct<ACT>(p, v, row, col, lmax);
           }
         }
       }
+      });
       }
     });
     if (p.amax) {
@@ -829,6 +844,8 @@ __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
   const int64_t total = (int64_t)p.M * n8;
   const int64_t plane = (int64_t)p.M * p.N;
   float lmax = 0.f;
+  with_act(p.act, [&](auto ac) {
+  constexpr int ACT = decltype(ac)::value;
   for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total; w += (int64_t)gridDim.x * blockDim.x) {
     const int row = (int)(w / n8);
     const int col = (int)(w - (int64_t)row * n8) * 8;
@@ -841,8 +858,9 @@ __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
     }
     float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
                   a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
-    epi_oct(p, v, row, col, lmax);
+    epi_oct<ACT>(p, v, row, col, lmax);
   }
+  });
   if (p.amax) {
     lmax = wave_max(lmax);
     if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));

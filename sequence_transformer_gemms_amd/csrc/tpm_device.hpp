@@ -124,46 +124,88 @@ __device__ inline uint8_t f32_to_e5m2_rne_sat(float f) {
 // ------------------------------------------------------------ activations
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
 
-__device__ inline float act_fwd(float z, int act) {
-  switch (act) {
-    case ACT_RELU: return z > 0.f ? z : 0.f;
+// Activation and its derivative with the activation fixed at compile time,
+// so that element loops carry no per-element dispatch; act_fwd / act_grad
+// take it at run time.
+template <int ACT>
+__device__ inline float act_fwd_c(float z) {
+  if constexpr (ACT == ACT_RELU) {
+    return z > 0.f ? z : 0.f;
+  } else if constexpr (ACT == ACT_GELU_ERF) {
     // z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2: no cancellation in 1 + erf(.)
     // for negative z, where the product is small
-    case ACT_GELU_ERF: return 0.5f * z * erfcf(-z * 0.70710678118654752f);
-    case ACT_GELU_TANH: {
-      // 0.5 z (1 + tanh u) = z / (1 + exp(-2u)), free of the same cancellation
-      float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-      return z / (1.f + expf(-2.f * u));
-    }
-    case ACT_SILU: return z / (1.f + expf(-z));  // z sigma(z); -0 once expf overflows
+    return 0.5f * z * erfcf(-z * 0.70710678118654752f);
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    // 0.5 z (1 + tanh u) = z / (1 + exp(-2u)), free of the same cancellation
+    float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+    return z / (1.f + expf(-2.f * u));
+  } else if constexpr (ACT == ACT_SILU) {
+    return z / (1.f + expf(-z));  // z sigma(z); -0 once expf overflows
+  } else {
+    return z;
+  }
+}
+
+template <int ACT>
+__device__ inline float act_grad_c(float z) {
+  if constexpr (ACT == ACT_RELU) {
+    return z > 0.f ? 1.f : 0.f;
+  } else if constexpr (ACT == ACT_GELU_ERF) {
+    float cdf = 0.5f * erfcf(-z * 0.70710678118654752f);
+    float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+    return cdf + z * pdf;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    // with s = (1 + tanh u) / 2 = 1 / (1 + e), e = exp(-2u):
+    // d/dz = s + 2 z s (1 - s) du/dz, and 1 - s = e s
+    float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+    float e = expf(-2.f * u);
+    float sg = 1.f / (1.f + e);
+    float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
+    return sg + 2.f * z * sg * (e * sg) * du;
+  } else if constexpr (ACT == ACT_SILU) {
+    // sigma(z) (1 + z sigma(-z)), both logistic values taken directly so
+    // that neither 1 - sigma nor inf * 0 appears at large |z|
+    const float sp = 1.f / (1.f + expf(-z)), sn = 1.f / (1.f + expf(z));
+    return sp * (1.f + z * sn);
+  } else {
+    return 1.f;
+  }
+}
+
+__device__ inline float act_fwd(float z, int act) {
+  switch (act) {
+    case ACT_RELU: return act_fwd_c<ACT_RELU>(z);
+    case ACT_GELU_ERF: return act_fwd_c<ACT_GELU_ERF>(z);
+    case ACT_GELU_TANH: return act_fwd_c<ACT_GELU_TANH>(z);
+    case ACT_SILU: return act_fwd_c<ACT_SILU>(z);
     default: return z;
   }
 }
 
 __device__ inline float act_grad(float z, int act) {
   switch (act) {
-    case ACT_RELU: return z > 0.f ? 1.f : 0.f;
-    case ACT_GELU_ERF: {
-      float cdf = 0.5f * erfcf(-z * 0.70710678118654752f);
-      float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
-      return cdf + z * pdf;
-    }
-    case ACT_GELU_TANH: {
-      // with s = (1 + tanh u) / 2 = 1 / (1 + e), e = exp(-2u):
-      // d/dz = s + 2 z s (1 - s) du/dz, and 1 - s = e s
-      float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-      float e = expf(-2.f * u);
-      float sg = 1.f / (1.f + e);
-      float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
-      return sg + 2.f * z * sg * (e * sg) * du;
-    }
-    case ACT_SILU: {
-      // sigma(z) (1 + z sigma(-z)), both logistic values taken directly so
-      // that neither 1 - sigma nor inf * 0 appears at large |z|
-      const float sp = 1.f / (1.f + expf(-z)), sn = 1.f / (1.f + expf(z));
-      return sp * (1.f + z * sn);
-    }
+    case ACT_RELU: return act_grad_c<ACT_RELU>(z);
+    case ACT_GELU_ERF: return act_grad_c<ACT_GELU_ERF>(z);
+    case ACT_GELU_TANH: return act_grad_c<ACT_GELU_TANH>(z);
+    case ACT_SILU: return act_grad_c<ACT_SILU>(z);
     default: return 1.f;
+  }
+}
+
+// Calls f(std::integral_constant-like tag) with the activation as a
+// compile-time value: one branch per epilogue pass instead of per element.
+template <int N>
+struct ActTag {
+  static constexpr int value = N;
+};
+template <class F>
+__device__ __forceinline__ void with_act(int act, F&& f) {
+  switch (act) {
+    case ACT_RELU: f(ActTag<ACT_RELU>{}); break;
+    case ACT_GELU_ERF: f(ActTag<ACT_GELU_ERF>{}); break;
+    case ACT_GELU_TANH: f(ActTag<ACT_GELU_TANH>{}); break;
+    case ACT_SILU: f(ActTag<ACT_SILU>{}); break;
+    default: f(ActTag<ACT_NONE>{}); break;
   }
 }
 
