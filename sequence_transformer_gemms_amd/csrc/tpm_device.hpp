@@ -124,6 +124,30 @@ __device__ inline uint8_t f32_to_e5m2_rne_sat(float f) {
 // ------------------------------------------------------------ activations
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
 
+// Elementary functions of the epilogues on the hardware transcendental
+// units (v_exp_f32 = 2^x, v_rcp_f32 = 1/x, each within about one ulp):
+// exp(x) = 2^(x log2 e) and a / b = a * (1 / b), a few instructions where
+// the library's correctly rounded forms take dozens per element.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Standard normal tail Q(z) = P(Z > z) = erfc(z / sqrt 2) / 2 for z >= 0, and
+// exp(-z^2 / 2) beside it, with erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 +
+// t a5)))) exp(-x^2), t = 1 / (1 + p x): Hastings' approximation as given
+// by Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
+// (absolute error below 1.5e-7 for x >= 0).  Q carries that absolute
+// error, so Phi(z) = 1 - Q(z) (z >= 0) and Phi(z) = Q(-z) (z < 0) are
+// accurate to about 2e-7 absolute, GeLU(z) = z Phi(z) to 3e-6 relative for
+// z >= -2 and 2.2e-7 absolute below.
+__device__ __forceinline__ float normal_tail(float az, float& e) {
+  const float x = az * 0.70710678118654752f;
+  const float t = fast_rcp(1.f + 0.3275911f * x);
+  e = fast_exp(-x * x);
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f +
+                                                                                 t * 1.061405429f))));
+  return 0.5f * poly * e;
+}
+
 // Activation and its derivative with the activation fixed at compile time,
 // so that element loops carry no per-element dispatch; act_fwd / act_grad
 // take it at run time.
@@ -132,15 +156,17 @@ __device__ inline float act_fwd_c(float z) {
   if constexpr (ACT == ACT_RELU) {
     return z > 0.f ? z : 0.f;
   } else if constexpr (ACT == ACT_GELU_ERF) {
-    // z * Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2: no cancellation in 1 + erf(.)
+    // z * Phi(z), Phi from the normal tail: no cancellation in 1 + erf(.)
     // for negative z, where the product is small
-    return 0.5f * z * erfcf(-z * 0.70710678118654752f);
+    float e;
+    const float q = normal_tail(fabsf(z), e);
+    return z * (z >= 0.f ? 1.f - q : q);
   } else if constexpr (ACT == ACT_GELU_TANH) {
     // 0.5 z (1 + tanh u) = z / (1 + exp(-2u)), free of the same cancellation
     float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-    return z / (1.f + expf(-2.f * u));
+    return z * fast_rcp(1.f + fast_exp(-2.f * u));
   } else if constexpr (ACT == ACT_SILU) {
-    return z / (1.f + expf(-z));  // z sigma(z); -0 once expf overflows
+    return z * fast_rcp(1.f + fast_exp(-z));  // z sigma(z); -0 once exp overflows
   } else {
     return z;
   }
@@ -151,21 +177,23 @@ __device__ inline float act_grad_c(float z) {
   if constexpr (ACT == ACT_RELU) {
     return z > 0.f ? 1.f : 0.f;
   } else if constexpr (ACT == ACT_GELU_ERF) {
-    float cdf = 0.5f * erfcf(-z * 0.70710678118654752f);
-    float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
-    return cdf + z * pdf;
+    // Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi)
+    float e;
+    const float q = normal_tail(fabsf(z), e);
+    const float cdf = z >= 0.f ? 1.f - q : q;
+    return cdf + z * (e * 0.39894228040143268f);
   } else if constexpr (ACT == ACT_GELU_TANH) {
-    // with s = (1 + tanh u) / 2 = 1 / (1 + e), e = exp(-2u):
-    // d/dz = s + 2 z s (1 - s) du/dz, and 1 - s = e s
+    // with s = (1 + tanh u) / 2 = sigma(2u): d/dz = s + 2 z s (1 - s) du/dz,
+    // 1 - s = sigma(-2u) taken directly (no inf * 0 once exp(-2u) overflows)
     float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-    float e = expf(-2.f * u);
-    float sg = 1.f / (1.f + e);
+    float sg = fast_rcp(1.f + fast_exp(-2.f * u));
+    float sn = fast_rcp(1.f + fast_exp(2.f * u));
     float du = 0.79788456080286536f * (1.f + 3.f * 0.044715f * z * z);
-    return sg + 2.f * z * sg * (e * sg) * du;
+    return sg + 2.f * z * sg * sn * du;
   } else if constexpr (ACT == ACT_SILU) {
     // sigma(z) (1 + z sigma(-z)), both logistic values taken directly so
     // that neither 1 - sigma nor inf * 0 appears at large |z|
-    const float sp = 1.f / (1.f + expf(-z)), sn = 1.f / (1.f + expf(z));
+    const float sp = fast_rcp(1.f + fast_exp(-z)), sn = fast_rcp(1.f + fast_exp(z));
     return sp * (1.f + z * sn);
   } else {
     return 1.f;

@@ -1143,3 +1143,32 @@ def test_linear_bwd_empty_contractions():
     sync()
     assert torch.count_nonzero(dW).item() == 0
     assert torch.count_nonzero(dX).item() == 0
+
+
+@pytest.mark.parametrize("act", [_abi.ACT_GELU_ERF, _abi.ACT_GELU_TANH, _abi.ACT_SILU, _abi.ACT_RELU]
+                         if torch.cuda.is_available() else [])
+def test_epilogue_activation_accuracy(act):
+    # the epilogue's activation and derivative on exact inputs: a rank-one
+    # product puts every bf16 value z of [-12, 12] through the forward
+    # epilogue (Y = act(z)) and, with Z = z saved and a product of 1, the
+    # DACT epilogue (Y = act'(z)), fp32 outputs, against the oracle's float64
+    # functions: within 1e-5 relative + 3e-7 absolute (the hardware exp / rcp
+    # and, for GeLU-erf, Abramowitz & Stegun 7.1.26 with its 1.5e-7 bound)
+    z = np.unique(formats.round_bf16(np.linspace(-12.0, 12.0, 20001)))
+    z = np.concatenate([z, np.zeros((-len(z)) % 8)])
+    M, K, N = len(z), 16, 8
+    a = np.zeros((M, K), np.float32)
+    a[:, 0] = z
+    b = np.zeros((K, N), np.float32)
+    b[0, :] = 1.0
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(dev_bf16(a), dev_bf16(b), Y, act=act)
+    ones = np.zeros((M, K), np.float32)
+    ones[:, 0] = 1.0
+    Z = dev_f32(np.repeat(z[:, None], N, axis=1))
+    G = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(dev_bf16(ones), dev_bf16(b), G, epilogue=_abi.EPI_DACT, act=act, aux=Z)
+    sync()
+    for got, ref in ((f64(Y)[:, 0], ops.act_fwd(z, act)), (f64(G)[:, 0], ops.act_grad(z, act))):
+        assert np.all(np.isfinite(got))
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 3e-7), float(np.max(np.abs(got - ref)))
