@@ -666,12 +666,14 @@ def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10)
 def recorded_traffic():
     """HBM bytes per step of the GEMM launches, as measured with rocprofv3
     FETCH_SIZE / WRITE_SIZE (profiles/gemm_traffic.md), or None when the GEMM
-    source has changed since the counters were taken."""
+    sources (kernel file and the two headers it includes) have changed since
+    the counters were taken."""
     import hashlib
     import re
     try:
         text = open(os.path.join(ROOT, "profiles", "gemm_traffic.md")).read()
-        src = open(os.path.join(ROOT, "sequence_transformer_gemms_amd", "csrc", "gemm_mfma.hip"), "rb").read()
+        src = b"".join(open(os.path.join(ROOT, "sequence_transformer_gemms_amd", "csrc", f), "rb").read()
+                       for f in ("gemm_mfma.hip", "tpm_device.hpp", "tpm_internal.hpp"))
     except OSError:
         return None
     m_b = re.search(r"traffic_bytes_per_step:\s*(\d+)", text)
