@@ -442,7 +442,8 @@ def run_yardstick(torch, tpm):
     """Yardsticks for the GEMM kernel on one square bf16 product (M = N = K =
     8192, random normal operands): ours and torch.matmul (hipBLASLt) in the
     three operand layouts (A and B row-major; B stored [N, K]; A stored
-    [K, M]), then ours on streams restricted to 128 and 64 CUs, which shows
+    [K, M]), then ours on streams restricted to a half and a quarter of the
+    CUs (128 and 64 on MI355X), which shows
     how the per-CU rate depends on how many CUs share the L2s and the
     fabric.  Median of 10 calls each, HIP events; prints one JSON line."""
     n = 8192
@@ -474,12 +475,13 @@ def run_yardstick(torch, tpm):
     for name, (ours, blas) in layouts.items():
         out[f"ours_{name}"] = round(fl / (med(ours) * 1e-3) / 1e12, 1)
         out[f"hipblaslt_{name}"] = round(fl / (med(blas) * 1e-3) / 1e12, 1)
-    for keep in (128, 64):
-        comp, _ = tpm.masked_streams(producer_cus=256 - keep)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for keep in (ncu // 2, ncu // 4):
+        comp, _ = tpm.masked_streams(producer_cus=ncu - keep)
         with torch.cuda.stream(comp):
             t = med(lambda: tpm.seq_chunk_gemm(a, b, y), reps=6, stream=comp)
         out[f"ours_NN_{keep}cus"] = round(fl / (t * 1e-3) / 1e12, 1)
-        out[f"ours_NN_{keep}cus_per_cu_as_256"] = round(fl / (t * 1e-3) / 1e12 * 256 / keep, 1)
+        out[f"ours_NN_{keep}cus_per_cu_as_{ncu}"] = round(fl / (t * 1e-3) / 1e12 * ncu / keep, 1)
     print(json.dumps({"yardstick": out}), flush=True)
 
 
