@@ -42,7 +42,11 @@ typedef enum { TPM_F32 = 0, TPM_BF16 = 1, TPM_FP8_E4M3 = 2, TPM_FP8_E5M2 = 3 } t
 /* Activations.  GELU_ERF: 0.5 z (1 + erf(z / sqrt 2)); GELU_TANH: the tanh
  * approximation; RELU: max(z, 0) with derivative 1 only where z > 0
  * ("Tensor parallelism" algorithm page, section "Code"); SILU: z sigma(z),
- * sigma the logistic function (the gate of SwiGLU). */
+ * sigma the logistic function (the gate of SwiGLU).  Evaluated in fp32 in
+ * the GEMM epilogues on the hardware exp2 / reciprocal units; erf through
+ * Hastings' approximation (Abramowitz & Stegun eq. 7.1.26, absolute error
+ * below 1.5e-7): each activation and its derivative are within 1e-5
+ * relative + 3e-7 absolute of the exact function. */
 typedef enum {
   TPM_ACT_NONE = 0, TPM_ACT_RELU = 1, TPM_ACT_GELU_ERF = 2, TPM_ACT_GELU_TANH = 3, TPM_ACT_SILU = 4
 } tpm_act;
