@@ -296,7 +296,7 @@ __device__ __forceinline__ void store_oct(void* base, int64_t ld, bool f32, int 
     i32x4 yy;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      yy[e] = (int)((uint32_t)f32_to_bf16_rne(v[2 * e]) | ((uint32_t)f32_to_bf16_rne(v[2 * e + 1]) << 16));
+      yy[e] = (int)pack_bf16x2(v[2 * e], v[2 * e + 1]);
     *(i32x4*)((uint16_t*)base + (int64_t)row * ld + col) = yy;
   }
 }
@@ -357,7 +357,7 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
         i32x4 zz;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          zz[e] = (int)((uint32_t)f32_to_bf16_rne(v[2 * e]) | ((uint32_t)f32_to_bf16_rne(v[2 * e + 1]) << 16));
+          zz[e] = (int)pack_bf16x2(v[2 * e], v[2 * e + 1]);
         *(i32x4*)((uint16_t*)p.aux + (int64_t)row * p.ldaux + col) = zz;
       }
     }
@@ -378,8 +378,9 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
     i32x4 yy;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t b0 = f32_to_bf16_rne(v[2 * e]), b1 = f32_to_bf16_rne(v[2 * e + 1]);
-      yy[e] = (int)(b0 | (b1 << 16));
+      const uint32_t w = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      const uint32_t b0 = w & 0xFFFFu, b1 = w >> 16;
+      yy[e] = (int)w;
       if (p.amax) lmax = fmaxf(lmax, fmaxf(fabsf(bf16_to_f32((uint16_t)b0)), fabsf(bf16_to_f32((uint16_t)b1))));
     }
     *(i32x4*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;

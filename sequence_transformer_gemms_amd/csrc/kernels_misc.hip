@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(1024) reduce_bf16_vec(int T, int64_t rows, int
     i32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      o[e] = (int)((uint32_t)f32_to_bf16_rne(s[2 * e]) | ((uint32_t)f32_to_bf16_rne(s[2 * e + 1]) << 16));
+      o[e] = (int)pack_bf16x2(s[2 * e], s[2 * e + 1]);
     __builtin_nontemporal_store(o, (i32x4*)(out + r * ldo + c));
   }
 }

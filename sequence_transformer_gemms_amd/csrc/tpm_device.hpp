@@ -42,6 +42,14 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, a in
+// the low half: one v_cvt_pk_bf16_f32.  Equal to f32_to_bf16_rne on every
+// non-NaN input (a NaN stays a quiet NaN, not necessarily 0x7FC0).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 __device__ inline float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }

@@ -1172,3 +1172,37 @@ def test_epilogue_activation_accuracy(act):
     for got, ref in ((f64(Y)[:, 0], ops.act_fwd(z, act)), (f64(G)[:, 0], ops.act_grad(z, act))):
         assert np.all(np.isfinite(got))
         assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 3e-7), float(np.max(np.abs(got - ref)))
+
+
+def test_bf16_output_rounding_ties_and_subnormals():
+    # the epilogue's fp32 -> bf16 rounding on exact fp32 inputs: Y = x + y
+    # with x, y bf16 whose exponents differ by at most 16 (so x + y is exact
+    # in fp32 but has bits below bf16 precision), exact ties (y = half an
+    # ulp of x, both parities), signs, and subnormal magnitudes; the bf16
+    # output must equal the oracle's nearest-even rounding bit for bit
+    g = np.random.default_rng(131)
+    n = 1 << 14
+    x = formats.round_bf16(g.standard_normal(n) * np.exp2(g.integers(-20, 20, n)))
+    y = formats.round_bf16(x * np.exp2(-g.integers(0, 17, n).astype(np.float64)) * g.choice([-1.0, 1.0], n)
+                           * (1 + g.integers(0, 128, n) / 128.0))
+    ties_x = formats.round_bf16(np.abs(g.standard_normal(1024)) + 1.0)
+    ties_y = np.exp2(np.floor(np.log2(ties_x)) - 8)                  # half an ulp of x
+    sub_x = formats.round_bf16(g.standard_normal(1024) * 2.0 ** -130)
+    sub_y = formats.round_bf16(g.standard_normal(1024) * 2.0 ** -133)
+    X = np.concatenate([x, ties_x, sub_x])
+    Yv = np.concatenate([y, ties_y, sub_y])
+    ok = np.isfinite(X) & np.isfinite(Yv)
+    X, Yv = X[ok], Yv[ok]
+    assert np.all((X + Yv).astype(np.float32).astype(np.float64) == X + Yv)   # exact in fp32
+    M = (len(X) + 7) // 8 * 8
+    a = np.zeros((M, 8), np.float64)
+    a[:len(X), 0], a[:len(X), 1] = X, Yv
+    b = np.zeros((8, 8), np.float64)
+    b[0, :] = b[1, :] = 1.0
+    out = torch.empty(M, 8, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(si.to_bf16(a.astype(np.float32)).cuda(), si.to_bf16(b.astype(np.float32)).cuda(), out)
+    sync()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)[:len(X), 0]
+    # the accumulator starts at +0, so -0 + -0 gives +0 there
+    want = formats.f32_to_bf16_bits((0.0 + X + Yv).astype(np.float32))
+    assert np.array_equal(got, want)
