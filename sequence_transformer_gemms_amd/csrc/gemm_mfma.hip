@@ -316,9 +316,11 @@ __device__ __forceinline__ void epi_gated_oct(const GemmParams& p, const float (
   store_oct(p.Y, p.ldy, p.y_f32, row, col, h);
 }
 
-// (ACT: the activation p.act, fixed at compile time by with_act)
-template <int ACT>
-__device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax) {
+// (ACT: the activation p.act, fixed at compile time by with_act; ZPRE: the
+// DACT epilogue's bf16 Z of these 8 columns already loaded, in zpre)
+template <int ACT, bool ZPRE = false>
+__device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax,
+                                        i32x4 zpre = i32x4{0, 0, 0, 0}) {
   if (p.epi == EPI_DGATED) {
     // v = dH; aux = [G | U]: Y[:, col] = dG = dH U act'(G), Y[:, N + col] = dU = dH act(G)
     float g[8], u[8], du[8];
@@ -332,7 +334,13 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
     store_oct(p.Y, p.ldy, p.y_f32, row, p.gu_off + col, du);
   } else if (p.epi == EPI_DACT) {
     float z[8];
-    if (p.aux_f32) {
+    if constexpr (ZPRE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[2 * e] = bf16_to_f32((uint16_t)((uint32_t)zpre[e] & 0xFFFFu));
+        z[2 * e + 1] = bf16_to_f32((uint16_t)((uint32_t)zpre[e] >> 16));
+      }
+    } else if (p.aux_f32) {
       const f32x4* src = (const f32x4*)((const float*)p.aux + (int64_t)row * p.ldaux + col);
       const f32x4 z0 = src[0], z1 = src[1];
 #pragma unroll
@@ -739,6 +747,40 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       // read back 8 consecutive columns per lane, 8 lanes per row
       with_act(p.act, [&](auto ac) {
       constexpr int ACT = decltype(ac)::value;
+      if (p.epi == EPI_DACT && !p.aux_f32 && p.splits == 1) {
+        // DACT with a bf16 Z: the Z loads of four row groups are issued
+        // together before any is used, instead of one exposed load latency
+        // per row group
+        constexpr int GRP = 4;
+        static_assert((EPI_ROWS / 8) % GRP == 0, "row groups");
+#pragma unroll 1
+        for (int it0 = 0; it0 < EPI_ROWS / 8; it0 += GRP) {
+          i32x4 zq[GRP];
+#pragma unroll
+          for (int g = 0; g < GRP; ++g) {
+            const int row = tl.m0 + wm + EPI_ROWS * rp + (it0 + g) * 8 + (lane >> 3);
+            const int col = tl.n0 + wn + EPI_COLS * cp + (lane & 7) * 8;
+            zq[g] = i32x4{0, 0, 0, 0};
+            if (row < tl.m_end && col < p.N)
+              zq[g] = *(const i32x4*)((const uint16_t*)p.aux + (int64_t)row * p.ldaux + col);
+          }
+#pragma unroll
+          for (int g = 0; g < GRP; ++g) {
+            const int rl = (it0 + g) * 8 + (lane >> 3);
+            const int cl = (lane & 7) * 8;
+            const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
+            const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+            const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+            const int col = tl.n0 + wn + EPI_COLS * cp + cl;
+            if (row < tl.m_end && col < p.N) {
+              float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                            v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+              epi_oct<ACT, true>(p, v, row, col, lmax, zq[g]);
+            }
+          }
+        }
+        return;
+      }
 #pragma unroll 1
       for (int it = 0; it < EPI_ROWS / 8; ++it) {
         const int rl = it * 8 + (lane >> 3);

@@ -64,13 +64,36 @@ def test_every_gemm_variant_is_compiled(asm):
     assert set(meta) == set(bodies)
 
 
+def k_loops(body):
+    """Instruction lists of the K loops of a kernel body: loop bodies (a label
+    and the backward branch to it) holding at least 16 MFMAs."""
+    code = [ln for ln in body if ln and not ln.startswith(";")]
+    labels = {}
+    for i, ln in enumerate(code):
+        m = re.match(r"^(\.LBB\d+_\d+):", ln)
+        if m:
+            labels[m.group(1)] = i
+    loops, seen = [], set()
+    for i, ln in enumerate(code):
+        m = re.match(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\d+_\d+)", ln)
+        if m and m.group(1) in labels and labels[m.group(1)] < i and m.group(1) not in seen:
+            seg = code[labels[m.group(1)]:i + 1]
+            if sum(x.startswith("v_mfma") for x in seg) >= 16 and len(seg) < 1000:
+                seen.add(m.group(1))
+                loops.append(seg)
+    return loops
+
+
 def test_no_full_vmcnt_wait_before_lds_reads(asm):
+    # in the K loop (the epilogue may wait for its own global loads)
     bodies, _ = kernels(asm)
     for name, body in bodies.items():
-        code = [ln for ln in body if ln and not ln.startswith(";")]
-        bad = [i for i in range(len(code) - 1)
-               if re.match(r"s_waitcnt\s+vmcnt\(0\)", code[i]) and code[i + 1].startswith("ds_read")]
-        assert not bad, f"{name}: {len(bad)} x 's_waitcnt vmcnt(0)' right before an LDS read"
+        loops = k_loops(body)
+        assert loops, f"{name}: no K loop found"
+        for code in loops:
+            bad = [i for i in range(len(code) - 1)
+                   if re.match(r"s_waitcnt\s+vmcnt\(0\)", code[i]) and code[i + 1].startswith("ds_read")]
+            assert not bad, f"{name}: {len(bad)} x 's_waitcnt vmcnt(0)' right before an LDS read in the K loop"
 
 
 def test_no_register_spills_and_lds_fits(asm):
