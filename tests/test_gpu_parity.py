@@ -1206,3 +1206,21 @@ def test_bf16_output_rounding_ties_and_subnormals():
     # the accumulator starts at +0, so -0 + -0 gives +0 there
     want = formats.f32_to_bf16_bits((0.0 + X + Yv).astype(np.float32))
     assert np.array_equal(got, want)
+
+
+def test_dact_epilogue_integer_exact_ragged_and_strided_z():
+    # DACT with ReLU' in {0, 1} on integer products is exact: Y must equal
+    # bf16(A.B * relu'(Z)) bit for bit.  Ragged rows and columns (300 =
+    # 256 + 44, 264 = 256 + 8) exercise the masked loads of Z, and Z is a view
+    # into a wider array (leading dimension N + 24)
+    M, N, K = 300, 264, 200
+    a = si.small_ints((M, K), 141)
+    b = si.small_ints((N, K), 142)
+    zfull = si.small_ints((M, N + 24), 143).astype(np.float32) - 0.5      # no zeros: relu' is unambiguous
+    Zd = dev_bf16(zfull)[:, :N]
+    assert Zd.stride(0) == N + 24
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(dev_bf16(a), dev_bf16(b), Y, trans_b=True, epilogue=_abi.EPI_DACT, act=_abi.ACT_RELU, aux=Zd)
+    sync()
+    exact = (a.astype(np.float64) @ b.astype(np.float64).T) * (zfull[:, :N] > 0)
+    assert np.array_equal(f64(Y), formats.round_bf16(exact))
