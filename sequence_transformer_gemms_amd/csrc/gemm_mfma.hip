@@ -687,16 +687,15 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
                           v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
             if (p.aux) store_oct(p.aux, p.ldaux, false, row, col, v);  // pre-activation, bf16
-            uint32_t lo = 0, hi = 0;
+            float q[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float h = act_fwd_c<ACT>(v[e]);
               lmax = fmaxf(lmax, fabsf(h));
-              const uint32_t q = f32_to_e4m3_rne_sat(h * inv);
-              if (e < 4) lo |= q << (8 * e);
-              else hi |= q << (8 * (e - 4));
+              q[e] = h * inv;
             }
-            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) =
+                make_uint2(fp8x4<false>(q[0], q[1], q[2], q[3]), fp8x4<false>(q[4], q[5], q[6], q[7]));
           }
         }
         });
@@ -731,13 +730,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           if (ok) {
             const int E = max((int)((__float_as_uint(m) >> 23) & 0xFFu) - 8, 0);
             const float inv = __uint_as_float((uint32_t)(254 - E) << 23);   // 2^(127 - E)
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              lo |= (uint32_t)f32_to_e4m3_rne_sat(v[e] * inv) << (8 * e);
-              hi |= (uint32_t)f32_to_e4m3_rne_sat(v[4 + e] * inv) << (8 * e);
-            }
-            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) = make_uint2(lo, hi);
+            *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) =
+                make_uint2(fp8x4<false>(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                           fp8x4<false>(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
             if ((lane & 3) == 0)
               p.y_mx[mx_scale_offset((uint32_t)row, (uint32_t)col >> 5, (uint32_t)p.y_mx_steps)] = (uint8_t)E;
           }

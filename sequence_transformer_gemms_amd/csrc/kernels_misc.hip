@@ -82,17 +82,14 @@ __global__ void __launch_bounds__(256) quant_e4m3(const uint16_t* __restrict__ h
     const int64_t r = v / N8;
     const int64_t c = (v - r * N8) * 8;
     const i32x4 w = __builtin_nontemporal_load((const i32x4*)(h + r * ldh + c));
-    uint32_t lo = 0, hi = 0;
+    float f[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t u = (uint32_t)w[e];
-      const uint32_t c0 = f32_to_e4m3_rne_sat(bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv);
-      const uint32_t c1 = f32_to_e4m3_rne_sat(bf16_to_f32((uint16_t)(u >> 16)) * inv);
-      const uint32_t pair = c0 | (c1 << 8);
-      if (e < 2) lo |= pair << (16 * e);
-      else hi |= pair << (16 * (e - 2));
+      f[2 * e] = bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv;
+      f[2 * e + 1] = bf16_to_f32((uint16_t)(u >> 16)) * inv;
     }
-    *(uint2*)(q + r * ldq + c) = make_uint2(lo, hi);
+    *(uint2*)(q + r * ldq + c) = make_uint2(fp8x4<false>(f[0], f[1], f[2], f[3]), fp8x4<false>(f[4], f[5], f[6], f[7]));
   }
 }
 
@@ -135,21 +132,20 @@ __global__ void __launch_bounds__(256) cast_fp8_t(const uint16_t* __restrict__ x
     const int r = t >> 2, cg = (t & 3) * 16;
     const int64_t row = r0 + r, col = c0 + cg;
     if (row < rows && col < cols) {
-      uint32_t w[4];
+      float f[16];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const i32x4 v = *(const i32x4*)(x + row * ld + col + 8 * h);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t u = (uint32_t)v[e];
-          const float a = bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv, b = bf16_to_f32((uint16_t)(u >> 16)) * inv;
-          const uint32_t ca = E5M2 ? f32_to_e5m2_rne_sat(a) : f32_to_e4m3_rne_sat(a);
-          const uint32_t cb = E5M2 ? f32_to_e5m2_rne_sat(b) : f32_to_e4m3_rne_sat(b);
-          const int k = 4 * h + e;  // pair index 0..7 -> bytes 2k, 2k+1
-          if (k % 2 == 0) w[k / 2] = ca | (cb << 8);
-          else w[k / 2] |= (ca << 16) | (cb << 24);
+          f[8 * h + 2 * e] = bf16_to_f32((uint16_t)(u & 0xFFFFu)) * inv;
+          f[8 * h + 2 * e + 1] = bf16_to_f32((uint16_t)(u >> 16)) * inv;
         }
       }
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = fp8x4<E5M2>(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
       if (q) *(uint4*)(q + row * ldq + col) = make_uint4(w[0], w[1], w[2], w[3]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) tile[r][cg + i] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));

@@ -129,6 +129,38 @@ __device__ inline uint8_t f32_to_e5m2_rne_sat(float f) {
   return (uint8_t)(sign | code);
 }
 
+// Four fp32 values to four OCP fp8 codes (e4m3fn, or e5m2 when E5M2), byte e
+// of the result holding value e: the same codes as the integer encoders
+// above.  The hardware pack conversion (two values per instruction) rounds to
+// nearest-even and keeps the sign of zero, but turns a finite magnitude past
+// the format's largest value into NaN instead of saturating, so each input is
+// clamped to +-largest first; a group holding a NaN takes the integer
+// encoders.  The two agree on every fp32 bit pattern (checked exhaustively).
+template <bool E5M2>
+__device__ inline uint32_t fp8x4(float a, float b, float c, float d) {
+  if (__builtin_expect((a != a) | (b != b) | (c != c) | (d != d), 0)) {
+    if (E5M2)
+      return (uint32_t)f32_to_e5m2_rne_sat(a) | (uint32_t)f32_to_e5m2_rne_sat(b) << 8 |
+             (uint32_t)f32_to_e5m2_rne_sat(c) << 16 | (uint32_t)f32_to_e5m2_rne_sat(d) << 24;
+    return (uint32_t)f32_to_e4m3_rne_sat(a) | (uint32_t)f32_to_e4m3_rne_sat(b) << 8 |
+           (uint32_t)f32_to_e4m3_rne_sat(c) << 16 | (uint32_t)f32_to_e4m3_rne_sat(d) << 24;
+  }
+  constexpr float kMax = E5M2 ? 57344.0f : 448.0f;
+  a = fminf(fmaxf(a, -kMax), kMax);
+  b = fminf(fmaxf(b, -kMax), kMax);
+  c = fminf(fmaxf(c, -kMax), kMax);
+  d = fminf(fmaxf(d, -kMax), kMax);
+  int w;
+  if (E5M2) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
 // ------------------------------------------------------------ activations
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
 

@@ -591,6 +591,48 @@ def test_cast_fp8_bit_exact(dt):
     assert sc.item() == float(np.float32(amax / fmax))
 
 
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_cast_fp8_nan_tiny_and_saturating(dt):
+    # the cast's encoder at its edges: NaN elements (either sign; the amax
+    # skips them and they encode as 0x7F), magnitudes spread down through the
+    # format's subnormals to below half its smallest one (negative ones keep
+    # the sign of zero), and values whose scaled product rounds past the
+    # largest finite code (saturate)
+    rows, cols = 64, 128
+    rng = np.random.default_rng(137)
+    x = si.to_bf16(si.normal_f32((rows, cols), 138))
+    xi = x.view(torch.int16)
+    top = 6.5   # fp32(top * fp32(fmax / top)) > fmax for both formats
+    xi[0, :] = torch.from_numpy(formats.round_bf16(np.full(cols, top)).astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    k = np.arange(cols)
+    tiny = np.where(k % 2 == 0, 1.0, -1.0) * top * 2.0 ** -(1 + k % 40) * (1.0 + (k % 7) / 8.0)
+    xi[1, :] = torch.from_numpy(formats.round_bf16(tiny).astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    nan_pos = rng.choice(rows * cols - 2 * cols, size=9, replace=False) + 2 * cols
+    for j, pos in enumerate(nan_pos):
+        xi[pos // cols, pos % cols] = 0x7FC0 if j % 2 == 0 else -0x40   # +NaN / -NaN bf16
+    X = x.cuda()
+    code = _abi.FP8_E5M2 if dt == "e5m2" else _abi.FP8_E4M3
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.cast_fp8(X, code, q=q, qt=qt, scale_out=sc)
+    sync()
+    xv = f64(x)
+    assert np.isnan(xv).sum() == 9
+    fmax = np.float32(57344.0 if dt == "e5m2" else 448.0)
+    amax = np.float32(np.nanmax(np.abs(xv)))
+    assert amax == np.float32(top)
+    inv = np.float32(fmax / amax)
+    prod = (xv * float(inv)).astype(np.float32).astype(np.float64)
+    assert np.all(prod[0] > fmax)
+    want = formats.e5m2_encode(prod) if dt == "e5m2" else formats.e4m3_encode(prod)
+    got = q.cpu().numpy()
+    assert np.all(got[np.isnan(xv)] == 0x7F)
+    assert np.array_equal(got, want)
+    assert np.array_equal(qt.cpu().numpy(), want.T)
+    assert sc.item() == float(np.float32(amax / fmax))
+
+
 def test_fp8_mixed_format_gemm_integer_exact():
     # e5m2 x e4m3 and e4m3 x e5m2 through seq_chunk_gemm: integers in [-3, 3]
     # are exact in both formats, so the fp32 products are exact
