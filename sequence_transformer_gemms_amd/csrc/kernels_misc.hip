@@ -95,23 +95,58 @@ __global__ void __launch_bounds__(256) quant_e4m3(const uint16_t* __restrict__ h
 
 // ------------------------------------------- fp8 backward: amax, casts
 // max |x| of a bf16 [rows, cols] matrix into *out (fp32 bits as uint32,
-// non-negative floats order as integers; *out zeroed beforehand)
+// non-negative floats order as integers; *out zeroed beforehand).  A lane
+// keeps four 16-byte loads in flight: over the flat array when rows are
+// contiguous (DENSE: ld = cols), else along whole rows.  Each work-group
+// folds its 256 lanes' maxima through LDS and issues one atomic: atomics on
+// the one word, one per wave of a grid sized to the matrix, had serialised
+// into most of the kernel's time.
+__device__ inline float absmax_bf16x8(float m, const i32x4& w) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] & 0xFFFFu))));
+    m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] >> 16))));
+  }
+  return m;
+}
+
+template <bool DENSE>
 __global__ void __launch_bounds__(256) amax_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t c8, int64_t ld,
                                                  uint32_t* out) {
+  __shared__ float wmax[4];
   float m = 0.f;
-  const int64_t total = rows * c8;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = v / c8, c = (v - r * c8) * 8;
-    const i32x4 w = *(const i32x4*)(x + r * ld + c);
+  if (DENSE) {
+    const int64_t total = rows * c8;   // 16-byte groups
+    for (int64_t v0 = (int64_t)blockIdx.x * 1024 + threadIdx.x; v0 < total; v0 += (int64_t)gridDim.x * 1024) {
+      i32x4 w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] & 0xFFFFu))));
-      m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)w[e] >> 16))));
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + 256 * u;
+        w[u] = v < total ? *(const i32x4*)(x + v * 8) : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = absmax_bf16x8(m, w[u]);
+    }
+  } else {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const uint16_t* xr = x + r * ld;
+      for (int64_t c0 = threadIdx.x; c0 < c8; c0 += 4 * 256) {
+        i32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t c = c0 + 256 * u;
+          w[u] = c < c8 ? *(const i32x4*)(xr + c * 8) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = absmax_bf16x8(m, w[u]);
+      }
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(out, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 // Current-scaling cast of a bf16 [rows, cols] matrix to fp8 (e4m3 or e5m2,
@@ -357,8 +392,14 @@ hipError_t launch_quant_e4m3(const uint16_t* h, int64_t M, int64_t N, int64_t ld
 }
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t* out, hipStream_t s) {
-  const int64_t work = rows * (cols / 8);
-  amax_bf16<<<grid_for(work, 256), 256, 0, s>>>(x, rows, cols / 8, ld, out);
+  // at most 8 work-groups per CU
+  if (ld == cols) {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((rows * (cols / 8) + 1023) / 1024, 2048));
+    amax_bf16<true><<<grid, 256, 0, s>>>(x, rows, cols / 8, ld, out);
+  } else {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(rows, 2048));
+    amax_bf16<false><<<grid, 256, 0, s>>>(x, rows, cols / 8, ld, out);
+  }
   return hipGetLastError();
 }
 

@@ -633,6 +633,36 @@ def test_cast_fp8_nan_tiny_and_saturating(dt):
     assert sc.item() == float(np.float32(amax / fmax))
 
 
+@pytest.mark.parametrize("strided", [False, True])
+def test_cast_fp8_amax_many_rows_ragged_columns(strided):
+    # more rows than the amax kernel's grid and a row of 258 16-byte groups
+    # (the last load batch of a row only partly valid), on a contiguous matrix
+    # (flat walk) and on a column slice of a wider one (row walk; the larger
+    # values beyond the slice must not count); the largest magnitude sits in
+    # the tail of a late row
+    rows, cols = 4112, 2064
+    x = si.to_bf16(si.normal_f32((rows, cols), 139))
+    x[4100, 2063] = -9.75
+    if strided:
+        big = torch.full((rows, cols + 48), 100.0, dtype=torch.bfloat16)
+        big[:, :cols] = x
+        X = big.cuda()[:, :cols]
+        assert X.stride() == (cols + 48, 1)
+    else:
+        X = x.cuda()
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.cast_fp8(X, _abi.FP8_E4M3, q=q, scale_out=sc)
+    sync()
+    xv = f64(x)
+    amax = np.float32(np.max(np.abs(xv)))
+    assert amax == np.float32(9.75)
+    assert sc.item() == float(np.float32(amax / np.float32(448.0)))
+    inv = np.float32(np.float32(448.0) / amax)
+    want = formats.e4m3_encode((xv * float(inv)).astype(np.float32).astype(np.float64))
+    assert np.array_equal(q.cpu().numpy(), want)
+
+
 def test_fp8_mixed_format_gemm_integer_exact():
     # e5m2 x e4m3 and e4m3 x e5m2 through seq_chunk_gemm: integers in [-3, 3]
     # are exact in both formats, so the fp32 products are exact
