@@ -678,8 +678,11 @@ def test_fp8_mixed_format_gemm_integer_exact():
         assert np.array_equal(f64(Y), ref)
 
 
-def test_mlp_bwd_fp8_small():
-    M, D, F, T = 512, 512, 2048, 4
+@pytest.mark.parametrize("M,D,F", [(512, 512, 2048), (528, 272, 320)])
+def test_mlp_bwd_fp8_small(M, D, F):
+    # the second shape leaves ragged 64 x 64 tiles in the casts and transposes
+    # and ragged K in every GEMM
+    T = 4
     Ft = F // T
     xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 1))
     wuq, su = si.to_e4m3_current(si.normal_f32((D, Ft), 2, 0.02))      # the pages' layouts
@@ -704,6 +707,12 @@ def test_mlp_bwd_fp8_small():
     # dY's e5m2 codes are bit-exact (the same fp32 arithmetic on the same bf16 values)
     dy8 = ws[2048:2048 + M * D].cpu().numpy().reshape(M, D)
     assert np.array_equal(formats.e5m2_to_f64(dy8), r["dYq"])
+    # the transposed copies of dY's and X's codes are exact transposes
+    md = (M * D + 255) // 256 * 256
+    dy8t = ws[2048 + md:2048 + md + M * D].cpu().numpy().reshape(D, M)
+    assert np.array_equal(dy8t, dy8.T)
+    x8t = ws[2048 + 2 * md:2048 + 2 * md + M * D].cpu().numpy().reshape(D, M)
+    assert np.array_equal(x8t, xq.view(torch.uint8).numpy().T)
     off = 2048 + 3 * ((M * D + 255) // 256 * 256)
     dz = ws[off:off + 2 * M * Ft].view(torch.bfloat16).view(M, Ft)
     assert nerr(dz, r["dZ"]) <= TOL["bf16"]
