@@ -216,32 +216,43 @@ def tp_mlp_fwd_fp8(xq, sx, wq_up, s_up, wq_down, s_down, act=ACT_GELU_ERF):
     z = gemm(xq, wq_up) * (float(np.float32(sx)) * float(np.float32(s_up)))
     h = act_fwd(z, act)
     hb = formats.round_bf16(h)
-    amax = float(np.max(np.abs(hb))) if hb.size else 0.0
+    q = quantize_current(hb, "e4m3")
+    p = gemm(q["dec"], wq_down) * (q["s"] * float(np.float32(s_down)))
+    return dict(Z=z, H=h, Hb=hb, amax=q["amax"], inv=q["inv"], sH=q["s"], Hq_codes=q["codes"], P=p)
+
+
+def quantize_current(v, fmt: str):
+    """Per-tensor current scaling ([CG] "Supported quantization recipes", FP8
+    with current scaling; the formula is the reading the pages leave open)
+    of a tensor v whose values are already fp32-representable (here always
+    bf16 values), to fp8 format fmt ('e4m3', largest 448, or 'e5m2',
+    largest 57344):
+        amax = max |v|
+        inv  = fp32(fmax / amax)      (1 when amax == 0)
+        q    = enc(fp32(v * inv))     nearest even, saturating
+        s    = fp32(amax / fmax)      (1 when amax == 0), the dequant factor
+    The two fp32 roundings are the GPU path's: inv is an fp32 quotient and
+    the scaled value an fp32 product, each rounded once."""
+    enc, dec_tab, fmax = ((formats.e4m3_encode, formats.e4m3_to_f64, formats.E4M3_MAX) if fmt == "e4m3"
+                          else (formats.e5m2_encode, formats.e5m2_to_f64, formats.E5M2_MAX))
+    v = np.asarray(v, dtype=np.float64)
+    amax = float(np.max(np.abs(v))) if v.size else 0.0
+    a32 = np.float32(amax)
+    assert float(a32) == amax, "amax must be fp32-representable"
     if amax == 0.0:
-        inv32 = np.float32(1.0)
-        sh32 = np.float32(1.0)
+        inv32, s32 = np.float32(1.0), np.float32(1.0)
     else:
-        inv32 = np.float32(np.float32(448.0) / np.float32(amax))
-        sh32 = np.float32(np.float32(amax) / np.float32(448.0))
-    prod32 = (hb.astype(np.float32) * inv32).astype(np.float32)
-    hq_codes = formats.e4m3_encode(prod32.astype(np.float64))
-    hq = formats.e4m3_to_f64(hq_codes)
-    p = gemm(hq, wq_down) * (float(sh32) * float(np.float32(s_down)))
-    return dict(Z=z, H=h, Hb=hb, amax=amax, inv=float(inv32), sH=float(sh32),
-                Hq_codes=hq_codes, P=p)
+        inv32 = np.float32(np.float32(fmax) / a32)
+        s32 = np.float32(a32 / np.float32(fmax))
+    prod32 = (v.astype(np.float32) * inv32).astype(np.float32)
+    codes = enc(prod32.astype(np.float64))
+    return dict(codes=codes, dec=dec_tab(codes), inv=float(inv32), s=float(s32), amax=amax)
 
 
 # ------------------------------------------------- partial_reduce_seqshard
-def _current_scale(v, fmax):
-    """Per-tensor current scaling of v to a format with largest value fmax:
-    (inv, s) = (fp32(fmax / amax), fp32(amax / fmax)), both 1 when amax = 0."""
-    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0.0)
-    if amax == 0:
-        return np.float32(1.0), np.float32(1.0), 0.0
-    return np.float32(np.float32(fmax) / amax), np.float32(amax / np.float32(fmax)), float(amax)
 
 
-def tp_mlp_bwd_fp8(x8, sx, wu8, su, wd8, sd, z, h8, sh, dy, act=ACT_GELU_ERF):
+def tp_mlp_bwd_fp8(x8, sx, wu8, su, wd8, sd, z, h8, sh, dy, act=ACT_GELU_ERF, dz_stored=None):
     """fp8 backward of one rank's MLP share (the backward the fp8 recipes of
     [CG] "Supported quantization recipes" imply; the pages do not spell it
     out): activations and weights in e4m3 with their forward scales,
@@ -254,20 +265,23 @@ def tp_mlp_bwd_fp8(x8, sx, wu8, su, wd8, sd, z, h8, sh, dy, act=ACT_GELU_ERF):
         dW_up,t   = (Xq^T . dZq) * s_X * s_dZ
         dX_t      = (dZq . W_up,t^T) * s_dZ * s_Wu
     Inputs: decoded e4m3 values of X [M, D], W_up,t [D, F/T], W_down,t
-    [F/T, D], H [M, F/T] with their fp32 scales; Z and dY as bf16 values."""
+    [F/T, D], H [M, F/T] with their fp32 scales; Z and dY as bf16 values.
+    dz_stored: the stored bf16 dZ a GPU produced (its saved intermediate, an
+    input of the later GEMMs); when given, the chain continues from it."""
     f = lambda v: float(np.float32(v))
-    dy = np.asarray(dy, dtype=np.float64)
-    inv_dy, s_dy, amax_dy = _current_scale(dy, formats.E5M2_MAX)
-    dyq = formats.e5m2_to_f64(formats.e5m2_encode((dy * float(inv_dy)).astype(np.float32).astype(np.float64)))
-    dh = gemm(dyq, np.asarray(wd8, dtype=np.float64).T) * (float(s_dy) * f(sd))
+    qy = quantize_current(dy, "e5m2")
+    dyq, s_dy = qy["dec"], qy["s"]
+    dh = gemm(dyq, np.asarray(wd8, dtype=np.float64).T) * (s_dy * f(sd))
     dz = formats.round_bf16(dh * act_grad(np.asarray(z, dtype=np.float64), act))
-    inv_dz, s_dz, amax_dz = _current_scale(dz, formats.E5M2_MAX)
-    dzq = formats.e5m2_to_f64(formats.e5m2_encode((dz * float(inv_dz)).astype(np.float32).astype(np.float64)))
-    dw_down = gemm(np.asarray(h8, dtype=np.float64).T, dyq) * (f(sh) * float(s_dy))
-    dw_up = gemm(np.asarray(x8, dtype=np.float64).T, dzq) * (f(sx) * float(s_dz))
-    dx = gemm(dzq, np.asarray(wu8, dtype=np.float64).T) * (float(s_dz) * f(su))
-    return dict(dYq=dyq, s_dY=float(s_dy), amax_dY=amax_dy, dH=dh, dZ=dz, dZq=dzq, s_dZ=float(s_dz),
-                amax_dZ=amax_dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
+    if dz_stored is not None:
+        dz = np.asarray(dz_stored, dtype=np.float64)
+    qz = quantize_current(dz, "e5m2")
+    dzq, s_dz = qz["dec"], qz["s"]
+    dw_down = gemm(np.asarray(h8, dtype=np.float64).T, dyq) * (f(sh) * s_dy)
+    dw_up = gemm(np.asarray(x8, dtype=np.float64).T, dzq) * (f(sx) * s_dz)
+    dx = gemm(dzq, np.asarray(wu8, dtype=np.float64).T) * (s_dz * f(su))
+    return dict(dYq=dyq, s_dY=s_dy, amax_dY=qy["amax"], dH=dh, dZ=dz, dZq=dzq, s_dZ=s_dz,
+                amax_dZ=qz["amax"], dW_down=dw_down, dW_up=dw_up, dX=dx)
 
 
 def fp8_delayed_scale(amax_history):
@@ -336,7 +350,7 @@ def partial_reduce_seqshard(partials, rank: int):
 
 
 # -------------------------------------------------------------- tp_mlp_bwd
-def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None):
+def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None, dz_stored=None):
     """Backward of one rank's MLP share ([TSP] both derivations; [TP] "Code"):
         dH_t      = dY . W_down,t^T        (row-parallel input gradient shard)
         dZ_t      = dH_t * act'(Z_t)
@@ -345,11 +359,13 @@ def tp_mlp_bwd(x, w_up_t, w_down_t, z, h, dy, act=ACT_GELU_ERF, store=None):
         dX_t      = dZ_t . W_up,t^T        (full [M,D] partial, summed across
                                             ranks by all-reduce / reduce-scatter)
     Z and H are the saved forward values (inputs here).  store='bf16': the
-    two GEMMs that consume dZ_t read it as stored in bf16."""
+    two GEMMs that consume dZ_t read it as stored in bf16.  dz_stored: the
+    dZ_t a GPU stored (its saved intermediate): the two GEMMs that consume
+    dZ_t read it instead."""
     dh = gemm(dy, np.asarray(w_down_t, dtype=np.float64).T)
     dz = dh * act_grad(np.asarray(z, dtype=np.float64), act)
     dw_down = gemm(np.asarray(h, dtype=np.float64).T, dy)
-    dzs = _stored(dz, store)
+    dzs = _stored(dz, store) if dz_stored is None else np.asarray(dz_stored, dtype=np.float64)
     dw_up = gemm(np.asarray(x, dtype=np.float64).T, dzs)
     dx = gemm(dzs, np.asarray(w_up_t, dtype=np.float64).T)
     return dict(dH=dh, dZ=dz, dW_down=dw_down, dW_up=dw_up, dX=dx)
@@ -409,12 +425,6 @@ def gated_mlp_bwd(x, w_gate_t, w_up_t, w_down_t, g, u, h, dy, act=ACT_SILU, stor
     xt = np.asarray(x, dtype=np.float64).T
     dx = gemm(dgs, np.asarray(w_gate_t, dtype=np.float64).T) + gemm(dus, np.asarray(w_up_t, dtype=np.float64).T)
     return dict(dH=dh, dG=dg, dU=du, dW_down=dw_down, dW_gate=gemm(xt, dgs), dW_up=gemm(xt, dus), dX=dx)
-
-
-def linear_bwd(x, w, dy):
-    """Backward of Y = X W: dW = X^T dY, dX = dY W^T ([TSP] derivations)."""
-    return dict(dW=gemm(np.asarray(x, dtype=np.float64).T, dy),
-                dX=gemm(dy, np.asarray(w, dtype=np.float64).T))
 
 
 # ------------------------------------------------------- unsharded reference
