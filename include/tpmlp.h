@@ -19,10 +19,17 @@
  * (watchdog) is reported by tpm_poll_device_error() after the stream has
  * been synchronised.
  *
- * Device pointers used by the matrix-core path must be 16-byte aligned and
- * leading dimensions must be multiples of 8 (bf16) or 16 (fp8); N and K
- * must be multiples of 8 (bf16) or 16 (fp8).  M is free.  The fp32 path has
- * no alignment or size restriction.
+ * Shapes and alignment: any M, N, K >= 0 and any leading dimensions are
+ * accepted ("Tensor parallelism", section "Implementation notes", asks only
+ * that the sharded dimensions divide by T).  The matrix-core kernel takes a
+ * GEMM whose rows are whole 16-byte chunks: N % 8 == 0; K and the operands'
+ * leading dimensions multiples of 8 (bf16) or 16 (fp8); ldy, ldaux % 4 == 0;
+ * A, B, Y, aux 16-byte aligned; with trans_a, M % 8 == 0; fp8 operands
+ * stored K-major; each operand under 4 GiB.  Any other GEMM runs on a
+ * predicated LDS-tiled FMA kernel (same results up to fp32 summation order,
+ * far slower), which takes the FWD / DACT epilogues, scales and amax but not
+ * chunk gating, range signalling, the gated epilogues or MXFP8 / fp8
+ * outputs: those return TPM_EUNSUPPORTED unless the fast-path conditions hold.
  */
 #ifndef TPMLP_H
 #define TPMLP_H
@@ -99,8 +106,9 @@ typedef enum {
  *    (e.g. X^T in a weight gradient).
  * B: trans_b = 0 -> B is [K, ldb >= N] (the pages' W[K,N]); trans_b = 1 ->
  *    B is stored [N, ldb >= K] and op(B) = B^T (e.g. W^T in dX = dY W^T).
- * a_dtype == b_dtype in {F32, BF16, FP8_E4M3}.  fp8 operands must be
- *    stored K-major (trans_a = 0, trans_b = 1); fp32 accumulation always.
+ * a_dtype == b_dtype in {F32, BF16}, or both fp8 (E4M3 / E5M2, not both
+ *    E5M2); fp32 accumulation always.  fp8 operands stored K-major
+ *    (trans_a = 0, trans_b = 1) run on the matrix cores.
  * a_scale, b_scale: device fp32 dequantisation factors (value = code *
  *    scale), or NULL for 1.
  * Y: [M, ldy >= N], y_dtype F32 or BF16 (round to nearest even).
@@ -116,6 +124,10 @@ typedef enum {
  *    given, no row of chunk c is read before chunk_ready[c] >= epoch
  *    (wrap-around compare); the flags are written by the producer of the
  *    chunk (tpm_signal_chunk).  The result does not depend on the order.
+ *    A chunk-gated A must be stored token-major (trans_a = 0) with its
+ *    base and every chunk boundary ((M / num_chunks) * lda * element size)
+ *    on a 128-byte line, so no cache line of a chunk is fetched before its
+ *    flag is seen (else TPM_EUNSUPPORTED).
  * workspace: device, >= tpm_workspace_bytes(TPM_OP_SEQ_CHUNK_GEMM, ...);
  *    required when chunk_ready or amax_out is given, else may be NULL
  *    (then no split-K: a GEMM with few output tiles runs on fewer CUs).
@@ -139,10 +151,13 @@ int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
  *   H_t = act(Z_t)              local activation
  *   P_t = H_t . W_down,t        row-parallel partial [M, D]
  *
- * X: [M, D] (the all-gathered token rows), W_up_t: [D, F/T], W_down_t:
- * [F/T, D], all dense (leading dimension = row width), dtype BF16, F32 or
- * FP8_E4M3.  Z_t (optional), H_t: [M, F/T]; P_t: [M, D]; stored as BF16
- * (F32 when dtype is F32).
+ * X: [M, D] (the all-gathered token rows), dtype BF16, F32 or FP8_E4M3;
+ * all arrays dense (leading dimension = row width).  BF16 / F32 weights in
+ * the pages' layout: W_up_t [D, F/T], W_down_t [F/T, D].  FP8_E4M3 weights
+ * stored K-major (the transposed copies fp8 recipes keep): W_up_t [F/T, D],
+ * W_down_t [D, F/T]; the leading dimensions are taken from D and F/T, so a
+ * weight in the other layout is not detected.  Z_t (optional), H_t:
+ * [M, F/T]; P_t: [M, D]; stored as BF16 (F32 when dtype is F32).
  * FP8 (current scaling, "Supported quantization recipes"): scales = device
  * fp32[3] = {s_X, s_Wup, s_Wdown}; H is stored bf16, its amax taken over the
  * stored values, and GEMM2 reads H quantised to e4m3 with inv = 448/amax;
@@ -204,8 +219,8 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
  *                              shard of the input gradient)
  *
  * X [M, K], W [K, N] (the shard as the rank stores it), dY [M, N]: dense
- * row-major device arrays, 16-byte aligned, dtype BF16 (M, N, K multiples
- * of 8: every operand row is whole 16-byte chunks) or F32.  dW in
+ * row-major device arrays, dtype BF16 or F32 (shapes the matrix-core kernel
+ * does not take run both products on the predicated kernel).  dW in
  * dw_dtype (BF16 or F32; F32 only with dtype F32), dX in dtype.  The two
  * products read the same dY and are independent; for BF16 they run as one
  * launch whose work-groups take tiles of either product from per-XCD
@@ -217,8 +232,7 @@ int tp_mlp_bwd(int64_t M, int64_t D, int64_t F, int T, int rank,
  * (control words and split-K partial sums).  M == 0 writes zeros to dW,
  * N == 0 zeros to dX (empty arrays may be null).  Errors: TPM_EINVAL (null
  * pointer to a non-empty array, negative size, bad dtype), TPM_EWORKSPACE (workspace too small),
- * TPM_EUNSUPPORTED (misaligned operand or size, operand >= 4 GiB); nothing is
- * enqueued on error.  Asynchronous on `stream`.
+ * nothing is enqueued on error.  Asynchronous on `stream`.
  */
 int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
                   const void* X, const void* W, const void* dY, int dtype,
@@ -388,14 +402,22 @@ int tpm_cast_fp8(int64_t rows, int64_t cols, const void* x, int64_t ld, int dtyp
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * tp_mlp_bwd_fp8 -- tp_mlp_bwd in fp8 (hybrid recipe: activations and
- * weights e4m3 with their forward scales, gradients e5m2 with current
- * scaling):
- *   dY [M, D] bf16 -> e5m2 (current scaling) and its transpose;
+ * tp_mlp_bwd_fp8 -- tp_mlp_bwd in fp8 (hybrid recipe of "Collective GEMMs in
+ * Tensor Sequence Parallelism", section "Supported quantization recipes":
+ * activations and weights e4m3 with their forward scales, gradients e5m2
+ * with current scaling):
  *   H_t [M, F/T] bf16 (the forward's) -> e4m3 transposed (current scaling,
- *     the codes the forward's GEMM2 read);
- *   dZ_t = (dY . W_down,t^T) * act'(Z_t), stored bf16, -> e5m2 and transpose;
- *   dW_down,t = H_t^T . dY,  dW_up,t = X^T . dZ_t,  dX_t = dZ_t . W_up,t^T.
+ *     the codes the forward's GEMM2 read); X's codes transposed;
+ *   dZ_t = (dYq . W_down,t^T) * act'(Z_t), chunk-fed by dY's rows, stored
+ *     bf16, -> e5m2 (current scaling) and its transpose;
+ *   dW_down,t = H_t^T . dYq,  dW_up,t = X^T . dZ_t,  dX_t = dZ_t . W_up,t^T.
+ * dY [M, D]: dy_dtype TPM_BF16 -> cast here to e5m2 with current scaling
+ * (every row must be resident: dy_ready must be NULL); TPM_FP8_E5M2 -> dY
+ * holds e5m2 codes already quantised by their producers with the
+ * dequantisation factor *dy_scale (device fp32), as an all-gather of
+ * quantised gradients delivers them; its rows may then arrive in chunks:
+ * num_chunks / dy_chunk_order / dy_ready / epoch as in seq_chunk_gemm (the
+ * dZ GEMM waits per chunk; dY's transposed copy for dW_down is made after it).
  * X [M, D] e4m3 codes; W_up_t [D, F/T] and W_down_t [F/T, D] e4m3 codes in
  * the pages' layouts (the transposes of the forward's K-major copies);
  * scales = device fp32 {sX, sWup, sWdown}; Z_t bf16 (pre-activation).
@@ -405,8 +427,9 @@ int tpm_cast_fp8(int64_t rows, int64_t cols, const void* x, int64_t ld, int dtyp
  */
 int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
                    const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
-                   const void* Z_t, const void* H_t, const void* dY, int act,
+                   const void* Z_t, const void* H_t, const void* dY, int dy_dtype, const float* dy_scale, int act,
                    void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                   int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace needed by an operation (bytes).  For TPM_OP_MLP_FWD /
@@ -449,11 +472,12 @@ int tpm_write_chunks(void* dst, const void* src, int64_t chunk_bytes, int num_ch
                      const uint8_t* copy, uint32_t* ready, uint32_t epoch, uint32_t* counters, void* stream);
 
 /* After synchronising the stream: TPM_OK, or TPM_ETIMEOUT if a chunk wait
- * of the last chunk-gated call on this workspace gave up.  Only chunk-gated
- * (and fp8) calls reset the error word, so on a workspace that has seen none
- * it reads whatever the memory held (zero-fill a new workspace).  Blocking
- * copy of one device word. */
-int tpm_poll_device_error(const void* workspace, size_t workspace_bytes);
+ * of the last chunk-gated call on this workspace gave up (its error word
+ * then holds one specific 32-bit value, which every chunk-gated call clears
+ * before its kernels run; any other content reads as TPM_OK).  workspace:
+ * device, at least its 2 KiB control block.  Blocking copy of one device
+ * word; TPM_EWORKSPACE for NULL. */
+int tpm_poll_device_error(const void* workspace);
 
 /* Number of polls a device-side chunk wait makes before it gives up and
  * flags TPM_ETIMEOUT (default 1 << 22, a few seconds).  Process-wide. */

@@ -275,16 +275,21 @@ def cast_fp8(x, dtype, q=None, qt=None, scale_out=None, workspace=None, stream=N
 
 
 def tp_mlp_bwd_fp8(X, W_up_t, W_down_t, Z_t, H_t, dY, dW_up_t, dW_down_t, dX_t, *, T, rank, scales,
-                   act=ACT_GELU_ERF, workspace=None, stream=None):
+                   act=ACT_GELU_ERF, dy_scale=None, num_chunks=1, dy_chunk_order=None, dy_ready=None, epoch=0,
+                   workspace=None, stream=None):
     """fp8 backward: X [M, D] e4m3 codes, W_up_t [D, F/T] and W_down_t [F/T, D]
     e4m3 codes (the pages' layouts), scales = device fp32 {sX, sWup, sWdown};
-    Z_t, H_t [M, F/T] bf16, dY [M, D] bf16; dW_up_t, dW_down_t (bf16 / fp32),
+    Z_t, H_t [M, F/T] bf16; dY [M, D] bf16 (cast here with current scaling,
+    all rows resident) or uint8 e5m2 codes with dy_scale (device fp32), whose
+    rows may arrive in chunks (dy_ready); dW_up_t, dW_down_t (bf16 / fp32),
     dX_t bf16."""
     M, D = X.shape
     Ft = H_t.shape[1]
+    codes = dY.dtype == torch.uint8
     rc = lib.tp_mlp_bwd_fp8(M, D, Ft * T, T, rank, _ptr(X), _ptr(W_up_t), _ptr(W_down_t), _ptr(scales),
-                            _ptr(Z_t), _ptr(H_t), _ptr(dY), act, _ptr(dW_up_t), _ptr(dW_down_t), _ptr(dX_t),
-                            dtype_code(dW_up_t.dtype), _ptr(workspace),
+                            _ptr(Z_t), _ptr(H_t), _ptr(dY), FP8_E5M2 if codes else BF16, _ptr(dy_scale), act,
+                            _ptr(dW_up_t), _ptr(dW_down_t), _ptr(dX_t), dtype_code(dW_up_t.dtype),
+                            num_chunks, _abi.int_array(dy_chunk_order), _ptr(dy_ready), epoch, _ptr(workspace),
                             workspace.numel() if workspace is not None else 0, _stream(stream))
     return check(rc)
 
@@ -326,7 +331,7 @@ def write_chunks(dst, src, num_chunks: int, order, ready, epoch: int, counters, 
 
 
 def poll_device_error(workspace) -> int:
-    return int(lib.tpm_poll_device_error(_ptr(workspace), workspace.numel()))
+    return int(lib.tpm_poll_device_error(_ptr(workspace)))
 
 
 def set_wait_limit(polls: int) -> None:

@@ -109,8 +109,9 @@ lib.tpm_cast_fp8.argtypes = [_i64, _i64, _vp, _i64, _i32, _vp, _i64, _vp, _i64, 
 lib.tp_mlp_bwd_fp8.restype = _i32
 lib.tp_mlp_bwd_fp8.argtypes = [_i64, _i64, _i64, _i32, _i32,
                                _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _i32, _vp, _i32,
                                _vp, _vp, _vp, _i32,
-                               _vp, _vp, _vp, _i32,
+                               _i32, _vp, _vp, _u32,
                                _vp, _sz, _vp]
 lib.partial_reduce_seqshard.restype = _i32
 lib.partial_reduce_seqshard.argtypes = [_i32, _i64, _i64, _i32,
@@ -123,7 +124,7 @@ lib.tpm_signal_chunk.argtypes = [_vp, _vp, _u32]
 lib.tpm_write_chunks.restype = _i32
 lib.tpm_write_chunks.argtypes = [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _u32, _vp, _vp]
 lib.tpm_poll_device_error.restype = _i32
-lib.tpm_poll_device_error.argtypes = [_vp, _sz]
+lib.tpm_poll_device_error.argtypes = [_vp]
 lib.tpm_set_wait_limit.restype = _i32
 lib.tpm_set_wait_limit.argtypes = [_u32]
 lib.tpm_last_error.restype = ctypes.c_char_p

@@ -142,6 +142,31 @@ struct GemmDesc {
 
 size_t mx_scales_bytes(int64_t rows, int64_t k) { return (size_t)((rows + 31) / 32) * 32 * (size_t)(k / 32); }
 
+// Rows the predicated kernel takes (its grid's y dimension is M / 16).
+constexpr int64_t kGenericMaxM = 65535 * 16;
+
+// Why the matrix-core kernel cannot take this GEMM, or nullptr if it can.
+// Its loads and stores move 16-byte chunks through buffer descriptors of
+// at most 4 GiB; anything else runs on the predicated kernel.
+const char* fast_path_blocker(const GemmDesc& g) {
+  if (g.adt == TPM_F32) return "fp32 operands";
+  const int q = g.adt == TPM_BF16 ? 8 : 16;
+  if (is_fp8(g.adt) && (g.ta || !g.tb)) return "fp8 operands stored MN-major";
+  if (g.N % 8 != 0) return "N % 8 != 0";
+  if (g.K % q != 0) return "K not a whole number of 16-byte chunks";
+  if (g.ldy % 4 != 0 || (g.aux && g.ldaux % 4 != 0)) return "ldy or ldaux % 4 != 0";
+  if ((g.y_mx || g.y_qs) && g.ldy % 8 != 0) return "fp8 output with ldy % 8 != 0";
+  if (((uintptr_t)g.Y & 15) || (g.aux && ((uintptr_t)g.aux & 15))) return "Y or aux not 16-byte aligned";
+  if (g.K == 0) return nullptr;
+  if (g.ta && g.M % 8 != 0) return "trans_a with M % 8 != 0";
+  if (g.lda % q != 0 || g.ldb % q != 0) return "lda or ldb not a whole number of 16-byte chunks";
+  if (!aligned16(g.A) || !aligned16(g.B)) return "A or B not 16-byte aligned";
+  const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
+  const double a_ext = (double)a_rows * g.lda * esize(g.adt), b_ext = (double)b_rows * g.ldb * esize(g.bdt);
+  if (a_ext >= 4294967040.0 || b_ext >= 4294967040.0) return "an operand spans >= 4 GiB";
+  return nullptr;
+}
+
 // Full host-side validation of one GEMM; returns TPM_OK or an error code.
 int check_gemm(const GemmDesc& g, const char* who) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return fail(TPM_EINVAL, "%s: negative size", who);
@@ -203,24 +228,28 @@ int check_gemm(const GemmDesc& g, const char* who) {
   if (g.adt == TPM_F32) {
     if (g.ydt != TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: fp32 operands give fp32 output", who);
     if (g.ready || g.done) return fail(TPM_EUNSUPPORTED, "%s: chunk gating is implemented on the bf16/fp8 path", who);
+  }
+  const char* why = fast_path_blocker(g);
+  if (why) {
+    // the predicated kernel: FWD / DACT epilogues, per-tensor scales, amax
+    if (g.ready || g.done)
+      return fail(TPM_EUNSUPPORTED, "%s: chunk gating needs the matrix-core kernel (%s)", who, why);
+    if (gated || g.a_mx || g.b_mx || g.y_mx || g.y_qs)
+      return fail(TPM_EUNSUPPORTED, "%s: this epilogue or format needs the matrix-core kernel (%s)", who, why);
+    if (g.M > kGenericMaxM) return fail(TPM_EUNSUPPORTED, "%s: M > %lld on the predicated path (%s)", who,
+                                        (long long)kGenericMaxM, why);
     return TPM_OK;
   }
-  const int q = g.adt == TPM_BF16 ? 8 : 16;
-  if (is_fp8(g.adt) && (g.ta || !g.tb))
-    return fail(TPM_EUNSUPPORTED, "%s: fp8 operands must be stored K-major (trans_a=0, trans_b=1)", who);
-  if (g.N % 8 != 0 || g.K % q != 0) return fail(TPM_EUNSUPPORTED, "%s: N %% 8 and K %% %d must be 0", who, q);
-  if (g.ldy % 4 != 0 || (g.aux && g.ldaux % 4 != 0)) return fail(TPM_EUNSUPPORTED, "%s: ldy/ldaux %% 4 != 0", who);
-  if ((g.y_mx || g.y_qs) && g.ldy % 8 != 0) return fail(TPM_EUNSUPPORTED, "%s: an fp8 output needs ldy %% 8 == 0", who);
-  if (((uintptr_t)g.Y & 15) || (g.aux && ((uintptr_t)g.aux & 15)))
-    return fail(TPM_EUNSUPPORTED, "%s: device pointers must be 16-byte aligned", who);
-  if (g.K == 0) return TPM_OK;  // Y = epilogue(0): the operands are never read
-  if (g.ta && g.M % 8 != 0) return fail(TPM_EUNSUPPORTED, "%s: M %% 8 must be 0 with trans_a", who);
-  if (g.lda % q != 0 || g.ldb % q != 0) return fail(TPM_EUNSUPPORTED, "%s: lda/ldb must be multiples of %d", who, q);
-  if (!aligned16(g.A) || !aligned16(g.B)) return fail(TPM_EUNSUPPORTED, "%s: operands must be 16-byte aligned", who);
-  const int64_t a_rows = g.ta ? g.K : g.M, b_rows = g.tb ? g.N : g.K;
-  const double a_ext = (double)a_rows * g.lda * esize(g.adt), b_ext = (double)b_rows * g.ldb * esize(g.bdt);
-  if (a_ext >= 4294967040.0 || b_ext >= 4294967040.0)
-    return fail(TPM_EUNSUPPORTED, "%s: an operand spans >= 4 GiB", who);
+  if (g.ready) {
+    // A chunk's rows are loaded only after its flag is seen, and no cache
+    // line of a chunk may be fetched earlier as part of another chunk's
+    // rows: A token-major, its base and every chunk boundary on a 128-byte
+    // cache line.
+    if (g.ta) return fail(TPM_EUNSUPPORTED, "%s: a chunk-gated A must be stored token-major (trans_a = 0)", who);
+    const int64_t chunk_bytes = (g.M / g.groups) * g.lda * esize(g.adt);
+    if (((uintptr_t)g.A & 127) || chunk_bytes % 128 != 0)
+      return fail(TPM_EUNSUPPORTED, "%s: a chunk-gated A needs a 128-byte aligned base and chunk boundaries", who);
+  }
   return TPM_OK;
 }
 
@@ -250,6 +279,8 @@ void make_params(const GemmDesc& g, int S, GemmParams& p) {
   p.b_bytes = g.K == 0 ? 0u : (uint32_t)(b_rows * g.ldb * esize(g.bdt));
   p.a_mx = g.a_mx; p.b_mx = g.b_mx; p.y_mx = g.y_mx; p.y_q_scale = g.y_qs;
   p.f8fmt = (g.adt == TPM_FP8_E5M2 ? 1 : 0) | (g.bdt == TPM_FP8_E5M2 ? 2 : 0);
+  p.a_dt = g.adt;
+  p.b_dt = g.bdt;
   p.mx_steps = (int)(g.K / 128);
   p.y_mx_steps = (int)(g.N / 128);
   p.a_mx_bytes = g.a_mx ? (uint32_t)mx_scales_bytes(g.M, g.K) : 0u;
@@ -267,9 +298,9 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   if (g.M == 0 || g.N == 0) return TPM_OK;
   GemmParams p;
   hipError_t e;
-  if (g.adt == TPM_F32) {
+  if (fast_path_blocker(g)) {
     make_params(g, 1, p);
-    e = launch_gemm_f32(p, g.ta, g.tb, s);
+    e = launch_gemm_generic(p, g.ta, g.tb, s);
     return e == hipSuccess ? TPM_OK : hip_fail(e, who);
   }
   // split-K when the plan asks for it and the scratch is there (chunk-gated
@@ -424,12 +455,12 @@ int tpm_signal_chunk(void* stream, uint32_t* flag, uint32_t value) {
   return e == hipSuccess ? TPM_OK : hip_fail(e, "tpm_signal_chunk");
 }
 
-int tpm_poll_device_error(const void* workspace, size_t workspace_bytes) {
-  if (!workspace || workspace_bytes < kCtrlBytes) return fail(TPM_EWORKSPACE, "tpm_poll_device_error: workspace");
+int tpm_poll_device_error(const void* workspace) {
+  if (!workspace) return fail(TPM_EWORKSPACE, "tpm_poll_device_error: null workspace");
   uint32_t w = 0;
   hipError_t e = hipMemcpy(&w, workspace, 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "tpm_poll_device_error");
-  if (w != 0) return fail(TPM_ETIMEOUT, "a device-side chunk wait gave up (watchdog)");
+  if (w == kErrTimeout) return fail(TPM_ETIMEOUT, "a device-side chunk wait gave up (watchdog)");
   return TPM_OK;
 }
 
@@ -481,6 +512,8 @@ int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
   if (M % T != 0) return fail(TPM_EINVAL, "%s: M %% T != 0", who);
   if (!valid_dt(dtype)) return fail(TPM_EINVAL, "%s: bad dtype", who);
   if (dtype == TPM_FP8_E4M3 && !scales) return fail(TPM_EINVAL, "%s: fp8 needs scales", who);
+  if (dtype == TPM_FP8_E4M3 && (F / T) % 8 != 0)
+    return fail(TPM_EUNSUPPORTED, "%s: fp8 needs F/T %% 8 == 0 (H is quantised 8 columns at a time)", who);
   if (!H_t || !P_t) return fail(TPM_EINVAL, "%s: null H_t or P_t", who);
   const int64_t Ft = F / T;
   const size_t need = tpm_workspace_bytes(TPM_OP_MLP_FWD, M, D, F, T, num_chunks, dtype);
@@ -498,9 +531,9 @@ int tp_mlp_fwd(int64_t M, int64_t D, int64_t F, int T, int rank,
   const int ydt = dtype == TPM_F32 ? TPM_F32 : TPM_BF16;
   const bool fp8 = dtype == TPM_FP8_E4M3;
   float* amax = fp8 ? (float*)(ctrl + kCtrlAmax) : nullptr;
-  // GEMM1: column-parallel, chunk-fed.  fp8 weights arrive as W[K,N]
-  // row-major like every other dtype; the fp8 kernel wants K-major B, so
-  // fp8 W_up,t / W_down,t are taken as stored transposed ([N, K]).
+  // GEMM1: column-parallel, chunk-fed.  bf16 / fp32 weights are the pages'
+  // W[K,N]; fp8 weights are stored K-major (W_up,t as [F/T, D], W_down,t as
+  // [D, F/T]), the transposed copies the fp8 recipes keep, as B^T.
   GemmDesc g1{M, Ft, D, X, D, false, dtype, fp8 ? scales + 0 : nullptr,
               W_up_t, fp8 ? D : Ft, fp8, dtype, fp8 ? scales + 1 : nullptr,
               H_t, Ft, ydt, TPM_EPI_FWD, act, Z_t, Ft, amax,
@@ -548,8 +581,6 @@ int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
   auto given = [](const void* p, int64_t rows, int64_t cols) { return p != nullptr || rows == 0 || cols == 0; };
   if (!given(X, M, K) || !given(W, K, N) || !given(dY, M, N) || !given(dW, K, N) || !given(dX, M, K))
     return fail(TPM_EINVAL, "%s: null pointer", who);
-  if (dtype == TPM_BF16 && (M % 8 || N % 8 || K % 8))
-    return fail(TPM_EUNSUPPORTED, "%s: bf16 M, N and K must be multiples of 8 (16-byte rows)", who);
   const size_t need = tpm_workspace_bytes(TPM_OP_LINEAR_BWD, M, N, K, 1, 1, dtype);
   if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
   uint32_t* ctrl = (uint32_t*)workspace;
@@ -572,8 +603,9 @@ int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
     if (rc != TPM_OK) return rc;
   }
   hipStream_t s = (hipStream_t)stream;
-  if (dtype != TPM_BF16 || K == 0 || N == 0 || M == 0) {
-    // fp32 (the small exact-arithmetic path), or one product empty
+  if (dtype != TPM_BF16 || K == 0 || N == 0 || M == 0 || fast_path_blocker(g_dw) || fast_path_blocker(g_dx)) {
+    // fp32, ragged or unaligned shapes (the predicated kernel), or one
+    // product empty: the two products one after the other
     for (const GemmDesc* g : {&g_dw, &g_dx}) {
       int rc = run_gemm(*g, s, who);
       if (rc != TPM_OK) return rc;
@@ -700,8 +732,9 @@ int tpm_cast_fp8(int64_t rows, int64_t cols, const void* x, int64_t ld, int dtyp
 
 int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
                    const void* X, const void* W_up_t, const void* W_down_t, const float* scales,
-                   const void* Z_t, const void* H_t, const void* dY, int act,
+                   const void* Z_t, const void* H_t, const void* dY, int dy_dtype, const float* dy_scale, int act,
                    void* dW_up_t, void* dW_down_t, void* dX_t, int dw_dtype,
+                   int num_chunks, const int32_t* dy_chunk_order, const uint32_t* dy_ready, uint32_t epoch,
                    void* workspace, size_t workspace_bytes, void* stream) {
   const char* who = "tp_mlp_bwd_fp8";
   if (T < 1 || T > TPM_MAX_CHUNKS || rank < 0 || rank >= T) return fail(TPM_EINVAL, "%s: bad T/rank", who);
@@ -710,9 +743,16 @@ int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
   const int64_t Ft = F / T;
   if (M % 16 != 0 || D % 16 != 0 || Ft % 16 != 0) return fail(TPM_EUNSUPPORTED, "%s: M, D, F/T multiples of 16", who);
   if (dw_dtype != TPM_BF16 && dw_dtype != TPM_F32) return fail(TPM_EINVAL, "%s: dw_dtype", who);
+  if (dy_dtype != TPM_BF16 && dy_dtype != TPM_FP8_E5M2) return fail(TPM_EINVAL, "%s: dy_dtype BF16 or FP8_E5M2", who);
+  const bool dy_codes = dy_dtype == TPM_FP8_E5M2;
+  if (dy_codes && !dy_scale) return fail(TPM_EINVAL, "%s: e5m2 dY needs dy_scale", who);
+  if (!dy_codes && dy_ready)
+    return fail(TPM_EUNSUPPORTED, "%s: a chunk-fed dY must arrive quantised (dy_dtype FP8_E5M2): the current "
+                "scale of a bf16 dY needs every row", who);
+  if (num_chunks < 1 || num_chunks > TPM_MAX_CHUNKS) return fail(TPM_EINVAL, "%s: num_chunks", who);
   if (!X || !W_up_t || !W_down_t || !scales || !Z_t || !H_t || !dY || !dW_up_t || !dW_down_t || !dX_t)
     return fail(TPM_EINVAL, "%s: null pointer", who);
-  const size_t need = tpm_workspace_bytes(TPM_OP_MLP_BWD_FP8, M, D, F, T, 1, TPM_FP8_E4M3);
+  const size_t need = tpm_workspace_bytes(TPM_OP_MLP_BWD_FP8, M, D, F, T, num_chunks, TPM_FP8_E4M3);
   if (!workspace || workspace_bytes < need) return fail(TPM_EWORKSPACE, "%s: workspace of %zu bytes required", who, need);
   if (!aligned16(dY) || !aligned16(H_t)) return fail(TPM_EUNSUPPORTED, "%s: dY, H_t must be 16-byte aligned", who);
   uint32_t* ctrl = (uint32_t*)workspace;
@@ -729,12 +769,19 @@ int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
   float* part = (float*)w;
   const size_t part_bytes = workspace_bytes - (size_t)(w - (char*)workspace);
   const int e4 = TPM_FP8_E4M3, e5 = TPM_FP8_E5M2;
-  // dZ = (dY8 . W_down^T) * act'(Z), bf16, amax   W_down_t [Ft, D]: stored [N=Ft, K=D]
-  GemmDesc g_dz{M, Ft, D, dy8, D, false, e5, cw + 1, W_down_t, D, true, e4, scales + 2,
+  // dY's codes and dequantisation factor: the caller's (chunk-fed), or this
+  // call's current-scaling cast of the bf16 dY
+  const uint8_t* dyq = dy_codes ? (const uint8_t*)dY : dy8;
+  const float* s_dy = dy_codes ? dy_scale : cw + 1;
+  int32_t corder[TPM_MAX_CHUNKS];
+  if (dy_chunk_order) std::memcpy(corder, dy_chunk_order, sizeof(int32_t) * num_chunks);
+  else ring_order(T, num_chunks, rank, corder);
+  // dZ = (dYq . W_down^T) * act'(Z), bf16, amax   W_down_t [Ft, D]: stored [N=Ft, K=D]; chunk-fed by dY rows
+  GemmDesc g_dz{M, Ft, D, dyq, D, false, e5, s_dy, W_down_t, D, true, e4, scales + 2,
                 dz, Ft, TPM_BF16, TPM_EPI_DACT, act, const_cast<void*>(Z_t), Ft, cw + 2,
-                1, nullptr, nullptr, nullptr, 0, ctrl};
-  // dW_down = H^T . dY:  A = H8^T [Ft, M], B stored [N=D, K=M] = dY8^T
-  GemmDesc g_wd{Ft, D, M, h8t, M, false, e4, cw + 5, dy8t, M, true, e5, cw + 1,
+                num_chunks, corder, dy_ready, nullptr, epoch, ctrl};
+  // dW_down = H^T . dY:  A = H8^T [Ft, M], B stored [N=D, K=M] = dYq^T
+  GemmDesc g_wd{Ft, D, M, h8t, M, false, e4, cw + 5, dy8t, M, true, e5, s_dy,
                 dW_down_t, D, dw_dtype, TPM_EPI_FWD, TPM_ACT_NONE, nullptr, 0, nullptr,
                 1, nullptr, nullptr, nullptr, 0, ctrl};
   // dW_up = X^T . dZ:  A = X8^T [D, M], B stored [N=Ft, K=M] = dZ8^T
@@ -754,16 +801,21 @@ int tp_mlp_bwd_fp8(int64_t M, int64_t D, int64_t F, int T, int rank,
   if (M == 0 || D == 0 || Ft == 0) return TPM_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_ctrl_init(ctrl, kCtrlF8 + 8, s);
-  // gradient and activation casts: dY -> e5m2 (+ transpose), H -> e4m3 transposed, X transposed
-  if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)dY, M, D, D, (uint32_t*)(cw + 0), s);
-  if (e == hipSuccess) e = launch_cast_fp8_t((const uint16_t*)dY, M, D, D, cw + 0, true, dy8, D, dy8t, M, cw + 1, s);
+  // activation casts (independent of dY): H -> e4m3 transposed, X transposed
   if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)H_t, M, Ft, Ft, (uint32_t*)(cw + 4), s);
   if (e == hipSuccess) e = launch_cast_fp8_t((const uint16_t*)H_t, M, Ft, Ft, cw + 4, false, nullptr, 0, h8t, M, cw + 5, s);
   if (e == hipSuccess) e = launch_transpose_u8((const uint8_t*)X, M, D, D, x8t, M, s);
+  // bf16 dY: its current-scaling cast to e5m2, row-major and transposed
+  if (!dy_codes) {
+    if (e == hipSuccess) e = launch_amax_bf16((const uint16_t*)dY, M, D, D, (uint32_t*)(cw + 0), s);
+    if (e == hipSuccess) e = launch_cast_fp8_t((const uint16_t*)dY, M, D, D, cw + 0, true, dy8, D, dy8t, M, cw + 1, s);
+  }
   if (e != hipSuccess) return hip_fail(e, who);
   int rc = run_gemm(g_dz, s, who);
   if (rc != TPM_OK) return rc;
-  e = launch_cast_fp8_t(dz, M, Ft, Ft, cw + 2, true, dz8, Ft, dz8t, M, cw + 3, s);
+  // e5m2 dY: every chunk has landed once the dZ GEMM is done; its transposed copy for dW_down
+  if (dy_codes) e = launch_transpose_u8(dyq, M, D, D, dy8t, M, s);
+  if (e == hipSuccess) e = launch_cast_fp8_t(dz, M, Ft, Ft, cw + 2, true, dz8, Ft, dz8t, M, cw + 3, s);
   if (e != hipSuccess) return hip_fail(e, who);
   for (const GemmDesc* g : {&g_wd, &g_wu, &g_dx}) {
     rc = run_gemm(*g, s, who);

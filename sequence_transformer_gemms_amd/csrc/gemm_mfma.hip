@@ -246,7 +246,7 @@ __device__ __forceinline__ bool wait_group(const GemmParams& p, int g) {
       const uint32_t v = __hip_atomic_load(p.ready + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int32_t)(v - p.epoch) >= 0) break;
       if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++polls > p.wait_limit) {
-        __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.err, kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bad = 1;
         break;
       }

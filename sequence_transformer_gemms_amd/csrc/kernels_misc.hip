@@ -7,7 +7,8 @@
 //   * fp8 current scaling of the intermediate activation (FP8 current-scaling
 //     recipe, "Supported quantization recipes")
 //   * control-word initialisation and chunk-ready signalling
-//   * an LDS-tiled fp32 FMA GEMM for the small fp32 configuration.
+//   * an LDS-tiled FMA GEMM with predicated loads: the fp32 configuration,
+//     and shapes, layouts or alignments the matrix-core kernel does not take.
 #include "tpm_device.hpp"
 #include "tpm_internal.hpp"
 
@@ -313,26 +314,42 @@ __global__ void signal_flag(uint32_t* flag, uint32_t value) {
 // ------------------------------------------------------------ fp32 GEMM
 // 16 x 16 output tile per 256-thread block, K staged through LDS in steps
 // of 16; one output element per thread, fp32 FMA accumulation in ascending k.
-__global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmParams p, int trans_a, int trans_b) {
+// Element e of an operand of element type dt (TPM dtype codes: 0 fp32,
+// 1 bf16, 2 e4m3fn, 3 e5m2), widened to fp32.
+__device__ inline float load_elem(const void* base, int dt, int64_t e) {
+  switch (dt) {
+    case 0: return ((const float*)base)[e];
+    case 1: return bf16_to_f32(((const uint16_t*)base)[e]);
+    case 2: return e4m3_to_f32(((const uint8_t*)base)[e]);
+    default: return e5m2_to_f32(((const uint8_t*)base)[e]);
+  }
+}
+
+// Predicated GEMM for shapes and layouts the matrix-core kernel does not
+// take (any M, N, K >= 0, any leading dimensions and alignments, any element
+// type on either side, fp8 in either layout): 16 x 16 output tile per
+// work-group staged through LDS, one output per thread, fp32 FMA in
+// ascending k.  Same epilogues as the matrix-core kernel: scale, FWD (aux
+// receives the pre-activation, then act) or DACT (times act'(aux)), amax of
+// the stored values, fp32 or bf16 output (nearest even).
+__global__ void __launch_bounds__(256) gemm_generic_kernel(const GemmParams p, int trans_a, int trans_b) {
   __shared__ float As[16][17];
   __shared__ float Bs[16][17];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int row = blockIdx.y * 16 + ty;
   const int col = blockIdx.x * 16 + tx;
-  const float* A = (const float*)p.A;
-  const float* B = (const float*)p.B;
   float acc = 0.f;
   for (int k0 = 0; k0 < p.K; k0 += 16) {
-    {  // A tile: As[ty][tx] = op(A)[blockIdx.y*16 + ty][k0 + tx]
+    {  // As[ty][tx] = op(A)[blockIdx.y*16 + ty][k0 + tx]
       const int r = blockIdx.y * 16 + ty, k = k0 + tx;
       float v = 0.f;
-      if (r < p.M && k < p.K) v = trans_a ? A[(int64_t)k * p.lda + r] : A[(int64_t)r * p.lda + k];
+      if (r < p.M && k < p.K) v = load_elem(p.A, p.a_dt, trans_a ? (int64_t)k * p.lda + r : (int64_t)r * p.lda + k);
       As[ty][tx] = v;
     }
-    {  // B tile: Bs[ty][tx] = op(B)[k0 + ty][blockIdx.x*16 + tx]
+    {  // Bs[ty][tx] = op(B)[k0 + ty][blockIdx.x*16 + tx]
       const int k = k0 + ty, c = blockIdx.x * 16 + tx;
       float v = 0.f;
-      if (k < p.K && c < p.N) v = trans_b ? B[(int64_t)c * p.ldb + k] : B[(int64_t)k * p.ldb + c];
+      if (k < p.K && c < p.N) v = load_elem(p.B, p.b_dt, trans_b ? (int64_t)c * p.ldb + k : (int64_t)k * p.ldb + c);
       Bs[ty][tx] = v;
     }
     __syncthreads();
@@ -340,24 +357,38 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmParams p, int t
     for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[kk][tx], acc);
     __syncthreads();
   }
-  if (row >= p.M || col >= p.N) return;
-  float s = 1.f;
-  if (p.a_scale) s *= *p.a_scale;
-  if (p.b_scale) s *= *p.b_scale;
-  float v = acc * s;
-  if (p.epi == EPI_DACT) {
-    const float z = p.aux_f32 ? ((const float*)p.aux)[(int64_t)row * p.ldaux + col]
-                              : bf16_to_f32(((const uint16_t*)p.aux)[(int64_t)row * p.ldaux + col]);
-    v *= act_grad(z, p.act);
-  } else {
-    if (p.aux) {
-      if (p.aux_f32) ((float*)p.aux)[(int64_t)row * p.ldaux + col] = v;
-      else ((uint16_t*)p.aux)[(int64_t)row * p.ldaux + col] = f32_to_bf16_rne(v);
+  float stored = 0.f;
+  if (row < p.M && col < p.N) {
+    float s = 1.f;
+    if (p.a_scale) s *= *p.a_scale;
+    if (p.b_scale) s *= *p.b_scale;
+    float v = acc * s;
+    if (p.epi == EPI_DACT) {
+      const float z = p.aux_f32 ? ((const float*)p.aux)[(int64_t)row * p.ldaux + col]
+                                : bf16_to_f32(((const uint16_t*)p.aux)[(int64_t)row * p.ldaux + col]);
+      v *= act_grad(z, p.act);
+    } else {
+      if (p.aux) {
+        if (p.aux_f32) ((float*)p.aux)[(int64_t)row * p.ldaux + col] = v;
+        else ((uint16_t*)p.aux)[(int64_t)row * p.ldaux + col] = f32_to_bf16_rne(v);
+      }
+      v = act_fwd(v, p.act);
     }
-    v = act_fwd(v, p.act);
+    if (p.y_f32) {
+      ((float*)p.Y)[(int64_t)row * p.ldy + col] = v;
+      stored = v;
+    } else {
+      const uint16_t b = f32_to_bf16_rne(v);
+      ((uint16_t*)p.Y)[(int64_t)row * p.ldy + col] = b;
+      stored = bf16_to_f32(b);
+    }
   }
-  if (p.y_f32) ((float*)p.Y)[(int64_t)row * p.ldy + col] = v;
-  else ((uint16_t*)p.Y)[(int64_t)row * p.ldy + col] = f32_to_bf16_rne(v);
+  if (p.amax) {
+    float m = fabsf(stored);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, m));
+  }
 }
 
 int grid_for(int64_t work, int per_block) {
@@ -444,9 +475,10 @@ hipError_t launch_signal(uint32_t* flag, uint32_t value, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s) {
+hipError_t launch_gemm_generic(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
   dim3 grid((p.N + 15) / 16, (p.M + 15) / 16);
-  gemm_f32_kernel<<<grid, 256, 0, s>>>(p, trans_a ? 1 : 0, trans_b ? 1 : 0);
+  gemm_generic_kernel<<<grid, 256, 0, s>>>(p, trans_a ? 1 : 0, trans_b ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -54,6 +54,25 @@ __device__ inline float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Decodes of the fp8 formats from their bit fields.  e4m3fn: bias 7, field
+// 0 subnormal (m * 2^-9), S.1111.111 NaN, no infinity.  e5m2: bias 15,
+// field 0 subnormal (m * 2^-16), field 31 infinity (m = 0) or NaN.
+__device__ inline float e4m3_to_f32(uint8_t c) {
+  const uint32_t sign = (uint32_t)(c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 15u && m == 7u) return __builtin_nanf("");
+  const float mag = e == 0u ? (float)m * 0.001953125f : __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | sign);
+}
+__device__ inline float e5m2_to_f32(uint8_t c) {
+  const uint32_t sign = (uint32_t)(c & 0x80u) << 24;
+  const uint32_t e = (c >> 2) & 0x1Fu, m = c & 3u;
+  float mag;
+  if (e == 31u) mag = m == 0u ? __builtin_inff() : __builtin_nanf("");
+  else mag = e == 0u ? (float)m * 1.52587890625e-05f : __builtin_bit_cast(float, ((e + 112u) << 23) | (m << 21));
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | sign);
+}
+
 // OCP e4m3fn encode of an fp32 value: nearest, ties to even, saturating to
 // +-448, NaN -> 0x7F, sign kept for zero.  Integer arithmetic on the fp32
 // bits, so the result does not depend on any hardware conversion mode.

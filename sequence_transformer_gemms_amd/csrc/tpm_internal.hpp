@@ -6,6 +6,9 @@
 namespace tpm {
 
 constexpr int kMaxGroups = 256;  // chunks or destination ranges per call
+// Value of a workspace's error word after a chunk wait gave up (the word is
+// zeroed by every chunk-gated call before its kernels run).
+constexpr uint32_t kErrTimeout = 0x54504D31u;
 
 // One GEMM launch: Y[M,N] = epilogue(op(A)[M,K] . op(B)[K,N]).
 // Rows of Y are cut into `num_groups` equal groups of `group_rows` rows
@@ -45,6 +48,7 @@ struct GemmParams {
   int y_mx_steps;
   const float* y_q_scale;    // fp8 per-tensor output: Y = e4m3(v / *y_q_scale) (or null)
   int f8fmt;                 // fp8 operand formats: bit 0 A is e5m2, bit 1 B is e5m2 (else e4m3)
+  int a_dt, b_dt;            // element types of A and B (tpm dtype codes), read by the generic kernel
   int gu_off;                // gated epilogues: column offset of the up half in B / aux / Y (= N)
   int bn_out;                // output columns per tile (256; 128 for EPI_GATED)
   int16_t order[kMaxGroups];
@@ -90,7 +94,9 @@ hipError_t launch_cast_fp8_t(const uint16_t* x, int64_t rows, int64_t cols, int6
 hipError_t launch_transpose_u8(const uint8_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* y, int64_t ldy,
                                hipStream_t s);
 hipError_t launch_mx_swizzle(const uint8_t* src, int64_t ld, int rows, int kblocks, uint8_t* dst, hipStream_t s);
-hipError_t launch_gemm_f32(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
+// Predicated LDS-tiled FMA GEMM: any shape, layout, alignment and element
+// types (a_dt / b_dt); FWD and DACT epilogues, amax, fp32 or bf16 output.
+hipError_t launch_gemm_generic(const GemmParams& p, bool trans_a, bool trans_b, hipStream_t s);
 hipError_t launch_ctrl_init(uint32_t* words, int n, hipStream_t s);
 hipError_t launch_reduce(int T, int64_t rows, int64_t D, const void* partials, int64_t pstride,
                          int64_t ld, int in_f32, void* out, int64_t ldo, int out_f32, hipStream_t s);

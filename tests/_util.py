@@ -84,3 +84,40 @@ def e5m2_cast_ambiguity(v_exact, delta, inv):
     lo = cast(formats.round_bf16(v_exact - delta))
     hi = cast(formats.round_bf16(v_exact + delta))
     return q, np.maximum(np.abs(lo - q), np.abs(hi - q))
+
+
+def assert_fp8_h_consistent(h_gpu, codes_gpu, s_gpu, ref, max_flip=2e-3):
+    """The fp8 current-scaling step of H on the GPU against the oracle's
+    chain (ops.tp_mlp_fwd_fp8 result `ref`):
+    * the codes and the scale are exactly the quantisation of the bf16 H the
+      GPU stored (the same fp32 arithmetic on the same values);
+    * so, with the same amax, a code can differ from the oracle's only where
+      the GPU's bf16 H differs from the oracle's rounding of the exact H
+      (an fp32 accumulation rounding a value near a bf16 boundary the other
+      way); such a one-ulp step crosses one of e4m3's rounding boundaries
+      at most one time in 8, so code differences stay well below the bf16
+      ones;
+    * code differences stay below `max_flip`.  (bf16 differences are
+      frequent among the smallest |H|, GeLU's negative tail, where the
+      epilogue's fp32 evaluation is accurate to an absolute 3e-7 rather than
+      to a bf16 ulp, but there one bf16 ulp is far from e4m3's steps at the
+      scale of the largest |H|.)  A different amax can only come from the
+      largest element rounding the other way.
+    Returns the fractions of bf16 and of code differences."""
+    from oracle import ops as _ops
+    q = _ops.quantize_current(h_gpu, "e4m3")
+    assert np.array_equal(codes_gpu, q["codes"])
+    assert s_gpu == q["s"]
+    hb_diff = h_gpu != ref["Hb"]
+    flips = codes_gpu != ref["Hq_codes"]
+    if q["amax"] == ref["amax"]:
+        assert not np.any(flips & ~hb_diff)
+        # a one-ulp bf16 step (2^-7 .. 2^-8 of a value across a binade)
+        # crosses one of e4m3's rounding boundaries (2^-3 .. 2^-4 of a value
+        # apart; coarser still among e4m3's subnormals) with probability at
+        # most 2^-7 / 2^-4 = 1/8
+        assert np.mean(flips) <= np.mean(hb_diff) / 8 + 1e-5, (np.mean(flips), np.mean(hb_diff))
+        assert np.mean(flips) < max_flip, np.mean(flips)
+    else:
+        assert np.any(hb_diff & ((np.abs(h_gpu) == q["amax"]) | (np.abs(ref["Hb"]) == ref["amax"])))
+    return float(np.mean(hb_diff)), float(np.mean(flips))

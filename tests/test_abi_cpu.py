@@ -72,13 +72,30 @@ def test_seq_chunk_gemm_validation():
     assert gemm(ydt=X.FP8_E4M3) == X.EINVAL
     assert gemm(epi=X.EPI_DACT) == X.EINVAL               # DACT needs Z
     assert gemm(act=9) == X.EINVAL
-    assert gemm(N=100) == X.EUNSUPPORTED                  # N % 8
-    assert gemm(K=100, lda=256) == X.EUNSUPPORTED         # K % 8
-    assert gemm(A=FAKE + 2) == X.EUNSUPPORTED             # misaligned
-    assert gemm(adt=X.FP8_E4M3, bdt=X.FP8_E4M3, tb=0) == X.EUNSUPPORTED  # fp8 wants K-major B
     assert gemm(ready=FAKE) == X.EWORKSPACE               # flags need the workspace
+    assert gemm(adt=X.FP8_E5M2, bdt=X.FP8_E5M2, tb=1) == X.EUNSUPPORTED   # e5m2 x e5m2
     assert gemm(adt=X.F32, bdt=X.F32, ydt=X.BF16) == X.EUNSUPPORTED
     assert "seq_chunk_gemm" in X.last_error()
+
+
+def test_chunk_gating_needs_whole_cache_lines_and_the_fast_path():
+    """A chunk-gated A: token-major, base and chunk boundaries on 128-byte
+    lines (no line of a chunk is fetched before its flag); and shapes the
+    matrix-core kernel does not take cannot be gated."""
+    from sequence_transformer_gemms_amd import _abi as X
+    g = lambda **kw: gemm(ready=FAKE, ws=FAKE, wsb=1 << 16, **kw)
+    assert g(ta=1, lda=256) == X.EUNSUPPORTED                        # chunks would be column slices
+    assert "token-major" in X.last_error()
+    assert g(A=FAKE + 16) == X.EUNSUPPORTED                          # base not on a 128-byte line
+    assert "128-byte" in X.last_error()
+    # K = lda = 520 bf16: 1040-byte rows, one row per chunk -> boundaries off the lines
+    assert g(K=520, lda=520, C=256) == X.EUNSUPPORTED
+    assert "128-byte" in X.last_error()
+    assert g(N=100) == X.EUNSUPPORTED                                # ragged N: predicated kernel, no gating
+    assert "matrix-core" in X.last_error()
+    assert g(A=FAKE + 2) == X.EUNSUPPORTED                           # misaligned A
+    # fp8 output and gated epilogues need the fast path too
+    assert gemm(N=100, epi=X.EPI_GATED, ldb=512, ldaux=512, aux=FAKE) == X.EUNSUPPORTED
 
 
 def test_mlp_and_reduce_validation():
@@ -91,7 +108,10 @@ def test_mlp_and_reduce_validation():
         return L.tp_mlp_fwd(a["M"], a["D"], a["F"], a["T"], a["rank"], FAKE, FAKE, FAKE, X.BF16, None,
                             X.ACT_GELU_ERF, None, FAKE, FAKE, None, 4, None, None, 0, None, None, None, 0, None)
     assert fwd(F=1002) == X.EINVAL      # F % T
-    assert fwd(F=1000) == X.EUNSUPPORTED  # F/T = 250 is not a multiple of 8
+    fp8 = lambda **kw: (lambda a: L.tp_mlp_fwd(a["M"], a["D"], a["F"], a["T"], a["rank"], FAKE, FAKE, FAKE,
+                                                X.FP8_E4M3, FAKE, X.ACT_GELU_ERF, None, FAKE, FAKE, None, 4, None,
+                                                None, 0, None, None, FAKE, 1 << 30, None))(args(**kw))
+    assert fp8(F=1000) == X.EUNSUPPORTED  # fp8: F/T = 250 is not a multiple of the quantiser's 8 columns
     assert fwd(M=510) == X.EINVAL       # M % T
     assert fwd(rank=4) == X.EINVAL
     assert fwd(T=0) == X.EINVAL
@@ -144,4 +164,20 @@ def test_linear_bwd_host_errors_without_device():
     assert f(8, 8, 8, 16, 16, 16, _abi.FP8_E4M3, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EINVAL
     assert f(8, 8, 8, 16, 16, 16, _abi.F32, 16, 16, _abi.BF16, 16, 1 << 20, None) == _abi.EUNSUPPORTED
     assert f(8, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 4, None) == _abi.EWORKSPACE
-    assert f(300, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.BF16, 16, 1 << 30, None) == _abi.EUNSUPPORTED
+    assert f(8, 8, 8, 16, 16, 16, _abi.BF16, 16, 16, _abi.FP8_E4M3, 16, 1 << 30, None) == _abi.EINVAL
+
+
+def test_fp8_backward_chunk_feed_needs_quantised_dy():
+    from sequence_transformer_gemms_amd import _abi as X
+    f = X.lib.tp_mlp_bwd_fp8
+    call = lambda dyt, dys, ready: f(512, 256, 1024, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dyt, dys,
+                                     X.ACT_GELU_ERF, FAKE, FAKE, FAKE, X.BF16, 4, None, ready, 1, FAKE, 1 << 30, None)
+    assert call(X.BF16, None, FAKE) == X.EUNSUPPORTED       # bf16 dY: its current scale needs every row
+    assert "quantised" in X.last_error()
+    assert call(X.FP8_E5M2, None, FAKE) == X.EINVAL         # e5m2 dY needs its scale
+    assert call(X.FP8_E4M3, FAKE, None) == X.EINVAL
+
+
+def test_poll_device_error_null_workspace():
+    from sequence_transformer_gemms_amd import _abi as X
+    assert X.lib.tpm_poll_device_error(None) == X.EWORKSPACE

@@ -14,7 +14,8 @@ import sequence_transformer_gemms_amd as tpm
 from sequence_transformer_gemms_amd import _abi
 import synthetic_inputs as si
 from oracle import formats, ops
-from tests._util import TOL, assert_mx_close, bf16_either, f64, nerr
+from tests import _util
+from tests._util import TOL, assert_mx_close, f64, nerr
 
 pytestmark = pytest.mark.gpu
 
@@ -52,14 +53,9 @@ def test_c2_projection_full_size_resident_and_arriving():
     ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
     tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_order=order, workspace=ws)
     sync()
-    rows, cols = pick(M, 48, 21), pick(N, 48, 22)
-    ref, _ = ops.seq_chunk_gemm(f64(x[rows]), f64(w[:, cols]))
-    got = host64(Y[rows][:, cols])
-    assert nerr(got, ref) <= TOL["bf16"]
-    # whole rows too (every column tile of the sampled token rows)
-    r2 = rows[:4]
-    ref_rows, _ = ops.seq_chunk_gemm(f64(x[r2]), f64(w))
-    assert nerr(host64(Y[r2]), ref_rows) <= TOL["bf16"]
+    ref, _ = ops.seq_chunk_gemm(f64(x), f64(w))             # the whole output
+    assert nerr(Y, ref) <= TOL["bf16"]
+    del ref
 
     compute, producer = tpm.masked_streams(producer_cus=8)
     Xa = torch.zeros_like(X)
@@ -97,11 +93,13 @@ def test_c3_mlp_forward_full_size_and_reduction():
                    range_done=done, epoch=3, workspace=ws)
     sync()
     assert torch.all(done == 3)
-    rows = pick(M, 24, 31)
-    ref = ops.tp_mlp_fwd(f64(x[rows]), f64(wu), f64(wd), ops.ACT_GELU_ERF, store="bf16")
-    assert nerr(host64(Z[rows]), ref["Z"]) <= TOL["bf16"]
-    assert nerr(host64(H[rows]), ref["H"]) <= TOL["bf16"]
-    assert nerr(host64(P[rows]), ref["P"]) <= TOL["bf16"]
+    # whole outputs: Z and H against the exact product, P against the exact
+    # product of the H the GPU stored
+    ref = ops.tp_mlp_fwd(f64(x), f64(wu), f64(wd), ops.ACT_GELU_ERF)
+    assert nerr(Z, ref["Z"]) <= TOL["bf16"]
+    assert nerr(H, ref["H"]) <= TOL["bf16"]
+    assert nerr(P, ops.gemm(f64(H), f64(wd))) <= TOL["bf16"]
+    del ref
     del X, Wu, Wd, H, Z, P, ws
     torch.cuda.empty_cache()
 
@@ -151,34 +149,33 @@ def _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C):
     return H, P, sH, ws
 
 
-def test_c4_fp8_mlp_forward_full_size_sampled():
+def test_c4_fp8_mlp_forward_full_size():
     """Llama3-405B-shaped MLP share, fp8 e4m3 with per-tensor current scales:
-    8192 tokens, D = 16384, F/T = 6656, 16 chunks of 512.  H (bf16, before
-    its own quantisation) is checked on sampled rows against the oracle; the
-    scale of H must be max|H| / 448 of the H the kernel produced; P is
-    checked on sampled rows against the unquantised-H product within the
-    e4m3 rounding bound of H (relative 2^-4 per element, plus half the
-    smallest subnormal step times the scale)."""
+    8192 tokens, D = 16384, F/T = 6656, 16 chunks of 512, against the
+    oracle's whole fp8 chain (H, its amax and e4m3 codes, P) at full size.
+    H is stored in bf16 (bf16 tolerance); the codes and scale are exactly
+    the quantisation of the GPU's own H, and differ from the oracle's codes
+    only where the GPU's bf16 H does (tests/_util.assert_fp8_h_consistent)."""
     M, D, F, T, C = 8192, 16384, 53248, 8, 16
     Ft = F // T
     xq, sx, wuq, su, wdq, sd = _c4_inputs(M, D, F, T)
     H, P, sH, ws = _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C)
-    rows = pick(M, 12, 41)
-    x_r = f64(xq[rows]) * float(sx)                    # decoded operands
-    wu_d = f64(wuq).T * float(su)                      # [D, Ft]
-    wd_d = f64(wdq).T * float(sd)                      # [Ft, D]
-    h_ref, _ = ops.seq_chunk_gemm(x_r, wu_d, act=ops.ACT_GELU_ERF)
-    h_gpu = host64(H[rows])
-    assert nerr(h_gpu, h_ref) <= TOL["bf16"]
-    amax = float(torch.max(torch.abs(H.float())).item())
-    assert abs(sH.item() - np.float32(np.float32(amax) / np.float32(448.0))) <= 1e-6 * sH.item()
-    assert amax >= float(np.max(np.abs(formats.round_bf16(h_ref)))) * (1 - 2 ** -8)
-    hb = formats.round_bf16(h_ref)
-    p_ref, _ = ops.seq_chunk_gemm(hb, wd_d)
-    bound = (2.0 ** -4 * np.abs(hb) + 2.0 ** -10 * sH.item()) @ np.abs(wd_d)
-    p_gpu = host64(P[rows])
-    # bf16 rounding of P and fp32 accumulation on top of the quantisation bound
-    assert np.all(np.abs(p_gpu - p_ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(p_ref) + 1e-6)
+    hq = ws[2048:2048 + M * Ft].cpu().numpy().reshape(M, Ft)
+    h_gpu, p_gpu, s_gpu = f64(H), f64(P), sH.item()
+    del H, P, ws
+    torch.cuda.empty_cache()
+    ref = ops.tp_mlp_fwd_fp8(f64(xq), sx, f64(wuq).T, su, f64(wdq).T, sd, ops.ACT_GELU_ERF)
+    assert nerr(h_gpu, ref["H"]) <= TOL["bf16"]
+    hb_diff, flips = _util.assert_fp8_h_consistent(h_gpu, hq, s_gpu, ref)
+    # GEMM2 against the exact product of the codes and scale the GPU gave it;
+    # the whole chain (the oracle's own codes) is reported beside it: its
+    # largest normalised difference comes from the code differences above
+    # (about seven per 6656-term output row)
+    wd_dec = f64(wdq).T * float(np.float32(sd))
+    p_own = ops.gemm(formats.e4m3_to_f64(hq), wd_dec) * s_gpu
+    assert nerr(p_gpu, p_own) <= TOL["fp8"]
+    print(f"C4 full size: bf16 H differs from the oracle's rounding at {hb_diff:.2e}, e4m3 codes at {flips:.2e}; "
+          f"P vs the GPU's codes {nerr(p_gpu, p_own):.2e}, vs the oracle's whole chain {nerr(p_gpu, ref['P']):.2e}")
 
 
 def test_c4_fp8_mlp_forward_full_width_end_to_end():
@@ -189,12 +186,11 @@ def test_c4_fp8_mlp_forward_full_width_end_to_end():
     xq, sx, wuq, su, wdq, sd = _c4_inputs(M, D, F, T)
     H, P, sH, ws = _c4_run(xq, sx, wuq, su, wdq, sd, M, D, F, T, C)
     ref = ops.tp_mlp_fwd_fp8(f64(xq), sx, f64(wuq).T, su, f64(wdq).T, sd, ops.ACT_GELU_ERF)
-    assert nerr(host64(H), ref["H"]) <= TOL["fp8"]
+    assert nerr(host64(H), ref["H"]) <= TOL["bf16"]
     assert nerr(host64(P), ref["P"]) <= TOL["fp8"]
-    assert abs(sH.item() - ref["sH"]) <= 1e-2 * ref["sH"]
     Ft = F // T
     hq = ws[2048:2048 + M * Ft].cpu().numpy().reshape(M, Ft)
-    assert np.mean(hq != ref["Hq_codes"]) < 1e-2
+    _util.assert_fp8_h_consistent(host64(H), hq, sH.item(), ref, max_flip=1e-2)
 
 
 # ------------------------------------------------------------------ C5
@@ -245,56 +241,32 @@ def test_c5_layer_step_full_size_sampled():
     tpm.tp_linear_bwd(dev["x"], dev["wq"], dev["dq"], g_qkv2, dx_q2, workspace=ws_l)
     sync()
     B = TOL["bf16"]
-    rows = pick(M, 16, 51)
     X, WU, WD, DY = f64(x), f64(wu), f64(wd), f64(dy)
-    # projections, row samples
-    assert nerr(host64(qkv[rows]), ops.seq_chunk_gemm(X[rows], f64(wq))[0]) <= B
-    assert nerr(host64(o_part[rows]), ops.seq_chunk_gemm(f64(a[rows]), f64(wo))[0]) <= B
-    # MLP forward and backward, row samples (the backward reads Z and H as
-    # stored in bf16, and dZ as stored in bf16)
-    fw = ops.tp_mlp_fwd(X[rows], WU, WD, ops.ACT_GELU_ERF, store="bf16")
-    for name, t in (("Z", z), ("H", h), ("P", p)):
-        assert nerr(host64(t[rows]), fw[name]) <= B, name
-    zb, hb = formats.round_bf16(fw["Z"]), formats.round_bf16(fw["H"])
-    bw = ops.tp_mlp_bwd(X[rows], WU, WD, zb, hb, DY[rows], ops.ACT_GELU_ERF, store="bf16")
-    assert nerr(host64(dx[rows]), bw["dX"]) <= B
-    assert nerr(host64(d_attn[rows]), ops.seq_chunk_gemm(f64(dyo[rows]), f64(wo), trans_b=True)[0]) <= B
-    assert nerr(host64(dx_q[rows]), ops.seq_chunk_gemm(f64(dq[rows]), f64(wq), trans_b=True)[0]) <= B
-    assert nerr(host64(d_attn2[rows]), ops.linear_bwd(f64(a[rows]), f64(wo), f64(dyo[rows]))["dX"]) <= B
-    assert nerr(host64(dx_q2[rows]), ops.linear_bwd(X[rows], f64(wq), f64(dq[rows]))["dX"]) <= B
-    # weight gradients: dW_down rows f need the H columns f over all tokens;
-    # dW_up columns f need the dZ columns f over all tokens.  Their inputs H,
-    # Z and dZ are bf16 intermediates that the GPU rounds from fp32 values:
-    # an element whose exact value lies within fp32 accumulation error of a
-    # bf16 rounding boundary may round either way, and over 4096 tokens one
-    # such flip of a large H (ulp 2^-6 at |H| ~ 3) moves a weight gradient
-    # by ~0.03, more than 2e-2 * (1 + |ref|) where the gradient is near 0.
-    # Either rounding is valid, so the bound adds, per token, the size of
-    # the other rounding where one exists, times the other operand.
-    fcols = pick(Ft, 8, 52)
-    zc = X @ WU[:, fcols]                                          # exact Z[:, f] over all tokens
-    zb, zamb = bf16_either(zc)
-    hb, hamb = bf16_either(ops.act_fwd(zc, ops.ACT_GELU_ERF))
-    ref = hb.T @ DY
-    tol = B * (1 + np.abs(ref)) + hamb.T @ np.abs(DY)
-    assert np.all(np.abs(host64(g_down[fcols]) - ref) <= tol)
-    dh = DY @ WD[fcols].T
-    dz_exact = dh * ops.act_grad(zb, ops.ACT_GELU_ERF)
-    dz_other = dh * ops.act_grad(zb + zamb * np.sign(zc - zb), ops.ACT_GELU_ERF)   # Z rounded the other way
-    dzb, dzamb = bf16_either(dz_exact)
-    amb = dzamb + np.where(zamb > 0, np.abs(dz_other - dz_exact), 0.0)
-    ref = X.T @ dzb
-    tol = B * (1 + np.abs(ref)) + np.abs(X).T @ amb
-    assert np.all(np.abs(host64(g_up[:, fcols]) - ref) <= tol)
-    orows = pick(Da, 8, 53)
-    assert nerr(host64(g_o[orows]), ops.seq_chunk_gemm(f64(a[:, orows]), f64(dyo), trans_a=True)[0]) <= B
-    qcols = pick(Nq, 8, 54)
-    assert nerr(host64(g_qkv[:, qcols]), ops.seq_chunk_gemm(X, f64(dq[:, qcols]), trans_a=True)[0]) <= B
-    # dW_o rows i need A's column i; dW_qkv columns j need dQKV's column j
-    ref_o = ops.linear_bwd(f64(a[:, orows]), f64(wo)[orows], f64(dyo))["dW"]
-    assert nerr(host64(g_o2[orows]), ref_o) <= B
-    ref_q = ops.linear_bwd(X, f64(wq)[:, qcols], f64(dq[:, qcols]))["dW"]
-    assert nerr(host64(g_qkv2[:, qcols]), ref_q) <= B
+    WQ, WO, A_, DQ, DYO = f64(wq), f64(wo), f64(a), f64(dq), f64(dyo)
+    # every output in full, each GEMM against the exact product of the inputs
+    # the GPU gave it: the saved Z and H of the forward and the dZ the
+    # backward stored (its workspace, after the control block) are the GPU's
+    # own, so no bf16 rounding of an intermediate is re-derived here
+    assert nerr(qkv, X @ WQ) <= B
+    assert nerr(o_part, A_ @ WO) <= B
+    Zx = X @ WU
+    assert nerr(z, Zx) <= B
+    assert nerr(h, ops.act_fwd(Zx, ops.ACT_GELU_ERF)) <= B
+    Zg, Hg = f64(z), f64(h)
+    assert nerr(p, Hg @ WD) <= B
+    dz = f64(ws_b[2048:2048 + 2 * M * Ft].view(torch.bfloat16).view(M, Ft))
+    bw = ops.tp_mlp_bwd(X, WU, WD, Zg, Hg, DY, ops.ACT_GELU_ERF, dz_stored=dz)
+    assert nerr(dz, bw["dZ"]) <= B
+    assert nerr(g_down, bw["dW_down"]) <= B
+    assert nerr(g_up, bw["dW_up"]) <= B
+    assert nerr(dx, bw["dX"]) <= B
+    ref_da, ref_go = DYO @ WO.T, A_.T @ DYO
+    ref_gq, ref_dxq = X.T @ DQ, DQ @ WQ.T
+    assert nerr(d_attn, ref_da) <= B and nerr(g_o, ref_go) <= B
+    assert nerr(g_qkv, ref_gq) <= B and nerr(dx_q, ref_dxq) <= B
+    # the paired launches of the resident step
+    assert nerr(d_attn2, ref_da) <= B and nerr(g_o2, ref_go) <= B
+    assert nerr(g_qkv2, ref_gq) <= B and nerr(dx_q2, ref_dxq) <= B
 
 
 # ------------------------------------------------- tensor-parallel degree sweep
@@ -372,36 +344,22 @@ def test_gated_mlp_worked_example_full_size_sampled():
     assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
     B = TOL["bf16"]
     Xf, WG, WU, WDf, DY = f64(x), f64(wg), f64(wu), f64(wd), f64(dy)
-    rows = pick(M, 12, 61)
-    fw = ops.gated_mlp_fwd(Xf[rows], WG, WU, WDf, act, store="bf16")
-    assert nerr(host64(GU[rows][:, :Ft]), fw["G"]) <= B and nerr(host64(GU[rows][:, Ft:]), fw["U"]) <= B
-    assert nerr(host64(H[rows]), fw["H"]) <= B
-    assert nerr(host64(P[rows]), fw["P"]) <= B
-    gb, ub, hb = (formats.round_bf16(fw[k]) for k in ("G", "U", "H"))
-    bw = ops.gated_mlp_bwd(Xf[rows], WG, WU, WDf, gb, ub, hb, DY[rows], act, store="bf16")
-    assert nerr(host64(dX[rows]), bw["dX"]) <= B
-    # weight gradients on sampled columns over all tokens
-    fcols = pick(Ft, 6, 62)
-    g_ex, u_ex = Xf @ WG[:, fcols], Xf @ WU[:, fcols]                 # exact G, U columns
-    gb, gamb = bf16_either(g_ex)
-    ub, uamb = bf16_either(u_ex)
-    hb, hamb = bf16_either(ops.act_fwd(g_ex, act) * u_ex)
-    ref = hb.T @ DY                                                    # rows fcols of dW_down
-    tol = B * (1 + np.abs(ref)) + hamb.T @ np.abs(DY)
-    assert np.all(np.abs(host64(dWd[fcols]) - ref) <= tol)
-    dh = DY @ WDf[fcols].T                                             # dH columns, exact
-    g_o = gb + gamb * np.sign(g_ex - gb)                               # G saved the other way
-    u_o = ub + uamb * np.sign(u_ex - ub)
-    dg = dh * ub * ops.act_grad(gb, act)
-    du = dh * ops.act_fwd(gb, act)
-    dg_in = np.where(gamb > 0, np.abs(dh * ub * ops.act_grad(g_o, act) - dg), 0.0) + \
-        np.where(uamb > 0, np.abs(dh * u_o * ops.act_grad(gb, act) - dg), 0.0)
-    du_in = np.where(gamb > 0, np.abs(dh * ops.act_fwd(g_o, act) - du), 0.0)
-    for got, val, amb_in in ((dWgu[:, fcols], dg, dg_in), (dWgu[:, Ft + fcols], du, du_in)):
-        vb, vamb = bf16_either(val)
-        ref = Xf.T @ vb
-        tol = B * (1 + np.abs(ref)) + np.abs(Xf).T @ (vamb + amb_in)
-        assert np.all(np.abs(host64(got) - ref) <= tol)
+    # whole outputs; each GEMM against the exact product of the inputs the
+    # GPU gave it (its saved [G | U] and H, and the [dG | dU] the backward
+    # stored in its workspace after the control block)
+    G_ex, U_ex = Xf @ WG, Xf @ WU
+    GUg, Hg = f64(GU), f64(H)
+    assert nerr(GUg[:, :Ft], G_ex) <= B and nerr(GUg[:, Ft:], U_ex) <= B
+    assert nerr(Hg, ops.act_fwd(G_ex, act) * U_ex) <= B
+    assert nerr(P, Hg @ WDf) <= B
+    dgu = f64(wsb[2048:2048 + 2 * M * 2 * Ft].view(torch.bfloat16).view(M, 2 * Ft))
+    dh = DY @ WDf.T
+    g, u = GUg[:, :Ft], GUg[:, Ft:]
+    assert nerr(dgu[:, :Ft], dh * u * ops.act_grad(g, act)) <= B
+    assert nerr(dgu[:, Ft:], dh * ops.act_fwd(g, act)) <= B
+    assert nerr(dWd, Hg.T @ DY) <= B
+    assert nerr(dWgu, Xf.T @ dgu) <= B
+    assert nerr(dX, dgu @ np.concatenate([WG, WU], axis=1).T) <= B
 
 
 # ------------------------------------------------------------ MXFP8 (C4 shape)

@@ -714,29 +714,71 @@ def test_mlp_bwd_fp8_small(M, D, F):
     x8t = ws[2048 + 2 * md:2048 + 2 * md + M * D].cpu().numpy().reshape(D, M)
     assert np.array_equal(x8t, xq.view(torch.uint8).numpy().T)
     off = 2048 + 3 * ((M * D + 255) // 256 * 256)
+    mf = (M * Ft + 255) // 256 * 256
     dz = ws[off:off + 2 * M * Ft].view(torch.bfloat16).view(M, Ft)
     assert nerr(dz, r["dZ"]) <= TOL["bf16"]
     assert nerr(dWd, r["dW_down"]) <= TOL["fp8"]
-    # dZ's e5m2 codes step by 2^-2 of a value: where the oracle's fp64 dZ
-    # lies within fp32 evaluation error of a bf16 or e5m2 rounding boundary
-    # the GPU's code may be the neighbour, and one such code moves a
-    # 512-token weight gradient by more than the fp8 tolerance.  The bound
-    # adds that code step, times the other operand, where it can occur.
-    inv = np.float32(np.float32(57344.0) / np.float32(r["amax_dZ"]))
-    g = ops.act_grad(f64(z), ops.ACT_GELU_ERF)
-    v = r["dH"] * g
-    # fp32 evaluation error of dZ: D products accumulated (D ulps of their
-    # absolute sum at most), then act' and one product
-    ddh = D * 2.0 ** -24 * (np.abs(r["dYq"]) @ np.abs(f64(wdq)).T) * r["s_dY"] * float(np.float32(sd))
-    q, amb = _util.e5m2_cast_ambiguity(v, ddh * np.abs(g) + 2.0 ** -20 * np.abs(v), inv)
-    assert np.array_equal(q, r["dZq"])
-    s_dz = r["s_dZ"]
-    Xd, Wud = f64(xq) * float(np.float32(sx)), f64(wuq) * float(np.float32(su))
-    tol_u = TOL["fp8"] * (1 + np.abs(r["dW_up"])) + np.abs(Xd).T @ amb * s_dz
-    assert np.all(np.abs(f64(dWu) - r["dW_up"]) <= tol_u)
-    tol_x = TOL["fp8"] * (1 + np.abs(r["dX"])) + amb @ np.abs(Wud).T * s_dz
-    assert np.all(np.abs(f64(dX) - r["dX"]) <= tol_x)
-    assert np.mean(amb > 0) < 0.05
+    # the later GEMMs read the dZ the GPU stored: the oracle continues from it
+    r2 = ops.tp_mlp_bwd_fp8(f64(xq), sx, f64(wuq), su, f64(wdq), sd, f64(z), h8, sh, f64(dy), ops.ACT_GELU_ERF,
+                            dz_stored=f64(dz))
+    dz8 = ws[off + 2 * mf:off + 2 * mf + M * Ft].cpu().numpy().reshape(M, Ft)
+    assert np.array_equal(formats.e5m2_to_f64(dz8), r2["dZq"])          # same fp32 arithmetic on the same bf16
+    assert nerr(dWu, r2["dW_up"]) <= TOL["fp8"]
+    assert nerr(dX, r2["dX"]) <= TOL["fp8"]
+    # the stored dZ differs from the oracle's own bf16 rounding of the exact
+    # value by one ulp in about 1 % of the elements (fp32 accumulation and
+    # GeLU' evaluated in fp32): the reason the later products are checked
+    # on the GPU's own dZ
+    assert np.mean(f64(dz) != r["dZ"]) < 2e-2
+
+
+def test_mlp_bwd_fp8_chunk_fed_e5m2_dy_matches_resident():
+    """dY arriving as e5m2 codes in chunks (quantised by its producers with
+    one current scale, as an all-gather of quantised gradients delivers it),
+    written by the side-stream writer on its own CUs while the dZ GEMM waits
+    per chunk: every output bitwise equal to the call that casts a resident
+    bf16 dY itself (the same codes and scale)."""
+    M, D, F, T, C = 1024, 512, 2048, 4, 8
+    Ft = F // T
+    xq, sx = si.to_e4m3_current(si.normal_f32((M, D), 1))
+    wuq, su = si.to_e4m3_current(si.normal_f32((D, Ft), 2, 0.02))
+    wdq, sd = si.to_e4m3_current(si.normal_f32((Ft, D), 3, 0.02))
+    z = si.to_bf16(si.normal_f32((M, Ft), 137)).cuda()
+    h = si.to_bf16(np.abs(si.normal_f32((M, Ft), 138))).cuda()
+    dy = si.to_bf16(si.normal_f32((M, D), 139)).cuda()
+    X, WU, WD = xq.cuda(), wuq.cuda(), wdq.cuda()
+    scales = dev_f32(np.array([sx, su, sd], np.float32))
+    e = lambda *sh: torch.empty(*sh, dtype=torch.bfloat16, device="cuda")
+    outs = []
+    ws = tpm.alloc_workspace(_abi.OP_MLP_BWD_FP8, M, D, F, T, C, _abi.FP8_E4M3)
+    ref = (e(D, Ft), e(Ft, D), e(M, D))
+    tpm.tp_mlp_bwd_fp8(X, WU, WD, z, h, dy, *ref, T=T, rank=0, scales=scales, act=_abi.ACT_GELU_ERF, workspace=ws)
+    # the producers' quantised dY: the same current-scaling cast
+    dy8 = torch.empty(M, D, dtype=torch.uint8, device="cuda")
+    s_dy = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.cast_fp8(dy, _abi.FP8_E5M2, q=dy8, scale_out=s_dy)
+    sync()
+    streams = tpm.masked_streams(producer_cus=8)
+    compute, producer = streams
+    landing = torch.zeros_like(dy8)
+    ready = torch.zeros(C, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(C, dtype=torch.int32, device="cuda")
+    order = si.ring_chunk_order(T, C, 1)
+    ws2 = tpm.alloc_workspace(_abi.OP_MLP_BWD_FP8, M, D, F, T, C, _abi.FP8_E4M3)
+    for epoch in (1, 2):
+        got = (e(D, Ft), e(Ft, D), e(M, D))
+        sync()
+        tpm.tp_mlp_bwd_fp8(X, WU, WD, z, h, landing, *got, T=T, rank=1, scales=scales, act=_abi.ACT_GELU_ERF,
+                           dy_scale=s_dy, num_chunks=C, dy_chunk_order=order, dy_ready=ready, epoch=epoch,
+                           workspace=ws2, stream=compute)
+        tpm.write_chunks(landing, dy8, C, order, ready, epoch, counters, stream=producer)
+        sync()
+        assert tpm.poll_device_error(ws2) == 0
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+        landing.zero_()
+    sync()
+    streams.close()
 
 
 # -------------------------------------------------------- fp8 delayed scaling
@@ -835,12 +877,10 @@ def test_mlp_fwd_fp8_small():
                    h_scale_out=sH, num_chunks=C, workspace=ws)
     sync()
     r = ops.tp_mlp_fwd_fp8(f64(xq), sx, f64(wuq).T, su, f64(wdq).T, sd, ops.ACT_GELU_ERF)
-    assert nerr(H, r["H"]) <= TOL["fp8"]
+    assert nerr(H, r["H"]) <= TOL["bf16"]                 # H is stored in bf16
     assert nerr(P, r["P"]) <= TOL["fp8"]
     hq = ws[2048:2048 + M * Ft].cpu().numpy().reshape(M, Ft)
-    flips = np.mean(hq != r["Hq_codes"])
-    assert flips < 1e-2, flips
-    assert abs(sH.item() - r["sH"]) <= 1e-2 * r["sH"]
+    _util.assert_fp8_h_consistent(f64(H), hq, sH.item(), r)
 
 
 # --------------------------------------------- chunk arrival on a side stream
@@ -1202,9 +1242,18 @@ def test_linear_bwd_rejects_bad_arguments():
     small = torch.zeros(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(tpm.TpmError):
         tpm.tp_linear_bwd(x, w, dy, dW, dX, workspace=small)        # workspace too small
+    # an operand off 16-byte alignment runs on the predicated kernel: the
+    # same (integer, exact) result as the aligned call
+    xi, wi, dyi = si.small_ints((64, 32), 451), si.small_ints((32, 48), 452), si.small_ints((64, 48), 453)
+    xa, wa, dya = dev_bf16(xi), dev_bf16(wi), dev_bf16(dyi)
     xm = torch.zeros(64 * 32 + 1, dtype=torch.bfloat16, device="cuda")[1:].view(64, 32)
-    with pytest.raises(tpm.TpmError):
-        tpm.tp_linear_bwd(xm, w, dy, dW, dX)                        # operand not 16-byte aligned
+    xm.copy_(xa)
+    dW2, dX2 = torch.empty_like(dW), torch.empty_like(dX)
+    tpm.tp_linear_bwd(xa, wa, dya, dW, dX)
+    tpm.tp_linear_bwd(xm, wa, dya, dW2, dX2)
+    sync()
+    assert torch.equal(dW, dW2) and torch.equal(dX, dX2)
+    assert np.array_equal(f64(dW2), formats.round_bf16(xi.T.astype(np.float64) @ dyi))
     with pytest.raises(ValueError):
         tpm.tp_linear_bwd(x, w, dy, dW, dX.float())                 # dX is written in the inputs' dtype
     with pytest.raises(ValueError):
@@ -1297,7 +1346,8 @@ def test_dact_epilogue_integer_exact_ragged_and_strided_z():
     M, N, K = 300, 264, 200
     a = si.small_ints((M, K), 141)
     b = si.small_ints((N, K), 142)
-    zfull = si.small_ints((M, N + 24), 143).astype(np.float32) - 0.5      # no zeros: relu' is unambiguous
+    zfull = si.small_ints((M, N + 24), 143).astype(np.float32)            # includes exact zeros: the kink
+    assert np.mean(zfull[:, :N] == 0) > 0.05
     Zd = dev_bf16(zfull)[:, :N]
     assert Zd.stride(0) == N + 24
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
@@ -1305,3 +1355,127 @@ def test_dact_epilogue_integer_exact_ragged_and_strided_z():
     sync()
     exact = (a.astype(np.float64) @ b.astype(np.float64).T) * (zfull[:, :N] > 0)
     assert np.array_equal(f64(Y), formats.round_bf16(exact))
+    # ReLU'(0) = 0 ("Tensor parallelism", section "Code": 1 only where z > 0)
+    kink = (zfull[:, :N] == 0) & ((a.astype(np.float64) @ b.astype(np.float64).T) != 0)
+    assert kink.any() and not f64(Y)[kink].any()
+
+
+# ------------------------------------------- predicated path (any shape / alignment)
+def _placed(x, ld, off, dtype=torch.bfloat16):
+    """A device view of host array x [rows, cols] at element offset `off` of a
+    flat buffer, leading dimension ld (pointer alignment follows `off`)."""
+    rows, cols = x.shape
+    buf = torch.full((rows * ld + off + 8,), float("nan") if dtype != torch.uint8 else 0,
+                     dtype=dtype if dtype != torch.uint8 else torch.uint8, device="cuda")
+    v = torch.as_strided(buf, (rows, cols), (ld, 1), off)
+    if dtype == torch.bfloat16:
+        v.copy_(si.to_bf16(x).cuda())
+    else:
+        v.copy_(x.cuda())
+    return v
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_gemm_ragged_n_k_integer_exact(ta, tb):
+    """N = 1001, K = 999 (no whole 16-byte chunks), every operand layout:
+    the predicated kernel, bit-exact on integer inputs; ReLU with its kink."""
+    M, N, K = 300, 1001, 999
+    a, b, A, B = _operands(M, N, K, ta, tb, lambda s, seed: si.small_ints(s, seed), 401)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    Yf = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    tpm.seq_chunk_gemm(dev_bf16(A), dev_bf16(B), Yf, trans_a=ta, trans_b=tb, M=M, N=N, K=K, act=_abi.ACT_RELU,
+                       aux=Z)
+    tpm.seq_chunk_gemm(dev_bf16(A), dev_bf16(B), Y, trans_a=ta, trans_b=tb, M=M, N=N, K=K, act=_abi.ACT_RELU,
+                       amax_out=amax, workspace=ws)
+    sync()
+    exact, _ = ops.seq_chunk_gemm(A, B, trans_a=ta, trans_b=tb)
+    assert np.array_equal(f64(Z), exact)
+    assert np.array_equal(f64(Yf), np.maximum(exact, 0))
+    assert np.array_equal(f64(Y), formats.round_bf16(np.maximum(exact, 0)))
+    assert amax.item() == float(np.max(formats.round_bf16(np.maximum(exact, 0))))
+
+
+def test_gemm_unaligned_pointers_and_leading_dimensions():
+    """Operands and output at odd element offsets (not 16-byte aligned) with
+    odd leading dimensions, float inputs, GeLU and a saved Z: against the
+    oracle, and integer inputs bit-exact; a DACT epilogue reading an
+    unaligned Z."""
+    M, N, K = 257, 136, 264
+    x = si.normal_f32((M, K), 411)
+    w = si.normal_f32((K, N), 412, 0.05)
+    A = _placed(x, K + 3, 3)
+    B = _placed(w, N + 5, 5)
+    Y = _placed(np.zeros((M, N), np.float32), N + 1, 1)
+    Z = _placed(np.zeros((M, N), np.float32), N + 7, 7)
+    assert A.data_ptr() % 16 and B.data_ptr() % 16 and Y.data_ptr() % 16
+    tpm.seq_chunk_gemm(A, B, Y, act=_abi.ACT_GELU_ERF, aux=Z)
+    sync()
+    y, z = ops.seq_chunk_gemm(f64(A), f64(B), act=_abi.ACT_GELU_ERF)
+    assert nerr(Y, y) <= TOL["bf16"] and nerr(Z, z) <= TOL["bf16"]
+    xi, wi = si.small_ints((M, K), 413), si.small_ints((K, N), 414)
+    A2, B2 = _placed(xi, K + 3, 3), _placed(wi, N + 5, 5)
+    tpm.seq_chunk_gemm(A2, B2, Y)
+    Zd = _placed(si.small_ints((M, N), 415).astype(np.float32), N + 7, 7)
+    D = _placed(np.zeros((M, N), np.float32), N + 1, 1)
+    tpm.seq_chunk_gemm(A2, B2, D, epilogue=_abi.EPI_DACT, act=_abi.ACT_RELU, aux=Zd)
+    sync()
+    exact = xi.astype(np.float64) @ wi.astype(np.float64)
+    assert np.array_equal(f64(Y), formats.round_bf16(exact))
+    assert np.array_equal(f64(D), formats.round_bf16(exact * (f64(Zd) > 0)))
+
+
+def test_gemm_fp8_mn_major_on_the_predicated_path():
+    """e4m3 operands in the pages' layout (B = W [K, N], not K-major) with
+    scales: integer codes, exact."""
+    M, N, K = 192, 200, 160
+    xi, wi = si.small_ints((M, K), 421), si.small_ints((K, N), 422)
+    X = si.to_e4m3_exact(xi).cuda()
+    W = si.to_e4m3_exact(wi).cuda()
+    sa = dev_f32(np.array([0.5], np.float32))
+    sb = dev_f32(np.array([0.25], np.float32))
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(X, W, Y, a_scale=sa, b_scale=sb)
+    sync()
+    assert np.array_equal(f64(Y), (xi.astype(np.float64) @ wi.astype(np.float64)) * 0.125)
+
+
+def test_linear_bwd_and_mlp_on_ragged_shapes():
+    """tp_linear_bwd with M, N, K not multiples of 8, and one rank's MLP
+    share whose F/T (250) and D (200) leave no whole 16-byte chunks: every
+    GEMM on the predicated kernel, checked against the oracle with the
+    GPU's saved Z, H and dZ as the inputs of the later products."""
+    M, N, K = 300, 100, 52
+    x, w, dy = si.normal_f32((M, K), 431), si.normal_f32((K, N), 432, 0.1), si.normal_f32((M, N), 433)
+    X, W, DY = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    dW = torch.empty(K, N, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(tpm.workspace_bytes(_abi.OP_LINEAR_BWD, M, N, K), dtype=torch.uint8, device="cuda")
+    tpm.tp_linear_bwd(X, W, DY, dW, dX, workspace=ws)
+    sync()
+    r = ops.linear_bwd(f64(X), f64(W), f64(DY))
+    assert nerr(dW, r["dW"]) <= TOL["bf16"] and nerr(dX, r["dX"]) <= TOL["bf16"]
+
+    M, D, F, T, C = 260, 200, 1000, 4, 4
+    Ft = F // T
+    x = dev_bf16(si.normal_f32((M, D), 441))
+    wu, wd = dev_bf16(si.normal_f32((D, Ft), 442, 0.05)), dev_bf16(si.normal_f32((Ft, D), 443, 0.05))
+    dy = dev_bf16(si.normal_f32((M, D), 444))
+    e = lambda *sh: torch.empty(*sh, dtype=torch.bfloat16, device="cuda")
+    Z, H, P, dWu, dWd, dXo = e(M, Ft), e(M, Ft), e(M, D), e(D, Ft), e(Ft, D), e(M, D)
+    wsb = tpm.alloc_workspace(_abi.OP_MLP_BWD, M, D, F, T, C, _abi.BF16)
+    tpm.tp_mlp_fwd(x, wu, wd, H, P, T=T, rank=0, act=_abi.ACT_GELU_ERF, Z_t=Z, num_chunks=C)
+    tpm.tp_mlp_bwd(x, wu, wd, Z, H, dy, dWu, dWd, dXo, T=T, rank=0, act=_abi.ACT_GELU_ERF, num_chunks=C,
+                   workspace=wsb)
+    sync()
+    X64, WU, WD, DY = f64(x), f64(wu), f64(wd), f64(dy)
+    fw = ops.tp_mlp_fwd(X64, WU, WD, ops.ACT_GELU_ERF)
+    assert nerr(Z, fw["Z"]) <= TOL["bf16"] and nerr(H, fw["H"]) <= TOL["bf16"]
+    assert nerr(P, ops.gemm(f64(H), WD)) <= TOL["bf16"]
+    dz = wsb[2048:2048 + 2 * M * Ft].view(torch.bfloat16).view(M, Ft)
+    bw = ops.tp_mlp_bwd(X64, WU, WD, f64(Z), f64(H), DY, ops.ACT_GELU_ERF, dz_stored=f64(dz))
+    assert nerr(dz, bw["dZ"]) <= TOL["bf16"]
+    for got, k in ((dWu, "dW_up"), (dWd, "dW_down"), (dXo, "dX")):
+        assert nerr(got, bw[k]) <= TOL["bf16"], k
