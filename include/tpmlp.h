@@ -143,6 +143,30 @@ int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * seq_chunk_gemm_noalloc -- seq_chunk_gemm for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation): the same arguments without the workspace and without
+ * chunk flags (its watchdog word would not be visible to the caller), the
+ * same kernels and split-K plan, hence the same results.  Control words and
+ * the fp32 split-K partial sums live in a library-owned device array of
+ * TPM_NOALLOC_SCRATCH_BYTES per GPU (2 KiB + 64 MiB), set up on the first
+ * call on a device and held until the process ends; the call allocates and
+ * frees nothing.  A GEMM whose split-K plan needs more scratch returns
+ * TPM_EUNSUPPORTED (nothing enqueued): use seq_chunk_gemm with a workspace.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or the same call replayed concurrently)
+ * race and give wrong results.  amax_out (device, optional) is zeroed by
+ * the call as in seq_chunk_gemm.
+ */
+#define TPM_NOALLOC_SCRATCH_BYTES ((size_t)2048 + ((size_t)64 << 20))
+int seq_chunk_gemm_noalloc(int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int trans_a, int a_dtype, const float* a_scale,
+                           const void* B, int64_t ldb, int trans_b, int b_dtype, const float* b_scale,
+                           void* Y, int64_t ldy, int y_dtype,
+                           int epilogue, int act, void* aux, int64_t ldaux, float* amax_out,
+                           int num_chunks, const int32_t* chunk_order, void* stream);
+
+/*
  * tp_mlp_fwd -- rank `rank` of a T-way tensor-parallel MLP ("Tensor
  * parallelism" algorithm page, section "How it works"; "Tensor and sequence
  * parallelism", section "Pair adjacent transformer projections"):

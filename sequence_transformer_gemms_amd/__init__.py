@@ -28,7 +28,7 @@ from ._abi import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, ACT_SILU, BF
                    OP_SEQ_CHUNK_GEMM, TpmError, check, lib)
 from .streams import masked_streams  # noqa: F401
 
-__all__ = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+__all__ = ["seq_chunk_gemm", "seq_chunk_gemm_noalloc", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "mx_scales_bytes", "mx_swizzle_scales",
            "tp_mlp_fwd_delayed", "fp8_delayed_scale", "cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",
@@ -102,6 +102,27 @@ def seq_chunk_gemm(A, B, Y, *, trans_a=False, trans_b=False, a_scale=None, b_sca
                             num_chunks, order, _ptr(chunk_ready), epoch,
                             _ptr(workspace), workspace.numel() if workspace is not None else 0,
                             _stream(stream))
+    return check(rc)
+
+
+def seq_chunk_gemm_noalloc(A, B, Y, *, trans_a=False, trans_b=False, a_scale=None, b_scale=None,
+                           epilogue=EPI_FWD, act=ACT_NONE, aux=None, amax_out=None, num_chunks=1,
+                           chunk_order=None, stream=None, M=None, N=None, K=None):
+    """seq_chunk_gemm without a workspace: control words and split-K partial
+    sums in the library's own per-GPU device array (no allocation; calls that
+    overlap on one GPU race).  No chunk flags."""
+    if M is None:
+        M = A.shape[1] if trans_a else A.shape[0]
+    if K is None:
+        K = A.shape[0] if trans_a else A.shape[1]
+    if N is None:
+        N = B.shape[0] if trans_b else B.shape[1]
+    rc = lib.seq_chunk_gemm_noalloc(M, N, K,
+                                    _ptr(A), _ld(A), int(trans_a), dtype_code(A.dtype), _ptr(a_scale),
+                                    _ptr(B), _ld(B), int(trans_b), dtype_code(B.dtype), _ptr(b_scale),
+                                    _ptr(Y), _ld(Y), dtype_code(Y.dtype),
+                                    epilogue, act, _ptr(aux), _ld(aux) if aux is not None else 0, _ptr(amax_out),
+                                    num_chunks, _abi.int_array(chunk_order), _stream(stream))
     return check(rc)
 
 

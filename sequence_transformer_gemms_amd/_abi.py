@@ -39,6 +39,13 @@ lib.seq_chunk_gemm.argtypes = [_i64, _i64, _i64,
                                _i32, _i32, _vp, _i64, _vp,
                                _i32, _vp, _vp, _u32,
                                _vp, _sz, _vp]
+lib.seq_chunk_gemm_noalloc.restype = _i32
+lib.seq_chunk_gemm_noalloc.argtypes = [_i64, _i64, _i64,
+                                       _vp, _i64, _i32, _i32, _vp,
+                                       _vp, _i64, _i32, _i32, _vp,
+                                       _vp, _i64, _i32,
+                                       _i32, _i32, _vp, _i64, _vp,
+                                       _i32, _vp, _vp]
 lib.tp_mlp_fwd.restype = _i32
 lib.tp_mlp_fwd.argtypes = [_i64, _i64, _i64, _i32, _i32,
                            _vp, _vp, _vp,
@@ -132,7 +139,7 @@ lib.tpm_last_error.argtypes = []
 lib.tpm_version.restype = ctypes.c_char_p
 lib.tpm_version.argtypes = []
 
-EXPORTS = ["seq_chunk_gemm", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
+EXPORTS = ["seq_chunk_gemm", "seq_chunk_gemm_noalloc", "tp_mlp_fwd", "tp_mlp_bwd", "tp_linear_bwd", "tp_gated_mlp_fwd", "tp_gated_mlp_bwd",
            "seq_chunk_gemm_mx", "tp_mlp_fwd_mx", "tpm_mx_scales_bytes", "tpm_mx_swizzle_scales",
            "tp_mlp_fwd_delayed", "tpm_fp8_delayed_scale", "tpm_cast_fp8", "tp_mlp_bwd_fp8",
            "partial_reduce_seqshard",

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/tpmlp.h"
@@ -294,6 +295,15 @@ void make_params(const GemmDesc& g, int S, GemmParams& p) {
   p.band_m = std::min(p.mt_per_group, 4);
 }
 
+// K-range splits the matrix-core path plans for a GEMM (1 on the predicated
+// path).  Chunk-gated GEMMs split too; range-done signalling needs whole
+// tiles, and the gated forward and the fp8 outputs pair or scale whole
+// tiles in their epilogues.
+int planned_splits(const GemmDesc& g) {
+  if (fast_path_blocker(g) || g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) return 1;
+  return plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+}
+
 int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   if (g.M == 0 || g.N == 0) return TPM_OK;
   GemmParams p;
@@ -303,10 +313,8 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
     e = launch_gemm_generic(p, g.ta, g.tb, s);
     return e == hipSuccess ? TPM_OK : hip_fail(e, who);
   }
-  // split-K when the plan asks for it and the scratch is there (chunk-gated
-  // GEMMs split too; range-done signalling needs whole tiles)
-  // (the gated forward pairs gate and up columns inside one tile: no split-K)
-  int S = (g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) ? 1 : plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+  // split-K when the plan asks for it and the scratch is there
+  int S = planned_splits(g);
   if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
   make_params(g, S, p);
   // persistent grid: one work-group per CU the stream may use.  A
@@ -494,6 +502,78 @@ int seq_chunk_gemm(int64_t M, int64_t N, int64_t K,
       e = launch_ctrl_init((uint32_t*)amax_out, 1, s);
       if (e != hipSuccess) return hip_fail(e, who);
     }
+  }
+  return run_gemm(g, s, who);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------- allocation-free calls
+namespace {
+
+// The scratch of seq_chunk_gemm_noalloc: control words, then the fp32
+// split-K partial sums.  One copy per GPU, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = kCtrlBytes + (size_t(64) << 20);
+static_assert(kNoAllocScratchBytes == TPM_NOALLOC_SCRATCH_BYTES, "header constant");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name is only a stand-in).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+int scratch_on_current_device(void** out, const char* who) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, who);
+  if (dev < 0 || dev >= 64) return fail(TPM_EUNSUPPORTED, "%s: device index %d", who, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return e != hipSuccess ? hip_fail(e, who) : fail(TPM_EHIP, "%s: no scratch", who);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TPM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int seq_chunk_gemm_noalloc(int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int trans_a, int a_dtype, const float* a_scale,
+                           const void* B, int64_t ldb, int trans_b, int b_dtype, const float* b_scale,
+                           void* Y, int64_t ldy, int y_dtype,
+                           int epilogue, int act, void* aux, int64_t ldaux, float* amax_out,
+                           int num_chunks, const int32_t* chunk_order, void* stream) {
+  const char* who = "seq_chunk_gemm_noalloc";
+  // validation and the split plan on the host, before any device call; a
+  // non-null placeholder stands for the control words until the device's
+  // scratch address is known
+  GemmDesc g{M, N, K, A, lda, trans_a != 0, a_dtype, a_scale, B, ldb, trans_b != 0, b_dtype, b_scale,
+             Y, ldy, y_dtype, epilogue, act, aux, ldaux, amax_out,
+             num_chunks, chunk_order, nullptr, nullptr, 0, reinterpret_cast<uint32_t*>(uintptr_t(256))};
+  int rc = check_gemm(g, who);
+  if (rc != TPM_OK) return rc;
+  if (amax_out && a_dtype == TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: amax on the fp32 path", who);
+  if (M == 0 || N == 0) return TPM_OK;
+  const int S = planned_splits(g);
+  const size_t need = kCtrlBytes + partial_bytes(M, N, S);
+  if (need > kNoAllocScratchBytes)
+    return fail(TPM_EUNSUPPORTED, "%s: this GEMM's split-K plan needs %zu bytes of scratch, more than the %zu the "
+                "library holds per GPU; call seq_chunk_gemm with a workspace", who, need, kNoAllocScratchBytes);
+  void* base = nullptr;
+  rc = scratch_on_current_device(&base, who);
+  if (rc != TPM_OK) return rc;
+  g.ctrl = (uint32_t*)base;
+  g.part = (float*)((char*)base + kCtrlBytes);
+  g.part_bytes = kNoAllocScratchBytes - kCtrlBytes;
+  hipStream_t s = (hipStream_t)stream;
+  if (amax_out) {
+    hipError_t e = launch_ctrl_init((uint32_t*)amax_out, 1, s);
+    if (e != hipSuccess) return hip_fail(e, who);
   }
   return run_gemm(g, s, who);
 }

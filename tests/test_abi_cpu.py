@@ -181,3 +181,15 @@ def test_fp8_backward_chunk_feed_needs_quantised_dy():
 def test_poll_device_error_null_workspace():
     from sequence_transformer_gemms_amd import _abi as X
     assert X.lib.tpm_poll_device_error(None) == X.EWORKSPACE
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch_on_the_host():
+    # QKV-like [8192, 1280] x K 8192: 160 tiles, K cut in 3 -> 126 MB of
+    # partials, more than the per-GPU scratch: rejected before any device call
+    from sequence_transformer_gemms_amd import _abi as X
+    f = X.lib.seq_chunk_gemm_noalloc
+    rc = f(8192, 1280, 8192, FAKE, 8192, 0, X.BF16, None, FAKE, 1280, 0, X.BF16, None, FAKE, 1280, X.BF16,
+           0, 0, None, 0, None, 1, None, None)
+    assert rc == X.EUNSUPPORTED and "scratch" in X.last_error()
+    assert f(-1, 8, 8, FAKE, 8, 0, X.BF16, None, FAKE, 8, 0, X.BF16, None, FAKE, 8, X.BF16,
+             0, 0, None, 0, None, 1, None, None) == X.EINVAL
