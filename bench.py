@@ -18,9 +18,23 @@ The 8 partials of each reduction are this rank's own (written by the GEMM
 into its slot) plus 7 seeded stand-ins for the peers' contributions.
 
 value = algorithmic GEMM work of the step (12 GEMMs, 2*M*N*K each,
-1907.0 GFLOP) / step time.  Extra lines: the same step with inputs resident
-(no chunk arrival), the 8 x [8192,8192] -> [1024,8192] reduction (GB/s), and
-the Llama3-70B (bf16) / 405B (fp8) shaped MLP forwards.
+1907.0 GFLOP) / step time, the step replayed from a HIP graph with every
+input resident.  The JSON line also carries:
+  roofline      the GEMMs' algorithmic rate from HIP events around each
+                GEMM call of the eager step, against the bf16 MFMA peak
+  system        GPU, ROCm and host, and the graphics clock observed while
+                the step's graph repeats (outside the timed region)
+  extra         the step with chunks arriving from a producer stream (only
+                the chunk-fed GEMMs on the CU-masked compute stream); the
+                single column-parallel projection (8192^3, 4 chunks, resident
+                and arriving); the 8 x [8192,8192] -> [1024,8192] reduction;
+                the Llama3-70B (bf16) / 405B (fp8, MXFP8, delayed scaling)
+                shaped MLP forwards, the fp8 backward and the gated MLP
+  cpu_baseline  the fp64 oracle's rate on the whole layer step (host cores)
+  parity        per workload, the GPU outputs against the oracle (max and
+                mean of |gpu - ref| / (1 + |ref|)) and the oracle's time;
+                bf16 workloads both against the oracle that reads back the
+                path's bf16-stored intermediates and against the exact layer
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
 """
@@ -47,7 +61,6 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--producer-cus", type=int, default=32,
                     help="CUs of the stream that writes arriving chunks in the arrival step (the others run the GEMMs)")
     ap.add_argument("--yardstick", action="store_true",
@@ -73,22 +86,29 @@ class Layer:
         self.Dattn = heads * hd                      # 1024
         self.C = T
         dev = "cuda"
-        bf = lambda x: si.to_bf16(x).to(dev)
+        # host bf16 copies of the inputs are kept for the oracle leg
+        self.host = {}
+
+        def bf(a, name=None):
+            h = si.to_bf16(a)
+            if name:
+                self.host[name] = h
+            return h.to(dev)
         M, D, Ft, Nq, Da = self.M, self.D, self.Ft, self.Nqkv, self.Dattn
         # seeds follow the workload recipe: X 1, W_up 2, W_down 3, dY_mlp 4,
         # W_qkv 5, W_o 6, attention output 7, dY_qkv 8, dY_o 9
-        x = bf(si.normal_f32((M, D), 1))
+        x = bf(si.normal_f32((M, D), 1), "x")
         self.x_src = x                                # the gathered rows as they land
         self.x_qkv = torch.empty_like(x)
         self.x_mlp = torch.empty_like(x)
-        self.w_qkv = bf(si.normal_f32((D, Nq), 5, 0.02))
-        self.w_up = bf(si.normal_f32((D, Ft), 2, 0.02))
-        self.w_o = bf(si.normal_f32((Da, D), 6, 0.02))
-        self.w_down = bf(si.normal_f32((Ft, D), 3, 0.02))
-        self.attn = bf(si.normal_f32((M, Da), 7))
-        self.dy_qkv = bf(si.normal_f32((M, Nq), 8))
-        self.dy_mlp_src = bf(si.normal_f32((M, D), 4))
-        self.dy_o_src = bf(si.normal_f32((M, D), 9))
+        self.w_qkv = bf(si.normal_f32((D, Nq), 5, 0.02), "w_qkv")
+        self.w_up = bf(si.normal_f32((D, Ft), 2, 0.02), "w_up")
+        self.w_o = bf(si.normal_f32((Da, D), 6, 0.02), "w_o")
+        self.w_down = bf(si.normal_f32((Ft, D), 3, 0.02), "w_down")
+        self.attn = bf(si.normal_f32((M, Da), 7), "attn")
+        self.dy_qkv = bf(si.normal_f32((M, Nq), 8), "dy_qkv")
+        self.dy_mlp_src = bf(si.normal_f32((M, D), 4), "dy_mlp")
+        self.dy_o_src = bf(si.normal_f32((M, D), 9), "dy_o")
         self.dy_mlp = torch.empty_like(self.dy_mlp_src)
         self.dy_o = torch.empty_like(self.dy_o_src)
         for dst, src in ((self.x_qkv, x), (self.x_mlp, x), (self.dy_mlp, self.dy_mlp_src),
@@ -102,26 +122,38 @@ class Layer:
         # partial stack: slot `rank` is written by the GEMMs, the other slots
         # hold the peers' stand-in partials (N(0,1), seeds 100 + t)
         self.stack = e(T, M, D)
+        rows = slice(rank * (M // T), (rank + 1) * (M // T))
+        self.host_standin_rows = {}
         for t in range(T):
             if t != rank:
-                self.stack[t] = bf(si.normal_f32((M, D), 100 + t))
+                h = si.to_bf16(si.normal_f32((M, D), 100 + t))
+                self.host_standin_rows[t] = h[rows].clone()
+                self.stack[t] = h.to(dev)
         self.slice_o, self.slice_mlp, self.slice_dxm, self.slice_dxq = (e(M // T, D) for _ in range(4))
         self.ws_fwd = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, self.C, tpm.BF16)
         self.ws_bwd = tpm.alloc_workspace(tpm.OP_MLP_BWD, M, D, F, T, self.C, tpm.BF16)
         # one workspace for all seq_chunk_gemm calls (stream-ordered): control
         # words plus the split-K scratch of the narrowest projections
-        shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1)]
+        shapes = [(M, Nq, D, T), (M, D, Da, T), (M, Da, D, T), (Da, D, M, 1), (D, Nq, M, 1), (M, D, Nq, 1),
+                  (M, Ft, D, T), (M, D, Ft, T), (Ft, D, M, 1), (D, Ft, M, 1), (M, D, Ft, 1)]
         self.ws_g = torch.zeros(max(tpm.workspace_bytes(tpm.OP_SEQ_CHUNK_GEMM, m, n, k, 1, c) for m, n, k, c in shapes),
                                 dtype=torch.uint8, device=dev)
         # and one for the paired backward launches of the two projections
         self.ws_l = torch.zeros(max(tpm.workspace_bytes(tpm.OP_LINEAR_BWD, M, n, k) for n, k in ((D, Da), (Nq, D))),
                                 dtype=torch.uint8, device=dev)
+        # the gated calls of the arrival step have a workspace of their own
+        self.ws_c = torch.zeros_like(self.ws_g)
+        self.dz = e(M, Ft)
         self.flags = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.counters = torch.zeros(4, self.C, dtype=torch.int32, device=dev)
         self.order = si.ring_chunk_order(T, self.C, rank)
         self.dest = si.dest_range_order(T, rank)
         self.producer_cus = producer_cus
         self.compute, self.side = tpm.masked_streams(producer_cus=producer_cus)
+        # the arrival step's main stream: a non-blocking stream, since the
+        # CU-masked streams are blocking ones and the null stream would order
+        # the producer's writes behind its own wait for the gated GEMM
+        self.main = torch.cuda.Stream()
         self.gemm_events = []
         fl = lambda m, n, k: 2.0 * m * n * k
         self.flops = (3 * fl(M, Nq, D) + 3 * fl(M, Ft, D) + 3 * fl(M, D, Da) + 3 * fl(M, D, Ft))
@@ -129,8 +161,8 @@ class Layer:
     # -- chunk arrival: the producer stream writes the remote chunks in ring
     # order (one tpm_write_chunks launch, which publishes each chunk's ready
     # flag as soon as its rows are in place; the rank's own chunks are only
-    # flagged).  The boundary event is recorded on the compute stream before
-    # the chunk-fed GEMM is enqueued; the writer is enqueued after it (its
+    # flagged).  The boundary event is recorded on the main stream before the
+    # chunk-fed GEMM is enqueued; the writer is enqueued after it (its
     # host-side launch cost overlaps the GEMM) but starts at the boundary.
     def _boundary(self):
         ev = self.torch.cuda.Event()
@@ -142,6 +174,20 @@ class Layer:
         self.side.wait_event(boundary)            # communication starts at the layer boundary
         self.tpm.write_chunks(dst, src, self.C, self.order, self.flags[which], epoch, self.counters[which],
                               copy=[c not in own for c in range(self.C)], stream=self.side)
+
+    def _gated(self, fn, boundary):
+        """A chunk-fed GEMM on the CU-masked compute stream (the producer has
+        the other CUs), ordered after the main stream's work up to
+        `boundary`; the main stream continues once it is done.  Every other
+        kernel of the step keeps all CUs."""
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        self.compute.wait_event(boundary)
+        with torch.cuda.stream(self.compute):
+            fn()
+        done = torch.cuda.Event()
+        done.record(self.compute)
+        main.wait_event(done)
 
     def _timed(self, fn, record):
         if not record:
@@ -162,82 +208,104 @@ class Layer:
         if err != 0:
             raise RuntimeError(f"device error {err} in a chunk-gated call (watchdog): the timing is invalid")
 
-    def step(self, epoch: int, arrive: bool = True, record: bool = False, check: bool = False):
+    def step(self, epoch: int, arrive: bool = False, record: bool = False, check: bool = False):
+        """One pass of the layer share.  arrive=False: every input resident,
+        the library's fused entry points (tp_mlp_fwd / tp_mlp_bwd /
+        tp_linear_bwd) on the current stream.  arrive=True: the four chunk-fed
+        GEMMs (QKV, MLP up, dZ, dA) wait for chunks the producer stream writes
+        meanwhile and run on the CU-masked compute stream; the other GEMMs
+        and the reductions run on the current stream with every CU (the MLP's
+        GEMMs then as separate seq_chunk_gemm calls)."""
+        if arrive:
+            return self._step_arriving(epoch, record, check)
         torch, tpm = self.torch, self.tpm
         T, r, C = self.T, self.rank, self.C
-        ready = (lambda i: self.flags[i]) if arrive else (lambda i: None)
         wsg = self.ws_g
         own_slot = self.stack[r]
-        # ---- forward, attention projections
-        b = self._boundary()
         self._timed(lambda: tpm.seq_chunk_gemm(self.x_qkv, self.w_qkv, self.qkv, num_chunks=C,
-                                               chunk_order=self.order, chunk_ready=ready(0), epoch=epoch,
-                                               workspace=wsg), record)
-        if arrive:
-            self._arrive(0, self.x_qkv, self.x_src, epoch, b)
-        self._check(wsg, check)
+                                               chunk_order=self.order, workspace=wsg), record)
         self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
                                                chunk_order=self.dest, workspace=wsg), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
-        # ---- forward, MLP
-        b = self._boundary()
         self._timed(lambda: tpm.tp_mlp_fwd(self.x_mlp, self.w_up, self.w_down, self.h, own_slot, T=T, rank=r,
                                            act=tpm.ACT_GELU_ERF, Z_t=self.z, num_chunks=C,
-                                           chunk_order=self.order, chunk_ready=ready(1), epoch=epoch,
-                                           workspace=self.ws_fwd), record)
-        if arrive:
-            self._arrive(1, self.x_mlp, self.x_src, epoch, b)
-        self._check(self.ws_fwd, check)
+                                           chunk_order=self.order, workspace=self.ws_fwd), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
-        # ---- backward, MLP
-        b = self._boundary()
         self._timed(lambda: tpm.tp_mlp_bwd(self.x_mlp, self.w_up, self.w_down, self.z, self.h, self.dy_mlp,
                                            self.g_up, self.g_down, own_slot, T=T, rank=r,
                                            act=tpm.ACT_GELU_ERF, num_chunks=C, dy_chunk_order=self.order,
-                                           dy_ready=ready(2), epoch=epoch, workspace=self.ws_bwd), record)
-        if arrive:
-            self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
-        self._check(self.ws_bwd, check)
+                                           workspace=self.ws_bwd), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
-        # ---- backward, O projection: dA = dY_o W_o^T, dW_o = A^T dY_o.  All of
-        # dY_o resident: one paired launch (tp_linear_bwd); with dY_o's rows
-        # arriving: dA chunk-fed, then dW_o (which needs every row)
-        if not arrive:
-            self._timed(lambda: tpm.tp_linear_bwd(self.attn, self.w_o, self.dy_o, self.g_o, self.d_attn,
-                                                  workspace=self.ws_l), record)
-        b = self._boundary() if arrive else None
-
-        def o_bwd_dgrad():
-            tpm.seq_chunk_gemm(self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C,
-                               chunk_order=self.order, chunk_ready=ready(3), epoch=epoch, workspace=wsg)
-
-        def o_bwd_wgrad():
-            tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg)
-        if arrive and check:
-            o_bwd_dgrad()
-            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
-            self._check(wsg, check)
-            o_bwd_wgrad()
-        elif arrive:
-            self._timed(lambda: (o_bwd_dgrad(), o_bwd_wgrad()), record)
-            self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
-
-        # ---- backward, QKV projection: dW_qkv = X^T dQKV, dX = dQKV W_qkv^T
-        # (partial), one paired launch
+        # O and QKV backward: dW and dX of each projection paired in one launch
+        self._timed(lambda: tpm.tp_linear_bwd(self.attn, self.w_o, self.dy_o, self.g_o, self.d_attn,
+                                              workspace=self.ws_l), record)
         self._timed(lambda: tpm.tp_linear_bwd(self.x_qkv, self.w_qkv, self.dy_qkv, self.g_qkv, own_slot,
                                               workspace=self.ws_l), record)
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
-        if arrive:
-            done = torch.cuda.Event()
-            done.record(self.side)
-            torch.cuda.current_stream().wait_event(done)
+
+    def _step_arriving(self, epoch, record, check):
+        torch, tpm = self.torch, self.tpm
+        T, r, C = self.T, self.rank, self.C
+        wsg, wsc = self.ws_g, self.ws_c
+        own_slot = self.stack[r]
+        act = tpm.ACT_GELU_ERF
+        # ---- forward, QKV projection: X rows arriving
+        b = self._boundary()
+        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            self.x_qkv, self.w_qkv, self.qkv, num_chunks=C, chunk_order=self.order, chunk_ready=self.flags[0],
+            epoch=epoch, workspace=wsc), b), record)
+        self._arrive(0, self.x_qkv, self.x_src, epoch, b)
+        self._check(wsc, check)
+        self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
+                                               chunk_order=self.dest, workspace=wsg), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
+        # ---- forward, MLP: GEMM1 chunk-fed + GeLU, GEMM2 on every CU
+        b = self._boundary()
+        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            self.x_mlp, self.w_up, self.h, act=act, aux=self.z, num_chunks=C, chunk_order=self.order,
+            chunk_ready=self.flags[1], epoch=epoch, workspace=wsc), b), record)
+        self._arrive(1, self.x_mlp, self.x_src, epoch, b)
+        self._check(wsc, check)
+        self._timed(lambda: tpm.seq_chunk_gemm(self.h, self.w_down, own_slot, num_chunks=T,
+                                               chunk_order=self.dest, workspace=wsg), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
+        # ---- backward, MLP: dZ chunk-fed by dY rows, then dW_down, dW_up, dX
+        b = self._boundary()
+        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            self.dy_mlp, self.w_down, self.dz, trans_b=True, epilogue=tpm.EPI_DACT, act=act, aux=self.z,
+            num_chunks=C, chunk_order=self.order, chunk_ready=self.flags[2], epoch=epoch, workspace=wsc), b),
+            record)
+        self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
+        self._check(wsc, check)
+        self._timed(lambda: (tpm.seq_chunk_gemm(self.h, self.dy_mlp, self.g_down, trans_a=True, workspace=wsg),
+                             tpm.seq_chunk_gemm(self.x_mlp, self.dz, self.g_up, trans_a=True, workspace=wsg),
+                             tpm.seq_chunk_gemm(self.dz, self.w_up, own_slot, trans_b=True, workspace=wsg)),
+                    record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
+        # ---- backward, O projection: dA chunk-fed by dY_o rows, then dW_o
+        b = self._boundary()
+        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C, chunk_order=self.order,
+            chunk_ready=self.flags[3], epoch=epoch, workspace=wsc), b), record)
+        self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
+        self._check(wsc, check)
+        self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg),
+                    record)
+        # ---- backward, QKV projection (paired dW and dX)
+        self._timed(lambda: tpm.tp_linear_bwd(self.x_qkv, self.w_qkv, self.dy_qkv, self.g_qkv, own_slot,
+                                              workspace=self.ws_l), record)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
+        done = torch.cuda.Event()
+        done.record(self.side)
+        torch.cuda.current_stream().wait_event(done)
 
 
-def time_steps(torch, layer, steps, warmup, arrive, epoch0):
-    """Warm-up, then `steps` timed steps on the compute stream (the CU-masked
-    one when chunks arrive from the producer stream, the default stream with
-    every CU when all chunks are resident)."""
-    stream = layer.compute if arrive else torch.cuda.default_stream()
+def time_steps(torch, layer, steps, warmup, arrive, epoch0, stream=None):
+    """Warm-up, then `steps` timed steps on `stream` (default: the default
+    stream for the resident step, the layer's non-blocking main stream for
+    the arrival step; every CU).  In the arrival step the chunk-fed GEMMs go
+    to the CU-masked compute stream and everything else stays on `stream`."""
+    stream = stream or (layer.main if arrive else torch.cuda.default_stream())
     with torch.cuda.stream(stream):
         for i in range(warmup):
             layer.step(epoch0 + i, arrive=arrive)
@@ -264,7 +332,7 @@ def time_steps(torch, layer, steps, warmup, arrive, epoch0):
 def time_steps_graph(torch, layer, steps, warmup):
     """The resident step captured once in a HIP graph and replayed: the same
     kernels with the same arguments, without the host launching each of
-    them.  Returns ms per step."""
+    them.  Returns ms per step and the graph."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -283,7 +351,7 @@ def time_steps_graph(torch, layer, steps, warmup):
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    return a.elapsed_time(b) / steps, g
 
 
 def arrival_step(torch, layer, args, ms_resident):
@@ -295,6 +363,11 @@ def arrival_step(torch, layer, args, ms_resident):
     7 x 8 MB) and the overlap efficiency
     (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
     ms, gemm_ms, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000)
+    torch.cuda.synchronize()
+    # the resident step confined to the compute stream's CUs: separates what
+    # the CU partition costs from what waiting for chunks costs
+    ms_res_masked, _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=3000,
+                                     stream=layer.compute)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     epoch = 5000
@@ -310,7 +383,10 @@ def arrival_step(torch, layer, args, ms_resident):
     return {"ms": round(ms, 4), "TFLOPS": round(layer.flops / (ms * 1e-3) / 1e12, 2),
             "gemm_TFLOPS": round(layer.flops / (gemm_ms * 1e-3) / 1e12, 2),
             "writer_only_ms": round(t_copy, 4), "overlap_efficiency": round(eff, 3),
-            "producer_cus": layer.producer_cus}
+            "resident_eager_ms_all_cus": round(ms_resident, 4),
+            "resident_eager_ms_on_compute_cus": round(ms_res_masked, 4),
+            "producer_cus": layer.producer_cus,
+            "streams": "chunk-fed GEMMs on the compute CUs, every other kernel on all CUs"}
 
 
 def bench_reduce(torch, tpm, si, iters=40):
@@ -322,8 +398,11 @@ def bench_reduce(torch, tpm, si, iters=40):
     single-launch median (one event pair per launch) is reported beside it."""
     T, M, D = 8, 8192, 8192
     P = torch.empty(T, M, D, dtype=torch.bfloat16, device="cuda")
+    host_rows = []                                  # rank 0's rows of each partial, for the oracle leg
     for t in range(T):
-        P[t] = si.to_bf16(si.normal_f32((M, D), 100 + t)).cuda()
+        h = si.to_bf16(si.normal_f32((M, D), 100 + t))
+        host_rows.append(h[:M // T].clone())
+        P[t] = h.cuda()
     out = torch.empty(M // T, D, dtype=torch.bfloat16, device="cuda")
     for r in range(T):
         tpm.partial_reduce_seqshard(P, out, T=T, rank=r)
@@ -346,10 +425,13 @@ def bench_reduce(torch, tpm, si, iters=40):
     ms = sorted(x.elapsed_time(y) for x, y in evs)
     med = ms[len(ms) // 2]
     nbytes = T * (M // T) * D * 2 + (M // T) * D * 2
+    tpm.partial_reduce_seqshard(P, out, T=T, rank=0)
+    torch.cuda.synchronize()
+    cap = {"partial_rows": host_rows, "out": out.cpu()}
     del P
     return dict(bytes=nbytes, ms_back_to_back=per_launch, GBs=nbytes / (per_launch * 1e-3) / 1e9,
                 frac_hbm_peak=nbytes / (per_launch * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                ms_single_launch_median=med, GBs_single_launch=nbytes / (med * 1e-3) / 1e9)
+                ms_single_launch_median=med, GBs_single_launch=nbytes / (med * 1e-3) / 1e9), cap
 
 
 def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
@@ -367,11 +449,14 @@ def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
         wdq, sd = si.to_e4m3_current(np.ascontiguousarray(wd.T))
         X, WU, WD = xq.to(dev), wuq.to(dev), wdq.to(dev)
         scales = torch.tensor([sx, su, sd], dtype=torch.float32, device=dev)
+        sH = torch.empty(1, dtype=torch.float32, device=dev)
         ws = tpm.alloc_workspace(tpm.OP_MLP_FWD, M, D, F, T, C, tpm.FP8_E4M3)
         call = lambda: tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, scales=scales,
-                                      num_chunks=C, workspace=ws)
+                                      h_scale_out=sH, num_chunks=C, workspace=ws)
+        cap = {"xq": xq, "sx": float(sx), "wuq": wuq, "su": float(su), "wdq": wdq, "sd": float(sd)}
     else:
-        X, WU, WD = si.to_bf16(x).to(dev), si.to_bf16(wu).to(dev), si.to_bf16(wd).to(dev)
+        cap = {"x": si.to_bf16(x), "wu": si.to_bf16(wu), "wd": si.to_bf16(wd)}
+        X, WU, WD = cap["x"].to(dev), cap["wu"].to(dev), cap["wd"].to(dev)
         call = lambda: tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, num_chunks=C)
     del x, wu, wd
     for _ in range(3):
@@ -389,8 +474,12 @@ def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
     flops = 2.0 * M * Ft * D * 2
     peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     tf = flops / (ms * 1e-3) / 1e12
+    cap.update(H=H.cpu(), P=P.cpu())
+    if fp8:
+        # H's e4m3 codes as GEMM2 read them (the workspace after its control block)
+        cap.update(Hq=ws[2048:2048 + M * Ft].cpu().view(M, Ft), sH=sH.item())
     return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="fp8_e4m3" if fp8 else "bf16", ms=ms, TFLOPS=tf,
-                frac_mfma_peak=tf / peak)
+                frac_mfma_peak=tf / peak), cap
 
 
 def sweep_point(torch, tpm, si, M, D, F, T, C, iters=10):
@@ -685,54 +774,356 @@ def recorded_traffic():
     return int(m_b.group(1))
 
 
-def cpu_baseline(sample_tokens: int, target_s: float = 20.0):
-    """The fp64 oracle, as it stands, on the first m tokens of the same layer
-    (all weights, D = 8192, F/T = 3584): the 12 GEMMs of the step at M = m.
-    A calibration run on `sample_tokens` tokens sets m so that the timed run
-    takes about `target_s` seconds (at most the full 4096 tokens).  Reported
-    in the step metric's unit."""
-    cal = _cpu_oracle_run(sample_tokens)
-    per_token_s = cal["seconds"] / sample_tokens
-    m = int(min(4096, max(256, (target_s / per_token_s) // 256 * 256)))
-    r = _cpu_oracle_run(m)
-    return dict(value=r["flops"] / r["seconds"] / 1e12, unit="TFLOPS", cores=r["threads"], kind="oracle",
-                sample=f"fp64 oracle, the 12 GEMMs + GeLU of the layer step on {m} of 4096 tokens "
-                       f"({r['flops'] / 1e9:.1f} GFLOP in {r['seconds']:.1f} s)")
+def capture_layer(torch, layer):
+    """One resident step (eager, every CU) after the timed runs; its outputs
+    and the host copies of its inputs, for the oracle leg."""
+    layer.step(0, arrive=False)
+    torch.cuda.synchronize()
+    out = {k: getattr(layer, k).cpu() for k in ("qkv", "slice_o", "z", "h", "slice_mlp", "g_down", "g_up",
+                                                "slice_dxm", "d_attn", "g_o", "g_qkv", "slice_dxq")}
+    # the dZ the MLP backward stored (its workspace, after the control block)
+    M, Ft = layer.M, layer.Ft
+    out["dz"] = layer.ws_bwd[2048:2048 + 2 * M * Ft].view(torch.bfloat16).view(M, Ft).cpu()
+    return {"inputs": dict(layer.host), "standin_rows": dict(layer.host_standin_rows), "out": out,
+            "T": layer.T, "rank": layer.rank}
 
 
-def _cpu_oracle_run(sample_tokens: int):
-    import numpy as np  # noqa: F401
+def bench_c2(torch, tpm, si, producer_cus, iters=10):
+    """The single column-parallel projection: X [8192, 8192] bf16 (N(0,1)),
+    rank 0's shard [8192, 8192] of W [8192, 32768] (N(0, 1/8192)), X cut
+    into 4 sequence chunks of 2048 tokens consumed in ring order [0, 3, 2, 1].
+    Resident (every CU; and on the compute stream's CUs alone), then with
+    chunks 1..3 written by the producer stream while the chunk-gated GEMM
+    runs on the compute stream (chunk 0 is this rank's own and only
+    flagged).  Medians of `iters` calls, HIP events; the arriving result
+    must equal the resident one bit for bit."""
+    import numpy as np
+    M, K, Nfull, T, C = 8192, 8192, 32768, 4, 4
+    N = Nfull // T
+    x = si.to_bf16(si.normal_f32((M, K), 1))
+    w = si.to_bf16(np.ascontiguousarray(si.normal_f32((K, Nfull), 2, 1.0 / np.sqrt(8192.0))[:, :N]))
+    X, W = x.cuda(), w.cuda()
+    Y, Y2 = (torch.empty(M, N, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    Xa = X.clone()
+    order = si.ring_chunk_order(T, C, 0)
+    copy = [c != 0 for c in range(C)]
+    ws = tpm.alloc_workspace(tpm.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=C)
+    flags = torch.zeros(C, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(C, dtype=torch.int32, device="cuda")
+    fl = 2.0 * M * N * K
+
+    def med(fn, stream):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[iters // 2]
+
+    epoch = [0]
+    out = {}
+    resident = lambda st: tpm.seq_chunk_gemm(X, W, Y, num_chunks=C, chunk_order=order, workspace=ws, stream=st)
+    t_res = med(lambda: resident(torch.cuda.current_stream()), torch.cuda.current_stream())
+    with tpm.masked_streams(producer_cus=producer_cus) as ms:
+        comp, prod = ms.compute, ms.producer
+        t_res_m = med(lambda: resident(comp), comp)
+
+        def arriving():
+            epoch[0] += 1
+            a = torch.cuda.Event()
+            a.record(comp)
+            prod.wait_event(a)
+            tpm.seq_chunk_gemm(Xa, W, Y2, num_chunks=C, chunk_order=order, chunk_ready=flags, epoch=epoch[0],
+                               workspace=ws, stream=comp)
+            tpm.write_chunks(Xa, X, C, order, flags, epoch[0], counters, copy=copy, stream=prod)
+            d = torch.cuda.Event()
+            d.record(prod)
+            comp.wait_event(d)
+
+        def writer():
+            epoch[0] += 1
+            tpm.write_chunks(Xa, X, C, order, flags, epoch[0], counters, copy=copy, stream=prod)
+        t_arr = med(arriving, comp)
+        err = tpm.poll_device_error(ws)
+        t_wr = med(writer, prod)
+    if err != 0:
+        raise RuntimeError(f"device error {err} in the chunk-gated C2 projection (watchdog)")
+    out.update(M=M, N=N, K=K, chunks=C, chunk_order=order, dtype="bf16",
+               resident_ms=round(t_res, 4), TFLOPS=round(fl / (t_res * 1e-3) / 1e12, 1),
+               frac_mfma_peak=round(fl / (t_res * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               resident_ms_on_compute_cus=round(t_res_m, 4),
+               arriving_ms=round(t_arr, 4), arriving_TFLOPS=round(fl / (t_arr * 1e-3) / 1e12, 1),
+               writer_only_ms=round(t_wr, 4),
+               overlap_efficiency=round((t_res + t_wr - t_arr) / min(t_res, t_wr), 3),
+               producer_cus=producer_cus, arriving_bitwise_equal_resident=bool(torch.equal(Y, Y2)))
+    cap = {"x": x, "w": w, "Y": Y.cpu()}
+    return out, cap
+
+
+def run_c1(torch, tpm, si):
+    """The tiny fp32 TP MLP (X [8, 32], A [32, 128] in 4 column shards,
+    B [128, 32] in 4 row shards, ReLU, the page's generator): the 4 ranks'
+    forwards and the 4 slices of the reduction, Y assembled from them."""
+    c = si.c1_tiny_mlp("page3")
+    m, d, f, T = c["m"], c["d"], c["f"], c["t"]
+    s = f // T
+    X = torch.from_numpy(c["x"]).cuda()
+    P = torch.empty(T, m, d, dtype=torch.float32, device="cuda")
+    for t in range(T):
+        wu = torch.from_numpy(c["a"][:, t * s:(t + 1) * s].copy()).cuda()
+        wd = torch.from_numpy(c["b"][t * s:(t + 1) * s, :].copy()).cuda()
+        H = torch.empty(m, s, dtype=torch.float32, device="cuda")
+        tpm.tp_mlp_fwd(X, wu, wd, H, P[t], T=T, rank=t, act=tpm.ACT_RELU)
+    Y = torch.empty(m, d, dtype=torch.float32, device="cuda")
+    for r in range(T):
+        tpm.partial_reduce_seqshard(P, Y[r * (m // T):(r + 1) * (m // T)], T=T, rank=r)
+    torch.cuda.synchronize()
+    return {"inputs": c, "Y": Y.cpu()}
+
+
+def system_info(torch):
+    """What the numbers were measured on."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": props.name, "gcn_arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1), "hip_runtime": torch.version.hip,
+            "torch": torch.__version__}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info.update(host_cpu=cpu, host_cpu_affinity=len(os.sched_getaffinity(0)),
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
+    return info
+
+
+def _sclk_file(torch):
+    p = torch.cuda.get_device_properties(0)
+    path = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0/pp_dpm_sclk"
+    return path if os.access(path, os.R_OK) else None
+
+
+def _read_sclk(path):
+    """The current graphics clock level (MHz) from the driver's DPM table:
+    the line marked '*'."""
+    for line in open(path):
+        if "*" in line:
+            digits = "".join(ch for ch in line.split(":", 1)[1] if ch.isdigit())
+            return int(digits) if digits else None
+    return None
+
+
+def observe_sclk(torch, replay, seconds=0.6):
+    """The graphics clock while the timed work repeats: `replay` runs back
+    to back (synchronising every 16 calls) for about `seconds` while a thread
+    samples the driver's current clock level every 5 ms.  Outside the timed
+    regions, so the sampling cannot perturb them.  None where the sysfs file
+    is not readable."""
+    import threading
+    path = _sclk_file(torch)
+    if path is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                v = _read_sclk(path)
+            except OSError:
+                v = None
+            if v:
+                samples.append(v)
+            stop.wait(0.005)
+    replay()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            replay()
+        torch.cuda.synchronize()
+        n += 16
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    v = sorted(samples)
+    return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v), "replays": n,
+            "source": "pp_dpm_sclk current level"}
+
+
+# ------------------------------------------------------------------ oracle leg
+def _err(pairs):
+    """max and mean over every element of |gpu - ref| / (1 + |ref|), and the
+    output holding the maximum."""
+    import numpy as np
+    mx, worst, tot, n = 0.0, None, 0.0, 0
+    for name, g, r in pairs:
+        e = np.abs(g - r) / (1.0 + np.abs(r))
+        m = float(e.max()) if e.size else 0.0
+        if worst is None or m > mx:
+            mx, worst = m, name
+        tot += float(e.sum())
+        n += e.size
+    return {"max_err": float(f"{mx:.4g}"), "mean_err": float(f"{tot / max(n, 1):.4g}"), "worst_output": worst}
+
+
+def _c5_oracle(ops, formats, h, standins, T, rank, reading, gpu=None):
+    """The layer step's outputs from the fp64 oracle, in one of three
+    readings of the values the path stores in bf16 between two of its
+    GEMMs (Z, H, dZ, this rank's partials):
+      'gpu_fed'  each GEMM against the exact product of the inputs the GPU
+                 gave it: the GPU's saved Z and H and its stored dZ are
+                 inputs (`gpu`), partials exact;
+      'mirrored' the oracle's own chain, every stored value rounded to bf16
+                 where the path stores it;
+      'exact'    the exact layer, nothing rounded."""
+    import numpy as np
+    rb = formats.round_bf16 if reading == "mirrored" else (lambda v: v)
+    X, WQ, WU, WO, WD = h["x"], h["w_qkv"], h["w_up"], h["w_o"], h["w_down"]
+    A, DQ, DY, DYO = h["attn"], h["dy_qkv"], h["dy_mlp"], h["dy_o"]
+    M = X.shape[0]
+    rows = slice(rank * (M // T), (rank + 1) * (M // T))
+
+    def reduce(own):
+        buf = np.stack([rb(own)[rows] if t == rank else standins[t] for t in range(T)])
+        return ops.partial_reduce_seqshard(buf, -1)
+    r = {"qkv": ops.gemm(X, WQ), "slice_o": reduce(ops.gemm(A, WO))}
+    if reading == "gpu_fed":
+        z, hh = ops.gemm(X, WU), None
+        r.update(z=z, h=ops.act_fwd(z, ops.ACT_GELU_ERF), slice_mlp=reduce(ops.gemm(gpu["h"], WD)))
+        bw = ops.tp_mlp_bwd(X, WU, WD, gpu["z"], gpu["h"], DY, ops.ACT_GELU_ERF, dz_stored=gpu["dz"])
+    else:
+        store = "bf16" if reading == "mirrored" else None
+        fw = ops.tp_mlp_fwd(X, WU, WD, ops.ACT_GELU_ERF, store=store)
+        r.update(z=fw["Z"], h=fw["H"], slice_mlp=reduce(fw["P"]))
+        bw = ops.tp_mlp_bwd(X, WU, WD, rb(fw["Z"]), rb(fw["H"]), DY, ops.ACT_GELU_ERF, store=store)
+    r.update(dz=bw["dZ"], g_down=bw["dW_down"], g_up=bw["dW_up"], slice_dxm=reduce(bw["dX"]))
+    lo = ops.linear_bwd(A, WO, DYO)
+    lq = ops.linear_bwd(X, WQ, DQ)
+    r.update(d_attn=lo["dX"], g_o=lo["dW"], g_qkv=lq["dW"], slice_dxq=reduce(lq["dX"]))
+    return r
+
+
+def cpu_leg(caps):
+    """The fp64 oracle on the host, after all GPU work: its time on each
+    configuration the GPU ran (the oracle as it stands, BLAS threads as the
+    host gives them), and the parity of the GPU's outputs against it.  The
+    layer step's oracle run is also the cpu_baseline figure.  bf16 configs
+    are compared with the oracle that reads back the path's bf16-stored
+    intermediates ('mirrored') and with the exact layer ('unmirrored')."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
-    import synthetic_inputs as si
-    from oracle import ops
-    m, D, Ft, Nq, Da = sample_tokens, 8192, 3584, 1280, 1024
-    f64 = lambda a: si.to_bf16(a).to(dtype=__import__("torch").float64).numpy()
-    x = f64(si.normal_f32((4096, D), 1)[:m])
-    w_qkv = f64(si.normal_f32((D, Nq), 5, 0.02))
-    w_up = f64(si.normal_f32((D, Ft), 2, 0.02))
-    w_o = f64(si.normal_f32((Da, D), 6, 0.02))
-    w_down = f64(si.normal_f32((Ft, D), 3, 0.02))
-    attn = f64(si.normal_f32((4096, Da), 7)[:m])
-    dy_qkv = f64(si.normal_f32((4096, Nq), 8)[:m])
-    dy_mlp = f64(si.normal_f32((4096, D), 4)[:m])
-    dy_o = f64(si.normal_f32((4096, D), 9)[:m])
-    t0 = time.perf_counter()
-    ops.seq_chunk_gemm(x, w_qkv)
-    ops.seq_chunk_gemm(attn, w_o)
-    fw = ops.tp_mlp_fwd(x, w_up, w_down, ops.ACT_GELU_ERF, store="bf16")
-    ops.tp_mlp_bwd(x, w_up, w_down, fw["Z"], fw["H"], dy_mlp, ops.ACT_GELU_ERF, store="bf16")
-    ops.linear_bwd(attn, w_o, dy_o)
-    ops.linear_bwd(x, w_qkv, dy_qkv)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * m * (3 * D * Nq + 3 * D * Ft + 3 * Da * D + 3 * Ft * D)
+    from oracle import formats, ops
+    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()
+    parity = {}
+    tol = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
     threads = 0
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 0)))
-    if threads == 0:
-        threads = len(os.sched_getaffinity(0))
-    return dict(seconds=dt, flops=flops, threads=threads)
+    threads = threads or len(os.sched_getaffinity(0))
+
+    # the layer step (4096 tokens): 12 GEMMs, GeLU and GeLU', 4 reductions
+    c5 = caps["c5"]
+    h = {k: f64(v) for k, v in c5["inputs"].items()}
+    standins = {t: f64(v) for t, v in c5["standin_rows"].items()}
+    got = {k: f64(v) for k, v in c5["out"].items()}
+    t0 = time.perf_counter()
+    ref = _c5_oracle(ops, formats, h, standins, c5["T"], c5["rank"], "gpu_fed", gpu=got)
+    t_c5 = time.perf_counter() - t0
+    fed = _err([(k, got[k], ref[k]) for k in got])
+    del ref
+    ref = _c5_oracle(ops, formats, h, standins, c5["T"], c5["rank"], "mirrored")
+    mir = _err([(k, got[k], ref[k]) for k in got])
+    del ref
+    ref = _c5_oracle(ops, formats, h, standins, c5["T"], c5["rank"], "exact")
+    exa = _err([(k, got[k], ref[k]) for k in got])
+    del ref, h, got
+    M, D, Ft, Nq, Da = 4096, 8192, 3584, 1280, 1024
+    c5_flops = 2.0 * M * (3 * D * Nq + 3 * D * Ft + 3 * Da * D + 3 * Ft * D)
+    parity["c5_layer_step"] = {
+        **fed, "tol": tol["bf16"], "outputs": "all 12 and the stored dZ, whole",
+        "reading": "each GEMM against the exact product of its GPU inputs (saved Z, H, stored dZ)",
+        "oracle_s": round(t_c5, 2),
+        "mirrored_chain": mir, "exact_layer": exa,
+        "note": "mirrored_chain: the oracle's own chain with the bf16 storage roundings; exact_layer: nothing "
+                "rounded.  Both re-derive Z, H and dZ, so a one-ulp difference of a stored value moves act' "
+                "and every weight gradient that reads it"}
+    cpu = dict(value=c5_flops / t_c5 / 1e12, unit="TFLOPS", cores=threads, kind="oracle",
+               sample=f"fp64 oracle, the whole layer step (12 GEMMs, GeLU and GeLU', 4 reductions; 4096 tokens, "
+                      f"{c5_flops / 1e9:.1f} GFLOP) in {t_c5:.1f} s")
+    if "c1" in caps:
+        c = caps["c1"]["inputs"]
+        t0 = time.perf_counter()
+        un = ops.mlp_unsharded(c["x"].astype(np.float64), c["a"].astype(np.float64), c["b"].astype(np.float64),
+                               ops.ACT_RELU)
+        parity["c1_tiny_mlp_fp32"] = {**_err([("Y", caps["c1"]["Y"].double().numpy(), un["Y"])]),
+                                      "tol": tol["f32"], "oracle_s": round(time.perf_counter() - t0, 4)}
+    if "c2" in caps:
+        c = caps["c2"]
+        x, w = f64(c["x"]), f64(c["w"])
+        t0 = time.perf_counter()
+        ref = ops.gemm(x, w)
+        t = time.perf_counter() - t0
+        parity["c2_projection"] = {**_err([("Y", f64(c["Y"]), ref)]), "tol": tol["bf16"], "outputs": "whole",
+                                   "oracle_s": round(t, 2), "unmirrored": "no stored intermediate"}
+        del x, w, ref
+    if "c3" in caps:
+        c = caps["c3"]
+        x, wu, wd = f64(c["x"]), f64(c["wu"]), f64(c["wd"])
+        H, P = f64(c["H"]), f64(c["P"])
+        t0 = time.perf_counter()
+        ref = ops.tp_mlp_fwd(x, wu, wd, ops.ACT_GELU_ERF, store="bf16")
+        t = time.perf_counter() - t0
+        mir = _err([("H", H, ref["H"]), ("P", P, ref["P"])])
+        p_exact = ops.gemm(ref["H"], wd)
+        unm = _err([("H", H, ref["H"]), ("P", P, p_exact)])
+        parity["c3_mlp_fwd"] = {**mir, "tol": tol["bf16"], "outputs": "H, P whole", "oracle_s": round(t, 2),
+                                "unmirrored_max_err": unm["max_err"], "unmirrored_mean_err": unm["mean_err"]}
+        del x, wu, wd, H, P, ref, p_exact
+    if "c3_reduce" in caps:
+        c = caps["c3_reduce"]
+        buf = np.stack([f64(r) for r in c["partial_rows"]])
+        t0 = time.perf_counter()
+        ref = ops.partial_reduce_seqshard(buf, -1)
+        t = time.perf_counter() - t0
+        parity["c3_reduce"] = {**_err([("slice", f64(c["out"]), ref)]), "tol": tol["bf16"],
+                               "outputs": "rank 0's slice, whole", "oracle_s": round(t, 2)}
+        del buf, ref
+    if "c4" in caps:
+        c = caps["c4"]
+        xq, wuq, wdq = (formats.e4m3_to_f64(c[k].numpy()) for k in ("xq", "wuq", "wdq"))
+        t0 = time.perf_counter()
+        ref = ops.tp_mlp_fwd_fp8(xq, c["sx"], wuq.T, c["su"], wdq.T, c["sd"], ops.ACT_GELU_ERF)
+        t = time.perf_counter() - t0
+        H, P, hq = f64(c["H"]), f64(c["P"]), c["Hq"].numpy()
+        # GEMM2 against the exact product of the codes and scale the GPU gave it
+        p_own = ops.gemm(formats.e4m3_to_f64(hq), wdq.T * float(np.float32(c["sd"]))) * c["sH"]
+        parity["c4_fp8_mlp_fwd"] = {**_err([("P", P, p_own)]), "tol": tol["fp8"],
+                                    "outputs": "P whole, against the GPU's own e4m3 H and scale",
+                                    "H_max_err": _err([("H", H, ref["H"])])["max_err"], "H_tol": tol["bf16"],
+                                    "h_code_diff_fraction": float(np.mean(hq != ref["Hq_codes"])),
+                                    "h_scale_equal": bool(c["sH"] == ref["sH"]),
+                                    "whole_chain_P_max_err": _err([("P", P, ref["P"])])["max_err"],
+                                    "oracle_s": round(t, 2)}
+    return cpu, parity
 
 
 def main():
@@ -763,10 +1154,13 @@ def main():
     # headline: the rank's step with every chunk already in place (flags
     # not consulted), on the default stream with every CU
     ms_eager, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=0)
-    ms = time_steps_graph(torch, layer, args.steps, args.warmup)
+    ms, graph = time_steps_graph(torch, layer, args.steps, args.warmup)
     flops = layer.flops
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    system = system_info(torch)
+    system["sclk_during_step_replays"] = observe_sclk(torch, graph.replay)
+    del graph
     rec = {
         "metric": "TFLOPS/GPU on TP-rank MLP fwd+bwd (% of MFMA peak); reduce GB/s",
         "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -786,16 +1180,23 @@ def main():
                      "kernel": "gemm_kernel / gemm_pair_kernel (bf16 MFMA): the step's 12 GEMMs in 10 launches "
                                "(each projection backward's dW and dX paired in one)",
                      "gemm_ms_per_step": round(gemm_ms, 4)},
+        "system": system,
     }
+    caps = {}
     if not args.no_extra:
         extra = {"arrival_step": arrival_step(torch, layer, args, ms_eager)}
-        del layer
+    if not args.no_cpu_baseline:
+        caps["c5"] = capture_layer(torch, layer)
+    del layer
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra["c2_projection"], caps["c2"] = bench_c2(torch, tpm, si, args.producer_cus)
         torch.cuda.empty_cache()
-        extra["reduce_c3"] = bench_reduce(torch, tpm, si)
+        extra["reduce_c3"], caps["c3_reduce"] = bench_reduce(torch, tpm, si)
         torch.cuda.empty_cache()
-        extra["mlp_fwd_c3_bf16"] = bench_mlp_fwd(torch, tpm, si, 8192, 8192, 28672, 8, 8, False)
+        extra["mlp_fwd_c3_bf16"], caps["c3"] = bench_mlp_fwd(torch, tpm, si, 8192, 8192, 28672, 8, 8, False)
         torch.cuda.empty_cache()
-        extra["mlp_fwd_c4_fp8"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
+        extra["mlp_fwd_c4_fp8"], caps["c4"] = bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)
         torch.cuda.empty_cache()
         extra["mlp_fwd_c4_mxfp8"] = bench_mlp_fwd_mx(torch, tpm, si)
         torch.cuda.empty_cache()
@@ -804,9 +1205,10 @@ def main():
         extra["mlp_bwd_c4_fp8"] = bench_mlp_bwd_fp8(torch, tpm)
         torch.cuda.empty_cache()
         extra["gated_mlp_worked_example"] = bench_gated_mlp(torch, tpm, si)
+        caps["c1"] = run_c1(torch, tpm, si)
         rec["extra"] = extra
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+        rec["cpu_baseline"], rec["parity"] = cpu_leg(caps)
     print(json.dumps(rec))
 
 

@@ -10,6 +10,14 @@ never start.  Giving the two streams disjoint CU masks removes that
 dependency; the library sizes its persistent grid from the mask of the
 stream it is called on.
 
+Both are blocking streams (the CU-mask creation call takes no flags), so
+HIP's null stream orders itself against them: work enqueued on either waits
+for the null stream's earlier work, and the null stream's work waits for
+theirs.  A null stream that waits for a chunk-gated GEMM therefore holds
+back a writer enqueued on the producer afterwards, and the GEMM waits for
+that writer: issue the surrounding work on a non-blocking stream
+(torch.cuda.Stream()), never on the null stream, while a gated GEMM waits.
+
 The streams are created with hipExtStreamCreateWithCUMask and owned by the
 returned MaskedStreams object, which destroys them (after synchronising
 them) on close(), at the end of a `with` block, or at interpreter exit,
