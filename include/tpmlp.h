@@ -124,6 +124,13 @@ typedef enum {
  *    given, no row of chunk c is read before chunk_ready[c] >= epoch
  *    (wrap-around compare); the flags are written by the producer of the
  *    chunk (tpm_signal_chunk).  The result does not depend on the order.
+ *    The producer must be able to run while the call waits: on CUs the
+ *    gated kernel does not hold (a CU-masked pair of streams), and not
+ *    ordered behind it -- e.g. not enqueued on a blocking stream after the
+ *    null stream was made to wait for the gated call (HIP's null stream
+ *    orders itself against blocking streams, and streams created with a CU
+ *    mask are blocking).  A wait that cannot end gives up after the
+ *    watchdog limit with TPM_ETIMEOUT in the workspace's error word.
  *    A chunk-gated A must be stored token-major (trans_a = 0) with its
  *    base and every chunk boundary ((M / num_chunks) * lda * element size)
  *    on a 128-byte line, so no cache line of a chunk is fetched before its

@@ -10,10 +10,12 @@
 // the caller's order; a tile of group g may wait for ready[g] >= epoch, and
 // the last finished tile of group g publishes done[g] = epoch.
 //
-// Tile: 256 x 256 per work-group of 4 waves (2 x 2), each wave 128 x 128
-// with v_mfma_f32_32x32x16_bf16 (16 accumulators of 16 floats).  K steps of
-// 64 bf16 are staged global -> LDS with buffer_load ... lds (no VGPR
-// staging), double-buffered (2 x 64 KB).  Operands stored K-major are read
+// Tile: 256 x 256 per work-group.  bf16: 8 waves (2 x 4, two per SIMD),
+// each wave 128 x 64 with v_mfma_f32_32x32x16_bf16 (8 accumulators of 16
+// floats); fp8: 4 waves (2 x 2), each 128 x 128.  K steps of 64 bf16 (128
+// fp8) are staged global -> LDS with buffer_load ... lds (no VGPR staging)
+// through a ring of five 32 KB operand tiles, A two steps and B one step
+// ahead of the step being computed.  Operands stored K-major are read
 // with ds_read_b128; operands stored MN-major (the pages' W[K,N], or X^T in
 // weight gradients) are read with ds_read_b64_tr_b16, which transposes 16-bit
 // elements across each 16-lane group.  The MFMA is issued with the operands
@@ -33,8 +35,19 @@ namespace {
 constexpr int BM = kTileM, BN = kTileN;
 constexpr int ROW_BYTES = 128;                   // K bytes per staged row (64 bf16 / 128 fp8)
 constexpr int TILE_BYTES = 256 * ROW_BYTES;      // one operand tile of one K step: 32 KB
-constexpr int SLOT_BYTES = 2 * TILE_BYTES;       // A + B
-constexpr int NSLOT = 2;                         // K steps held in LDS
+// LDS ring of five operand tiles: A of step k in tile (2k) mod 5, B of step k
+// in tile (2k+1) mod 5 (steps counted from the start of the work unit).
+// While step k is read, steps k+1 and A of k+2 are held or landing, so the A
+// tiles are loaded two steps ahead and the B tiles one step ahead: about 1.5
+// steps (96 KB) in flight per CU, which the global -> LDS path needs to keep
+// up with the matrix cores (one step in flight delivers ~24 bytes/clock/CU,
+// the 256 x 256 tile consumes 32).  The ring takes the whole 160 KB.
+constexpr int NHALF = 5;
+constexpr int RING_BYTES = NHALF * TILE_BYTES;
+// two control words in the ring's last bytes, used only between work units
+// (no operand load in flight): the pair kernel's ticket and the chunk wait's
+// outcome
+constexpr int CTRL_TICKET = RING_BYTES - 16, CTRL_WAIT = RING_BYTES - 32;
 static_assert(ROW_BYTES == kStepBytes, "host-side K step");
 // Wave layouts of the 256 x 256 tile: NW = 4 waves as 2 x 2 (128 x 128 per
 // wave, one wave per SIMD) or NW = 8 waves as 2 x 4 (128 x 64 per wave, two
@@ -54,8 +67,8 @@ struct Layout {
   static constexpr int EPI_WAVE_FLOATS = EPI_ROWS * EPI_LD;
   static constexpr int COL_PASSES = WN / EPI_COLS;
   static constexpr int PASSES = (128 / EPI_ROWS) * COL_PASSES;
-  static constexpr int SMEM = (NSLOT * SLOT_BYTES > NW * EPI_WAVE_FLOATS * 4) ? NSLOT * SLOT_BYTES
-                                                                               : NW * EPI_WAVE_FLOATS * 4;
+  static constexpr int SMEM = RING_BYTES;
+  static_assert(NW * EPI_WAVE_FLOATS * 4 <= CTRL_WAIT, "epilogue staging stays clear of the control words");
 };
 
 // K-major tile: 256 rows x 128 bytes of K, one 128-byte LDS line per row.
@@ -182,6 +195,23 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
   load16_to_lds(rs, voff, lds_tile + (j * THREADS + wave * 64) * 16);
 }
 
+// LDS fragment reads through a restrict-qualified pointer parameter: the
+// compiler then knows each read from its own scope, so it does not make the
+// read wait for the LDS DMA writes in flight (which the kernel orders itself
+// with vmcnt waits and barriers).
+__device__ __forceinline__ i32x4 lds_read16(const char* __restrict__ p) {
+  return *(const lds_i32x4*)((lds_void*)p);
+}
+// two transposed 8-byte reads 2048 bytes (four K rows of an MN-major tile)
+// apart: a 32 x 16 bf16 MFMA fragment
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* __restrict__ p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_void*)p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_void*)(p + 2048)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // One 32 (rows) x 16 (K) bf16 fragment for a 32x32x16 MFMA operand:
 // lane l holds row rb + l%32, K elements 8*(l/32) .. +7 of substep kk (0..3).
 template <bool KMAJ>
@@ -235,8 +265,8 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ bool wait_group(const GemmParams& p, int g) {
-  __shared__ int timed_out;
+__device__ __forceinline__ bool wait_group(const GemmParams& p, int g, char* smem) {
+  volatile int& timed_out = *reinterpret_cast<volatile int*>(smem + CTRL_WAIT);
   if (threadIdx.x == 0) {
     int bad = 0;
     uint32_t polls = 0;
@@ -411,7 +441,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
   constexpr int KSUB = FP8 ? 1 : 2;        // MFMA substeps per K step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int wm = (wave / LY::WAVES_N) * 128;
   const int wn = (wave % LY::WAVES_N) * LY::WN;
 
@@ -434,7 +464,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     const int kend = min(nk, kbeg + p.ksteps_per_split);
     const int nks = kend - kbeg;
     __syncthreads();  // the previous tile's epilogue staging is done with the LDS
-    if (p.ready) wait_group(p, tl.g);
+    if (p.ready) wait_group(p, tl.g, smem);
 
     f32x16 acc[4][NF];
 #pragma unroll
@@ -445,39 +475,150 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-    auto slot = [&](int k) { return smem + (k & (NSLOT - 1)) * SLOT_BYTES; };
-    // Load L (0 .. 2*LOADS-1) of K step k of this split into its slot.  Steps
-    // past the end of the split load zeros (out-of-range offsets) into a slot
-    // that no later step of this tile reads, so the issue pattern and the
-    // load counts are the same for every step.
-    auto load_one = [&](int L, int k) {
-      char* dst = slot(k);
-      const int k0 = k < nks ? (kbeg + k) * KSTEP : p.K;
-      if (L < LOADS) issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k0, p.K, dst, L);
-      else issue_one<BKM, ESZ, THREADS, GATED>(rb, ldb_b, tl.n0, p.N, k0, p.K, dst + TILE_BYTES, L - LOADS, p.gu_off);
+    // the ring tiles of step k (counted from kbeg)
+    auto a_tile = [&](int k) { return smem + ((2 * k) % NHALF) * TILE_BYTES; };
+    auto b_tile = [&](int k) { return smem + ((2 * k + 1) % NHALF) * TILE_BYTES; };
+
+    // ---- per-lane address parts, fixed for the whole unit.
+    // LDS reads.  K-major tile, fragment of rows wbase + 32 i, chunk
+    // c = 2 kk + lane/32 (bf16; fp8: 4 kk + lane/32 and + 2): with
+    // l = lane % 32 the swizzled position is (lane/32 ^ s(l)) ^ K for a
+    // constant K in {0, 2, 4, 6} (the fragment parity flips bit 2), so the
+    // address is wbase*128 + 4096 i + kpart[K/2].  MN-major tile, fragment
+    // of columns wbase + 32 i: the K rows a lane reads differ by constants
+    // (8192 kk + 2048 hh), so the address is mpart(i) + that constant.
+    // (the thread index passes through an empty asm statement so that these
+    // values are computed per unit instead of being hoisted to the kernel
+    // start, where in the pair kernel they would stay live through the
+    // other GEMM's loop)
+    uint32_t tid_u = (uint32_t)tid;
+    asm volatile("" : "+v"(tid_u));
+    const uint32_t lane_u = tid_u & 63u;
+    const uint32_t l32 = lane_u & 31u;
+    const uint32_t p0 = (lane_u >> 5) ^ (((l32 & 7u) ^ (l32 >> 3)) & 7u);
+    uint32_t kpart[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kpart[q] = l32 * 128u + ((p0 ^ (2u * (uint32_t)q)) * 16u);
+    const uint32_t g4 = lane_u >> 4, j16 = lane_u & 15u;
+    const uint32_t klane = (8u * (g4 >> 1) + (j16 >> 2)) * 512u + 8u * (j16 & 1u);
+    const uint32_t mlo = 2u * (g4 & 1u) + ((j16 & 3u) >> 1);
+    const uint32_t msw = swz_mn(j16 >> 2);
+    auto mpart = [&](int wbase, int i) {
+      return klane + (((((uint32_t)wbase >> 3) + 4u * (uint32_t)i + mlo) ^ msw) << 4);
     };
-    auto read_set = [&](const char* __restrict__ st, int kk, Frag (&af)[4], Frag (&bfr)[NF]) {
+    // A step's read offsets (bytes from smem): K-major: o[q] = tile +
+    // wbase*128 + kpart[q]; MN-major: o[i] = tile + mpart(wbase, i).  Every
+    // LDS read address is formed as smem + offset, so that the compiler sees
+    // each read based on the restrict-qualified LDS block (with that
+    // provenance it does not drain the in-flight LDS DMA before a read).
+    struct Bases {
+      uint32_t o[4];
+    };
+    auto bases = [&](uint32_t tile, auto kmc, int wbase, int nfr) {
+      Bases b;
+      if constexpr (decltype(kmc)::value) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i, kk);
-        else af[i] = read_frag<AK>(st, wm + 32 * i, kk);
+        for (int q = 0; q < 4; ++q) b.o[q] = tile + (uint32_t)wbase * 128u + kpart[q];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b.o[i] = i < nfr ? tile + mpart(wbase, i) : tile;
       }
+      return b;
+    };
+    auto frag = [&](const Bases& b, auto kmc, int i, int kk) -> Frag {
+      if constexpr (FP8) {
+        const int q = (2 * kk) ^ (2 * (i & 1));
+        const i32x4 lo = lds_read16(smem + b.o[q] + 4096 * i);
+        const i32x4 hi = lds_read16(smem + b.o[q ^ 1] + 4096 * i);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else if constexpr (decltype(kmc)::value) {
+        const int q = kk ^ (2 * (i & 1));
+        return __builtin_bit_cast(bf16x8, lds_read16(smem + b.o[q] + 4096 * i));
+      } else {
+        return lds_read_tr_pair(smem + b.o[i] + 8192 * kk);
+      }
+    };
+    auto step_bases = [&](int k, Bases& ba, Bases& bb) {
+      ba = bases((uint32_t)(((2 * k) % NHALF) * TILE_BYTES), IC<AK>{}, wm, 4);
+      bb = bases((uint32_t)(((2 * k + 1) % NHALF) * TILE_BYTES), IC<BKM>{}, wn, NF);
+    };
+
+    // DMA loads.  Load j of an operand tile stages LDS chunk j*THREADS + tid.
+    // In a full tile (every row of the operand tile inside the matrix) and a
+    // full K step, its global offset is a per-lane part fixed for the unit
+    // plus a uniform part (row block of load j, K position of the step), which
+    // goes into the scalar offset: no vector arithmetic per load.  Other steps
+    // (the last one of a ragged K, those past the end of the split) and tiles
+    // that cross the matrix edge take the checked form (issue_one).
+    const bool a_full = tl.m0 + BM <= tl.m_end;
+    const bool b_full = tl.n0 + (GATED ? BN / 2 : BN) <= p.N;
+    auto lane_off = [&](auto kmc, int64_t ld_bytes, int mn0, int par, auto gc, int up_off) -> uint32_t {
+      if constexpr (decltype(kmc)::value) {
+        // K-major: row block tid/8, chunk (tid%8) ^ swz_k(row); the row's
+        // bits 3-5 come from tid/64 and, with 4 waves, from load j's parity
+        uint32_t c = (tid_u & 7u) ^ ((tid_u >> 3) & 7u) ^ ((tid_u >> 6) & 7u);
+        if (THREADS == 256) c ^= 4u * (uint32_t)par;
+        return (uint32_t)(((int64_t)(tid_u >> 3)) * ld_bytes) + c * 16u;
+      } else {
+        // MN-major (bf16): K row tid/32 (plus the load's row block), chunk
+        // (tid%32) ^ swz_mn(row % 4)
+        const uint32_t c = (tid_u & 31u) ^ swz_mn((tid_u >> 5) & 3u);
+        int mn, src;
+        if constexpr (decltype(gc)::value) {
+          mn = mn0 + (int)(c >> 3) * 32 + (int)(c & 3u) * 8;
+          src = mn + (((c >> 2) & 1u) ? up_off : 0);
+        } else {
+          mn = mn0 + (int)c * 8;
+          src = mn;
+        }
+        return (uint32_t)(((int64_t)(tid_u >> 5)) * ld_bytes + (int64_t)src * 2);
+      }
+    };
+    uint32_t va[2], vb[2];
 #pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j, kk);
-        else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
+    for (int par = 0; par < 2; ++par) {
+      va[par] = lane_off(IC<AK>{}, lda_b, tl.m0, par, IC<false>{}, 0);
+      vb[par] = lane_off(IC<BKM>{}, ldb_b, tl.n0, par, IC<GATED>{}, p.gu_off);
+    }
+    // uniform part of load j of step k (full steps only)
+    auto uni_off = [&](auto kmc, int64_t ld_bytes, int mn0, int j, int k) -> uint32_t {
+      const int k0 = (kbeg + k) * KSTEP;
+      if constexpr (decltype(kmc)::value)
+        return (uint32_t)((int64_t)(mn0 + j * (THREADS / 8)) * ld_bytes + (int64_t)k0 * ESZ);
+      else
+        return (uint32_t)((int64_t)(k0 + j * (THREADS / 32)) * ld_bytes);
+    };
+    // Load L (0 .. 2*LOADS-1: A loads, then B loads) of K step k of this
+    // split into its ring tile.  Steps past the end of the split load zeros
+    // (out-of-range offsets) into ring tiles that no later step of this unit
+    // reads, so the issue pattern and the load counts are the same for every
+    // step.  FAST: both operand tiles are full and the step is full and
+    // inside the split (see above).
+    auto load_one = [&](int L, int k, auto fc) {
+      constexpr bool FAST = decltype(fc)::value;
+      if (L < LOADS) {
+        if constexpr (FAST)
+          load16_to_lds_s(ra, va[L & 1], uni_off(IC<AK>{}, lda_b, tl.m0, L, k), a_tile(k) + (L * THREADS + wave * 64) * 16);
+        else
+          issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k < nks ? (kbeg + k) * KSTEP : p.K, p.K, a_tile(k),
+                                      L);
+      } else {
+        const int j = L - LOADS;
+        if constexpr (FAST)
+          load16_to_lds_s(rb, vb[j & 1], uni_off(IC<BKM>{}, ldb_b, tl.n0, j, k), b_tile(k) + (j * THREADS + wave * 64) * 16);
+        else
+          issue_one<BKM, ESZ, THREADS, GATED>(rb, ldb_b, tl.n0, p.N, k < nks ? (kbeg + k) * KSTEP : p.K, p.K,
+                                              b_tile(k), j, p.gu_off);
       }
     };
     // fragment r of a set in the order the MFMAs first need them: A0, B0..B(NF-1), A1, A2, A3
-    auto read_one = [&](const char* __restrict__ st, int kk, int r, Frag (&af)[4], Frag (&bfr)[NF]) {
+    auto read_one = [&](const Bases& sa, const Bases& sb, int kk, int r, Frag (&af)[4], Frag (&bfr)[NF]) {
       if (r == 0 || r > NF) {
         const int i = r == 0 ? 0 : r - NF;
-        if constexpr (FP8) af[i] = read_frag_fp8(st, wm + 32 * i, kk);
-        else af[i] = read_frag<AK>(st, wm + 32 * i, kk);
+        af[i] = frag(sa, IC<AK>{}, i, kk);
       } else {
         const int j = r - 1;
-        if constexpr (FP8) bfr[j] = read_frag_fp8(st + TILE_BYTES, wn + 32 * j, kk);
-        else bfr[j] = read_frag<BKM>(st + TILE_BYTES, wn + 32 * j, kk);
+        bfr[j] = frag(sb, IC<BKM>{}, j, kk);
       }
     };
     auto mfma_row = [&](const Frag& a, const Frag (&bfr)[NF], f32x16 (&accrow)[NF]) {
@@ -489,14 +630,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           accrow[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], a, accrow[j], 0, 0, 0);
       }
     };
-    // Loads of one K step are issued in three parts: part 0 right after the
-    // barrier that frees the slot (last phase of the step two before), parts
-    // 1 and 2 in the first two phases of the step before.  Each part's loads
-    // are spread between the MFMA row groups of its phase.
-    constexpr int TOTAL_LOADS = 2 * LOADS;
-    constexpr int P0 = TOTAL_LOADS / 3, P1 = (TOTAL_LOADS - P0) / 2, P2 = TOTAL_LOADS - P0 - P1;
-    // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
-    // loads L0 .. L0+NL-1 of K step kl spread between the row groups.
+    // During step k the loads of step k+2 are issued: A's in the first two
+    // phases (into the tile B of step k-1 left), B's right after the barrier
+    // that frees step k's tiles (into A of step k's).  Each part's loads are
+    // spread between the MFMA row groups of its phase.
+    constexpr int LA0 = LOADS / 2, LA1 = LOADS - LOADS / 2;
     // MXFP8: the scale dwords of K step s for this lane's fragments (4 rows
     // of A, NF of B; bytes = the step's four 32-element blocks), and the same
     // shifted right by 8 bytes for lanes 32-63, which hold the second 32 K
@@ -526,9 +664,13 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         for (int j = 0; j < NF; ++j) sb_cur[j] = (int)((uint32_t)sb_next[j] >> h8);
       }
     };
+    // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
+    // loads L0 .. L0+NL-1 of K step kl spread between the row groups and the
+    // reads R0 .. R0+NR-1 of the next set (substep rkk of bases rsa / rsb)
+    // one after each MFMA.
     auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl,
-                         auto r0c, auto nrc, const char* __restrict__ rst, int rkk, Frag (&rfa)[4], Frag (&rfb)[NF],
-                         auto opc) {
+                         auto fastc, auto r0c, auto nrc, const Bases& rsa, const Bases& rsb, int rkk, Frag (&rfa)[4],
+                         Frag (&rfb)[NF], auto opc) {
       constexpr int OPS = decltype(opc)::value;  // MX: byte of the scale dwords (0: substep 0, 2: substep 1)
       constexpr int I0 = decltype(i0c)::value, NI = decltype(nic)::value;
       constexpr int L0 = decltype(l0c)::value, NL = decltype(nlc)::value;
@@ -549,75 +691,96 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             acc[I0 + ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[I0 + ii], acc[I0 + ii][j], 0, 0, 0);
           static_for<NR>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            if constexpr (r * NM / NR == m) read_one(rst, rkk, R0 + r, rfa, rfb);
+            if constexpr (r * NM / NR == m) read_one(rsa, rsb, rkk, R0 + r, rfa, rfb);
           });
           __builtin_amdgcn_sched_barrier(0);
         });
         static_for<NL>([&](auto lc) {
           constexpr int l = decltype(lc)::value;
-          if constexpr (l * NI / NL == ii) load_one(L0 + l, kl);
+          if constexpr (l * NI / NL == ii) load_one(L0 + l, kl, fastc);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // Wait until all of this thread's loads have landed and its LDS reads are
-    // done, then synchronise the work-group with a bare s_barrier
-    // (__syncthreads() would add a full fence).  The empty asm statements keep
-    // the compiler from moving LDS accesses across it.
-    auto step_barrier = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    // Wait until this thread's loads of the next step have landed (only the
+    // A loads of the step after it, issued last, may still be in flight: the
+    // NPEND most recent vector-memory operations) and its LDS reads are done,
+    // then synchronise the work-group with a bare s_barrier (__syncthreads()
+    // would add a full fence).  The empty asm statements keep the compiler
+    // from moving LDS accesses across it.
+    auto step_barrier = [&](auto npc) {
+      constexpr int NPEND = decltype(npc)::value;
+      static_assert(NPEND < 64, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((NPEND & 15) | 0x0070 | ((NPEND >> 4) << 14));  // vmcnt(NPEND) lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
 
-    // Software pipeline over two K-step slots.  Step kt runs in four phases
+    // Software pipeline over the five-tile ring.  Step kt runs in four phases
     // (bf16: its four K=16 substeps; fp8: its two K=64 substeps, accumulator
     // rows 0-1 then 2-3).  The fragments of the next substep are read from
     // LDS while the current one's MFMAs run, one read after each MFMA in the
     // order the next phase first needs them.  Before the last phase every
     // thread waits for its loads of step kt+1 and for its reads of step kt,
     // and the barrier then (a) makes step kt+1 visible, whose first fragments
-    // are read during the last phase, and (b) frees step kt's slot, which the
-    // loads of step kt+2 start refilling in that same phase.
+    // are read during the last phase, and (b) frees step kt's tiles, into
+    // whose A tile the B loads of step kt+2 go in that same phase.
     Frag fa[2][4], fb[2][NF];
     load_scales(kbeg);
-    static_for<TOTAL_LOADS>([&](auto lc) { load_one(decltype(lc)::value, 0); });
-    step_barrier();
-    read_set(slot(0), 0, fa[0], fb[0]);
-    static_for<P0>([&](auto lc) { load_one(decltype(lc)::value, 1); });
+    static_for<2 * LOADS>([&](auto lc) { load_one(decltype(lc)::value, 0, IC<false>{}); });
+    static_for<2 * LOADS>([&](auto lc) { load_one(decltype(lc)::value, 1, IC<false>{}); });
+    step_barrier(IC<2 * LOADS>{});
     constexpr int NRD = 4 + NF;  // fragment reads per set
-    for (int kt = 0; kt < nks; ++kt) {
-      const char* cur = slot(kt);
-      const char* nx = slot(kt + 1);
-      const int kn = kt + 1;
+    Bases ca, cb;
+    step_bases(0, ca, cb);
+    static_for<NRD>([&](auto rc) { read_one(ca, cb, 0, decltype(rc)::value, fa[0], fb[0]); });
+    auto body = [&](int kt, auto fc) {
+      Bases na, nb;
+      step_bases(kt + 1, na, nb);
+      const int kl = kt + 2;
       if constexpr (FP8) {
         // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0.
-        // MX: the scales of step kt+1 load during phase 0 and land by the
-        // barrier (which waits for every load of this thread).
+        // MX: the scales of step kt+1 load during phase 0, before this
+        // step's operand loads, and land by the barrier.
         take_scales();
-        load_scales(kbeg + kn);
-        mfma_rows(IC<0>{}, IC<2>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD / 2>{}, cur, 1, fa[1], fb[1],
-                  IC<0>{});
-        mfma_rows(IC<2>{}, IC<2>{}, IC<P0 + P1>{}, IC<P2>{}, fa[0], fb[0], kn, IC<NRD / 2>{}, IC<NRD - NRD / 2>{}, cur, 1,
+        load_scales(kbeg + kt + 1);
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<LA0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD / 2>{}, ca, cb, 1,
                   fa[1], fb[1], IC<0>{});
-        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kn, IC<0>{}, IC<0>{}, cur, 0, fa[0], fb[0], IC<2>{});
-        step_barrier();
-        mfma_rows(IC<2>{}, IC<2>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0],
+        mfma_rows(IC<2>{}, IC<2>{}, IC<LA0>{}, IC<LA1>{}, fa[0], fb[0], kl, fc, IC<NRD / 2>{}, IC<NRD - NRD / 2>{}, ca,
+                  cb, 1, fa[1], fb[1], IC<0>{});
+        mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<0>{}, ca, cb, 0, fa[0], fb[0],
                   IC<2>{});
+        step_barrier(IC<LOADS>{});
+        mfma_rows(IC<2>{}, IC<2>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, na, nb, 0,
+                  fa[0], fb[0], IC<2>{});
       } else {
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0>{}, IC<P1>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 1, fa[1], fb[1],
-                  IC<0>{});
-        mfma_rows(IC<0>{}, IC<4>{}, IC<P0 + P1>{}, IC<P2>{}, fa[1], fb[1], kn, IC<0>{}, IC<NRD>{}, cur, 2, fa[0], fb[0],
-                  IC<0>{});
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kn, IC<0>{}, IC<NRD>{}, cur, 3, fa[1], fb[1],
-                  IC<0>{});
-        step_barrier();
-        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<P0>{}, fa[1], fb[1], kt + 2, IC<0>{}, IC<NRD>{}, nx, 0, fa[0], fb[0],
-                  IC<0>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<LA0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 1, fa[1],
+                  fb[1], IC<0>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<LA0>{}, IC<LA1>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 2, fa[0],
+                  fb[0], IC<0>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 3, fa[1],
+                  fb[1], IC<0>{});
+        step_barrier(IC<LOADS>{});
+        mfma_rows(IC<0>{}, IC<4>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, na, nb, 0,
+                  fa[0], fb[0], IC<0>{});
       }
-    }
-    __syncthreads();  // every wave is done reading the ring before the epilogue stages into it
+      ca = na;
+      cb = nb;
+    };
+    // In a unit whose operand tiles are both full, steps whose loads (of
+    // step kt+2) are full and inside the split take the fast form:
+    // kt + 2 < nfull, where only the split's last step can be partial (the
+    // last step of a K that is not a multiple of the step).
+    const int nfull = (a_full && b_full) ? (kend * KSTEP <= p.K ? nks : nks - 1) : 0;
+    int kt = 0;
+    for (; kt + 2 < nfull; ++kt) body(kt, IC<true>{});
+    for (; kt < nks; ++kt) body(kt, IC<false>{});
+    // every wave is done reading the ring, and every DMA write into it has
+    // landed (the loads past the end of the split), before the epilogue
+    // stages into it
+    wait_vmem();
+    __syncthreads();
 
     // ---- epilogue.  Lane l holds rows m0+wm+32i+l%32 and columns
     //      n0+wn+32j+8q+4*(l/32)+{0..3} in acc[i][j][4q..4q+3].  Each wave
@@ -845,11 +1008,11 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
 template <int NW, bool AK0, bool BK0, bool AK1, bool BK1, int FIRST>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_pair_kernel(const GemmParams p0, const GemmParams p1,
                                                               uint32_t* queue) {
-  // the ticket word sits just past the tile's LDS block, inside the same
-  // array: a __shared__ variable of its own makes the compiler wait for all
-  // LDS DMA before every LDS read of the K loop
-  __shared__ __attribute__((aligned(1024))) char smem[Layout<NW>::SMEM + 16];
-  volatile int* ticket_word = reinterpret_cast<volatile int*>(smem + Layout<NW>::SMEM);
+  // the ticket word is a control word of the ring (a __shared__ variable of
+  // its own makes the compiler wait for all LDS DMA before every LDS read of
+  // the K loop); tickets are taken between work units, with no load in flight
+  __shared__ __attribute__((aligned(1024))) char smem[Layout<NW>::SMEM];
+  volatile int* ticket_word = reinterpret_cast<volatile int*>(smem + CTRL_TICKET);
   const int x = blockIdx.x & 7;
   const int n0 = p0.total_tiles * p0.splits, n1 = p1.total_tiles * p1.splits;
   const int b0 = (int)((int64_t)x * n0 / 8), c0 = (int)((int64_t)(x + 1) * n0 / 8) - b0;
