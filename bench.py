@@ -78,7 +78,7 @@ class Layer:
     """Device buffers and the step of the C5 workload (one TP=8 rank)."""
 
     def __init__(self, torch, tpm, si, M=4096, D=8192, F=28672, T=8, rank=0, heads=8, kv=1, hd=128,
-                 producer_cus=32):
+                 producer_cus=32, arrival_plan="gated_only"):
         self.torch, self.tpm = torch, tpm
         self.M, self.D, self.T, self.rank = M, D, T, rank
         self.Ft = F // T
@@ -149,6 +149,11 @@ class Layer:
         self.order = si.ring_chunk_order(T, self.C, rank)
         self.dest = si.dest_range_order(T, rank)
         self.producer_cus = producer_cus
+        self.arrival_plan = arrival_plan
+        own = set(range(rank * (self.C // T), (rank + 1) * (self.C // T)))
+        self._copy = [c not in own for c in range(self.C)]
+        self._evpool = [torch.cuda.Event() for _ in range(64)]
+        self._evi = 0
         self.compute, self.side = tpm.masked_streams(producer_cus=producer_cus)
         # the arrival step's main stream: a non-blocking stream, since the
         # CU-masked streams are blocking ones and the null stream would order
@@ -161,33 +166,22 @@ class Layer:
     # -- chunk arrival: the producer stream writes the remote chunks in ring
     # order (one tpm_write_chunks launch, which publishes each chunk's ready
     # flag as soon as its rows are in place; the rank's own chunks are only
-    # flagged).  The boundary event is recorded on the main stream before the
-    # chunk-fed GEMM is enqueued; the writer is enqueued after it (its
-    # host-side launch cost overlaps the GEMM) but starts at the boundary.
-    def _boundary(self):
-        ev = self.torch.cuda.Event()
-        ev.record(self.torch.cuda.current_stream())
-        return ev
+    # flagged), starting when the stream that runs the chunk-fed GEMM reaches
+    # it.  Events come from a pool made once (a wait enqueued on a stream
+    # refers to the record made before it, so reusing an event later is
+    # safe), and every call names its stream: the host then keeps ahead of
+    # the GPU.
+    def _ev(self):
+        e = self._evpool[self._evi % len(self._evpool)]
+        self._evi += 1
+        return e
 
-    def _arrive(self, which, dst, src, epoch, boundary):
-        own = set(range(self.rank * (self.C // self.T), (self.rank + 1) * (self.C // self.T)))
-        self.side.wait_event(boundary)            # communication starts at the layer boundary
-        self.tpm.write_chunks(dst, src, self.C, self.order, self.flags[which], epoch, self.counters[which],
-                              copy=[c not in own for c in range(self.C)], stream=self.side)
-
-    def _gated(self, fn, boundary):
-        """A chunk-fed GEMM on the CU-masked compute stream (the producer has
-        the other CUs), ordered after the main stream's work up to
-        `boundary`; the main stream continues once it is done.  Every other
-        kernel of the step keeps all CUs."""
-        torch = self.torch
-        main = torch.cuda.current_stream()
-        self.compute.wait_event(boundary)
-        with torch.cuda.stream(self.compute):
-            fn()
-        done = torch.cuda.Event()
-        done.record(self.compute)
-        main.wait_event(done)
+    def _hand(self, frm, to):
+        """Continue on stream `to` after everything enqueued on `frm`."""
+        if frm is not to:
+            e = self._ev()
+            e.record(frm)
+            to.wait_event(e)
 
     def _timed(self, fn, record):
         if not record:
@@ -244,60 +238,69 @@ class Layer:
         tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
 
     def _step_arriving(self, epoch, record, check):
-        torch, tpm = self.torch, self.tpm
+        """The step with the four chunk-fed GEMMs (QKV, MLP up, dZ, dA) on
+        the CU-masked compute stream, each fed by a producer launch on the
+        other CUs.  Plan 'gated_only': every other kernel runs on the main
+        stream with all CUs (a hand-over between streams before and after
+        each chunk-fed GEMM).  Plan 'grouped': the forward's O projection,
+        MLP down and their reductions, and dW_o, stay on the compute stream
+        next to the chunk-fed GEMMs, so that only the two long backward
+        groups run on all CUs (four hand-overs per step instead of eight)."""
+        tpm = self.tpm
         T, r, C = self.T, self.rank, self.C
-        wsg, wsc = self.ws_g, self.ws_c
-        own_slot = self.stack[r]
+        wsg, wsc, own = self.ws_g, self.ws_c, self.stack[r]
         act = tpm.ACT_GELU_ERF
-        # ---- forward, QKV projection: X rows arriving
-        b = self._boundary()
-        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+        main, comp, side = self.torch.cuda.current_stream(), self.compute, self.side
+        rest = comp if self.arrival_plan == "grouped" else main
+        cur = [main]
+
+        def on(st):
+            self._hand(cur[0], st)
+            cur[0] = st
+
+        def gated(which, dst, src, fn):
+            on(comp)
+            boundary = self._ev()
+            boundary.record(comp)               # communication starts at the layer boundary
+            fn(comp)
+            side.wait_event(boundary)
+            tpm.write_chunks(dst, src, C, self.order, self.flags[which], epoch, self.counters[which],
+                             copy=self._copy, stream=side)
+            self._check(wsc, check)
+
+        # forward: QKV (X rows arriving), O partial + reduction, MLP up + GeLU
+        # (X rows arriving), MLP down partial + reduction
+        gated(0, self.x_qkv, self.x_src, lambda st: tpm.seq_chunk_gemm(
             self.x_qkv, self.w_qkv, self.qkv, num_chunks=C, chunk_order=self.order, chunk_ready=self.flags[0],
-            epoch=epoch, workspace=wsc), b), record)
-        self._arrive(0, self.x_qkv, self.x_src, epoch, b)
-        self._check(wsc, check)
-        self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.w_o, own_slot, num_chunks=T,
-                                               chunk_order=self.dest, workspace=wsg), record)
-        tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r)
-        # ---- forward, MLP: GEMM1 chunk-fed + GeLU, GEMM2 on every CU
-        b = self._boundary()
-        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            epoch=epoch, workspace=wsc, stream=st))
+        on(rest)
+        tpm.seq_chunk_gemm(self.attn, self.w_o, own, num_chunks=T, chunk_order=self.dest, workspace=wsg, stream=rest)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_o, T=T, rank=r, stream=rest)
+        gated(1, self.x_mlp, self.x_src, lambda st: tpm.seq_chunk_gemm(
             self.x_mlp, self.w_up, self.h, act=act, aux=self.z, num_chunks=C, chunk_order=self.order,
-            chunk_ready=self.flags[1], epoch=epoch, workspace=wsc), b), record)
-        self._arrive(1, self.x_mlp, self.x_src, epoch, b)
-        self._check(wsc, check)
-        self._timed(lambda: tpm.seq_chunk_gemm(self.h, self.w_down, own_slot, num_chunks=T,
-                                               chunk_order=self.dest, workspace=wsg), record)
-        tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r)
-        # ---- backward, MLP: dZ chunk-fed by dY rows, then dW_down, dW_up, dX
-        b = self._boundary()
-        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            chunk_ready=self.flags[1], epoch=epoch, workspace=wsc, stream=st))
+        on(rest)
+        tpm.seq_chunk_gemm(self.h, self.w_down, own, num_chunks=T, chunk_order=self.dest, workspace=wsg, stream=rest)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_mlp, T=T, rank=r, stream=rest)
+        # backward, MLP: dZ (dY rows arriving), then dW_down, dW_up, dX
+        gated(2, self.dy_mlp, self.dy_mlp_src, lambda st: tpm.seq_chunk_gemm(
             self.dy_mlp, self.w_down, self.dz, trans_b=True, epilogue=tpm.EPI_DACT, act=act, aux=self.z,
-            num_chunks=C, chunk_order=self.order, chunk_ready=self.flags[2], epoch=epoch, workspace=wsc), b),
-            record)
-        self._arrive(2, self.dy_mlp, self.dy_mlp_src, epoch, b)
-        self._check(wsc, check)
-        self._timed(lambda: (tpm.seq_chunk_gemm(self.h, self.dy_mlp, self.g_down, trans_a=True, workspace=wsg),
-                             tpm.seq_chunk_gemm(self.x_mlp, self.dz, self.g_up, trans_a=True, workspace=wsg),
-                             tpm.seq_chunk_gemm(self.dz, self.w_up, own_slot, trans_b=True, workspace=wsg)),
-                    record)
-        tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r)
-        # ---- backward, O projection: dA chunk-fed by dY_o rows, then dW_o
-        b = self._boundary()
-        self._timed(lambda: self._gated(lambda: tpm.seq_chunk_gemm(
+            num_chunks=C, chunk_order=self.order, chunk_ready=self.flags[2], epoch=epoch, workspace=wsc, stream=st))
+        on(main)
+        tpm.seq_chunk_gemm(self.h, self.dy_mlp, self.g_down, trans_a=True, workspace=wsg, stream=main)
+        tpm.seq_chunk_gemm(self.x_mlp, self.dz, self.g_up, trans_a=True, workspace=wsg, stream=main)
+        tpm.seq_chunk_gemm(self.dz, self.w_up, own, trans_b=True, workspace=wsg, stream=main)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxm, T=T, rank=r, stream=main)
+        # backward, O projection: dA (dY_o rows arriving), dW_o; QKV (paired)
+        gated(3, self.dy_o, self.dy_o_src, lambda st: tpm.seq_chunk_gemm(
             self.dy_o, self.w_o, self.d_attn, trans_b=True, num_chunks=C, chunk_order=self.order,
-            chunk_ready=self.flags[3], epoch=epoch, workspace=wsc), b), record)
-        self._arrive(3, self.dy_o, self.dy_o_src, epoch, b)
-        self._check(wsc, check)
-        self._timed(lambda: tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg),
-                    record)
-        # ---- backward, QKV projection (paired dW and dX)
-        self._timed(lambda: tpm.tp_linear_bwd(self.x_qkv, self.w_qkv, self.dy_qkv, self.g_qkv, own_slot,
-                                              workspace=self.ws_l), record)
-        tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r)
-        done = torch.cuda.Event()
-        done.record(self.side)
-        torch.cuda.current_stream().wait_event(done)
+            chunk_ready=self.flags[3], epoch=epoch, workspace=wsc, stream=st))
+        on(rest)
+        tpm.seq_chunk_gemm(self.attn, self.dy_o, self.g_o, trans_a=True, workspace=wsg, stream=rest)
+        on(main)
+        tpm.tp_linear_bwd(self.x_qkv, self.w_qkv, self.dy_qkv, self.g_qkv, own, workspace=self.ws_l, stream=main)
+        tpm.partial_reduce_seqshard(self.stack, self.slice_dxq, T=T, rank=r, stream=main)
+        self._hand(side, main)                  # the step ends when the producer is done too
 
 
 def time_steps(torch, layer, steps, warmup, arrive, epoch0, stream=None):
@@ -359,34 +362,42 @@ def arrival_step(torch, layer, args, ms_resident):
     chunks that a producer stream writes in ring order while they run, the
     producer confined to `producer_cus` CUs (32 by default: about 0.67 TB/s
     of chunk writes, the order of a rank's ingress over 7 xGMI links) and
-    the GEMMs to the others.  Reports the writer's time alone (4 launches of
-    7 x 8 MB) and the overlap efficiency
-    (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
-    ms, gemm_ms, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000)
-    torch.cuda.synchronize()
+    the GEMMs to the others.  Timed under both stream plans (Layer's
+    _step_arriving); the headline figures are those of the layer's plan.
+    Reports the writer's time alone (4 launches of 7 x 8 MB) and the overlap
+    efficiency (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
+    plans = {}
+    first = layer.arrival_plan
+    for i, plan in enumerate((first, "gated_only" if first == "grouped" else "grouped")):
+        layer.arrival_plan = plan
+        plans[plan], _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000 + 500 * i)
+        torch.cuda.synchronize()
+    layer.arrival_plan = first
+    ms = plans[first]
     # the resident step confined to the compute stream's CUs: separates what
     # the CU partition costs from what waiting for chunks costs
     ms_res_masked, _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=3000,
                                      stream=layer.compute)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    epoch = 5000
+    pairs = ((layer.x_qkv, layer.x_src), (layer.x_mlp, layer.x_src), (layer.dy_mlp, layer.dy_mlp_src),
+             (layer.dy_o, layer.dy_o_src))
     for rep in range(2):
         a.record(layer.side)
-        for which, (dst, src) in enumerate(((layer.x_qkv, layer.x_src), (layer.x_mlp, layer.x_src),
-                                            (layer.dy_mlp, layer.dy_mlp_src), (layer.dy_o, layer.dy_o_src))):
-            layer._arrive(which, dst, src, epoch + rep, a)
+        for which, (dst, src) in enumerate(pairs):
+            layer.tpm.write_chunks(dst, src, layer.C, layer.order, layer.flags[which], 5000 + rep,
+                                   layer.counters[which], copy=layer._copy, stream=layer.side)
         b.record(layer.side)
         torch.cuda.synchronize()
     t_copy = a.elapsed_time(b)
-    eff = (ms_resident + t_copy - ms) / min(ms_resident, t_copy)
+    eff = lambda t: round((ms_resident + t_copy - t) / min(ms_resident, t_copy), 3)
     return {"ms": round(ms, 4), "TFLOPS": round(layer.flops / (ms * 1e-3) / 1e12, 2),
-            "gemm_TFLOPS": round(layer.flops / (gemm_ms * 1e-3) / 1e12, 2),
-            "writer_only_ms": round(t_copy, 4), "overlap_efficiency": round(eff, 3),
+            "writer_only_ms": round(t_copy, 4), "overlap_efficiency": eff(ms),
+            "plan": first, "plans_ms": {k: round(v, 4) for k, v in plans.items()},
+            "plans_overlap_efficiency": {k: eff(v) for k, v in plans.items()},
             "resident_eager_ms_all_cus": round(ms_resident, 4),
             "resident_eager_ms_on_compute_cus": round(ms_res_masked, 4),
-            "producer_cus": layer.producer_cus,
-            "streams": "chunk-fed GEMMs on the compute CUs, every other kernel on all CUs"}
+            "producer_cus": layer.producer_cus}
 
 
 def bench_reduce(torch, tpm, si, iters=40):
