@@ -63,29 +63,6 @@ def assert_mx_close(codes, e, h, delta, frac=1e-2):
     assert np.mean(same & (codes != ref_codes)) < frac
 
 
-def bf16_either(v, rel=2.0 ** -16):
-    """(round_bf16(v), d): d is |other bf16 candidate - rounded| where v lies
-    within a relative distance `rel` of a rounding boundary (an fp32
-    evaluation may round it the other way), else 0."""
-    rb = formats.round_bf16(v)
-    lo, hi = formats.round_bf16(v * (1 - rel)), formats.round_bf16(v * (1 + rel))
-    other = np.where(lo != rb, lo, hi)
-    return rb, np.abs(other - rb)
-
-
-def e5m2_cast_ambiguity(v_exact, delta, inv):
-    """A gradient the GPU evaluates in fp32 (within delta of the exact
-    v_exact), stores in bf16 and casts to e5m2 as code(fp32(x * inv)):
-    returns (the value in code units of the oracle's rounding of v_exact, d),
-    d bounding how far the GPU's code value may land from it - the casts
-    are monotone, so it lies between those of v_exact -+ delta."""
-    cast = lambda b: formats.e5m2_to_f64(formats.e5m2_encode((b * float(inv)).astype(np.float32).astype(np.float64)))
-    q = cast(formats.round_bf16(v_exact))
-    lo = cast(formats.round_bf16(v_exact - delta))
-    hi = cast(formats.round_bf16(v_exact + delta))
-    return q, np.maximum(np.abs(lo - q), np.abs(hi - q))
-
-
 def assert_fp8_h_consistent(h_gpu, codes_gpu, s_gpu, ref, max_flip=2e-3):
     """The fp8 current-scaling step of H on the GPU against the oracle's
     chain (ops.tp_mlp_fwd_fp8 result `ref`):
