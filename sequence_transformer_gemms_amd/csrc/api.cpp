@@ -102,6 +102,70 @@ size_t partial_bytes(int64_t M, int64_t N, int S) {
   return S > 1 ? round_up((size_t)S * (size_t)M * (size_t)N * 4, 256) : 0;
 }
 
+// Split plan of one launch: S K-range splits of every tile (few tiles), or
+// a tail split.  Whole tiles fill rounds of kPlanCUs work-groups; when the
+// last round is partly empty, most CUs idle through one whole tile time.  A
+// tail split takes the tiles of the last tail_cols tile columns out of the
+// whole-tile rounds and cuts each into tail_pieces K ranges, which fill the
+// idle slots and one short round after; a second kernel sums each tile's
+// fp32 partials in piece order and applies the epilogue.  Whether an output
+// element is split depends only on its column and on (M, N, K, element
+// type): any chunk count and chunk order give the same bits.  At most
+// kPlanCUs pieces (64 MiB of partials when the tile rows are whole).
+// The plan minimises an estimate, in K steps, of the busiest work-group's
+// time under the round-robin schedule: whole tiles cost nk + 2, pieces
+// ceil(nk / P) + 4 (a 256 KB fp32 store), and the finalisation pass
+// tail_tiles * P / 32 (256 KB per piece read at ~6 TB/s, a K step being
+// ~1.5 us); at least 8 K steps per piece.
+struct SplitPlan {
+  int S = 1;
+  int tail_cols = 0, tail_pieces = 1;
+};
+
+SplitPlan plan_gemm(int64_t M, int64_t N, int64_t K, int groups, int dt) {
+  SplitPlan pl;
+  pl.S = plan_splits(M, N, K, groups, dt);
+  if (pl.S > 1 || dt == TPM_F32 || M <= 0 || N <= 0 || K <= 0) return pl;
+  const int64_t mt = (M + kTileM - 1) / kTileM, nt = (N + kTileN - 1) / kTileN;
+  const int64_t total = mt * nt, G = kPlanCUs;
+  if (total <= G) return pl;
+  const int64_t nk = (K * esize(dt) + kStepBytes - 1) / kStepBytes;
+  const double tw = (double)nk + 2.0;
+  double best = (double)((total + G - 1) / G) * tw;
+  for (int64_t c = 1; c < nt && c * mt <= G; ++c) {
+    const int64_t tail = c * mt, whole = total - tail;
+    const int64_t whole_rounds = (whole + G - 1) / G;
+    for (int P = 2; P <= 8 && tail * P <= G && nk / P >= 8; ++P) {
+      const int64_t rounds = (whole + tail * P + G - 1) / G;
+      const double tp = (double)((nk + P - 1) / P) + 4.0;
+      const double cost = (double)whole_rounds * tw + (double)(rounds - whole_rounds) * tp + (double)(tail * P) / 32.0;
+      if (cost < best) {
+        best = cost;
+        pl.tail_cols = (int)c;
+        pl.tail_pieces = P;
+      }
+    }
+  }
+  return pl;
+}
+
+// Row tiles of a launch over M rows in `groups` equal groups.
+int64_t row_tiles(int64_t M, int groups) {
+  groups = std::max(groups, 1);
+  return ((M / groups + kTileM - 1) / kTileM) * groups;
+}
+
+size_t plan_bytes(const SplitPlan& pl, int64_t M, int64_t N, int groups) {
+  if (pl.S > 1) return partial_bytes(M, N, pl.S);
+  if (pl.tail_pieces <= 1) return 0;
+  return round_up((size_t)row_tiles(M, groups) * pl.tail_cols * pl.tail_pieces * kTileM * kTileN * 4, 256);
+}
+
+// Partial-sum scratch of the launch plan_gemm makes for this shape.
+size_t plan_bytes(int64_t M, int64_t N, int64_t K, int groups, int dt) {
+  return plan_bytes(plan_gemm(M, N, K, groups, dt), M, N, groups);
+}
+
 // Split plan of the paired launch of a linear layer's backward (dW = X^T dY:
 // [K, N] over M; dX = dY W^T: [M, K] over N; S[0], S[1]).  The launch
 // shares the two GEMMs' K steps over kPlanCUs work-groups; a GEMM whose
@@ -254,9 +318,10 @@ int check_gemm(const GemmDesc& g, const char* who) {
   return TPM_OK;
 }
 
-// Kernel parameters of one checked GEMM with S K-range splits (the caller
-// has made sure the partial-sum scratch holds S > 1 splits).
-void make_params(const GemmDesc& g, int S, GemmParams& p) {
+// Kernel parameters of one checked GEMM under split plan pl (the caller has
+// made sure the partial-sum scratch holds what the plan needs).
+void make_params(const GemmDesc& g, const SplitPlan& pl, GemmParams& p) {
+  const int S = pl.S;
   std::memset(&p, 0, sizeof(p));
   p.A = g.A; p.B = g.B; p.Y = g.Y; p.aux = g.aux;
   p.a_scale = g.asc; p.b_scale = g.bsc; p.amax = g.amax;
@@ -293,15 +358,34 @@ void make_params(const GemmDesc& g, int S, GemmParams& p) {
   p.tiles_per_group = p.mt_per_group * p.nt;
   p.total_tiles = p.tiles_per_group * p.num_groups;
   p.band_m = std::min(p.mt_per_group, 4);
+  p.units = p.total_tiles * S;
+  p.nt_w = p.nt;
+  p.tpg_w = p.tiles_per_group;
+  p.tail_start = p.units;
+  p.tail_tiles = p.tail_cols = p.tail_ksteps = 0;
+  p.tail_pieces = 1;
+  if (S == 1 && pl.tail_pieces > 1 && pl.tail_cols > 0 && pl.tail_cols < p.nt) {
+    p.tail_cols = pl.tail_cols;
+    p.tail_pieces = pl.tail_pieces;
+    p.tail_ksteps = (int)((nk + pl.tail_pieces - 1) / pl.tail_pieces);
+    p.nt_w = p.nt - pl.tail_cols;
+    p.tpg_w = p.mt_per_group * p.nt_w;
+    p.tail_tiles = p.mt_per_group * pl.tail_cols * p.num_groups;
+    p.tail_start = p.tpg_w * p.num_groups;
+    p.units = p.tail_start + p.tail_tiles * pl.tail_pieces;
+    p.partial = g.part;
+  }
 }
 
-// K-range splits the matrix-core path plans for a GEMM (1 on the predicated
+// Split plan the matrix-core path makes for a GEMM (none on the predicated
 // path).  Chunk-gated GEMMs split too; range-done signalling needs whole
 // tiles, and the gated forward and the fp8 outputs pair or scale whole
-// tiles in their epilogues.
-int planned_splits(const GemmDesc& g) {
-  if (fast_path_blocker(g) || g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) return 1;
-  return plan_splits(g.M, g.N, g.K, g.groups, g.adt);
+// tiles in their epilogues.  The plan depends on the shape, the chunk count
+// and the element type only, never on the stream or the grid, so that a
+// chunk-fed call and a resident one give the same bits.
+SplitPlan planned_split(const GemmDesc& g) {
+  if (fast_path_blocker(g) || g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) return SplitPlan{};
+  return plan_gemm(g.M, g.N, g.K, g.groups, g.adt);
 }
 
 int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
@@ -309,14 +393,15 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   GemmParams p;
   hipError_t e;
   if (fast_path_blocker(g)) {
-    make_params(g, 1, p);
+    make_params(g, SplitPlan{}, p);
     e = launch_gemm_generic(p, g.ta, g.tb, s);
     return e == hipSuccess ? TPM_OK : hip_fail(e, who);
   }
-  // split-K when the plan asks for it and the scratch is there
-  int S = planned_splits(g);
-  if (S > 1 && (!g.part || g.part_bytes < partial_bytes(g.M, g.N, S))) S = 1;
-  make_params(g, S, p);
+  // split-K or a tail split when the plan asks for it and the scratch is there
+  SplitPlan pl = planned_split(g);
+  const size_t need = plan_bytes(pl, g.M, g.N, g.groups);
+  if (need > 0 && (!g.part || g.part_bytes < need)) pl = SplitPlan{};
+  make_params(g, pl, p);
   // persistent grid: one work-group per CU the stream may use.  A
   // chunk-gated GEMM on a stream that may use every CU leaves one CU per XCD
   // to a producer that runs kernels on this device; a stream with a CU mask
@@ -325,7 +410,7 @@ int run_gemm(const GemmDesc& g, hipStream_t s, const char* who) {
   const int avail = stream_cus(s);
   int grid = (g.ready && avail == cus) ? cus - 8 : avail;
   grid = std::max(8, grid);
-  grid = std::min(grid, p.total_tiles * p.splits);
+  grid = std::min(grid, p.units);
   if (g.adt == TPM_BF16) e = launch_gemm_bf16(p, !g.ta, g.tb, grid, s);
   else e = launch_gemm_fp8(p, !g.ta, g.tb, grid, s);
   return e == hipSuccess ? TPM_OK : hip_fail(e, who);
@@ -362,7 +447,7 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
   if (M < 0 || N < 0 || K < 0 || num_chunks < 1) return 0;
   switch (op) {
     case TPM_OP_SEQ_CHUNK_GEMM:
-      return kCtrlBytes + partial_bytes(M, N, plan_splits(M, N, K, num_chunks, dtype));
+      return kCtrlBytes + plan_bytes(M, N, K, num_chunks, dtype);
     case TPM_OP_LINEAR_BWD: {
       int S[2];
       plan_linear_bwd(M, N, K, dtype, S);
@@ -372,25 +457,25 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       const size_t hq = dtype == TPM_FP8_E4M3 ? round_up((size_t)M * (size_t)Ft, 256) : 0;
-      const size_t part = std::max(partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype)),
-                                   partial_bytes(M, D, plan_splits(M, D, Ft, T, dtype)));
+      const size_t part = std::max(plan_bytes(M, Ft, D, num_chunks, dtype),
+                                   plan_bytes(M, D, Ft, T, dtype));
       return kCtrlBytes + hq + part;
     }
     case TPM_OP_MLP_BWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       const size_t dz = round_up((size_t)M * (size_t)Ft * (size_t)esize(dtype == TPM_F32 ? TPM_F32 : TPM_BF16), 256);
-      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype));
-      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, dtype)));
-      part = std::max(part, partial_bytes(D, Ft, plan_splits(D, Ft, M, 1, dtype)));
-      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, dtype)));
+      size_t part = plan_bytes(M, Ft, D, num_chunks, dtype);
+      part = std::max(part, plan_bytes(Ft, D, M, 1, dtype));
+      part = std::max(part, plan_bytes(D, Ft, M, 1, dtype));
+      part = std::max(part, plan_bytes(M, D, Ft, 1, dtype));
       return kCtrlBytes + dz + part;
     }
     case TPM_OP_MX_MLP_FWD:
     case TPM_OP_FP8_DELAYED_MLP_FWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
-      return kCtrlBytes + partial_bytes(M, D, plan_splits(M, D, Ft, T, TPM_FP8_E4M3));
+      return kCtrlBytes + plan_bytes(M, D, Ft, T, TPM_FP8_E4M3);
     }
     case TPM_OP_CAST_FP8:
       return kCtrlBytes;
@@ -398,26 +483,26 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       const int f8 = TPM_FP8_E4M3;
-      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, 1, f8));
-      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, f8)));
-      part = std::max(part, partial_bytes(D, Ft, plan_splits(D, Ft, M, 1, f8)));
-      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, Ft, 1, f8)));
+      size_t part = plan_bytes(M, Ft, D, 1, f8);
+      part = std::max(part, plan_bytes(Ft, D, M, 1, f8));
+      part = std::max(part, plan_bytes(D, Ft, M, 1, f8));
+      part = std::max(part, plan_bytes(M, D, Ft, 1, f8));
       const size_t md = round_up((size_t)M * (size_t)D, 256), mf = round_up((size_t)M * (size_t)Ft, 256);
       return kCtrlBytes + 3 * md + 2 * mf + 3 * mf + part;   // dY8, dY8^T, X8^T; dZ (bf16); dZ8, dZ8^T, H8^T
     }
     case TPM_OP_GATED_MLP_FWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
-      return kCtrlBytes + partial_bytes(M, D, plan_splits(M, D, Ft, T, dtype));
+      return kCtrlBytes + plan_bytes(M, D, Ft, T, dtype);
     }
     case TPM_OP_GATED_MLP_BWD: {
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       const size_t dgu = round_up((size_t)M * (size_t)(2 * Ft) * 2, 256);
-      size_t part = partial_bytes(M, Ft, plan_splits(M, Ft, D, num_chunks, dtype));
-      part = std::max(part, partial_bytes(Ft, D, plan_splits(Ft, D, M, 1, dtype)));
-      part = std::max(part, partial_bytes(D, 2 * Ft, plan_splits(D, 2 * Ft, M, 1, dtype)));
-      part = std::max(part, partial_bytes(M, D, plan_splits(M, D, 2 * Ft, 1, dtype)));
+      size_t part = plan_bytes(M, Ft, D, num_chunks, dtype);
+      part = std::max(part, plan_bytes(Ft, D, M, 1, dtype));
+      part = std::max(part, plan_bytes(D, 2 * Ft, M, 1, dtype));
+      part = std::max(part, plan_bytes(M, D, 2 * Ft, 1, dtype));
       return kCtrlBytes + dgu + part;
     }
     default: return 0;
@@ -559,8 +644,7 @@ int seq_chunk_gemm_noalloc(int64_t M, int64_t N, int64_t K,
   if (rc != TPM_OK) return rc;
   if (amax_out && a_dtype == TPM_F32) return fail(TPM_EUNSUPPORTED, "%s: amax on the fp32 path", who);
   if (M == 0 || N == 0) return TPM_OK;
-  const int S = planned_splits(g);
-  const size_t need = kCtrlBytes + partial_bytes(M, N, S);
+  const size_t need = kCtrlBytes + plan_bytes(planned_split(g), M, N, num_chunks);
   if (need > kNoAllocScratchBytes)
     return fail(TPM_EUNSUPPORTED, "%s: this GEMM's split-K plan needs %zu bytes of scratch, more than the %zu the "
                 "library holds per GPU; call seq_chunk_gemm with a workspace", who, need, kNoAllocScratchBytes);
@@ -693,9 +777,9 @@ int tp_linear_bwd(int64_t M, int64_t N, int64_t K,
     return TPM_OK;
   }
   GemmParams p_dw, p_dx;
-  make_params(g_dw, S[0], p_dw);
-  make_params(g_dx, S[1], p_dx);
-  const int units = p_dw.total_tiles * p_dw.splits + p_dx.total_tiles * p_dx.splits;
+  make_params(g_dw, SplitPlan{S[0]}, p_dw);
+  make_params(g_dx, SplitPlan{S[1]}, p_dx);
+  const int units = p_dw.units + p_dx.units;
   // at least one work-group per XCD queue, at most one per CU the stream may use
   const int grid = std::max(8, std::min(stream_cus(s), units));
   const int first = p_dx.ksteps_per_split > p_dw.ksteps_per_split ? 1 : 0;

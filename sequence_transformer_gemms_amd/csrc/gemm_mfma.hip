@@ -91,7 +91,8 @@ struct Tile {
 
 struct Unit {
   Tile tl;
-  int split;
+  int split;   // K range: split of every tile, or the piece of a tail tile
+  int tail;    // tail slot of the tile (0 .. tail_tiles - 1), -1 for a whole-range unit
 };
 
 // Work unit u -> (split, tile).  Units of one XCD (work-group ids congruent
@@ -103,10 +104,14 @@ struct Unit {
 // outermost index, except in a chunk-gated GEMM, where they come right
 // after the group: every unit of a chunk precedes the next chunk's, so the
 // work-groups' first units are the earliest chunks' and later chunks are
-// only waited for by units of a later round.
+// only waited for by units of a later round.  A tail split takes the last
+// tail_cols tile columns out of every group: the whole tiles of the other
+// columns come first, then the pieces of the tail tiles, piece-major (the
+// tiles an XCD works on at once read the same K range), each piece in the
+// group order.
 __device__ __forceinline__ int xcd_logical(const GemmParams& p, int u) {
   const int G = gridDim.x;
-  const int total = p.total_tiles * p.splits;
+  const int total = p.units;
   int L = u;
   if ((G & 7) == 0) {
     const int r = u / G;
@@ -118,36 +123,61 @@ __device__ __forceinline__ int xcd_logical(const GemmParams& p, int u) {
   return L;
 }
 
-// Logical unit L (0 .. total_tiles * splits - 1) -> (split, tile).
-__device__ __forceinline__ Unit logical_unit(const GemmParams& p, int L) {
-  Unit un;
-  int pos, q;
-  if (p.ready) {
-    const int per_group = p.tiles_per_group * p.splits;
-    pos = L / per_group;
-    const int rem = L - pos * per_group;
-    un.split = rem / p.tiles_per_group;
-    q = rem - un.split * p.tiles_per_group;
-  } else {
-    un.split = L / p.total_tiles;
-    L -= un.split * p.total_tiles;
-    pos = L / p.tiles_per_group;
-    q = L - pos * p.tiles_per_group;
-  }
+// Position pos in the group order and index q within the group's tiles of
+// tile columns col0 .. col0 + ncols - 1 -> tile.
+__device__ __forceinline__ Tile tile_of(const GemmParams& p, int pos, int q, int ncols, int col0) {
   const int g = p.order[pos];
-  const int band = q / (p.band_m * p.nt);
+  const int band = q / (p.band_m * ncols);
   const int rem_m = p.mt_per_group - band * p.band_m;
   const int gm = rem_m < p.band_m ? rem_m : p.band_m;
-  const int idx = q - band * p.band_m * p.nt;
+  const int idx = q - band * p.band_m * ncols;
   const int mt = band * p.band_m + idx % gm;
-  const int ntile = idx / gm;
-  Tile& tl = un.tl;
+  const int ntile = col0 + idx / gm;
+  Tile tl;
   tl.g = g;
   const int gstart = g * p.group_rows;
   tl.m0 = gstart + mt * BM;
   const int gend = gstart + p.group_rows;
   tl.m_end = (tl.m0 + BM < gend) ? tl.m0 + BM : gend;
   tl.n0 = ntile * p.bn_out;
+  return tl;
+}
+
+// Tail tile t (0 .. tail_tiles - 1, in the group order) -> tile.
+__device__ __forceinline__ Tile tail_tile(const GemmParams& p, int t) {
+  const int per_group = p.mt_per_group * p.tail_cols;
+  const int pos = t / per_group;
+  return tile_of(p, pos, t - pos * per_group, p.tail_cols, p.nt - p.tail_cols);
+}
+
+// Logical unit L (0 .. units - 1) -> (split, tile).  Whole tiles cover tile
+// columns 0 .. nt_w - 1 (all of them without a tail split), tpg_w per group.
+__device__ __forceinline__ Unit logical_unit(const GemmParams& p, int L) {
+  Unit un;
+  un.tail = -1;
+  if (L >= p.tail_start) {
+    // piece un.split of tail tile un.tail (splits == 1)
+    const int j = L - p.tail_start;
+    un.split = j / p.tail_tiles;
+    un.tail = j - un.split * p.tail_tiles;
+    un.tl = tail_tile(p, un.tail);
+    return un;
+  }
+  int pos, q;
+  if (p.ready) {
+    const int per_group = p.tpg_w * p.splits;
+    pos = L / per_group;
+    const int rem = L - pos * per_group;
+    un.split = rem / p.tpg_w;
+    q = rem - un.split * p.tpg_w;
+  } else {
+    const int whole = p.tpg_w * p.num_groups;
+    un.split = L / whole;
+    L -= un.split * whole;
+    pos = L / p.tpg_w;
+    q = L - pos * p.tpg_w;
+  }
+  un.tl = tile_of(p, pos, q, p.nt_w, 0);
   return un;
 }
 
@@ -459,9 +489,10 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
 
   {
     const Tile& tl = un.tl;
-    // K steps [kbeg, kend) of this split
-    const int kbeg = un.split * p.ksteps_per_split;
-    const int kend = min(nk, kbeg + p.ksteps_per_split);
+    // K steps [kbeg, kend) of this split or tail piece
+    const int per = un.tail >= 0 ? p.tail_ksteps : p.ksteps_per_split;
+    const int kbeg = un.split * per;
+    const int kend = min(nk, kbeg + per);
     const int nks = kend - kbeg;
     __syncthreads();  // the previous tile's epilogue staging is done with the LDS
     if (p.ready) wait_group(p, tl.g, smem);
@@ -905,7 +936,8 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       // read back 8 consecutive columns per lane, 8 lanes per row
       with_act(p.act, [&](auto ac) {
       constexpr int ACT = decltype(ac)::value;
-      if (p.epi == EPI_DACT && !p.aux_f32 && p.splits == 1) {
+      const bool raw = p.splits > 1 || un.tail >= 0;  // fp32 partial of a K range
+      if (p.epi == EPI_DACT && !p.aux_f32 && !raw) {
         // DACT with a bf16 Z: the Z loads of four row groups are issued
         // together before any is used, instead of one exposed load latency
         // per row group
@@ -939,24 +971,43 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         }
         return;
       }
+      // the staged values of four row groups are read before any is used,
+      // so their LDS latency overlaps (with one wave per SIMD nothing else
+      // would hide it)
+      constexpr int GRP = 4;
+      static_assert((EPI_ROWS / 8) % GRP == 0, "row groups");
 #pragma unroll 1
-      for (int it = 0; it < EPI_ROWS / 8; ++it) {
-        const int rl = it * 8 + (lane >> 3);
-        const int cl = (lane & 7) * 8;
-        const f32x4 v0 = *(const f32x4*)(stage + rl * EPI_LD + cl);
-        const f32x4 v1 = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
-        const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
-        const int col = tl.n0 + wn + EPI_COLS * cp + cl;
-        if (row < tl.m_end && col < p.N) {
-          if (p.splits > 1) {
-            // raw fp32 partial of this K range; splitk_finalize sums them
-            f32x4* dst = (f32x4*)(p.partial + ((int64_t)un.split * p.M + row) * p.N + col);
-            dst[0] = v0;
-            dst[1] = v1;
-          } else {
-            float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
-                          v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
-            epi_oct<ACT>(p, v, row, col, lmax);
+      for (int it0 = 0; it0 < EPI_ROWS / 8; it0 += GRP) {
+        f32x4 v0s[GRP], v1s[GRP];
+#pragma unroll
+        for (int g = 0; g < GRP; ++g) {
+          const int rl = (it0 + g) * 8 + (lane >> 3);
+          const int cl = (lane & 7) * 8;
+          v0s[g] = *(const f32x4*)(stage + rl * EPI_LD + cl);
+          v1s[g] = *(const f32x4*)(stage + rl * EPI_LD + cl + 4);
+        }
+#pragma unroll
+        for (int g = 0; g < GRP; ++g) {
+          const f32x4 v0 = v0s[g], v1 = v1s[g];
+          const int rl = (it0 + g) * 8 + (lane >> 3);
+          const int cl = (lane & 7) * 8;
+          const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
+          const int col = tl.n0 + wn + EPI_COLS * cp + cl;
+          if (row < tl.m_end && col < p.N) {
+            if (raw) {
+              // raw fp32 partial of this K range; splitk_finalize or
+              // tail_finalize sums them
+              f32x4* dst = un.tail >= 0
+                  ? (f32x4*)(p.partial + ((int64_t)(un.split * p.tail_tiles + un.tail) * BM + (row - tl.m0)) * BN +
+                             (col - tl.n0))
+                  : (f32x4*)(p.partial + ((int64_t)un.split * p.M + row) * p.N + col);
+              dst[0] = v0;
+              dst[1] = v1;
+            } else {
+              float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
+                            v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
+              epi_oct<ACT>(p, v, row, col, lmax);
+            }
           }
         }
       }
@@ -989,8 +1040,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_kernel(const GemmParams p) {
   // the per-chunk wait needs no further invalidation (which would throw away
   // every tile's cached operands on each chunk arrival).
   if (p.ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int total_units = p.total_tiles * p.splits;
-  for (int u = blockIdx.x; u < total_units; u += gridDim.x)
+  for (int u = blockIdx.x; u < p.units; u += gridDim.x)
     run_unit<FP8, AK, BKM, NW, GATED, MX, F8F>(p, map_unit(p, u), smem);
 }
 
@@ -1014,7 +1064,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_pair_kernel(const GemmParams 
   __shared__ __attribute__((aligned(1024))) char smem[Layout<NW>::SMEM];
   volatile int* ticket_word = reinterpret_cast<volatile int*>(smem + CTRL_TICKET);
   const int x = blockIdx.x & 7;
-  const int n0 = p0.total_tiles * p0.splits, n1 = p1.total_tiles * p1.splits;
+  const int n0 = p0.units, n1 = p1.units;
   const int b0 = (int)((int64_t)x * n0 / 8), c0 = (int)((int64_t)(x + 1) * n0 / 8) - b0;
   const int b1 = (int)((int64_t)x * n1 / 8), c1 = (int)((int64_t)(x + 1) * n1 / 8) - b1;
   // (every thread reads a ticket before thread 0 can take the next one:
@@ -1068,16 +1118,57 @@ __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
   }
 }
 
+// Tail finalisation: each tail tile's pieces summed in ascending piece order
+// (deterministic), scaled, then the epilogue; one work-group per 8 rows of a
+// tail tile, 8 consecutive columns per lane.
+__global__ void __launch_bounds__(256) tail_finalize(const GemmParams p) {
+  float scale = 1.f;
+  if (p.a_scale) scale *= *p.a_scale;
+  if (p.b_scale) scale *= *p.b_scale;
+  constexpr int BLOCKS_PER_TILE = BM / 8;
+  const int t = blockIdx.x / BLOCKS_PER_TILE;
+  const int r = (blockIdx.x - t * BLOCKS_PER_TILE) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 8;
+  const Tile tl = tail_tile(p, t);
+  const int row = tl.m0 + r, col = tl.n0 + c;
+  float lmax = 0.f;
+  if (row < tl.m_end && col < p.N) {
+    const int64_t piece = (int64_t)p.tail_tiles * BM * BN;
+    const float* src = p.partial + ((int64_t)t * BM + r) * BN + c;
+    f32x4 a0 = __builtin_nontemporal_load((const f32x4*)src);
+    f32x4 a1 = __builtin_nontemporal_load((const f32x4*)src + 1);
+    for (int sp = 1; sp < p.tail_pieces; ++sp) {
+      a0 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece));
+      a1 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece) + 1);
+    }
+    float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
+                  a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
+    with_act(p.act, [&](auto ac) {
+      constexpr int ACT = decltype(ac)::value;
+      epi_oct<ACT>(p, v, row, col, lmax);
+    });
+  }
+  if (p.amax) {
+    lmax = wave_max(lmax);
+    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));
+  }
+}
+
 }  // namespace
 
 static hipError_t finalize_if_split(const GemmParams& p, hipStream_t s) {
-  if (p.splits <= 1) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t work = (int64_t)p.M * (p.N / 8);
-  int64_t blocks = (work + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  splitk_finalize<<<(int)blocks, 256, 0, s>>>(p);
+  if (p.splits > 1) {
+    int64_t work = (int64_t)p.M * (p.N / 8);
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    splitk_finalize<<<(int)blocks, 256, 0, s>>>(p);
+  } else if (p.tail_pieces > 1) {
+    tail_finalize<<<p.tail_tiles * (BM / 8), 256, 0, s>>>(p);
+  } else {
+    return hipSuccess;
+  }
   return hipGetLastError();
 }
 

@@ -36,7 +36,17 @@ struct GemmParams {
   int act, epi, y_f32, aux_f32;
   int splits;                // K-range splits (1: none); > 1 needs `partial`
   int ksteps_per_split;      // K steps (of 32 bf16 / 64 fp8) per split
-  float* partial;            // device fp32 [splits][M][N] partial sums
+  float* partial;            // device fp32 [splits][M][N] partial sums, or the tail's pieces
+  // Tail split (splits == 1 only): the tiles of the last tail_cols tile
+  // columns (tail_tiles of them, t = their index in the group order) are cut
+  // into tail_pieces K ranges of tail_ksteps steps, units tail_start + piece
+  // * tail_tiles + t, whose fp32 partials go to partial[piece][t][256][256].
+  // Units 0 .. tail_start - 1 are the whole tiles of the first nt_w tile
+  // columns, tpg_w per group.  Without a tail: tail_cols = 0, nt_w = nt,
+  // tail_start = units.
+  int units;                 // work units of the launch
+  int nt_w, tpg_w;
+  int tail_start, tail_tiles, tail_cols, tail_pieces, tail_ksteps;
   // MXFP8 (fp8 kernel only): E8M0 block scales of A and B in the MFMA
   // layout (mx_scale_offset), K / 128 records per 32-row group; y_mx: Y is
   // written as MXFP8 codes with its scales there (N / 128 records per group)

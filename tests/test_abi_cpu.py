@@ -40,9 +40,41 @@ def test_workspace_sizes():
     assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4096, 1280, 8192, 1, 8, _abi.BF16) == 2048 + 3 * 4096 * 1280 * 4
     # bwd keeps dZ [M, F/T] bf16 after the 2 KiB control block
     assert ws(_abi.OP_MLP_BWD, 4096, 8192, 28672, 8, 8, _abi.BF16) == 2048 + 4096 * 3584 * 2
-    # fp8 fwd keeps the quantised H [M, F/T]
-    assert ws(_abi.OP_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048 + 8192 * 6656
+    # fp8 fwd keeps the quantised H [M, F/T], then the tail split's partials:
+    # GEMM1 has 32 x 26 = 832 tiles; the first 24 tile columns fill 3 rounds
+    # and the last 2 columns' 64 tiles are cut into 4 pieces of 32 K steps
+    tail = 64 * 4 * 256 * 256 * 4
+    assert ws(_abi.OP_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048 + 8192 * 6656 + tail
     assert ws(_abi.OP_MLP_FWD, 8192, 8192, 28672, 8, 8, _abi.BF16) == 2048
+
+
+def test_tail_split_plan():
+    from sequence_transformer_gemms_amd import _abi
+    ws = _abi.lib.tpm_workspace_bytes
+    piece = 256 * 256 * 4
+    # 17 x 16 = 272 tiles: the first 15 tile columns (255 tiles) fill one
+    # round, the last column's 17 tiles are cut into 2 pieces of 8 K steps
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 1024, 1, 1, _abi.BF16) == 2048 + 17 * 2 * piece
+    # same with 64 K steps: 8 pieces of 8 steps
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 4096, 1, 1, _abi.BF16) == 2048 + 17 * 8 * piece
+    # 8 K steps: too short to cut
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 512, 1, 1, _abi.BF16) == 2048
+    # fp8 steps hold 128 K elements: K = 2048 is 16 steps
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 2048, 1, 1, _abi.FP8_E4M3) == 2048 + 17 * 2 * piece
+    # whole rounds, or a last round that no tail of whole columns helps: none
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 8192, 8192, 8192, 1, 1, _abi.BF16) == 2048
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 8192, 3584, 8192, 1, 8, _abi.BF16) == 2048
+    # the plan does not depend on the chunk count; the partials do, through
+    # the row tiles (2 chunks of 2176 rows: 9 row tiles each)
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 1024, 1, 2, _abi.BF16) == 2048 + 18 * 2 * piece
+    # fp32: never split
+    assert ws(_abi.OP_SEQ_CHUNK_GEMM, 4352, 4096, 4096, 1, 1, _abi.F32) == 2048
+    # fp8 backward of the 405B-shaped rank: dZ (32 x 26 tiles, 128 steps: the
+    # last 2 columns in 4 pieces) and dW_up (64 x 26 tiles, 64 steps: the
+    # last 2 columns in 2 pieces) each take 256 pieces; dW_down (26 x 64) none
+    md, mf = 8192 * 16384, 8192 * 6656
+    assert ws(_abi.OP_MLP_BWD_FP8, 8192, 16384, 53248, 8, 1, _abi.FP8_E4M3) == \
+        2048 + 3 * md + 5 * mf + 256 * piece
 
 
 FAKE = 1 << 20  # a non-null, 16-byte-aligned address that is never dereferenced

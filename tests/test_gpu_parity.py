@@ -1077,6 +1077,106 @@ def test_split_k_sum_is_deterministic():
     assert all(torch.equal(o, outs[0]) for o in outs[1:])
 
 
+def test_tail_split_bf16():
+    # 17 x 16 = 272 output tiles: the whole tiles of the first 15 tile
+    # columns fill one round; the last (ragged) column's 17 tiles, the ragged
+    # last row tile among them, are cut into 2 K ranges whose fp32 partials a
+    # second kernel sums in piece order before the epilogue
+    M, N, K = 4312, 4072, 1024
+    piece = 256 * 256 * 4
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    assert ws.numel() == 2048 + 17 * 2 * piece
+    a = si.small_ints((M, K), 91)
+    b = si.small_ints((K, N), 92)
+    A, B = dev_bf16(a), dev_bf16(b)
+    exact = a.astype(np.float64) @ b.astype(np.float64)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    Y0 = torch.empty_like(Y)
+    tpm.seq_chunk_gemm(A, B, Y, workspace=ws)
+    tpm.seq_chunk_gemm(A, B, Y0)                     # no scratch: whole tiles only
+    sync()
+    assert np.array_equal(f64(Y), exact) and np.array_equal(f64(Y0), exact)
+    # float inputs: GeLU + Z save + amax through the finalisation, repeatable
+    x = dev_bf16(si.normal_f32((M, K), 93))
+    w = dev_bf16(si.normal_f32((K, N), 94, 0.02))
+    outs = []
+    for _ in range(2):
+        Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        Z = torch.empty_like(Yb)
+        amax = torch.empty(1, dtype=torch.float32, device="cuda")
+        tpm.seq_chunk_gemm(x, w, Yb, act=_abi.ACT_GELU_ERF, aux=Z, amax_out=amax, workspace=ws)
+        sync()
+        outs.append((Yb, Z, amax))
+    y, z = ops.seq_chunk_gemm(f64(x), f64(w), act=_abi.ACT_GELU_ERF)
+    Yb, Z, amax = outs[0]
+    assert nerr(Yb, y) <= TOL["bf16"] and nerr(Z, z) <= TOL["bf16"]
+    assert amax.item() == float(np.max(np.abs(f64(Yb))))
+    assert torch.equal(outs[1][0], Yb) and torch.equal(outs[1][1], Z) and torch.equal(outs[1][2], amax)
+    # DACT epilogue through the tail path, K-major B
+    wt = dev_bf16(si.normal_f32((N, K), 95, 0.02))
+    zin = dev_bf16(si.normal_f32((M, N), 96))
+    Yd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tpm.seq_chunk_gemm(x, wt, Yd, trans_b=True, epilogue=_abi.EPI_DACT, act=_abi.ACT_GELU_ERF, aux=zin,
+                       workspace=ws)
+    sync()
+    yd, _ = ops.seq_chunk_gemm(f64(x), f64(wt), trans_b=True, act=_abi.ACT_GELU_ERF, dact_z=f64(zin))
+    assert nerr(Yd, yd) <= TOL["bf16"]
+
+
+def test_tail_split_bits_independent_of_chunking():
+    # The tail split cuts the last tile column whatever the chunking, so a
+    # chunk-gated call (2 chunks of 2156 rows fed in the order [1, 0], flags
+    # already set, one CU per XCD left to a producer), the same call
+    # resident, and an unchunked call give the same bits.
+    M, N, K = 4312, 4072, 1024
+    ws2 = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, num_chunks=2)
+    ws1 = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K)
+    assert ws2.numel() == 2048 + 18 * 2 * 256 * 256 * 4     # 9 row tiles per chunk
+    x = dev_bf16(si.normal_f32((M, K), 97))
+    w = dev_bf16(si.normal_f32((K, N), 98, 0.02))
+    flags = torch.full((2,), 5, dtype=torch.int32, device="cuda")
+    Yg = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Yr, Y1 = torch.empty_like(Yg), torch.empty_like(Yg)
+    tpm.seq_chunk_gemm(x, w, Yg, act=_abi.ACT_RELU, num_chunks=2, chunk_order=[1, 0], chunk_ready=flags,
+                       epoch=5, workspace=ws2)
+    sync()
+    assert tpm.poll_device_error(ws2) == 0
+    tpm.seq_chunk_gemm(x, w, Yr, act=_abi.ACT_RELU, num_chunks=2, chunk_order=[1, 0], workspace=ws2)
+    tpm.seq_chunk_gemm(x, w, Y1, act=_abi.ACT_RELU, workspace=ws1)
+    sync()
+    assert torch.equal(Yg, Yr) and torch.equal(Yr, Y1)
+    y, _ = ops.seq_chunk_gemm(f64(x), f64(w), act=_abi.ACT_RELU)
+    assert nerr(Yr, y) <= TOL["bf16"]
+
+
+def test_tail_split_fp8():
+    # e4m3, K = 2048 (16 steps of 128): 17 x 16 tiles, the last column's 17
+    # cut in 2
+    M, N, K = 4352, 4096, 2048
+    ws = tpm.alloc_workspace(_abi.OP_SEQ_CHUNK_GEMM, M, N, K, dtype=_abi.FP8_E4M3)
+    assert ws.numel() == 2048 + 17 * 2 * 256 * 256 * 4
+    a = si.small_ints((M, K), 99, -4, 4)
+    bt = si.small_ints((N, K), 100, -4, 4)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(si.to_e4m3_exact(a).cuda(), si.to_e4m3_exact(bt).cuda(), Y, trans_b=True, workspace=ws)
+    sync()
+    assert np.array_equal(f64(Y), a.astype(np.float64) @ bt.astype(np.float64).T)
+    x = si.normal_f32((M, K), 101)
+    wv = si.normal_f32((N, K), 102, 0.02)
+    xq, sx = si.to_e4m3_current(x)
+    wq, sw = si.to_e4m3_current(wv)
+    scales = dev_f32(np.array([sx, sw], dtype=np.float32))
+    Yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty_like(Yb)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    tpm.seq_chunk_gemm(xq.cuda(), wq.cuda(), Yb, trans_b=True, a_scale=scales[0:1], b_scale=scales[1:2],
+                       act=_abi.ACT_GELU_ERF, aux=Z, amax_out=amax, workspace=ws)
+    sync()
+    y, z = ops.seq_chunk_gemm(f64(xq), f64(wq), trans_b=True, a_scale=sx, b_scale=sw, act=_abi.ACT_GELU_ERF)
+    assert nerr(Yb, y) <= TOL["fp8"] and nerr(Z, z) <= TOL["fp8"]
+    assert amax.item() == float(np.max(np.abs(f64(Yb))))
+
+
 def test_chunk_gating_reads_fresh_data_after_stale_reads():
     # The consumer GEMM first reads X while it holds zeros (so caches may hold
     # those lines), then the chunks are rewritten with real data on a side
