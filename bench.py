@@ -400,6 +400,39 @@ def arrival_step(torch, layer, args, ms_resident):
             "producer_cus": layer.producer_cus}
 
 
+WARM_S = 0.3
+
+
+def warm(torch, call, warm_s=WARM_S):
+    """Run `call` for at least warm_s seconds (and 3 times).  Under sustained
+    matrix-core load the chip settles at a power-limited clock within a
+    fraction of a second; timing after a few calls only would measure part
+    of the run at the higher clock of a cool chip."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
+        call()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def event_median(torch, call, iters):
+    """Median duration (ms, HIP events on the current stream) of `iters`
+    back-to-back calls of `call`, after warm()."""
+    warm(torch, call)
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+
+
 def bench_reduce(torch, tpm, si, iters=40):
     """8 bf16 partials [8192, 8192] -> rank slice [1024, 8192]; the rank
     rotates 0..7 so each launch reads a different 134 MB (the 1 GiB stack
@@ -470,18 +503,7 @@ def bench_mlp_fwd(torch, tpm, si, M, D, F, T, C, fp8, iters=10):
         X, WU, WD = cap["x"].to(dev), cap["wu"].to(dev), cap["wd"].to(dev)
         call = lambda: tpm.tp_mlp_fwd(X, WU, WD, H, P, T=T, rank=0, act=tpm.ACT_GELU_ERF, num_chunks=C)
     del x, wu, wd
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    evs = []
-    for _ in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    ms = event_median(torch, call, iters)
     flops = 2.0 * M * Ft * D * 2
     peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     tf = flops / (ms * 1e-3) / 1e12
@@ -517,18 +539,7 @@ def sweep_point(torch, tpm, si, M, D, F, T, C, iters=10):
                                  num_chunks=C, dy_chunk_order=order, dy_ready=flags, epoch=1, workspace=wsb)
     out = {}
     for name, fn, gemms in (("fwd", fwd, 2), ("bwd", bwd, 4)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        evs = []
-        for _ in range(iters):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+        ms = event_median(torch, fn, iters)
         tf = gemms * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "TFLOPS": round(tf, 1), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
     assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
@@ -555,9 +566,7 @@ def run_yardstick(torch, tpm):
 
     def med(fn, reps=10, stream=None):
         stream = stream or torch.cuda.current_stream()
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        warm(torch, fn)
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -620,19 +629,8 @@ def bench_mlp_fwd_delayed(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, i
                                workspace=ws)
         tpm.fp8_delayed_scale(hist, hs)
         step[0] += 1
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    evs = []
-    for _ in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
+    ms = event_median(torch, call, iters)
     assert tpm.poll_device_error(ws) == 0
-    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
     tf = 2.0 * M * Ft * D * 2 / (ms * 1e-3) / 1e12
     return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="fp8_e4m3 (delayed scaling, history 16)", ms=ms, TFLOPS=tf,
                 frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
@@ -666,18 +664,7 @@ def bench_mlp_bwd_fp8(torch, tpm, M=8192, D=16384, F=53248, T=8, iters=10):
     ws = tpm.alloc_workspace(tpm.OP_MLP_BWD_FP8, M, D, F, T, 1, tpm.FP8_E4M3)
     call = lambda: tpm.tp_mlp_bwd_fp8(X, WU, WD, Z, H, dY, dWu, dWd, dX, T=T, rank=0, scales=scales,
                                       act=tpm.ACT_GELU_ERF, workspace=ws)
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    evs = []
-    for _ in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+    ms = event_median(torch, call, iters)
     tf = 4 * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
     return dict(M=M, D=D, F=F, T=T, dtype="fp8 (e4m3 activations / weights, e5m2 gradients)", ms=ms, TFLOPS=tf,
                 frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
@@ -702,19 +689,8 @@ def bench_mlp_fwd_mx(torch, tpm, si, M=8192, D=16384, F=53248, T=8, C=16, iters=
     order = si.ring_chunk_order(T, C, 0)
     call = lambda: tpm.tp_mlp_fwd_mx(X, Xs, WU, WUs, WD, WDs, H, Hs, P, T=T, rank=0, act=tpm.ACT_GELU_ERF,
                                      num_chunks=C, chunk_order=order, workspace=ws)
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    evs = []
-    for _ in range(iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
+    ms = event_median(torch, call, iters)
     assert tpm.poll_device_error(ws) == 0
-    ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
     tf = 2.0 * M * Ft * D * 2 / (ms * 1e-3) / 1e12
     return dict(M=M, D=D, F=F, T=T, chunks=C, dtype="mxfp8 (e4m3, 32-element E8M0 blocks)", ms=ms, TFLOPS=tf,
                 frac_mfma_peak=tf / FP8_PEAK_TFLOPS)
@@ -745,18 +721,7 @@ def bench_gated_mlp(torch, tpm, si, M=8192, D=4096, F=16384, T=4, C=4, iters=10)
                                        num_chunks=C, dy_chunk_order=order, workspace=wsb)
     out = {"M": M, "D": D, "F": F, "T": T, "chunks": C, "act": "silu (SwiGLU)", "dtype": "bf16"}
     for name, fn, units in (("fwd", fwd, 3), ("bwd", bwd, 6)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        evs = []
-        for _ in range(iters):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in evs)[iters // 2]
+        ms = event_median(torch, fn, iters)
         tf = units * 2.0 * M * Ft * D / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "TFLOPS": round(tf, 1), "frac_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
     assert tpm.poll_device_error(wsf) == 0 and tpm.poll_device_error(wsb) == 0
@@ -824,9 +789,7 @@ def bench_c2(torch, tpm, si, producer_cus, iters=10):
     fl = 2.0 * M * N * K
 
     def med(fn, stream):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        warm(torch, fn)
         ts = []
         for _ in range(iters):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
