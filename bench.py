@@ -357,46 +357,70 @@ def time_steps_graph(torch, layer, steps, warmup):
     return a.elapsed_time(b) / steps, g
 
 
-def arrival_step(torch, layer, args, ms_resident):
+def arrival_step(torch, layer, args):
     """The same step with the chunk-fed GEMMs (QKV, MLP up, dZ, dA) gated on
     chunks that a producer stream writes in ring order while they run, the
     producer confined to `producer_cus` CUs (32 by default: about 0.67 TB/s
     of chunk writes, the order of a rank's ingress over 7 xGMI links) and
     the GEMMs to the others.  Timed under both stream plans (Layer's
-    _step_arriving); the headline figures are those of the layer's plan.
-    Reports the writer's time alone (4 launches of 7 x 8 MB) and the overlap
-    efficiency (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
-    plans = {}
+    _step_arriving), next to the resident step on every CU and on the
+    compute stream's CUs alone (what the CU partition costs), and the
+    writer alone (4 launches of 7 x 8 MB).  The clock under sustained load
+    depends on how long and how hard the chip has been busy, so after a
+    warm-up the variants are timed in turn, three rounds, and each figure
+    is the median of its three.  Overlap efficiency:
+    (t_resident + t_copy - t_overlap) / min(t_resident, t_copy)."""
     first = layer.arrival_plan
-    for i, plan in enumerate((first, "gated_only" if first == "grouped" else "grouped")):
+    plans = (first, "gated_only" if first == "grouped" else "grouped")
+    epoch = [1000]
+
+    def arriving(plan):
         layer.arrival_plan = plan
-        plans[plan], _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=1000 + 500 * i)
-        torch.cuda.synchronize()
-    layer.arrival_plan = first
-    ms = plans[first]
-    # the resident step confined to the compute stream's CUs: separates what
-    # the CU partition costs from what waiting for chunks costs
-    ms_res_masked, _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=3000,
-                                     stream=layer.compute)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms, _, _ = time_steps(torch, layer, args.steps, args.warmup, arrive=True, epoch0=epoch[0])
+        epoch[0] += args.steps + args.warmup + 2
+        layer.arrival_plan = first
+        return ms
+
     pairs = ((layer.x_qkv, layer.x_src), (layer.x_mlp, layer.x_src), (layer.dy_mlp, layer.dy_mlp_src),
              (layer.dy_o, layer.dy_o_src))
-    for rep in range(2):
-        a.record(layer.side)
-        for which, (dst, src) in enumerate(pairs):
-            layer.tpm.write_chunks(dst, src, layer.C, layer.order, layer.flags[which], 5000 + rep,
-                                   layer.counters[which], copy=layer._copy, stream=layer.side)
-        b.record(layer.side)
-        torch.cuda.synchronize()
-    t_copy = a.elapsed_time(b)
-    eff = lambda t: round((ms_resident + t_copy - t) / min(ms_resident, t_copy), 3)
+
+    def writer(stream):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(3):
+            a.record(stream)
+            for which, (dst, src) in enumerate(pairs):
+                layer.tpm.write_chunks(dst, src, layer.C, layer.order, layer.flags[which], epoch[0],
+                                       layer.counters[which], copy=layer._copy, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            epoch[0] += 1
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[1]
+
+    variants = {
+        "resident": lambda: time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=0)[0],
+        "resident_compute": lambda: time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=0,
+                                               stream=layer.compute)[0],
+        **{p: (lambda p=p: arriving(p)) for p in plans},
+        "writer": lambda: writer(layer.side),
+    }
+    warm(torch, lambda: layer.step(0, arrive=False))
+    runs = {k: [] for k in variants}
+    for _ in range(3):
+        for k, f in variants.items():
+            runs[k].append(f())
+            torch.cuda.synchronize()
+    med = {k: sorted(v)[1] for k, v in runs.items()}
+    t_res, t_copy, ms = med["resident"], med["writer"], med[first]
+    eff = lambda p: round((t_res + t_copy - med[p]) / min(t_res, t_copy), 3)
     return {"ms": round(ms, 4), "TFLOPS": round(layer.flops / (ms * 1e-3) / 1e12, 2),
-            "writer_only_ms": round(t_copy, 4), "overlap_efficiency": eff(ms),
-            "plan": first, "plans_ms": {k: round(v, 4) for k, v in plans.items()},
-            "plans_overlap_efficiency": {k: eff(v) for k, v in plans.items()},
-            "resident_eager_ms_all_cus": round(ms_resident, 4),
-            "resident_eager_ms_on_compute_cus": round(ms_res_masked, 4),
+            "writer_only_ms": round(t_copy, 4), "overlap_efficiency": eff(first),
+            "plan": first, "plans_ms": {k: round(med[k], 4) for k in plans},
+            "plans_overlap_efficiency": {k: eff(k) for k in plans},
+            "resident_eager_ms_all_cus": round(t_res, 4),
+            "resident_eager_ms_on_compute_cus": round(med["resident_compute"], 4),
+            "rounds_ms": {k: [round(x, 4) for x in v] for k, v in runs.items()},
             "producer_cus": layer.producer_cus}
 
 
@@ -1158,7 +1182,7 @@ def main():
     }
     caps = {}
     if not args.no_extra:
-        extra = {"arrival_step": arrival_step(torch, layer, args, ms_eager)}
+        extra = {"arrival_step": arrival_step(torch, layer, args)}
     if not args.no_cpu_baseline:
         caps["c5"] = capture_layer(torch, layer)
     del layer
