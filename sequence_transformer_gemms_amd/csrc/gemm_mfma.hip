@@ -330,6 +330,48 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Epilogue shapes fixed at compile time, so that the element-wise code tests
+// no parameter per element: tested per element, the flags and pointers the
+// general path needs do not all fit in scalar registers next to the main
+// loop's, and the compiler keeps them in vector-register lanes that it reads
+// back one at a time.  FK_FWD: forward with a bf16 output; FK_DACT: the
+// activation-gradient epilogue (bf16 Z, bf16 output); FK_AUX: the
+// pre-activation saved as bf16; FK_AMAX: the output's amax recorded; FK_RAW:
+// the fp32 partial of a K range; FK_ANY: everything else, tested at run time.
+enum { FK_ANY = 0, FK_FWD = 1, FK_AUX = 2, FK_AMAX = 4, FK_DACT = 8, FK_RAW = 16 };
+// The shapes of the general epilogue loop (FK_RAW only when RAW) and of
+// the DACT loop (Z preloaded; none unless DACT).  Each shape is another copy
+// of the loop: the fp8 kernels, whose one wave per SIMD holds 128 x 128
+// accumulators, take only the forward shapes, which keep them free of
+// register spills.
+template <bool RAW, class F>
+__device__ __forceinline__ void with_fk_general(int fk, F&& f) {
+  switch (fk) {
+    case FK_FWD: f(IC<FK_FWD>{}); break;
+    case FK_FWD | FK_AUX: f(IC<FK_FWD | FK_AUX>{}); break;
+    case FK_FWD | FK_AMAX: f(IC<FK_FWD | FK_AMAX>{}); break;
+    case FK_FWD | FK_AUX | FK_AMAX: f(IC<FK_FWD | FK_AUX | FK_AMAX>{}); break;
+    case FK_RAW:
+      if constexpr (RAW) {
+        f(IC<FK_RAW>{});
+        break;
+      }
+      [[fallthrough]];
+    default: f(IC<FK_ANY>{}); break;
+  }
+}
+template <bool DACT, class F>
+__device__ __forceinline__ void with_fk_dact(int fk, F&& f) {
+  if constexpr (DACT) {
+    switch (fk) {
+      case FK_DACT: f(IC<FK_DACT>{}); return;
+      case FK_DACT | FK_AMAX: f(IC<FK_DACT | FK_AMAX>{}); return;
+      default: break;
+    }
+  }
+  f(IC<FK_ANY>{});
+}
+
 // Epilogue of eight consecutive output columns (row, col..col+7) of one lane.
 // 8 consecutive values of a row-major bf16 or fp32 matrix
 __device__ __forceinline__ void load_oct(const void* base, int64_t ld, bool f32, int row, int col, float (&v)[8]) {
@@ -376,11 +418,46 @@ __device__ __forceinline__ void epi_gated_oct(const GemmParams& p, const float (
   store_oct(p.Y, p.ldy, p.y_f32, row, col, h);
 }
 
+// bf16 store of 8 consecutive output values, with their amax when AMAX.
+template <bool AMAX>
+__device__ __forceinline__ void store_y_bf16(const GemmParams& p, const float (&v)[8], int row, int col,
+                                             float& lmax) {
+  i32x4 yy;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    yy[e] = (int)w;
+    if constexpr (AMAX)
+      lmax = fmaxf(lmax, fmaxf(fabsf(bf16_to_f32((uint16_t)(w & 0xFFFFu))), fabsf(bf16_to_f32((uint16_t)(w >> 16)))));
+  }
+  *(i32x4*)((uint16_t*)p.Y + (int64_t)row * p.ldy + col) = yy;
+}
+
 // (ACT: the activation p.act, fixed at compile time by with_act; ZPRE: the
-// DACT epilogue's bf16 Z of these 8 columns already loaded, in zpre)
-template <int ACT, bool ZPRE = false>
+// DACT epilogue's bf16 Z of these 8 columns already loaded, in zpre; FK: the
+// epilogue shape when fixed at compile time)
+template <int ACT, bool ZPRE = false, int FK = FK_ANY>
 __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax,
                                         i32x4 zpre = i32x4{0, 0, 0, 0}) {
+  if constexpr ((FK & FK_FWD) != 0) {
+    if constexpr ((FK & FK_AUX) != 0) store_oct(p.aux, p.ldaux, false, row, col, v);  // pre-activation
+    if constexpr (ACT != ACT_NONE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = act_fwd_c<ACT>(v[e]);
+    }
+    store_y_bf16<(FK & FK_AMAX) != 0>(p, v, row, col, lmax);
+    return;
+  }
+  if constexpr ((FK & FK_DACT) != 0) {
+    static_assert(ZPRE, "the DACT shape takes its Z preloaded");
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] *= act_grad_c<ACT>(bf16_to_f32((uint16_t)((uint32_t)zpre[e] & 0xFFFFu)));
+      v[2 * e + 1] *= act_grad_c<ACT>(bf16_to_f32((uint16_t)((uint32_t)zpre[e] >> 16)));
+    }
+    store_y_bf16<(FK & FK_AMAX) != 0>(p, v, row, col, lmax);
+    return;
+  }
   if (p.epi == EPI_DGATED) {
     // v = dH; aux = [G | U]: Y[:, col] = dG = dH U act'(G), Y[:, N + col] = dU = dH act(G)
     float g[8], u[8], du[8];
@@ -943,6 +1020,8 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         // per row group
         constexpr int GRP = 4;
         static_assert((EPI_ROWS / 8) % GRP == 0, "row groups");
+        with_fk_dact<!FP8>(p.y_f32 ? FK_ANY : (FK_DACT | (p.amax ? FK_AMAX : 0)), [&](auto fkc) {
+        constexpr int FK = decltype(fkc)::value;
 #pragma unroll 1
         for (int it0 = 0; it0 < EPI_ROWS / 8; it0 += GRP) {
           i32x4 zq[GRP];
@@ -965,10 +1044,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             if (row < tl.m_end && col < p.N) {
               float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
                             v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
-              epi_oct<ACT, true>(p, v, row, col, lmax, zq[g]);
+              epi_oct<ACT, true, FK>(p, v, row, col, lmax, zq[g]);
             }
           }
         }
+        });
         return;
       }
       // the staged values of four row groups are read before any is used,
@@ -976,6 +1056,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       // would hide it)
       constexpr int GRP = 4;
       static_assert((EPI_ROWS / 8) % GRP == 0, "row groups");
+      const int fk = raw ? FK_RAW
+                         : (p.epi == EPI_FWD && !p.y_f32 && !(p.aux && p.aux_f32))
+                               ? (FK_FWD | (p.aux ? FK_AUX : 0) | (p.amax ? FK_AMAX : 0)) : FK_ANY;
+      with_fk_general<!FP8>(fk, [&](auto fkc) {
+      constexpr int FK = decltype(fkc)::value;
 #pragma unroll 1
       for (int it0 = 0; it0 < EPI_ROWS / 8; it0 += GRP) {
         f32x4 v0s[GRP], v1s[GRP];
@@ -994,7 +1079,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           const int row = tl.m0 + wm + EPI_ROWS * rp + rl;
           const int col = tl.n0 + wn + EPI_COLS * cp + cl;
           if (row < tl.m_end && col < p.N) {
-            if (raw) {
+            if (FK == FK_RAW || (FK == FK_ANY && raw)) {
               // raw fp32 partial of this K range; splitk_finalize or
               // tail_finalize sums them
               f32x4* dst = un.tail >= 0
@@ -1006,11 +1091,12 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             } else {
               float v[8] = {v0[0] * scale, v0[1] * scale, v0[2] * scale, v0[3] * scale,
                             v1[0] * scale, v1[1] * scale, v1[2] * scale, v1[3] * scale};
-              epi_oct<ACT>(p, v, row, col, lmax);
+              epi_oct<ACT, false, FK>(p, v, row, col, lmax);
             }
           }
         }
       }
+      });
       });
       }
     });
