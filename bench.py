@@ -345,6 +345,7 @@ def time_steps_graph(torch, layer, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         layer.step(0, arrive=False)
+    warm(torch, g.replay)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -428,10 +429,12 @@ WARM_S = 0.3
 
 
 def warm(torch, call, warm_s=WARM_S):
-    """Run `call` for at least warm_s seconds (and 3 times).  Under sustained
-    matrix-core load the chip settles at a power-limited clock within a
-    fraction of a second; timing after a few calls only would measure part
-    of the run at the higher clock of a cool chip."""
+    """Run `call` for at least warm_s seconds (and 3 times).  After the GPU
+    has idled (inputs made on the host, another workload's set-up), its
+    clock takes a fraction of a second of sustained matrix-core load to
+    reach the power-limited level that load settles at; timing after a few
+    calls only would measure part of that transition (on the layer step
+    about 2 % slower than the settled rate)."""
     t0 = time.perf_counter()
     n = 0
     while n < 3 or time.perf_counter() - t0 < warm_s:
@@ -1150,7 +1153,10 @@ def main():
     layer = Layer(torch, tpm, si, producer_cus=args.producer_cus)
     torch.cuda.synchronize()
     # headline: the rank's step with every chunk already in place (flags
-    # not consulted), on the default stream with every CU
+    # not consulted), on the default stream with every CU; the clock first
+    # settles under the step's own load (warm), then W untimed and K timed
+    # steps
+    warm(torch, lambda: layer.step(0, arrive=False))
     ms_eager, gemm_ms, wall = time_steps(torch, layer, args.steps, args.warmup, arrive=False, epoch0=0)
     ms, graph = time_steps_graph(torch, layer, args.steps, args.warmup)
     flops = layer.flops
@@ -1171,7 +1177,8 @@ def main():
                                "is extra.arrival_step)",
                    "tokens": 4096, "hidden": 8192, "ffn": 28672, "tp": 8, "chunks": 8,
                    "gflop_per_step": round(flops / 1e9, 1), "frac_mfma_peak": round(value / BF16_PEAK_TFLOPS, 4),
-                   "launch": "hip_graph", "ms_per_step_eager": round(ms_eager, 4)},
+                   "launch": "hip_graph", "ms_per_step_eager": round(ms_eager, 4),
+                   "warmup_min_seconds": WARM_S},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(),
                      "traffic_unit": "bytes per step (the 12 GEMMs in 10 launches + split-K finalisation)",
