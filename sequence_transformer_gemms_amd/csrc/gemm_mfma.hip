@@ -295,6 +295,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// amax of a 256-thread work-group's values into *amax: one atomic per
+// work-group (per-wave atomics on one address, thousands within a few
+// microseconds, serialise).  Called by every thread.
+__device__ __forceinline__ void block_amax(float* amax, float v) {
+  __shared__ float wmax[4];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax((unsigned int*)amax, __builtin_bit_cast(unsigned int, m));
+  }
+}
+
 __device__ __forceinline__ bool wait_group(const GemmParams& p, int g, char* smem) {
   volatile int& timed_out = *reinterpret_cast<volatile int*>(smem + CTRL_WAIT);
   if (threadIdx.x == 0) {
@@ -1198,46 +1212,46 @@ __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
     epi_oct<ACT>(p, v, row, col, lmax);
   }
   });
-  if (p.amax) {
-    lmax = wave_max(lmax);
-    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));
-  }
+  if (p.amax) block_amax(p.amax, lmax);
 }
 
 // Tail finalisation: each tail tile's pieces summed in ascending piece order
-// (deterministic), scaled, then the epilogue; one work-group per 8 rows of a
-// tail tile, 8 consecutive columns per lane.
+// (deterministic), scaled, then the epilogue; one work-group per 64 rows of a
+// tail tile, 8 rows at a time, 8 consecutive columns per lane.
+constexpr int kTailRows = 64;
 __global__ void __launch_bounds__(256) tail_finalize(const GemmParams p) {
   float scale = 1.f;
   if (p.a_scale) scale *= *p.a_scale;
   if (p.b_scale) scale *= *p.b_scale;
-  constexpr int BLOCKS_PER_TILE = BM / 8;
+  constexpr int BLOCKS_PER_TILE = BM / kTailRows;
   const int t = blockIdx.x / BLOCKS_PER_TILE;
-  const int r = (blockIdx.x - t * BLOCKS_PER_TILE) * 8 + (threadIdx.x >> 5);
+  const int r0 = (blockIdx.x - t * BLOCKS_PER_TILE) * kTailRows + (threadIdx.x >> 5);
   const int c = (threadIdx.x & 31) * 8;
   const Tile tl = tail_tile(p, t);
-  const int row = tl.m0 + r, col = tl.n0 + c;
+  const int col = tl.n0 + c;
+  const int64_t piece = (int64_t)p.tail_tiles * BM * BN;
   float lmax = 0.f;
-  if (row < tl.m_end && col < p.N) {
-    const int64_t piece = (int64_t)p.tail_tiles * BM * BN;
-    const float* src = p.partial + ((int64_t)t * BM + r) * BN + c;
-    f32x4 a0 = __builtin_nontemporal_load((const f32x4*)src);
-    f32x4 a1 = __builtin_nontemporal_load((const f32x4*)src + 1);
-    for (int sp = 1; sp < p.tail_pieces; ++sp) {
-      a0 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece));
-      a1 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece) + 1);
+  with_act(p.act, [&](auto ac) {
+    constexpr int ACT = decltype(ac)::value;
+#pragma unroll 2
+    for (int i = 0; i < kTailRows / 8; ++i) {
+      const int r = r0 + 8 * i;
+      const int row = tl.m0 + r;
+      if (row < tl.m_end && col < p.N) {
+        const float* src = p.partial + ((int64_t)t * BM + r) * BN + c;
+        f32x4 a0 = __builtin_nontemporal_load((const f32x4*)src);
+        f32x4 a1 = __builtin_nontemporal_load((const f32x4*)src + 1);
+        for (int sp = 1; sp < p.tail_pieces; ++sp) {
+          a0 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece));
+          a1 += __builtin_nontemporal_load((const f32x4*)(src + sp * piece) + 1);
+        }
+        float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
+                      a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
+        epi_oct<ACT>(p, v, row, col, lmax);
+      }
     }
-    float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
-                  a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
-    with_act(p.act, [&](auto ac) {
-      constexpr int ACT = decltype(ac)::value;
-      epi_oct<ACT>(p, v, row, col, lmax);
-    });
-  }
-  if (p.amax) {
-    lmax = wave_max(lmax);
-    if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)p.amax, __builtin_bit_cast(unsigned int, lmax));
-  }
+  });
+  if (p.amax) block_amax(p.amax, lmax);
 }
 
 }  // namespace
@@ -1251,7 +1265,7 @@ static hipError_t finalize_if_split(const GemmParams& p, hipStream_t s) {
     if (blocks > 4096) blocks = 4096;
     splitk_finalize<<<(int)blocks, 256, 0, s>>>(p);
   } else if (p.tail_pieces > 1) {
-    tail_finalize<<<p.tail_tiles * (BM / 8), 256, 0, s>>>(p);
+    tail_finalize<<<p.tail_tiles * (BM / kTailRows), 256, 0, s>>>(p);
   } else {
     return hipSuccess;
   }

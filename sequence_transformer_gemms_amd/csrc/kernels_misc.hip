@@ -199,28 +199,49 @@ __global__ void __launch_bounds__(256) cast_fp8_t(const uint16_t* __restrict__ x
   }
 }
 
-// Byte transpose [rows, cols] -> [cols, rows] (fp8 codes), 64 x 64 tiles.
+// Byte transpose [rows, cols] -> [cols, rows] (fp8 codes; rows and cols
+// multiples of 16), 128 x 128 tiles through LDS held as 32-bit words (row
+// pitch padded to 33 words): each thread loads 4 x 16 bytes of input rows,
+// then reads 16 words down one column of words (4 input columns x 16 input
+// rows), transposes the four 4 x 4 byte blocks in registers and stores 4
+// output rows of 16 bytes, 8 threads covering 128 bytes of an output row.
+constexpr int kTrTile = 128, kTrPitch = kTrTile / 4 + 1;
 __global__ void __launch_bounds__(256) transpose_u8(const uint8_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                     uint8_t* __restrict__ y, int64_t ldy) {
-  __shared__ uint8_t tile[64][64 + 16];
+  __shared__ uint32_t tile[kTrTile * kTrPitch];
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  {
-    const int r = t >> 2, cg = (t & 3) * 16;
+  const int64_t r0 = (int64_t)blockIdx.y * kTrTile, c0 = (int64_t)blockIdx.x * kTrTile;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = j * 256 + t;
+    const int r = idx >> 3, cg = (idx & 7) * 16;
     if (r0 + r < rows && c0 + cg < cols) {
       const uint4 v = *(const uint4*)(x + (r0 + r) * ld + c0 + cg);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tile[r][cg + i] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
+      uint32_t* d = tile + r * kTrPitch + cg / 4;
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
     }
   }
   __syncthreads();
-  const int oc = t >> 2, rg = (t & 3) * 16;
-  if (c0 + oc < cols && r0 + rg < rows) {
-    uint32_t w[4] = {0, 0, 0, 0};
+  const int g = t & 7, wc = t >> 3;  // input rows 16g .. 16g+15, input columns 4wc .. 4wc+3
+  if (r0 + 16 * g < rows) {
+    uint32_t out[4][4];                // [output row b][input rows 16g+4k .. +3]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i / 4] |= (uint32_t)tile[rg + i][oc] << (8 * (i % 4));
-    *(uint4*)(y + (c0 + oc) * ldy + r0 + rg) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t* src = tile + (16 * g + 4 * k) * kTrPitch + wc;
+      const uint32_t w0 = src[0], w1 = src[kTrPitch], w2 = src[2 * kTrPitch], w3 = src[3 * kTrPitch];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        out[b][k] = ((w0 >> (8 * b)) & 0xFFu) | (((w1 >> (8 * b)) & 0xFFu) << 8) |
+                    (((w2 >> (8 * b)) & 0xFFu) << 16) | (((w3 >> (8 * b)) & 0xFFu) << 24);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t oc = c0 + 4 * wc + b;
+      if (oc < cols) *(uint4*)(y + oc * ldy + r0 + 16 * g) = make_uint4(out[b][0], out[b][1], out[b][2], out[b][3]);
+    }
   }
 }
 
@@ -444,7 +465,7 @@ hipError_t launch_cast_fp8_t(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 hipError_t launch_transpose_u8(const uint8_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* y, int64_t ldy,
                                hipStream_t s) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  const dim3 grid((unsigned)((cols + kTrTile - 1) / kTrTile), (unsigned)((rows + kTrTile - 1) / kTrTile));
   transpose_u8<<<grid, 256, 0, s>>>(x, rows, cols, ld, y, ldy);
   return hipGetLastError();
 }
