@@ -379,12 +379,13 @@ void make_params(const GemmDesc& g, const SplitPlan& pl, GemmParams& p) {
 
 // Split plan the matrix-core path makes for a GEMM (none on the predicated
 // path).  Chunk-gated GEMMs split too; range-done signalling needs whole
-// tiles, and the gated forward and the fp8 outputs pair or scale whole
-// tiles in their epilogues.  The plan depends on the shape, the chunk count
+// tiles, and the gated forward and the MXFP8 output pair or scale whole
+// tiles in their epilogues (the finalisation passes write the delayed-
+// scaling fp8 output as the GEMM kernel does).  The plan depends on the shape, the chunk count
 // and the element type only, never on the stream or the grid, so that a
 // chunk-fed call and a resident one give the same bits.
 SplitPlan planned_split(const GemmDesc& g) {
-  if (fast_path_blocker(g) || g.done || g.epi == TPM_EPI_GATED || g.y_mx || g.y_qs) return SplitPlan{};
+  if (fast_path_blocker(g) || g.done || g.epi == TPM_EPI_GATED || g.y_mx) return SplitPlan{};
   return plan_gemm(g.M, g.N, g.K, g.groups, g.adt);
 }
 
@@ -471,11 +472,16 @@ size_t tpm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int T, int n
       part = std::max(part, plan_bytes(M, D, Ft, 1, dtype));
       return kCtrlBytes + dz + part;
     }
-    case TPM_OP_MX_MLP_FWD:
-    case TPM_OP_FP8_DELAYED_MLP_FWD: {
+    case TPM_OP_MX_MLP_FWD: {   // GEMM1 writes MXFP8 whole tiles: only GEMM2 may split
       if (T <= 0) return 0;
       const int64_t D = N, Ft = K / T;
       return kCtrlBytes + plan_bytes(M, D, Ft, T, TPM_FP8_E4M3);
+    }
+    case TPM_OP_FP8_DELAYED_MLP_FWD: {
+      if (T <= 0) return 0;
+      const int64_t D = N, Ft = K / T;
+      return kCtrlBytes + std::max(plan_bytes(M, Ft, D, num_chunks, TPM_FP8_E4M3),
+                                   plan_bytes(M, D, Ft, T, TPM_FP8_E4M3));
     }
     case TPM_OP_CAST_FP8:
       return kCtrlBytes;

@@ -912,6 +912,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     //      the element-wise code then runs in one compact loop and every
     //      global store is 16 bytes wide, eight lanes covering 128 bytes.
     float lmax = 0.f;
+    // a unit of a split K range stores its raw fp32 partial, whatever the
+    // output (a finalisation pass applies the epilogue)
+    const bool raw = p.splits > 1 || un.tail >= 0;
     float* stage = reinterpret_cast<float*>(smem) + wave * LY::EPI_WAVE_FLOATS;
     constexpr int EPI_LD = LY::EPI_LD, EPI_COLS = LY::EPI_COLS, EPI_ROWS = LY::EPI_ROWS;
     constexpr int FPP = EPI_COLS / 32;                 // column fragments per pass
@@ -953,7 +956,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           }
         }
         });
-      } else if (FP8 && p.y_q_scale) {
+      } else if (FP8 && p.y_q_scale && !raw) {
         // fp8 output with a scale fixed before the call (delayed scaling):
         // codes e4m3(v * fp32(1 / s)), nearest-even, saturating; amax of the
         // fp32 values quantised
@@ -984,7 +987,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
           }
         }
         });
-      } else if (FP8 && p.y_mx) {
+      } else if (FP8 && p.y_mx && !raw) {
         // MXFP8 output: each 32-column block of a row (4 lanes) shares one
         // scale 2^(E-127), E = exponent field of the block's amax - 8 (0 for
         // a zero block); codes are e4m3(v * 2^(127-E)), nearest-even,
@@ -1027,7 +1030,6 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       // read back 8 consecutive columns per lane, 8 lanes per row
       with_act(p.act, [&](auto ac) {
       constexpr int ACT = decltype(ac)::value;
-      const bool raw = p.splits > 1 || un.tail >= 0;  // fp32 partial of a K range
       if (p.epi == EPI_DACT && !p.aux_f32 && !raw) {
         // DACT with a bf16 Z: the Z loads of four row groups are issued
         // together before any is used, instead of one exposed load latency
@@ -1185,6 +1187,28 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_pair_kernel(const GemmParams 
 }
 
 
+// The epilogue of 8 summed values in a finalisation pass: the fp8 output of
+// delayed scaling as the GEMM kernel writes it (pre-activation saved as
+// bf16, codes e4m3(act(v) * fp32(1 / s)), amax of act(v)), else epi_oct.
+template <int ACT>
+__device__ __forceinline__ void finalize_oct(const GemmParams& p, float (&v)[8], int row, int col, float& lmax) {
+  if (p.y_q_scale) {
+    const float inv = 1.0f / *p.y_q_scale;
+    if (p.aux) store_oct(p.aux, p.ldaux, false, row, col, v);
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float h = act_fwd_c<ACT>(v[e]);
+      lmax = fmaxf(lmax, fabsf(h));
+      q[e] = h * inv;
+    }
+    *(uint2*)((uint8_t*)p.Y + (int64_t)row * p.ldy + col) =
+        make_uint2(fp8x4<false>(q[0], q[1], q[2], q[3]), fp8x4<false>(q[4], q[5], q[6], q[7]));
+    return;
+  }
+  epi_oct<ACT>(p, v, row, col, lmax);
+}
+
 // Split-K finalisation: Y = epilogue(scale * sum_{s=0}^{S-1} partial_s),
 // summed in ascending s (deterministic), 8 consecutive columns per lane.
 __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
@@ -1209,7 +1233,7 @@ __global__ void __launch_bounds__(256) splitk_finalize(const GemmParams p) {
     }
     float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
                   a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
-    epi_oct<ACT>(p, v, row, col, lmax);
+    finalize_oct<ACT>(p, v, row, col, lmax);
   }
   });
   if (p.amax) block_amax(p.amax, lmax);
@@ -1247,7 +1271,7 @@ __global__ void __launch_bounds__(256) tail_finalize(const GemmParams p) {
         }
         float v[8] = {a0[0] * scale, a0[1] * scale, a0[2] * scale, a0[3] * scale,
                       a1[0] * scale, a1[1] * scale, a1[2] * scale, a1[3] * scale};
-        epi_oct<ACT>(p, v, row, col, lmax);
+        finalize_oct<ACT>(p, v, row, col, lmax);
       }
     }
   });

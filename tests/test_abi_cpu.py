@@ -46,6 +46,10 @@ def test_workspace_sizes():
     tail = 64 * 4 * 256 * 256 * 4
     assert ws(_abi.OP_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048 + 8192 * 6656 + tail
     assert ws(_abi.OP_MLP_FWD, 8192, 8192, 28672, 8, 8, _abi.BF16) == 2048
+    # fp8 delayed scaling: GEMM1 writes e4m3 H directly and takes the same
+    # tail split; MXFP8: GEMM1 writes whole MX blocks, no split
+    assert ws(_abi.OP_FP8_DELAYED_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048 + tail
+    assert ws(_abi.OP_MX_MLP_FWD, 8192, 16384, 53248, 8, 16, _abi.FP8_E4M3) == 2048
 
 
 def test_tail_split_plan():

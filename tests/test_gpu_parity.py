@@ -782,10 +782,14 @@ def test_mlp_bwd_fp8_chunk_fed_e5m2_dy_matches_resident():
 
 
 # -------------------------------------------------------- fp8 delayed scaling
-def test_mlp_fwd_fp8_delayed_integer_exact():
+@pytest.mark.parametrize("M, D, F", [(256, 64, 512),
+                                     # 17 x 16 tiles for GEMM1 (the last tile column
+                                     # in 2 K pieces, finalised to e4m3), split-K GEMM2
+                                     (4352, 2048, 8192)])
+def test_mlp_fwd_fp8_delayed_integer_exact(M, D, F):
     # integer operands, ReLU: H is exact, H * fp32(1 / s_H) exact for s_H =
     # 1/16, so the e4m3 codes (saturating above 448) and the amax are bit-exact
-    M, D, F, T = 256, 64, 512, 2
+    T = 2
     Ft = F // T
     x, wu, wd = si.small_ints((M, D), 121), si.small_ints((D, Ft), 122), si.small_ints((Ft, D), 123)
     X = si.to_e4m3_exact(x).cuda()
