@@ -330,12 +330,19 @@ void make_params(const GemmDesc& g, const SplitPlan& pl, GemmParams& p) {
   p.group_cnt = g.ctrl ? g.ctrl + kCtrlCnt : nullptr;
   p.lda = g.lda; p.ldb = g.ldb; p.ldy = g.ldy; p.ldaux = g.ldaux;
   p.M = (int)g.M; p.N = (int)g.N; p.K = (int)g.K;
-  p.num_groups = g.groups;
-  p.group_rows = (int)(g.M / g.groups);
+  // Without chunk flags or range-done signalling the groups only order the
+  // tiles.  When their rows are whole tiles, the launch walks all of M as one
+  // group instead: its bands of band_m tile rows then span the groups, which
+  // gives the 32 tiles an XCD runs at once a squarer footprint of A and B
+  // panels in its L2.  The tiles, hence the results, are the same.
+  const bool one_group = !g.ready && !g.done && g.groups > 1 && (g.M / g.groups) % kTileM == 0;
+  const int groups = one_group ? 1 : g.groups;
+  p.num_groups = groups;
+  p.group_rows = (int)(g.M / groups);
   p.epoch = g.epoch;
   p.wait_limit = g_wait_limit;
   p.act = g.act; p.epi = g.epi; p.y_f32 = g.ydt == TPM_F32; p.aux_f32 = p.y_f32;
-  for (int i = 0; i < g.groups; ++i) p.order[i] = (int16_t)(g.order ? g.order[i] : i);
+  for (int i = 0; i < groups; ++i) p.order[i] = (int16_t)(g.order && !one_group ? g.order[i] : i);
   const int64_t nk = (g.K * esize(g.adt) + kStepBytes - 1) / kStepBytes;
   p.splits = S;
   p.ksteps_per_split = (int)((nk + S - 1) / S);

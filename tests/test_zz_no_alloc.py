@@ -1,7 +1,8 @@
 """The allocation-free entry point against seq_chunk_gemm with a workspace:
 two calls in a row (the second smaller, both planning split-K, so the
 second reuses the per-GPU scratch the first left behind), bit for bit; the
-amax is zeroed by each call."""
+amax is zeroed by each call.  A shape with a tail split (its last tile
+column in K pieces) takes the same scratch."""
 import numpy as np
 import pytest
 import torch
@@ -51,3 +52,12 @@ def test_noalloc_integer_exact_and_repeatable():
         tpm.seq_chunk_gemm_noalloc(A, B, Y)
         torch.cuda.synchronize()
         assert np.array_equal(f64(Y), a.astype(np.float64) @ b.astype(np.float64))
+
+
+def test_noalloc_tail_split_matches_workspace_call():
+    # 17 x 16 tiles: the last tile column's 17 tiles in 2 K pieces (8.9 MB of
+    # partials in the per-GPU scratch), then a smaller split-K call reusing it
+    M, N, K = 4312, 4072, 1024
+    assert tpm.workspace_bytes(_abi.OP_SEQ_CHUNK_GEMM, M, N, K) == 2048 + 17 * 2 * 256 * 256 * 4
+    _run_pair(M, N, K, 507, _abi.ACT_GELU_TANH, False)
+    _run_pair(256, 200, 2048, 509, _abi.ACT_NONE, True)
