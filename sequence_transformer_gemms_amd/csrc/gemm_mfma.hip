@@ -23,6 +23,12 @@
 // four consecutive output columns of one row: stores are 8 or 16 bytes wide.
 // fp8 (OCP e4m3fn) operands take the same 128-byte-per-row K-major staging
 // (128 K elements per step) and v_mfma_f32_32x32x64_f8f6f4.
+//
+// A launch may cut K into ranges: every tile's (few tiles), or only the
+// tiles of the last tile columns when whole tiles would leave the last round
+// of work-groups mostly empty; those units store fp32 partials, and a
+// finalisation kernel sums them in a fixed order and runs the epilogue.
+// The epilogue's common shapes are fixed at compile time per unit.
 #include <type_traits>
 
 #include "tpm_device.hpp"
