@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--yardstick", action="store_true",
                     help="bf16 GEMM 8192^3 in three layouts, ours next to torch.matmul (hipBLASLt), and ours on "
                          "256 / 128 / 64 CUs (CU-masked streams); one JSON line")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time only the fp8 configuration's workloads (MLP forward under current, MXFP8 and "
+                         "delayed scaling, and the fp8 backward) and print one JSON line; for profiling them")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: one line per (T, chunks) of the Llama3-70B MLP share "
                          "(8192 tokens, D 8192, F 28672), T in 1, 2, 4, 8 and chunks in T, 2T, 4T")
@@ -927,17 +930,44 @@ def _read_sclk(path):
     return None
 
 
+def _hwmon_files(torch):
+    """The board's power (W, instantaneous), power cap (W) and junction
+    temperature (C) files of the driver's hwmon directory for GPU 0, where
+    readable."""
+    import glob
+    p = torch.cuda.get_device_properties(0)
+    dev = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    out = {}
+    for h in glob.glob(dev + "/hwmon/hwmon*"):
+        for name, key in (("power1_input", "power"), ("power1_cap", "cap")):
+            if os.access(os.path.join(h, name), os.R_OK):
+                out[key] = os.path.join(h, name)
+        for i in range(1, 8):
+            lab = os.path.join(h, f"temp{i}_label")
+            if os.access(lab, os.R_OK) and open(lab).read().strip() == "junction":
+                out["junction"] = os.path.join(h, f"temp{i}_input")
+    return out
+
+
 def observe_sclk(torch, replay, seconds=0.6):
-    """The graphics clock while the timed work repeats: `replay` runs back
-    to back (synchronising every 16 calls) for about `seconds` while a thread
-    samples the driver's current clock level every 5 ms.  Outside the timed
-    regions, so the sampling cannot perturb them.  None where the sysfs file
-    is not readable."""
+    """The graphics clock, the board power and the junction temperature while
+    the timed work repeats: `replay` runs back to back (synchronising every
+    16 calls) for about `seconds` while a thread samples the driver's current
+    clock level and the hwmon power and temperature every 5 ms.  Outside the
+    timed regions, so the sampling cannot perturb them.  None where the clock
+    file is not readable."""
     import threading
     path = _sclk_file(torch)
     if path is None:
         return None
-    samples, stop = [], threading.Event()
+    hw = _hwmon_files(torch)
+    samples, power, temp, stop = [], [], [], threading.Event()
+
+    def rd(p, scale):
+        try:
+            return int(open(p).read().strip()) / scale
+        except (OSError, ValueError):
+            return None
 
     def sample():
         while not stop.is_set():
@@ -947,6 +977,14 @@ def observe_sclk(torch, replay, seconds=0.6):
                 v = None
             if v:
                 samples.append(v)
+            if "power" in hw:
+                w = rd(hw["power"], 1e6)
+                if w:
+                    power.append(w)
+            if "junction" in hw:
+                c = rd(hw["junction"], 1e3)
+                if c:
+                    temp.append(c)
             stop.wait(0.005)
     replay()
     torch.cuda.synchronize()
@@ -964,8 +1002,18 @@ def observe_sclk(torch, replay, seconds=0.6):
     if not samples:
         return None
     v = sorted(samples)
-    return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v), "replays": n,
-            "source": "pp_dpm_sclk current level"}
+    out = {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v), "replays": n,
+           "source": "pp_dpm_sclk current level"}
+    # the second half of the samples: the board's power follows the load
+    # within a few tens of milliseconds
+    if power:
+        pw = sorted(power[len(power) // 2:])
+        out["board_power_w_median"] = pw[len(pw) // 2]
+        out["board_power_cap_w"] = rd(hw["cap"], 1e6) if "cap" in hw else None
+    if temp:
+        tc = sorted(temp[len(temp) // 2:])
+        out["junction_c_median"] = tc[len(tc) // 2]
+    return out
 
 
 # ------------------------------------------------------------------ oracle leg
@@ -1143,6 +1191,16 @@ def main():
         return
     if args.yardstick:
         run_yardstick(torch, tpm)
+        return
+    if args.fp8:
+        out = {"mlp_fwd_c4_fp8": bench_mlp_fwd(torch, tpm, si, 8192, 16384, 53248, 8, 16, True)[0]}
+        torch.cuda.empty_cache()
+        out["mlp_fwd_c4_mxfp8"] = bench_mlp_fwd_mx(torch, tpm, si)
+        torch.cuda.empty_cache()
+        out["mlp_fwd_c4_fp8_delayed"] = bench_mlp_fwd_delayed(torch, tpm, si)
+        torch.cuda.empty_cache()
+        out["mlp_bwd_c4_fp8"] = bench_mlp_bwd_fp8(torch, tpm)
+        print(json.dumps(out))
         return
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
