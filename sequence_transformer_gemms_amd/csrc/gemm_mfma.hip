@@ -200,7 +200,7 @@ __device__ __forceinline__ Unit map_unit(const GemmParams& p, int u) { return lo
 // gate and up products of the same 32 output columns.
 template <bool KMAJ, int ESZ, int THREADS, bool GATED = false>
 __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_bytes, int mn0, int mn_end, int k0,
-                                          int K, char* lds_tile, int j, int up_off = 0) {
+                                          int K, uint32_t lds_tile, int j, int up_off = 0) {
   static_assert(KMAJ || ESZ == 2, "MN-major staging is bf16 only");
   static_assert(!(GATED && KMAJ), "gated staging is MN-major");
   constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
@@ -228,7 +228,7 @@ __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t ld_
     const bool ok = (k0 + (int)row < K) && (mn < mn_end);
     voff = ok ? (uint32_t)((int64_t)(k0 + (int)row) * ld_bytes + (int64_t)src * 2) : kOOB;
   }
-  load16_to_lds(rs, voff, lds_tile + (j * THREADS + wave * 64) * 16);
+  load16_to_lds(rs, voff, lds_tile + (uint32_t)((j * THREADS + wave * 64) * 16));
 }
 
 // LDS fragment reads through a restrict-qualified pointer parameter: the
@@ -603,9 +603,18 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-    // the ring tiles of step k (counted from kbeg)
-    auto a_tile = [&](int k) { return smem + ((2 * k) % NHALF) * TILE_BYTES; };
-    auto b_tile = [&](int k) { return smem + ((2 * k + 1) % NHALF) * TILE_BYTES; };
+    // Ring tiles as byte offsets from smem.  A step's tiles are two slots
+    // (mod 5) after the previous step's, so the loop carries the offsets of
+    // the step being loaded (ld_a, ld_b) and of the step read next (rd_a,
+    // rd_b) and advances them by one add and one select each.  DMA
+    // destinations are 32-bit LDS addresses: dma_w is this wave's 1 KB slice
+    // of a load (lane i writes 16 bytes at 16 i).
+    const uint32_t dma_w = lds_address(smem) + (uint32_t)wave * 1024u;
+    auto next_step = [](uint32_t o) {
+      o += 2u * TILE_BYTES;
+      return o >= (uint32_t)RING_BYTES ? o - (uint32_t)RING_BYTES : o;
+    };
+    uint32_t ld_a = 0u, ld_b = (uint32_t)TILE_BYTES;  // step 0: tiles 0 and 1
 
     // ---- per-lane address parts, fixed for the whole unit.
     // LDS reads.  K-major tile, fragment of rows wbase + 32 i, chunk
@@ -666,9 +675,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
         return lds_read_tr_pair(smem + b.o[i] + 8192 * kk);
       }
     };
-    auto step_bases = [&](int k, Bases& ba, Bases& bb) {
-      ba = bases((uint32_t)(((2 * k) % NHALF) * TILE_BYTES), IC<AK>{}, wm, 4);
-      bb = bases((uint32_t)(((2 * k + 1) % NHALF) * TILE_BYTES), IC<BKM>{}, wn, NF);
+    auto step_bases = [&](uint32_t tile_a, uint32_t tile_b, Bases& ba, Bases& bb) {
+      ba = bases(tile_a, IC<AK>{}, wm, 4);
+      bb = bases(tile_b, IC<BKM>{}, wn, NF);
     };
 
     // DMA loads.  Load j of an operand tile stages LDS chunk j*THREADS + tid.
@@ -722,21 +731,24 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     // reads, so the issue pattern and the load counts are the same for every
     // step.  FAST: both operand tiles are full and the step is full and
     // inside the split (see above).
+    // The tiles are those of ld_a / ld_b, which hold step k's.
     auto load_one = [&](int L, int k, auto fc) {
       constexpr bool FAST = decltype(fc)::value;
       if (L < LOADS) {
         if constexpr (FAST)
-          load16_to_lds_s(ra, va[L & 1], uni_off(IC<AK>{}, lda_b, tl.m0, L, k), a_tile(k) + (L * THREADS + wave * 64) * 16);
+          load16_to_lds_s(ra, va[L & 1], uni_off(IC<AK>{}, lda_b, tl.m0, L, k),
+                          dma_w + ld_a + (uint32_t)(L * THREADS * 16));
         else
-          issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k < nks ? (kbeg + k) * KSTEP : p.K, p.K, a_tile(k),
-                                      L);
+          issue_one<AK, ESZ, THREADS>(ra, lda_b, tl.m0, tl.m_end, k < nks ? (kbeg + k) * KSTEP : p.K, p.K,
+                                      lds_address(smem) + ld_a, L);
       } else {
         const int j = L - LOADS;
         if constexpr (FAST)
-          load16_to_lds_s(rb, vb[j & 1], uni_off(IC<BKM>{}, ldb_b, tl.n0, j, k), b_tile(k) + (j * THREADS + wave * 64) * 16);
+          load16_to_lds_s(rb, vb[j & 1], uni_off(IC<BKM>{}, ldb_b, tl.n0, j, k),
+                          dma_w + ld_b + (uint32_t)(j * THREADS * 16));
         else
           issue_one<BKM, ESZ, THREADS, GATED>(rb, ldb_b, tl.n0, p.N, k < nks ? (kbeg + k) * KSTEP : p.K, p.K,
-                                              b_tile(k), j, p.gu_off);
+                                              lds_address(smem) + ld_b, j, p.gu_off);
       }
     };
     // fragment r of a set in the order the MFMAs first need them: A0, B0..B(NF-1), A1, A2, A3
@@ -857,15 +869,22 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     Frag fa[2][4], fb[2][NF];
     load_scales(kbeg);
     static_for<2 * LOADS>([&](auto lc) { load_one(decltype(lc)::value, 0, IC<false>{}); });
+    uint32_t rd_a = next_step(ld_a), rd_b = next_step(ld_b);  // step 1
+    ld_a = rd_a;
+    ld_b = rd_b;
     static_for<2 * LOADS>([&](auto lc) { load_one(decltype(lc)::value, 1, IC<false>{}); });
+    ld_a = next_step(ld_a);  // step 2
+    ld_b = next_step(ld_b);
     step_barrier(IC<2 * LOADS>{});
     constexpr int NRD = 4 + NF;  // fragment reads per set
     Bases ca, cb;
-    step_bases(0, ca, cb);
+    step_bases(0u, (uint32_t)TILE_BYTES, ca, cb);
     static_for<NRD>([&](auto rc) { read_one(ca, cb, 0, decltype(rc)::value, fa[0], fb[0]); });
+    // step kt: reads the tiles of step kt + 1 (rd_*) and loads step kt + 2
+    // into ld_*
     auto body = [&](int kt, auto fc) {
       Bases na, nb;
-      step_bases(kt + 1, na, nb);
+      step_bases(rd_a, rd_b, na, nb);
       const int kl = kt + 2;
       if constexpr (FP8) {
         // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0.
@@ -895,6 +914,10 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       }
       ca = na;
       cb = nb;
+      rd_a = ld_a;
+      rd_b = ld_b;
+      ld_a = next_step(ld_a);
+      ld_b = next_step(ld_b);
     };
     // In a unit whose operand tiles are both full, steps whose loads (of
     // step kt+2) are full and inside the split take the fast form:

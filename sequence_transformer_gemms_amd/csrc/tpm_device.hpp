@@ -27,27 +27,35 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 constexpr uint32_t kOOB = 0xFFFFFFF0u;  // an offset no descriptor here covers
 
+// The 32-bit LDS byte address of a generic pointer into LDS.  Callers take
+// it once and form every DMA destination from it with 32-bit arithmetic: a
+// generic pointer cast per load costs a 64-bit add and a null check in
+// scalar instructions, in the instruction stream that feeds the matrix cores.
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
 // 16 bytes per lane from global memory straight into LDS; lane i of the wave
-// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address `lds`.
-// The (wave-uniform) LDS address passes through an empty asm statement, so the compiler
+// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS byte address
+// `lds`.  The address passes through an empty asm statement, so the compiler
 // cannot tie these DMA writes to the LDS block the kernel reads through a
 // restrict-qualified pointer, and does not drain every DMA in flight before
 // each such read: callers order DMA writes and LDS reads themselves (a
 // vmcnt wait and a work-group barrier), and wait for vmcnt(0) before they
 // write LDS that a DMA may still target.
-__device__ inline lds_void* lds_dma_address(void* lds) {
-  uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+__device__ inline lds_void* lds_dma_address(uint32_t lds) {
+  uint32_t a = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("" : "+s"(a));
   return (lds_void*)(uintptr_t)a;
 }
-__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dma_address(lds), 16, voff, 0, 0, 0);
 }
 
 // The same with a uniform part of the offset in the scalar offset register.
 // The hardware range check covers the vector offset only, so the sum must be
 // known to lie inside the buffer (callers use it for whole tiles only).
-__device__ inline void load16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+__device__ inline void load16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_dma_address(lds), 16, voff, soff, 0, 0);
 }
 
