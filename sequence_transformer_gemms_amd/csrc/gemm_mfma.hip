@@ -880,11 +880,20 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     Bases ca, cb;
     step_bases(0u, (uint32_t)TILE_BYTES, ca, cb);
     static_for<NRD>([&](auto rc) { read_one(ca, cb, 0, decltype(rc)::value, fa[0], fb[0]); });
-    // step kt: reads the tiles of step kt + 1 (rd_*) and loads step kt + 2
-    // into ld_*
+    // Step kt reads the tiles of step kt + 1 (rd_*) in its last phase and
+    // loads step kt + 2 into ld_*.  The next step's read bases and ring
+    // offsets are formed right before the step barrier, where the wave
+    // waits for its LDS reads anyway: with one wave per SIMD every other
+    // instruction sits in the issue stream between two MFMAs.  The current
+    // bases are dead by then, so the new ones take their registers.
+    uint32_t nld_a, nld_b;
+    auto advance = [&]() {
+      step_bases(rd_a, rd_b, ca, cb);
+      nld_a = next_step(ld_a);
+      nld_b = next_step(ld_b);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     auto body = [&](int kt, auto fc) {
-      Bases na, nb;
-      step_bases(rd_a, rd_b, na, nb);
       const int kl = kt + 2;
       if constexpr (FP8) {
         // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0.
@@ -898,8 +907,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
                   cb, 1, fa[1], fb[1], IC<0>{});
         mfma_rows(IC<0>{}, IC<2>{}, IC<0>{}, IC<0>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<0>{}, ca, cb, 0, fa[0], fb[0],
                   IC<2>{});
+        advance();
         step_barrier(IC<LOADS>{});
-        mfma_rows(IC<2>{}, IC<2>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, na, nb, 0,
+        mfma_rows(IC<2>{}, IC<2>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 0,
                   fa[0], fb[0], IC<2>{});
       } else {
         mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<LA0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 1, fa[1],
@@ -908,16 +918,15 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
                   fb[0], IC<0>{});
         mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 3, fa[1],
                   fb[1], IC<0>{});
+        advance();
         step_barrier(IC<LOADS>{});
-        mfma_rows(IC<0>{}, IC<4>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, na, nb, 0,
+        mfma_rows(IC<0>{}, IC<4>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 0,
                   fa[0], fb[0], IC<0>{});
       }
-      ca = na;
-      cb = nb;
       rd_a = ld_a;
       rd_b = ld_b;
-      ld_a = next_step(ld_a);
-      ld_b = next_step(ld_b);
+      ld_a = nld_a;
+      ld_b = nld_b;
     };
     // In a unit whose operand tiles are both full, steps whose loads (of
     // step kt+2) are full and inside the split take the fast form:
