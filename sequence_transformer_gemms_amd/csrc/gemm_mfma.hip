@@ -554,7 +554,8 @@ __device__ __forceinline__ void epi_oct(const GemmParams& p, float (&v)[8], int 
 
 // One work unit (a K range of one output tile) of the GEMM p, staged
 // through the work-group's LDS block `smem` (Layout<NW>::SMEM bytes).
-template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false, int F8F = 0>
+template <bool FP8, bool AK, bool BKM, int NW, bool GATED = false, bool MX = false, int F8F = 0,
+          bool BAR_BASES = true>
 __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, char* __restrict__ smem) {
   // fp8 formats of the MFMA operands (0 e4m3, 1 e5m2): the first operand
   // is the B fragment, the second the A fragment
@@ -885,15 +886,23 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     // offsets are formed right before the step barrier, where the wave
     // waits for its LDS reads anyway: with one wave per SIMD every other
     // instruction sits in the issue stream between two MFMAs.  The current
-    // bases are dead by then, so the new ones take their registers.
+    // bases are dead by then, so the new ones take their registers.  The
+    // pair kernel holds two GEMMs' unit code in one register budget: its
+    // second GEMM (both operands K-major) forms them at the top of the step
+    // instead (BAR_BASES false), since at the barrier they cost that kernel
+    // three VGPRs it does not have.
     uint32_t nld_a, nld_b;
     auto advance = [&]() {
-      step_bases(rd_a, rd_b, ca, cb);
+      if constexpr (BAR_BASES) step_bases(rd_a, rd_b, ca, cb);
       nld_a = next_step(ld_a);
       nld_b = next_step(ld_b);
       __builtin_amdgcn_sched_barrier(0);
     };
     auto body = [&](int kt, auto fc) {
+      Bases na, nb;  // the next step's bases when BAR_BASES is false
+      if constexpr (!BAR_BASES) step_bases(rd_a, rd_b, na, nb);
+      Bases& xa = BAR_BASES ? ca : na;
+      Bases& xb = BAR_BASES ? cb : nb;
       const int kl = kt + 2;
       if constexpr (FP8) {
         // phases 0-1 read substep 1; phase 3 reads step kt+1 substep 0.
@@ -909,7 +918,7 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
                   IC<2>{});
         advance();
         step_barrier(IC<LOADS>{});
-        mfma_rows(IC<2>{}, IC<2>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 0,
+        mfma_rows(IC<2>{}, IC<2>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, xa, xb, 0,
                   fa[0], fb[0], IC<2>{});
       } else {
         mfma_rows(IC<0>{}, IC<4>{}, IC<0>{}, IC<LA0>{}, fa[0], fb[0], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 1, fa[1],
@@ -920,8 +929,12 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
                   fb[1], IC<0>{});
         advance();
         step_barrier(IC<LOADS>{});
-        mfma_rows(IC<0>{}, IC<4>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, ca, cb, 0,
+        mfma_rows(IC<0>{}, IC<4>{}, IC<LOADS>{}, IC<LOADS>{}, fa[1], fb[1], kl, fc, IC<0>{}, IC<NRD>{}, xa, xb, 0,
                   fa[0], fb[0], IC<0>{});
+      }
+      if constexpr (!BAR_BASES) {
+        ca = na;
+        cb = nb;
       }
       rd_a = ld_a;
       rd_b = ld_b;
@@ -1216,11 +1229,11 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_pair_kernel(const GemmParams 
   };
   int i = take();
   if constexpr (FIRST == 0) {
-    for (; i < c0; i = take()) run_unit<false, AK0, BK0, NW>(p0, logical_unit(p0, b0 + i), smem);
-    for (; i < c0 + c1; i = take()) run_unit<false, AK1, BK1, NW>(p1, logical_unit(p1, b1 + i - c0), smem);
+    for (; i < c0; i = take()) run_unit<false, AK0, BK0, NW, false, false, 0, true>(p0, logical_unit(p0, b0 + i), smem);
+    for (; i < c0 + c1; i = take()) run_unit<false, AK1, BK1, NW, false, false, 0, false>(p1, logical_unit(p1, b1 + i - c0), smem);
   } else {
-    for (; i < c1; i = take()) run_unit<false, AK1, BK1, NW>(p1, logical_unit(p1, b1 + i), smem);
-    for (; i < c0 + c1; i = take()) run_unit<false, AK0, BK0, NW>(p0, logical_unit(p0, b0 + i - c1), smem);
+    for (; i < c1; i = take()) run_unit<false, AK1, BK1, NW, false, false, 0, false>(p1, logical_unit(p1, b1 + i), smem);
+    for (; i < c0 + c1; i = take()) run_unit<false, AK0, BK0, NW, false, false, 0, true>(p0, logical_unit(p0, b0 + i - c1), smem);
   }
 }
 
