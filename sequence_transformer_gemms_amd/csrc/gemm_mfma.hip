@@ -774,7 +774,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
     // During step k the loads of step k+2 are issued: A's in the first two
     // phases (into the tile B of step k-1 left), B's right after the barrier
     // that frees step k's tiles (into A of step k's).  Each part's loads are
-    // spread between the MFMA row groups of its phase.
+    // spread evenly over the MFMAs of its phase, so that no gap between two
+    // MFMAs holds more than one load's scalar set-up (with one wave per SIMD
+    // a gap longer than an MFMA's own duration idles the matrix core).
     constexpr int LA0 = LOADS / 2, LA1 = LOADS - LOADS / 2;
     // MXFP8: the scale dwords of K step s for this lane's fragments (4 rows
     // of A, NF of B; bytes = the step's four 32-element blocks), and the same
@@ -806,9 +808,9 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
       }
     };
     // MFMAs of accumulator rows I0 .. I0+NI-1 from one fragment set, with the
-    // loads L0 .. L0+NL-1 of K step kl spread between the row groups and the
     // reads R0 .. R0+NR-1 of the next set (substep rkk of bases rsa / rsb)
-    // one after each MFMA.
+    // one after each MFMA and the loads L0 .. L0+NL-1 of K step kl after
+    // every NM/NL-th MFMA.
     auto mfma_rows = [&](auto i0c, auto nic, auto l0c, auto nlc, const Frag (&fa)[4], const Frag (&fb)[NF], int kl,
                          auto fastc, auto r0c, auto nrc, const Bases& rsa, const Bases& rsb, int rkk, Frag (&rfa)[4],
                          Frag (&rfb)[NF], auto opc) {
@@ -834,11 +836,11 @@ __device__ __forceinline__ void run_unit(const GemmParams& p, const Unit& un, ch
             constexpr int r = decltype(rc)::value;
             if constexpr (r * NM / NR == m) read_one(rsa, rsb, rkk, R0 + r, rfa, rfb);
           });
+          static_for<NL>([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            if constexpr (l * NM / NL == m) load_one(L0 + l, kl, fastc);
+          });
           __builtin_amdgcn_sched_barrier(0);
-        });
-        static_for<NL>([&](auto lc) {
-          constexpr int l = decltype(lc)::value;
-          if constexpr (l * NI / NL == ii) load_one(L0 + l, kl, fastc);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
