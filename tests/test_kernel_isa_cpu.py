@@ -96,6 +96,19 @@ def test_no_full_vmcnt_wait_before_lds_reads(asm):
             assert not bad, f"{name}: {len(bad)} x 's_waitcnt vmcnt(0)' right before an LDS read in the K loop"
 
 
+def test_k_loop_forms_lds_dma_addresses_in_32_bits(asm):
+    # Casting a generic pointer to an LDS address per DMA load costs a 64-bit
+    # add, a compare against the null pointer and a select, all scalar
+    # instructions in front of every load (272 of them in the K loops when
+    # the loads took generic pointers).  The loops form the LDS addresses as
+    # 32-bit offsets; the null compare is the cast's signature.
+    bodies, _ = kernels(asm)
+    for name, body in bodies.items():
+        for code in k_loops(body):
+            casts = [ln for ln in code if re.match(r"s_cmp_lg_u64\s", ln)]
+            assert not casts, f"{name}: {len(casts)} x 's_cmp_lg_u64' (generic-to-LDS casts) in the K loop"
+
+
 def test_no_register_spills_and_lds_fits(asm):
     # (scalar registers that overflow go to VGPR lanes, not memory: allowed)
     _, meta = kernels(asm)
